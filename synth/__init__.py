@@ -1,0 +1,2 @@
+"""Seeded synthetic workloads shared by the oracle's tests, the HIP path's tests and the benchmark."""
+from .workloads import *  # noqa: F401,F403

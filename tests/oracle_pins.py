@@ -1,0 +1,381 @@
+"""Pins of the CPU oracle: checks against what the pages and the mathematics fix.
+
+Each ``pin_*`` takes an oracle module ``O`` (the real one, or a deliberately
+broken copy made by ``tests/test_oracle_mutants.py``) and raises if ``O``
+disagrees with the pages' printed values, a closed form, an invariant or a
+brute-force computation done here by other means.
+
+Pages cited:
+  [P1] "P09 · Paged KV 写入 + decode attention（参考实现）" (kuanzhou.online)
+  [P2] "PagedAttention kernel：paged KV cache 与 block table"
+       (inference-learning-path.pages.dev)
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import torch
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------------------
+# helpers local to the pins (independent of the oracle's own code)
+# ---------------------------------------------------------------------------
+
+def _dense_attention_loops(q, K, V, scale):
+    """Dense single-query attention, scalar Python loops and math.exp (brute
+    force for tiny inputs).  q [D], K [n, D], V [n, D] as nested floats."""
+    n, D = len(K), len(q)
+    s = [scale * sum(q[d] * K[j][d] for d in range(D)) for j in range(n)]
+    mx = max(s)
+    w = [math.exp(x - mx) for x in s]
+    tot = sum(w)
+    return [sum(w[j] * V[j][d] for j in range(n)) / tot for d in range(D)]
+
+
+def _paged_from_dense(rng, Ks, Vs, bs, extra_blocks, tail_value):
+    """Place per-sequence contiguous K/V ([n, KVH, D] each) into a randomly
+    permuted block pool, token by token.  Unused positions hold NaN.
+    Returns k_cache, v_cache, block_tables (tails = tail_value), context_lens."""
+    KVH, D = Ks[0].shape[1], Ks[0].shape[2]
+    nbs = [-(-k.shape[0] // bs) for k in Ks]
+    NB = sum(nbs) + extra_blocks
+    perm = rng.permutation(NB)
+    W = max(max(nbs), 1) + 2
+    kc = np.full((NB, bs, KVH, D), np.nan)
+    vc = np.full((NB, bs, KVH, D), np.nan)
+    tables = np.full((len(Ks), W), tail_value, dtype=np.int64)
+    nxt = 0
+    for b, (K, V) in enumerate(zip(Ks, Vs)):
+        for j in range(nbs[b]):
+            phys = int(perm[nxt])
+            nxt += 1
+            tables[b, j] = phys
+            for t in range(bs):
+                tok = j * bs + t
+                if tok < K.shape[0]:
+                    kc[phys, t] = K[tok]
+                    vc[phys, t] = V[tok]
+    lens = np.array([k.shape[0] for k in Ks], dtype=np.int64)
+    return kc.astype(np.float32), vc.astype(np.float32), tables, lens
+
+
+def _f32(x):
+    return np.asarray(x, dtype=np.float32)
+
+
+# ---------------------------------------------------------------------------
+# pins
+# ---------------------------------------------------------------------------
+
+def pin_bf16_widening(O):
+    """Every bf16 bit pattern widens to the value torch assigns it (an
+    independent implementation), NaNs to NaN."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = O.bf16_bits_to_f64(bits)
+    ref = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    # A few by hand: 1.0, -2.0, 0.25, pi rounded, smallest subnormal 2^-133, inf.
+    hand = {0x3F80: 1.0, 0xC000: -2.0, 0x3E80: 0.25, 0x4049: 3.140625,
+            0x0001: 2.0 ** -133, 0x7F80: math.inf}
+    for b, val in hand.items():
+        assert O.bf16_bits_to_f64(np.array([b], dtype=np.uint16))[0] == val
+
+
+def pin_m1_write_example(O):
+    """[P1] L1 hints, 例 1: the printed cache after a write with padding."""
+    g = _load("m1_write_example.json")
+    kc = np.zeros(g["cache_shape"], dtype=np.float32)
+    vc = np.zeros(g["cache_shape"], dtype=np.float32)
+    k = _f32(g["k"]).reshape(-1, 1, 1)
+    v = (k * np.float32(g["v_factor"])).astype(np.float32)
+    ret = O.write_kv(kc, vc, k, v, np.array(g["slot_mapping"], dtype=np.int64))
+    assert ret is None
+    assert np.array_equal(kc[:, :, 0, 0], _f32(g["k_cache_expected"]))
+    assert np.array_equal(vc[:, :, 0, 0], _f32(g["v_cache_expected"]))
+    assert not np.any(kc == g["absent_value"])          # invariant I1
+    assert not np.any(vc == np.float32(g["absent_value"]) * np.float32(g["v_factor"]))
+
+
+def _m2_inputs(O):
+    g = _load("m2_decode_example.json")
+    NB, bs, KVH, D = g["num_blocks"], g["block_size"], g["num_kv_heads"], g["head_dim"]
+    kc = np.zeros((NB, bs, KVH, D), dtype=np.float32)
+    vc = np.zeros((NB, bs, KVH, D), dtype=np.float32)
+    k = _f32(g["seq0_k"] + g["seq1_k"]).reshape(-1, KVH, D)
+    v = _f32(g["seq0_v"] + g["seq1_v"]).reshape(-1, KVH, D)
+    O.write_kv(kc, vc, k, v, np.array(g["seq0_slots"] + g["seq1_slots"], dtype=np.int64))
+    q = _f32([g["q_seq0"], g["q_seq1"]])
+    tables = np.array(g["block_tables"], dtype=np.int64)
+    lens = np.array(g["context_lens"], dtype=np.int64)
+    return g, q, kc, vc, tables, lens
+
+
+def pin_m2_decode_example(O):
+    """[P1] 逐步图 例 2: printed result to the page's 4 decimals, plus the
+    closed forms behind it (weights (a, b, a) with 2a + b = 1 give exactly
+    [3, 4]; head 1 gives ((1 + 8e^2), (2 + 10e^2)) / (1 + 2e^2); a one-token
+    sequence returns its V row exactly)."""
+    g, q, kc, vc, tables, lens = _m2_inputs(O)
+    # the write itself, as the figure draws the blocks
+    assert np.array_equal(kc[2, :, 0], _f32([[1, 0], [0, 1]]))
+    assert np.array_equal(kc[0, 0, 0], _f32([1, 1]))
+    assert np.array_equal(kc[3, 0, 0], _f32([2, 2]))
+    out = O.decode(q, kc, vc, tables, lens, g["scale"], "f32")
+    assert out.dtype == np.float64 and out.shape == (2, 2, 2)
+    tol = 0.5 * 10.0 ** -g["printed_digits"]
+    assert np.allclose(out, np.array(g["printed_result"]), atol=tol, rtol=0)
+    assert np.allclose(out[0, 0], [3.0, 4.0], atol=1e-12, rtol=0)
+    e2 = math.exp(2.0)
+    exact = [(1 + 8 * e2) / (1 + 2 * e2), (2 + 10 * e2) / (1 + 2 * e2)]
+    assert np.allclose(out[0, 1], exact, atol=1e-12, rtol=0)
+    assert np.array_equal(out[1], np.array([[7.0, 8.0], [7.0, 8.0]]))
+    # The printed probabilities follow from the printed scores.
+    for key, scores in g["printed_scores"].items():
+        s = np.array(scores)
+        p = np.exp(s - s.max()) / np.exp(s - s.max()).sum()
+        assert np.allclose(p, g["printed_probs"][key], atol=tol, rtol=0)
+
+
+def pin_m2_gather_truncation(O):
+    """[P1] 例 2 steps 3-4: the untruncated gather has a 4th row (block 0,
+    offset 1); truncation keeps exactly n = 3 rows (invariant I3).  Without
+    truncation the zero row would get weight e^0 and head 0 would read
+    [(6e + 3)/(2e + 2), (8e + 4)/(2e + 2)] ~ [2.5966, 3.4621] instead."""
+    g, q, kc, vc, tables, lens = _m2_inputs(O)
+    rows = O.gather_context(kc, tables[0], 3)
+    assert rows.shape == (3, 1, 2)
+    assert np.array_equal(rows[:, 0, :], _f32(g["printed_gathered_seq0_untruncated"][:3]))
+    out = O.decode(q, kc, vc, tables, lens, 1.0, "f32")
+    e = math.e
+    wrong = [(6 * e + 3) / (2 * e + 2), (8 * e + 4) / (2 * e + 2)]
+    assert abs(out[0, 0, 0] - wrong[0]) > 0.3
+
+
+def pin_gqa_map(O):
+    """Invariant I5 and 例 3: H=4, KVH=2 -> [0,0,1,1]; H=8, KVH=2 ->
+    [0,0,0,0,1,1,1,1]; and the decode itself uses that map (each kv head's
+    single V row identifies it)."""
+    assert [O.kv_head_of(h, 4, 2) for h in range(4)] == [0, 0, 1, 1]
+    assert [O.kv_head_of(h, 8, 2) for h in range(8)] == [0, 0, 0, 0, 1, 1, 1, 1]
+    for H, KVH in ((8, 2), (6, 3), (4, 4), (4, 1)):
+        D, bs = 2, 4
+        kc = np.zeros((2, bs, KVH, D), dtype=np.float32)
+        vc = np.zeros((2, bs, KVH, D), dtype=np.float32)
+        for c in range(KVH):
+            vc[1, 0, c] = [c + 1.0, -(c + 1.0)]
+        q = np.ones((1, H, D), dtype=np.float32)
+        out = O.decode(q, kc, vc, np.array([[1, 7]]), np.array([1]), 1.0, "f32")
+        G = H // KVH
+        expect = [h // G for h in range(H)]
+        assert [int(round(out[0, h, 0])) - 1 for h in range(H)] == expect
+
+
+def pin_slot_arithmetic(O):
+    """[P1] 关键问题 / L3 answers: slot 7 with bs 4 is block 1 offset 3;
+    n = 5 with bs 4 uses 2 table entries = 8 positions, 3 cut off; the flat
+    slot index equals block * bs + offset for every slot (细节)."""
+    assert O.slot_to_block_offset(7, 4) == (1, 3)
+    assert O.blocks_needed(5, 4) == 2 and O.blocks_needed(8, 4) == 2
+    assert O.blocks_needed(1, 16) == 1 and O.blocks_needed(16, 16) == 1 and O.blocks_needed(17, 16) == 2
+    for bs in (1, 2, 4, 16):
+        for s in range(3 * bs):
+            blk, off = O.slot_to_block_offset(s, bs)
+            assert blk * bs + off == s and 0 <= off < bs
+    # writing slot s lands on row s of the flattened cache
+    NB, bs = 3, 4
+    for s in range(NB * bs):
+        kc = np.zeros((NB, bs, 1, 1), dtype=np.float32)
+        vc = np.zeros_like(kc)
+        O.write_kv(kc, vc, _f32([[[5.0]]]), _f32([[[6.0]]]), np.array([s]))
+        assert np.flatnonzero(kc.reshape(-1)).tolist() == [s]
+        assert np.flatnonzero(vc.reshape(-1)).tolist() == [s]
+    # n = 5, bs = 4: exactly 5 rows come back, from the table's first 2 entries
+    kc = np.arange(3 * 4 * 1 * 1, dtype=np.float32).reshape(3, 4, 1, 1)
+    rows = O.gather_context(kc, np.array([2, 0, 99999]), 5)
+    assert rows[:, 0, 0].tolist() == [8.0, 9.0, 10.0, 11.0, 0.0]
+
+
+def pin_i1_padding_not_written(O):
+    """Invariant I1: a padding token whose values are all the sentinel 9.0
+    leaves no 9.0 anywhere, in particular not in the last slot (where a -1
+    index would land)."""
+    rng = np.random.default_rng(11)
+    NB, bs, KVH, D = 5, 4, 2, 3
+    kc = rng.standard_normal((NB, bs, KVH, D)).astype(np.float32)
+    vc = rng.standard_normal((NB, bs, KVH, D)).astype(np.float32)
+    k0, v0 = kc.copy(), vc.copy()
+    T = 6
+    k = rng.standard_normal((T, KVH, D)).astype(np.float32)
+    v = rng.standard_normal((T, KVH, D)).astype(np.float32)
+    slots = np.array([3, -1, 17, -1, 0, NB * bs - 2])
+    k[slots < 0] = 9.0
+    v[slots < 0] = 9.0
+    O.write_kv(kc, vc, k, v, slots)
+    assert (kc == 9).sum() == 0 and (vc == 9).sum() == 0
+    assert np.array_equal(kc[-1, -1], k0[-1, -1]) and np.array_equal(vc[-1, -1], v0[-1, -1])
+    # every other row is untouched, every written row holds its token bit-exactly
+    flat_k, flat_k0 = kc.reshape(NB * bs, KVH, D), k0.reshape(NB * bs, KVH, D)
+    written = {int(s): i for i, s in enumerate(slots) if s >= 0}
+    for s in range(NB * bs):
+        want = k[written[s]] if s in written else flat_k0[s]
+        assert np.array_equal(flat_k[s].view(np.uint32), want.view(np.uint32))
+
+
+def pin_i2_table_tail_not_read(O):
+    """Invariant I2: table tails of 99999 (beyond the pool) are never read;
+    tails pointing at NaN-filled blocks do not reach the output."""
+    rng = np.random.default_rng(12)
+    KVH, D, bs = 1, 3, 4
+    Ks = [rng.standard_normal((n, KVH, D)) for n in (5, 8, 1)]
+    Vs = [rng.standard_normal((n, KVH, D)) for n in (5, 8, 1)]
+    kc, vc, tables, lens = _paged_from_dense(rng, Ks, Vs, bs, extra_blocks=2, tail_value=99999)
+    q = rng.standard_normal((3, 2, D)).astype(np.float32)
+    out = O.decode(q, kc, vc, tables, lens, 0.5, "f32")
+    assert np.all(np.isfinite(out))
+    spare = [b for b in range(kc.shape[0]) if b not in set(tables[tables < kc.shape[0]].tolist())]
+    t2 = tables.copy()
+    for b in range(3):
+        nb = -(-int(lens[b]) // bs)
+        t2[b, nb:] = spare[0]
+    kc[spare[0]] = np.nan
+    vc[spare[0]] = np.nan
+    out2 = O.decode(q, kc, vc, t2, lens, 0.5, "f32")
+    assert np.array_equal(out, out2)
+
+
+def pin_i3_exactly_n_rows(O):
+    """Invariant I3: for n not a multiple of bs, the rows past n in the last
+    block (here NaN) take no part; the gather returns exactly n rows."""
+    rng = np.random.default_rng(13)
+    bs, KVH, D = 4, 2, 3
+    for n in (1, 3, 4, 5, 7, 8, 9):
+        Ks = [rng.standard_normal((n, KVH, D))]
+        Vs = [rng.standard_normal((n, KVH, D))]
+        kc, vc, tables, lens = _paged_from_dense(rng, Ks, Vs, bs, extra_blocks=1, tail_value=99999)
+        assert O.gather_context(kc, tables[0], n).shape == (n, KVH, D)
+        q = rng.standard_normal((1, 4, D)).astype(np.float32)
+        out = O.decode(q, kc, vc, tables, lens, 1.0, "f32")
+        assert np.all(np.isfinite(out)), n
+
+
+def pin_i4_dense_brute_force(O):
+    """Invariant I4 / 自检: paged decode equals dense attention over the
+    contiguous K/V (computed here with scalar loops), for random lengths
+    (1, multiples of bs, others), random block sizes, GQA groups, shuffled
+    physical blocks and garbage tails; fp64 agreement to 1e-12."""
+    rng = np.random.default_rng(14)
+    for trial in range(12):
+        bs = int(rng.choice([1, 2, 3, 4, 8]))
+        KVH = int(rng.choice([1, 2, 3]))
+        G = int(rng.choice([1, 2, 4]))
+        H, D = KVH * G, int(rng.choice([1, 2, 5]))
+        lens = [1, bs * int(rng.integers(1, 4)), int(rng.integers(1, 13))]
+        Ks = [rng.standard_normal((n, KVH, D)).astype(np.float32).astype(np.float64) for n in lens]
+        Vs = [rng.standard_normal((n, KVH, D)).astype(np.float32).astype(np.float64) for n in lens]
+        kc, vc, tables, cl = _paged_from_dense(rng, Ks, Vs, bs, extra_blocks=3, tail_value=77777)
+        q = rng.standard_normal((len(lens), H, D)).astype(np.float32)
+        scale = float(rng.uniform(0.1, 1.5))
+        out = O.decode(q, kc, vc, tables, cl, scale, "f32")
+        for b, n in enumerate(lens):
+            for h in range(H):
+                c = h // G
+                ref = _dense_attention_loops(
+                    [float(x) for x in q[b, h]],
+                    [[float(x) for x in Ks[b][j, c]] for j in range(n)],
+                    [[float(x) for x in Vs[b][j, c]] for j in range(n)], scale)
+                assert np.allclose(out[b, h], ref, atol=1e-12, rtol=1e-12), (trial, b, h)
+
+
+def pin_bf16_decode_dense(O):
+    """The bf16 path of the oracle widens the stored patterns exactly: a bf16
+    cache equals the f32 decode of the same values (each bf16 value is an
+    exact f32), which brute force checks above."""
+    rng = np.random.default_rng(15)
+    NB, bs, KVH, D, H = 6, 4, 2, 8, 4
+    vals = torch.from_numpy(rng.standard_normal((NB, bs, KVH, D)).astype(np.float32)).to(torch.bfloat16)
+    vals2 = torch.from_numpy(rng.standard_normal((NB, bs, KVH, D)).astype(np.float32)).to(torch.bfloat16)
+    qv = torch.from_numpy(rng.standard_normal((2, H, D)).astype(np.float32)).to(torch.bfloat16)
+    bits = lambda t: t.view(torch.int16).numpy().view(np.uint16)
+    f32 = lambda t: t.to(torch.float32).numpy()
+    tables = np.array([[3, 1, 99999], [5, 0, 2]])
+    lens = np.array([6, 9])
+    a = O.decode(bits(qv), bits(vals), bits(vals2), tables, lens, 0.3, "bf16")
+    b = O.decode(f32(qv), f32(vals), f32(vals2), tables, lens, 0.3, "f32")
+    assert np.array_equal(a, b)
+
+
+def pin_fold_matches_direct(O):
+    """[P2] 代码: the block-table walk with an online-softmax fold gives the
+    same result as the direct softmax (to fp64 rounding), including an
+    out-of-order table such as [3, 1] and a one-token sequence."""
+    rng = np.random.default_rng(16)
+    NB, bs, KVH, D, H = 5, 4, 2, 3, 4
+    kc = rng.standard_normal((NB, bs, KVH, D)).astype(np.float32)
+    vc = rng.standard_normal((NB, bs, KVH, D)).astype(np.float32)
+    q = rng.standard_normal((3, H, D)).astype(np.float32)
+    tables = np.array([[3, 1, 99999], [0, 99999, 99999], [4, 2, 1]])
+    lens = np.array([7, 1, 12])
+    a = O.decode(q, kc, vc, tables, lens, 0.7, "f32")
+    b = O.decode_online_fold(q, kc, vc, tables, lens, 0.7, "f32")
+    assert np.allclose(a, b, atol=1e-12, rtol=1e-12)
+
+
+def pin_scale_before_softmax(O):
+    """[P1] L3 answers: the scale multiplies the scores before the softmax.
+    Two tokens with raw scores (2, 0) and values (1, 0): the output is the
+    first token's weight, 1 / (1 + e^(-2 scale)) — a scale applied after the
+    softmax would instead give scale * 1 / (1 + e^(-2))."""
+    kc = np.zeros((1, 2, 1, 1), dtype=np.float32)
+    vc = np.zeros((1, 2, 1, 1), dtype=np.float32)
+    kc[0, 0, 0, 0], kc[0, 1, 0, 0] = 2.0, 0.0
+    vc[0, 0, 0, 0], vc[0, 1, 0, 0] = 1.0, 0.0
+    q = np.ones((1, 1, 1), dtype=np.float32)
+    for scale in (0.25, 1.0, 3.0):
+        out = O.decode(q, kc, vc, np.array([[0]]), np.array([2]), scale, "f32")
+        assert abs(out[0, 0, 0] - 1.0 / (1.0 + math.exp(-2.0 * scale))) < 1e-14
+
+
+def pin_n_zero_and_errors(O):
+    """Readings: n = 0 gives zeros; an in-use table entry outside the pool,
+    or a slot beyond the pool, is an error (not silently wrapped)."""
+    kc = np.ones((2, 2, 1, 2), dtype=np.float32)
+    q = np.ones((2, 1, 2), dtype=np.float32)
+    out = O.decode(q, kc, kc, np.array([[0], [1]]), np.array([0, 2]), 1.0, "f32")
+    assert np.array_equal(out[0], np.zeros((1, 2))) and np.array_equal(out[1], np.ones((1, 2)))
+    import pytest
+    with pytest.raises(O.OracleError):
+        O.decode(q, kc, kc, np.array([[0], [5]]), np.array([1, 1]), 1.0, "f32")
+    with pytest.raises(O.OracleError):
+        O.write_kv(kc.copy(), kc.copy(), np.ones((1, 1, 2), np.float32), np.ones((1, 1, 2), np.float32), np.array([4]))
+    with pytest.raises(O.OracleError):
+        O.write_kv(kc.copy(), kc.copy(), np.ones((2, 1, 2), np.float32), np.ones((2, 1, 2), np.float32), np.array([1, 1]))
+
+
+ALL_PINS = [
+    pin_bf16_widening,
+    pin_m1_write_example,
+    pin_m2_decode_example,
+    pin_m2_gather_truncation,
+    pin_gqa_map,
+    pin_slot_arithmetic,
+    pin_i1_padding_not_written,
+    pin_i2_table_tail_not_read,
+    pin_i3_exactly_n_rows,
+    pin_i4_dense_brute_force,
+    pin_bf16_decode_dense,
+    pin_fold_matches_direct,
+    pin_scale_before_softmax,
+    pin_n_zero_and_errors,
+]
