@@ -1,0 +1,227 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged KV write + paged decode hot path on one MI355X.
+
+One step = pa_write_kv of the batch's new tokens, then paged decode attention
+(the split-KV partial kernel and the partition merge) over the whole batch.
+Default workload: Llama-3-8B attention shape in bf16 (B=64, H=32, KVH=8,
+D=128, block size 16, context lengths U[1, 4096], shuffled blocks, 64 written
+tokens).  Inputs are seeded synthetic tensors already resident in HBM.
+
+By default a 1 GiB buffer is overwritten before every step (outside the
+step's timing events) so that the 256 MB last-level cache does not serve KV
+rows from the previous step; ``--hot`` skips that.
+
+Prints ONE JSON line.  `value` = KV bytes the decode must read (sum over
+sequences of n_b * 2 * KVH * D * elem) / mean step time, in GB/s (10^9 B/s).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+METRIC = "paged decode KV-read GB/s (% of HBM peak) + µs/step; write_kv GB/s"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_partial_traffic.json")
+DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_70_amd", "csrc", "pa_decode.hip")
+
+
+def _src_hash() -> str:
+    with open(DECODE_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def _traffic(workload: str):
+    """HBM bytes per partial-kernel launch from the committed rocprofv3 counter
+    summary, if it was taken on this workload and this kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256_16") != _src_hash() or t.get("workload") != workload:
+        return None
+    return t.get("bytes_per_launch")
+
+
+def _cpu_baseline(w, budget_s: float):
+    """The oracle (fp64 NumPy, untuned) on a bounded sample of the same
+    workload: whole sequences taken in a fixed order until about budget_s of
+    CPU work, scaled to GB/s of KV rows read."""
+    import numpy as np
+    import oracle as O
+    from tests.gpu_util import stored_np
+
+    cfg = w.cfg
+    kc, vc = stored_np(w.k_cache), stored_np(w.v_cache)
+    q, tbl, lens = stored_np(w.q), stored_np(w.block_tables), stored_np(w.context_lens)
+    elem = 4 if cfg.dtype == "f32" else 2
+    row = 2 * cfg.num_kv_heads * cfg.head_dim * elem
+    done, nbytes, t = 0, 0, 0.0
+    order = np.random.default_rng(0).permutation(len(lens))
+    while done < len(order) and t < budget_s:
+        b = int(order[done])
+        t0 = time.perf_counter()
+        O.decode(q[b:b + 1], kc, vc, tbl[b:b + 1], lens[b:b + 1], w.scale, cfg.dtype)
+        t += time.perf_counter() - t0
+        nbytes += int(lens[b]) * row
+        done += 1
+    threads = 1
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([1] + [int(i.get("num_threads", 1)) for i in threadpool_info()])
+    except Exception:  # noqa: BLE001
+        pass
+    return {
+        "value": round(nbytes / t / 1e9, 4),
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{done} of {len(lens)} sequences ({nbytes / 1e6:.1f} MB of KV rows) in {t:.1f} s, "
+                  f"fp64 NumPy, one sequence per call; host has {len(os.sched_getaffinity(0))} usable cores",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="llama3_8b_bf16")
+    ap.add_argument("--partition", type=int, default=0, help="tokens per split-KV partition (0 = library's choice)")
+    ap.add_argument("--hot", action="store_true", help="do not flush the last-level cache between steps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import paged_kv_cache_70_amd as pk
+    from synth import CONFIGS, make_workload
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    pk.load_library()
+    cfg = CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = make_workload(cfg, dev)
+    B, H, D = w.q.shape
+    W = w.block_tables.shape[1]
+    P = args.partition or pk.partition_size(B, H, W, w.k_cache)
+    ws = torch.empty(max(16, pk.workspace_bytes(B, H, W, w.k_cache, P)), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(w.q)
+    kc, vc = w.k_cache, w.v_cache
+    flush = None if args.hot else torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+
+    def step(ev=None):
+        if ev:
+            ev[0].record()
+        pk.write_kv(kc, vc, w.k_new, w.v_new, w.slot_mapping)
+        if ev:
+            ev[1].record()
+        pk.decode_partials(w.q, kc, vc, w.block_tables, w.context_lens, w.scale, out=out,
+                           workspace=ws, partition_size=P)
+        if ev:
+            ev[2].record()
+        pk.decode_merge(w.q, kc, w.block_tables, w.context_lens, out=out, workspace=ws,
+                        partition_size=P)
+        if ev:
+            ev[3].record()
+
+    for _ in range(args.warmup):
+        if flush is not None:
+            flush.fill_(1)
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        if flush is not None:
+            flush.fill_(i & 0xFF)
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    wr = [e[0].elapsed_time(e[1]) * 1e3 for e in events]     # µs
+    k2 = [e[1].elapsed_time(e[2]) * 1e3 for e in events]
+    k3 = [e[2].elapsed_time(e[3]) * 1e3 for e in events]
+    st = [e[0].elapsed_time(e[3]) * 1e3 for e in events]
+    mean = lambda x: sum(x) / len(x)
+
+    def pct(x, q):
+        s = sorted(x)
+        return s[min(len(s) - 1, int(q * len(s)))]
+
+    kv_bytes = w.kv_bytes()
+    elem = 4 if cfg.dtype == "f32" else 2
+    row = cfg.num_kv_heads * D * elem
+    n_valid = int((w.slot_mapping >= 0).sum())
+    write_bytes = n_valid * row * 2 * 2 + 8 * w.slot_mapping.numel()
+    step_us, k2_us, k3_us, wr_us = mean(st), mean(k2), mean(k3), mean(wr)
+    value = kv_bytes / (step_us * 1e-6) / 1e9
+    achieved = kv_bytes / (k2_us * 1e-6) / 1e9
+    traffic = _traffic(cfg.name)
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_us / 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded N(0,1) values, shuffled physical blocks)",
+        "config": {
+            "workload": cfg.name, "num_seqs": B, "num_heads": H, "num_kv_heads": cfg.num_kv_heads,
+            "head_dim": D, "block_size": cfg.block_size, "context_lens": list(cfg.ctx),
+            "write_tokens": int(w.slot_mapping.numel()), "partition_size": P,
+            "cache_flush_between_steps": flush is not None,
+        },
+        "hbm_frac_step": round(value / HBM_PEAK_GBPS, 4),
+        "decode_us": round(k2_us + k3_us, 2),
+        "decode_kv_GBps": round(kv_bytes / ((k2_us + k3_us) * 1e-6) / 1e9, 1),
+        "partial_kernel_us": round(k2_us, 2),
+        "merge_kernel_us": round(k3_us, 2),
+        "step_us_p10_p50_p90": [round(pct(st, 0.1), 2), round(pct(st, 0.5), 2), round(pct(st, 0.9), 2)],
+        "write_us": round(wr_us, 2),
+        "write_GBps": round(write_bytes / (wr_us * 1e-6) / 1e9, 2),
+        "kv_bytes_per_step": kv_bytes,
+        "wall_ms_per_step_incl_flush": round(wall / args.steps * 1e3, 4),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "kernel": "decode_partial_kernel",
+        },
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = _cpu_baseline(w, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

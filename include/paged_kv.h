@@ -1,0 +1,182 @@
+/*
+ * paged_kv.h — C ABI of the paged KV-cache write and paged decode attention
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The operations are the ones defined on the page "P09 · Paged KV 写入 +
+ * decode attention（参考实现）" (kuanzhou.online), sections 题面速览 and
+ * 框架视角 · shape trace, and described as a kernel on "PagedAttention
+ * kernel：paged KV cache 与 block table" (inference-learning-path.pages.dev),
+ * sections 直接答案 and 深入原理 (v1/v2 partitioning):
+ *
+ *   cache layout   [num_blocks, block_size, num_kv_heads, head_dim]
+ *   write          cache[slot / bs][slot % bs] = k[i]   (slot < 0: padding, skipped)
+ *   decode         per sequence b with n = context_lens[b]:
+ *                  K_b = cache[block_tables[b, :ceil(n/bs)]] flattened to tokens, first n rows
+ *                  out[b,h] = softmax(scale * q[b,h] . K_b[:, h / (H/KVH)]) . V_b[:, h / (H/KVH)]
+ *                  scores, softmax and the weighted sum in fp32; out in q's dtype.
+ *
+ * Conventions for every entry point
+ *   - Pointers marked "device" are HIP device pointers (any allocation the
+ *     current device can access); "host" pointers are ordinary host memory.
+ *   - Every tensor is dense row-major (C-contiguous) with the stated shape and
+ *     at least 16-byte aligned.  The caller owns every buffer; the library
+ *     allocates nothing and keeps no state between calls.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL means
+ *     the legacy default stream).  No call synchronises the host.
+ *   - Return value: PA_OK (0) or a negative pa_status.  Argument errors are
+ *     detected on the host before anything is enqueued; PA_ERR_LAUNCH reports
+ *     a failed kernel launch.  pa_status_string() names each code.
+ *   - Device-side preconditions (not checked on the host, since that would
+ *     need a device-to-host copy): non-negative slots are < num_blocks *
+ *     block_size and pairwise distinct; for j < ceil(n_b / bs),
+ *     0 <= block_tables[b, j] < num_blocks; 0 <= context_lens[b] <=
+ *     max_blocks_per_seq * block_size.  The kernels stay memory-safe when they
+ *     are violated: a slot outside the cache is skipped like padding, a table
+ *     entry outside the pool contributes no tokens, and a context length is
+ *     clamped to [0, max_blocks_per_seq * block_size].  Duplicate slots leave
+ *     one of the written rows (unspecified which).
+ */
+#ifndef PAGED_KV_H
+#define PAGED_KV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of q, k, v, the caches and out (all share one). */
+typedef enum pa_dtype {
+  PA_F32 = 0,  /* IEEE binary32 */
+  PA_BF16 = 1  /* bfloat16 (upper half of binary32); out is rounded to nearest even */
+} pa_dtype;
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_NULL = -1,         /* a required pointer is NULL */
+  PA_ERR_SHAPE = -2,        /* a size is negative/zero where it must be positive, or H % KVH != 0 */
+  PA_ERR_UNSUPPORTED = -3,  /* head_dim not in {64,128,256}, block_size not in {8,16,32,64}, unknown dtype,
+                               or a partition size that is not a positive multiple of block_size */
+  PA_ERR_WORKSPACE = -4,    /* workspace NULL or smaller than pa_decode_workspace_bytes() */
+  PA_ERR_ALIGN = -5,        /* a tensor pointer is not 16-byte aligned */
+  PA_ERR_LAUNCH = -6,       /* the HIP runtime rejected a kernel launch */
+  PA_ERR_TOO_LARGE = -7     /* sizes overflow the kernels' 32-bit grid/index limits */
+} pa_status;
+
+/* Geometry of the paged cache (k_cache and v_cache share it). */
+typedef struct pa_cache_desc {
+  int32_t num_blocks;    /* NB: physical blocks in the pool, > 0 */
+  int32_t block_size;    /* bs: tokens per block, one of 8, 16, 32, 64 */
+  int32_t num_kv_heads;  /* KVH, > 0 */
+  int32_t head_dim;      /* D, one of 64, 128, 256 */
+  int32_t dtype;         /* a pa_dtype */
+} pa_cache_desc;
+
+/*
+ * pa_write_kv — scatter new tokens' K/V rows into the paged cache, in place.
+ * "P09 · Paged KV 写入 + decode attention" (kuanzhou.online), 题面速览 (写) and
+ * shape trace write_kv steps 1-4: for every i with slot_mapping[i] >= 0,
+ * k_cache[slot / bs, slot % bs, :, :] = k[i] and the same for v.  Negative
+ * slots are padding (CUDA-graph padded batches use -1) and write nothing.
+ * The copy is bit-exact.
+ *
+ *   k_cache, v_cache  device, [NB, bs, KVH, D] of desc->dtype, updated in place
+ *   k, v              device, [num_tokens, KVH, D] of desc->dtype
+ *   slot_mapping      device, [num_tokens] int64 flat slot = block * bs + offset
+ *   num_tokens        T >= 0; T == 0 enqueues nothing and returns PA_OK
+ *   desc              host, cache geometry
+ *   stream            hipStream_t
+ */
+int pa_write_kv(void* k_cache, void* v_cache, const void* k, const void* v,
+                const int64_t* slot_mapping, int32_t num_tokens,
+                const pa_cache_desc* desc, void* stream);
+
+/*
+ * pa_decode_partition_size — the split-KV partition length (tokens) that
+ * pa_decode uses when it is passed partition_size == 0.  Partitioning is the
+ * "v2" scheme of "PagedAttention kernel：paged KV cache 与 block table",
+ * 深入原理: a long context is cut into partitions processed in parallel and
+ * merged afterwards.  Depends only on its arguments (no device access).
+ * Returns a positive multiple of desc->block_size, or a negative pa_status.
+ */
+int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_heads,
+                                 int32_t max_blocks_per_seq, const pa_cache_desc* desc);
+
+/*
+ * pa_decode_workspace_bytes — size of the fp32 workspace pa_decode needs for
+ * the per-partition partial results (max, sum, accumulator per head) of the
+ * split-KV path.  partition_size 0 selects pa_decode_partition_size().
+ * Returns 0 for invalid arguments.
+ */
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads,
+                                 int32_t max_blocks_per_seq, const pa_cache_desc* desc,
+                                 int32_t partition_size);
+
+/*
+ * pa_decode — paged decode attention, one query per sequence.
+ * "P09 · Paged KV 写入 + decode attention" (kuanzhou.online), 题面速览
+ * (decode 读) and shape trace decode steps 1-7; online softmax over the block
+ * table as on "PagedAttention kernel：paged KV cache 与 block table", 直接答案.
+ * Enqueues the partial kernel and, when some sequence spans more than one
+ * partition, the merge kernel (the same as pa_decode_partials followed by
+ * pa_decode_merge).
+ *
+ *   out                 device, [B, H, D] of desc->dtype (written)
+ *   q                   device, [B, H, D] of desc->dtype
+ *   k_cache, v_cache    device, [NB, bs, KVH, D] of desc->dtype
+ *   block_tables        device, [B, max_blocks_per_seq] int32; only the first
+ *                       ceil(context_lens[b] / bs) entries of row b are read
+ *   context_lens        device, [B] int32, tokens of each sequence (0 gives zeros)
+ *   scale               multiplies q.k before the softmax (typically 1/sqrt(D))
+ *   num_seqs, num_heads B > 0, H > 0 with H % KVH == 0
+ *   max_blocks_per_seq  table width W > 0
+ *   desc                host, cache geometry
+ *   partition_size      tokens per split-KV partition: 0 = automatic, else a
+ *                       positive multiple of block_size
+ *   workspace           device, >= pa_decode_workspace_bytes(...) bytes, no
+ *                       initial contents required; may be NULL only when
+ *                       workspace_bytes is 0 and the requirement is 0
+ *   stream              hipStream_t
+ */
+int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+              const int32_t* block_tables, const int32_t* context_lens, float scale,
+              int32_t num_seqs, int32_t num_heads, int32_t max_blocks_per_seq,
+              const pa_cache_desc* desc, int32_t partition_size,
+              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pa_decode_partials — first half of pa_decode (same arguments): every
+ * (sequence, kv head, partition) folds its tokens with an online softmax.
+ * Sequences that fit in one partition (and n == 0) get their final output
+ * written to `out`; the others leave fp32 partial results in `workspace`.
+ */
+int pa_decode_partials(void* out, const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* block_tables, const int32_t* context_lens, float scale,
+                       int32_t num_seqs, int32_t num_heads, int32_t max_blocks_per_seq,
+                       const pa_cache_desc* desc, int32_t partition_size,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pa_decode_merge — second half of pa_decode: for every sequence spanning
+ * more than one partition, combines the partial results of pa_decode_partials
+ * (max-rescaled sums: out = sum_p e^(m_p - M) acc_p / sum_p e^(m_p - M) l_p)
+ * and writes `out`.  Must follow pa_decode_partials on the same stream with
+ * the same arguments.
+ */
+int pa_decode_merge(void* out, const int32_t* context_lens,
+                    int32_t num_seqs, int32_t num_heads, int32_t max_blocks_per_seq,
+                    const pa_cache_desc* desc, int32_t partition_size,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static, NUL-terminated name of a pa_status code ("unknown status" otherwise). */
+const char* pa_status_string(int status);
+
+/* ABI version of this header: (major << 16) | minor. */
+int32_t pa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_KV_H */

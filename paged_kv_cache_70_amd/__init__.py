@@ -1,0 +1,21 @@
+"""Paged KV-cache write and paged decode attention for AMD MI355X (gfx950).
+
+The compute path is the HIP library ``libpaged_kv.so`` (C ABI in
+``include/paged_kv.h``); :mod:`paged_kv_cache_70_amd.api` marshals torch
+tensors into it.  Build the library with ``python -m paged_kv_cache_70_amd.build``.
+"""
+from .api import (  # noqa: F401
+    CacheDesc,
+    PaError,
+    abi_version,
+    cache_desc,
+    decode,
+    decode_merge,
+    decode_partials,
+    library_path,
+    load_library,
+    partition_size,
+    status_string,
+    workspace_bytes,
+    write_kv,
+)

@@ -1,0 +1,235 @@
+"""Python binding of ``libpaged_kv.so`` (the C ABI in ``include/paged_kv.h``).
+
+Argument marshalling only: every step of the write and the decode runs in the
+library's HIP kernels.  PyTorch supplies device memory and the current stream.
+There is no fallback: if the library is missing or no GPU is present, calls
+raise.
+
+Functions keep the names of the C entry points without the ``pa_`` prefix:
+
+    write_kv(k_cache, v_cache, k, v, slot_mapping)          -> None (in place)
+    decode(q, k_cache, v_cache, block_tables, context_lens, scale, ...) -> out
+    decode_partials(...), decode_merge(...)                  the two halves of decode
+    partition_size(...), workspace_bytes(...)                host-side planning queries
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "PaError",
+    "library_path",
+    "load_library",
+    "CacheDesc",
+    "cache_desc",
+    "write_kv",
+    "decode",
+    "decode_partials",
+    "decode_merge",
+    "partition_size",
+    "workspace_bytes",
+    "status_string",
+    "abi_version",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB: Optional[ctypes.CDLL] = None
+
+PA_F32, PA_BF16 = 0, 1
+_DTYPES = {torch.float32: PA_F32, torch.bfloat16: PA_BF16}
+
+
+class PaError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn}: {status_string(status)} (status {status})")
+        self.status = status
+
+
+class CacheDesc(ctypes.Structure):
+    _fields_ = [
+        ("num_blocks", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+    ]
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "libpaged_kv.so")
+
+
+def load_library() -> ctypes.CDLL:
+    """Load the in-tree library (built by ``paged_kv_cache_70_amd.build``)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m paged_kv_cache_70_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32, i64, sz, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+    pdesc = ctypes.POINTER(CacheDesc)
+    sig = {
+        "pa_write_kv": (ctypes.c_int, [vp, vp, vp, vp, vp, i32, pdesc, vp]),
+        "pa_decode_partition_size": (i32, [i32, i32, i32, pdesc]),
+        "pa_decode_workspace_bytes": (sz, [i32, i32, i32, pdesc, i32]),
+        "pa_decode": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, f32, i32, i32, i32, pdesc, i32, vp, sz, vp]),
+        "pa_decode_partials": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, f32, i32, i32, i32, pdesc, i32, vp, sz, vp]),
+        "pa_decode_merge": (ctypes.c_int, [vp, vp, i32, i32, i32, pdesc, i32, vp, sz, vp]),
+        "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "pa_abi_version": (i32, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _LIB = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().pa_status_string(int(status)).decode()
+
+
+def abi_version() -> int:
+    return int(load_library().pa_abi_version())
+
+
+def cache_desc(k_cache: torch.Tensor) -> CacheDesc:
+    if k_cache.dim() != 4:
+        raise ValueError("cache must be [num_blocks, block_size, num_kv_heads, head_dim]")
+    if k_cache.dtype not in _DTYPES:
+        raise TypeError(f"unsupported cache dtype {k_cache.dtype}")
+    NB, bs, KVH, D = k_cache.shape
+    return CacheDesc(NB, bs, KVH, D, _DTYPES[k_cache.dtype])
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU (got {t.device})")
+    if not t.is_contiguous():
+        # writing through a temporary copy would silently lose the result
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    return t.data_ptr()
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise PaError(fn, status)
+
+
+def write_kv(k_cache: torch.Tensor, v_cache: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+             slot_mapping: torch.Tensor) -> None:
+    """In place: cache[slot // bs, slot % bs] = k[i] (and v) for slot >= 0."""
+    lib = load_library()
+    desc = cache_desc(k_cache)
+    if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
+        raise ValueError("k_cache and v_cache must match")
+    T = slot_mapping.shape[0] if slot_mapping.dim() == 1 else -1
+    if T < 0:
+        raise ValueError("slot_mapping must be 1-D")
+    row = (desc.num_kv_heads, desc.head_dim)
+    for name, t in (("k", k), ("v", v)):
+        if tuple(t.shape) != (T, *row) or t.dtype != k_cache.dtype:
+            raise ValueError(f"{name} must be [{T}, {row[0]}, {row[1]}] of {k_cache.dtype}")
+    if T == 0:
+        return None
+    st = lib.pa_write_kv(_dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(k, "k"), _dev(v, "v"),
+                         _dev(slot_mapping, "slot_mapping", torch.int64), T, ctypes.byref(desc),
+                         _stream(k_cache))
+    _check("pa_write_kv", st)
+    return None
+
+
+def partition_size(num_seqs: int, num_heads: int, max_blocks_per_seq: int, k_cache: torch.Tensor) -> int:
+    desc = cache_desc(k_cache)
+    p = load_library().pa_decode_partition_size(num_seqs, num_heads, max_blocks_per_seq, ctypes.byref(desc))
+    _check("pa_decode_partition_size", p if p < 0 else 0)
+    return int(p)
+
+
+def workspace_bytes(num_seqs: int, num_heads: int, max_blocks_per_seq: int, k_cache: torch.Tensor,
+                    partition_size: int = 0) -> int:
+    desc = cache_desc(k_cache)
+    return int(load_library().pa_decode_workspace_bytes(num_seqs, num_heads, max_blocks_per_seq,
+                                                        ctypes.byref(desc), partition_size))
+
+
+def _decode_args(q, k_cache, v_cache, block_tables, context_lens, out, workspace, partition_size):
+    desc = cache_desc(k_cache)
+    if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
+        raise ValueError("k_cache and v_cache must match")
+    if q.dim() != 3 or q.dtype != k_cache.dtype or q.shape[2] != desc.head_dim:
+        raise ValueError("q must be [num_seqs, num_heads, head_dim] of the cache dtype")
+    B, H, D = q.shape
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [num_seqs, max_blocks_per_seq]")
+    if tuple(context_lens.shape) != (B,):
+        raise ValueError("context_lens must be [num_seqs]")
+    W = block_tables.shape[1]
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must be like q")
+    need = load_library().pa_decode_workspace_bytes(B, H, W, ctypes.byref(desc), partition_size)
+    if need == 0 and partition_size and partition_size % desc.block_size:
+        raise ValueError("partition_size must be a multiple of block_size")
+    if workspace is None:
+        workspace = torch.empty(max(int(need), 16), dtype=torch.uint8, device=q.device)
+    wbytes = workspace.numel() * workspace.element_size()
+    return desc, B, H, W, out, workspace, wbytes
+
+
+def _decode_call(fn_name, q, k_cache, v_cache, block_tables, context_lens, scale, out, workspace,
+                 partition_size):
+    lib = load_library()
+    desc, B, H, W, out, workspace, wbytes = _decode_args(
+        q, k_cache, v_cache, block_tables, context_lens, out, workspace, partition_size)
+    fn = getattr(lib, fn_name)
+    st = fn(_dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+            _dev(block_tables, "block_tables", torch.int32), _dev(context_lens, "context_lens", torch.int32),
+            float(scale), B, H, W, ctypes.byref(desc), int(partition_size), _dev(workspace, "workspace"),
+            wbytes, _stream(q))
+    _check(fn_name, st)
+    return out
+
+
+def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_tables: torch.Tensor,
+           context_lens: torch.Tensor, scale: float, *, out: Optional[torch.Tensor] = None,
+           workspace: Optional[torch.Tensor] = None, partition_size: int = 0) -> torch.Tensor:
+    """Paged decode attention; returns ``out`` [B, H, D] in q's dtype."""
+    return _decode_call("pa_decode", q, k_cache, v_cache, block_tables, context_lens, scale, out,
+                        workspace, partition_size)
+
+
+def decode_partials(q, k_cache, v_cache, block_tables, context_lens, scale, *, out, workspace,
+                    partition_size: int = 0) -> torch.Tensor:
+    return _decode_call("pa_decode_partials", q, k_cache, v_cache, block_tables, context_lens, scale,
+                        out, workspace, partition_size)
+
+
+def decode_merge(q_like: torch.Tensor, k_cache: torch.Tensor, block_tables: torch.Tensor,
+                 context_lens: torch.Tensor, *, out: torch.Tensor, workspace: torch.Tensor,
+                 partition_size: int = 0) -> torch.Tensor:
+    lib = load_library()
+    desc = cache_desc(k_cache)
+    B, H, _ = q_like.shape
+    W = block_tables.shape[1]
+    st = lib.pa_decode_merge(_dev(out, "out"), _dev(context_lens, "context_lens", torch.int32), B, H, W,
+                             ctypes.byref(desc), int(partition_size), _dev(workspace, "workspace"),
+                             workspace.numel() * workspace.element_size(), _stream(out))
+    _check("pa_decode_merge", st)
+    return out

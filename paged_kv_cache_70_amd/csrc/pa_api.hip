@@ -1,0 +1,247 @@
+// C-ABI entry points declared in include/paged_kv.h: argument checks, launch
+// planning and kernel launches on the caller's stream.  No allocation, no
+// host synchronisation, no state kept between calls.
+#include <limits.h>
+
+#include "../../include/paged_kv.h"
+#include "pa_internal.h"
+
+namespace pa {
+
+bool dtype_ok(int32_t dtype) { return dtype == PA_F32 || dtype == PA_BF16; }
+int32_t elem_bytes(int32_t dtype) { return dtype == PA_F32 ? 4 : 2; }
+
+static bool pow2_in(int32_t x, int32_t lo, int32_t hi) {
+  return x >= lo && x <= hi && (x & (x - 1)) == 0;
+}
+static int32_t ilog2(int32_t x) {
+  int32_t r = 0;
+  while ((1 << r) < x) ++r;
+  return r;
+}
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+static int check_desc(const pa_cache_desc* d) {
+  if (!d) return PA_ERR_NULL;
+  if (d->num_blocks <= 0 || d->num_kv_heads <= 0) return PA_ERR_SHAPE;
+  if (!dtype_ok(d->dtype)) return PA_ERR_UNSUPPORTED;
+  if (d->head_dim != 64 && d->head_dim != 128 && d->head_dim != 256) return PA_ERR_UNSUPPORTED;
+  if (!pow2_in(d->block_size, 8, 64)) return PA_ERR_UNSUPPORTED;
+  // byte offsets inside the pool are size_t; rows must fit 32-bit lane math
+  const int64_t row = (int64_t)d->num_kv_heads * d->head_dim * elem_bytes(d->dtype);
+  if (row > INT_MAX) return PA_ERR_TOO_LARGE;
+  return PA_OK;
+}
+
+// Query heads handled by one wavefront: the largest of 8, 4, 2, 1 dividing G.
+static int32_t heads_per_unit(int32_t G) {
+  for (int32_t c = 8; c > 1; c >>= 1)
+    if (G % c == 0) return c;
+  return 1;
+}
+
+// 16-byte loads per K per lane per tile: up to 4, and a tile (rows-per-load x
+// loads) never crosses a block boundary.
+static int32_t tile_unroll(const pa_cache_desc* d) {
+  const int32_t epv = 16 / elem_bytes(d->dtype);
+  const int32_t rpw = 64 / (d->head_dim / epv);
+  int32_t u = d->block_size / rpw;
+  return u >= 4 ? 4 : u;
+}
+
+// Tokens per split-KV partition chosen without looking at the (device-side)
+// context lengths: the smallest power-of-two multiple of the block size, at
+// least 256 tokens, that keeps the worst-case number of work units
+// (sequences x kv heads x head chunks x partitions of the longest possible
+// context) at or below kTargetUnits.
+static constexpr int64_t kTargetUnits = 8192;
+static int32_t auto_partition(int32_t B, int32_t H, int32_t W, const pa_cache_desc* d) {
+  const int32_t G = H / d->num_kv_heads;
+  const int64_t rows = (int64_t)B * d->num_kv_heads * (G / heads_per_unit(G));
+  const int64_t max_len = (int64_t)W * d->block_size;
+  int64_t P = 256;
+  if (P % d->block_size) P = d->block_size;
+  while (P < max_len && rows * ((max_len + P - 1) / P) > kTargetUnits) P *= 2;
+  return (int32_t)P;
+}
+
+struct Checked {
+  DecodePlan plan;
+  size_t ws_bytes;
+};
+
+static int check_decode_sizes(int32_t B, int32_t H, int32_t W, const pa_cache_desc* d,
+                              int32_t partition_size, Checked* out) {
+  int st = check_desc(d);
+  if (st) return st;
+  if (B <= 0 || H <= 0 || W <= 0) return PA_ERR_SHAPE;
+  if (H % d->num_kv_heads) return PA_ERR_SHAPE;
+  if (partition_size < 0 || (partition_size && partition_size % d->block_size))
+    return PA_ERR_UNSUPPORTED;
+  const int64_t max_len = (int64_t)W * d->block_size;
+  if (max_len > INT_MAX / 2) return PA_ERR_TOO_LARGE;
+  DecodePlan p;
+  const int32_t G = H / d->num_kv_heads;
+  p.heads_per_unit = heads_per_unit(G);
+  p.nchunks = G / p.heads_per_unit;
+  p.P = partition_size ? partition_size : auto_partition(B, H, W, d);
+  const int64_t maxP = (max_len + p.P - 1) / p.P;
+  // grid.y = KVH * nchunks and grid.z = B are limited to 65535; the merge
+  // kernel keeps one fp32 weight per partition in LDS (at most 64 KiB).
+  if ((int64_t)d->num_kv_heads * p.nchunks > 65535 || B > 65535 || H > 65535 || maxP > 16384)
+    return PA_ERR_TOO_LARGE;
+  p.maxP = (int32_t)maxP;
+  p.tile_unroll = tile_unroll(d);
+  out->plan = p;
+  const int64_t slots = (int64_t)B * H * maxP;
+  out->ws_bytes = maxP > 1 ? (size_t)slots * ((size_t)d->head_dim + 2) * sizeof(float) : 0;
+  return PA_OK;
+}
+
+static int decode_params(void* out, const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* block_tables, const int32_t* context_lens, float scale,
+                         int32_t B, int32_t H, int32_t W, const pa_cache_desc* d,
+                         void* workspace, size_t workspace_bytes, const Checked& ck,
+                         DecodeParams* prm) {
+  if (!out || !context_lens) return PA_ERR_NULL;
+  if (!aligned16(out)) return PA_ERR_ALIGN;
+  if (ck.ws_bytes) {
+    if (!workspace || workspace_bytes < ck.ws_bytes) return PA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return PA_ERR_ALIGN;
+  }
+  DecodeParams& p = *prm;
+  p.out = out;
+  const size_t acc_bytes = (size_t)B * H * ck.plan.maxP * d->head_dim * sizeof(float);
+  p.ws_acc = ck.ws_bytes ? static_cast<float*>(workspace) : nullptr;
+  p.ws_ml = ck.ws_bytes ? reinterpret_cast<float*>(static_cast<char*>(workspace) + acc_bytes) : nullptr;
+  p.q = q;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.tables = block_tables;
+  p.ctx = context_lens;
+  p.scale_log2 = scale * 1.4426950408889634f;   // log2(e)
+  p.B = B;
+  p.H = H;
+  p.KVH = d->num_kv_heads;
+  p.W = W;
+  p.NB = d->num_blocks;
+  p.bs_log2 = ilog2(d->block_size);
+  p.bs_mask = d->block_size - 1;
+  p.P = ck.plan.P;
+  p.maxP = ck.plan.maxP;
+  p.nchunks = ck.plan.nchunks;
+  p.max_tokens = W * d->block_size;
+  return PA_OK;
+}
+
+}  // namespace pa
+
+using namespace pa;
+
+extern "C" {
+
+int32_t pa_abi_version(void) { return (1 << 16) | 0; }
+
+const char* pa_status_string(int status) {
+  switch (status) {
+    case PA_OK: return "ok";
+    case PA_ERR_NULL: return "null pointer argument";
+    case PA_ERR_SHAPE: return "invalid size (non-positive, or num_heads not a multiple of num_kv_heads)";
+    case PA_ERR_UNSUPPORTED: return "unsupported head_dim, block_size, dtype or partition size";
+    case PA_ERR_WORKSPACE: return "workspace missing or smaller than pa_decode_workspace_bytes()";
+    case PA_ERR_ALIGN: return "tensor pointer not 16-byte aligned";
+    case PA_ERR_LAUNCH: return "HIP kernel launch failed";
+    case PA_ERR_TOO_LARGE: return "sizes exceed the kernels' grid or index limits";
+  }
+  return "unknown status";
+}
+
+int pa_write_kv(void* k_cache, void* v_cache, const void* k, const void* v,
+                const int64_t* slot_mapping, int32_t num_tokens, const pa_cache_desc* desc,
+                void* stream) {
+  int st = check_desc(desc);
+  if (st) return st;
+  if (num_tokens < 0) return PA_ERR_SHAPE;
+  if (num_tokens == 0) return PA_OK;
+  if (!k_cache || !v_cache || !k || !v || !slot_mapping) return PA_ERR_NULL;
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k) || !aligned16(v))
+    return PA_ERR_ALIGN;
+  const int64_t row_bytes = (int64_t)desc->num_kv_heads * desc->head_dim * elem_bytes(desc->dtype);
+  if ((int64_t)num_tokens * (row_bytes / 16) > (int64_t)UINT_MAX - 256) return PA_ERR_TOO_LARGE;
+  const int64_t num_slots = (int64_t)desc->num_blocks * desc->block_size;
+  hipError_t e = launch_write_kv(k_cache, v_cache, k, v, slot_mapping, num_tokens,
+                                 (int32_t)row_bytes, num_slots, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_heads, int32_t max_blocks_per_seq,
+                                 const pa_cache_desc* desc) {
+  Checked ck;
+  int st = check_decode_sizes(num_seqs, num_heads, max_blocks_per_seq, desc, 0, &ck);
+  return st ? st : ck.plan.P;
+}
+
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t max_blocks_per_seq,
+                                 const pa_cache_desc* desc, int32_t partition_size) {
+  Checked ck;
+  if (check_decode_sizes(num_seqs, num_heads, max_blocks_per_seq, desc, partition_size, &ck))
+    return 0;
+  return ck.ws_bytes;
+}
+
+static int decode_common(bool partials, bool merge, void* out, const void* q,
+                         const void* k_cache, const void* v_cache,
+                         const int32_t* block_tables, const int32_t* context_lens, float scale,
+                         int32_t num_seqs, int32_t num_heads, int32_t max_blocks_per_seq,
+                         const pa_cache_desc* desc, int32_t partition_size, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  Checked ck;
+  int st = check_decode_sizes(num_seqs, num_heads, max_blocks_per_seq, desc, partition_size, &ck);
+  if (st) return st;
+  if (partials) {
+    if (!q || !k_cache || !v_cache || !block_tables) return PA_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_ALIGN;
+  }
+  DecodeParams prm;
+  st = decode_params(out, q, k_cache, v_cache, block_tables, context_lens, scale, num_seqs,
+                     num_heads, max_blocks_per_seq, desc, workspace, workspace_bytes, ck, &prm);
+  if (st) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (partials && launch_decode_partials(prm, desc->dtype, desc->head_dim, ck.plan, s) != hipSuccess)
+    return PA_ERR_LAUNCH;
+  if (merge && ck.plan.maxP > 1 &&
+      launch_decode_merge(prm, desc->dtype, desc->head_dim, s) != hipSuccess)
+    return PA_ERR_LAUNCH;
+  return PA_OK;
+}
+
+int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+              const int32_t* block_tables, const int32_t* context_lens, float scale,
+              int32_t num_seqs, int32_t num_heads, int32_t max_blocks_per_seq,
+              const pa_cache_desc* desc, int32_t partition_size, void* workspace,
+              size_t workspace_bytes, void* stream) {
+  return decode_common(true, true, out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                       num_seqs, num_heads, max_blocks_per_seq, desc, partition_size, workspace,
+                       workspace_bytes, stream);
+}
+
+int pa_decode_partials(void* out, const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* block_tables, const int32_t* context_lens, float scale,
+                       int32_t num_seqs, int32_t num_heads, int32_t max_blocks_per_seq,
+                       const pa_cache_desc* desc, int32_t partition_size, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  return decode_common(true, false, out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                       num_seqs, num_heads, max_blocks_per_seq, desc, partition_size, workspace,
+                       workspace_bytes, stream);
+}
+
+int pa_decode_merge(void* out, const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                    int32_t max_blocks_per_seq, const pa_cache_desc* desc,
+                    int32_t partition_size, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  return decode_common(false, true, out, nullptr, nullptr, nullptr, nullptr, context_lens, 1.0f,
+                       num_seqs, num_heads, max_blocks_per_seq, desc, partition_size, workspace,
+                       workspace_bytes, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,465 @@
+// Paged decode attention for gfx950: split-KV partial kernel + partition merge.
+//
+// Operation: "P09 · Paged KV 写入 + decode attention" (kuanzhou.online),
+// 题面速览 (decode 读) and the decode shape trace: sequence b reads the first
+// n = context_lens[b] rows through block_tables[b, :ceil(n / bs)], query head h
+// uses kv head h / (H / KVH), and out = softmax(scale * q . K^T) . V in fp32.
+// The block-by-block online softmax is the scheme of "PagedAttention kernel：
+// paged KV cache 与 block table" (直接答案, 代码); splitting long contexts into
+// partitions merged afterwards is its "v2" (深入原理).
+//
+// Work decomposition (one 64-lane wavefront per work unit):
+//   unit = (partition p, kv head, chunk of GC query heads of that kv head, sequence b)
+//   The wavefront streams the partition's tokens tile by tile.  A tile is TT
+//   consecutive tokens inside one physical block; every lane issues U 16-byte
+//   loads for K and U for V per tile.  LPT = D / (elements per 16 B) lanes
+//   hold one token's D-row (256 contiguous bytes for D = 128 bf16), so one
+//   load instruction fetches RPW = 64 / LPT whole token rows.
+//   Each K row is loaded once and used by all GC query heads (the GQA group
+//   shares its kv head).  Partial dot products are summed across the LPT
+//   lanes of a row with DPP row rotations / quad permutes (no LDS traffic).
+//   Every row of lanes keeps its own running (max, sum, accumulator) for its
+//   tokens; the RPW row states are combined once at the end of the unit.
+//   Scores are kept in base-2 units (q.k * scale * log2 e) so that every
+//   exponential is one v_exp_f32.
+// A sequence that fits in one partition writes `out` directly; longer ones
+// write fp32 partials that the merge kernel combines:
+//   M = max_p m_p,  out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p.
+//
+// Masking uses selects (never multiply-by-zero), so rows beyond n in the last
+// block, whatever they hold (NaN included), cannot reach the output.
+#include <math.h>
+
+#include "pa_internal.h"
+
+namespace pa {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------------------
+// element types: 16-byte vectors of fp32 (4 values) or bf16 (8 values)
+// ---------------------------------------------------------------------------
+struct F32 {
+  static constexpr int EPV = 4;
+  // partial dot product of this lane's 4 q values with 4 k values
+  __device__ static __forceinline__ float dot(const u32x4& q, const u32x4& k) {
+    float s = __uint_as_float(q[0]) * __uint_as_float(k[0]);
+    s = fmaf(__uint_as_float(q[1]), __uint_as_float(k[1]), s);
+    s = fmaf(__uint_as_float(q[2]), __uint_as_float(k[2]), s);
+    s = fmaf(__uint_as_float(q[3]), __uint_as_float(k[3]), s);
+    return s;
+  }
+  __device__ static __forceinline__ void widen(const u32x4& v, float (&f)[EPV]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(v[i]);
+  }
+  __device__ static __forceinline__ void store(void* out, size_t idx, const float (&f)[EPV]) {
+    u32x4 w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = __float_as_uint(f[i]);
+    *reinterpret_cast<u32x4*>(static_cast<float*>(out) + idx) = w;
+  }
+};
+
+struct BF16 {
+  static constexpr int EPV = 8;
+  // bf16 x bf16 products are exact in fp32; v_dot2 adds two of them per step.
+  __device__ static __forceinline__ float dot(const u32x4& q, const u32x4& k) {
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      // Copy the lanes to scalars before the bit cast: a bit cast applied to
+      // an ext-vector element directly is lowered to element 0 by this clang.
+      const uint32_t qa = q[i], ka = k[i];
+      s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qa),
+                                          __builtin_bit_cast(bf16x2, ka), s, false);
+    }
+    return s;
+  }
+  // a bf16 is the high half of an fp32: widening is a shift / mask
+  __device__ static __forceinline__ void widen(const u32x4& v, float (&f)[EPV]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(v[i] << 16);
+      f[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
+    }
+  }
+  // round to nearest even (IEEE conversion semantics of __bf16)
+  __device__ static __forceinline__ void store(void* out, size_t idx, const float (&f)[EPV]) {
+    u32x4 w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      bf16x2 pr;
+      pr[0] = (__bf16)f[2 * i];
+      pr[1] = (__bf16)f[2 * i + 1];
+      w[i] = __builtin_bit_cast(uint32_t, pr);
+    }
+    *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + idx) = w;
+  }
+};
+
+// ---------------------------------------------------------------------------
+// cross-lane helpers
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over the LPT consecutive lanes that hold one token row; every lane of the
+// row receives the total.  Within 16 lanes: row_ror 8 and 4 (or the half-row
+// mirror for 8 lanes) fold the row onto quads, two quad permutes finish it.
+template <int LPT>
+__device__ __forceinline__ float row_sum(float x) {
+  static_assert(LPT == 4 || LPT == 8 || LPT == 16 || LPT == 32 || LPT == 64, "row width");
+  if constexpr (LPT >= 16) {
+    x += dpp<0x128>(x);  // row_ror:8
+    x += dpp<0x124>(x);  // row_ror:4
+  } else if constexpr (LPT == 8) {
+    x += dpp<0x141>(x);  // row_half_mirror
+  }
+  x += dpp<0x4E>(x);     // quad_perm [2,3,0,1]
+  x += dpp<0xB1>(x);     // quad_perm [1,0,3,2]
+  if constexpr (LPT >= 32) x += __shfl_xor(x, 16);
+  if constexpr (LPT >= 64) x += __shfl_xor(x, 32);
+  return x;
+}
+
+// Combine over the RPW rows of the wavefront (lanes LPT apart).
+template <int LPT>
+__device__ __forceinline__ float rows_max(float x) {
+#pragma unroll
+  for (int off = LPT; off < 64; off <<= 1) x = fmaxf(x, __shfl_xor(x, off));
+  return x;
+}
+template <int LPT>
+__device__ __forceinline__ float rows_sum(float x) {
+#pragma unroll
+  for (int off = LPT; off < 64; off <<= 1) x += __shfl_xor(x, off);
+  return x;
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ u32x4 load16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+// ---------------------------------------------------------------------------
+// K2: split-KV partial kernel
+// ---------------------------------------------------------------------------
+template <typename E, int D, int GC, int U>
+__global__ __launch_bounds__(64) void decode_partial_kernel(const DecodeParams prm) {
+  constexpr int EPV = E::EPV;
+  constexpr int LPT = D / EPV;       // lanes per token row
+  constexpr int RPW = 64 / LPT;      // token rows per load instruction
+  constexpr int TT = RPW * U;        // tokens per tile
+  constexpr int ESZ = 16 / EPV;      // bytes per element
+
+  const int p = blockIdx.x;
+  const int b = blockIdx.z;
+  const int kvh = blockIdx.y / prm.nchunks;
+  const int chunk = blockIdx.y - kvh * prm.nchunks;
+  const int G = prm.H / prm.KVH;
+  const int h0 = kvh * G + chunk * GC;
+
+  int n = prm.ctx[b];
+  n = n < 0 ? 0 : (n > prm.max_tokens ? prm.max_tokens : n);
+  const int nparts = (n + prm.P - 1) / prm.P;
+  if (p >= (nparts > 0 ? nparts : 1)) return;
+  const int t_begin = p * prm.P;
+  const int t_end = min(n, t_begin + prm.P);
+
+  const int lane = threadIdx.x;
+  const int r = lane / LPT;          // row of this lane within a load
+  const int c = lane - r * LPT;      // 16-byte piece of the D-row
+
+  // This lane's slice of the GC queries.
+  u32x4 qv[GC];
+  {
+    const char* qb = static_cast<const char*>(prm.q) +
+                     ((size_t)(b * prm.H + h0) * D + (size_t)c * EPV) * ESZ;
+#pragma unroll
+    for (int g = 0; g < GC; ++g) qv[g] = load16(qb + (size_t)g * D * ESZ);
+  }
+
+  float m[GC], l[GC], acc[GC][EPV];
+#pragma unroll
+  for (int g = 0; g < GC; ++g) {
+    m[g] = -INFINITY;
+    l[g] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) acc[g][e] = 0.0f;
+  }
+
+  const size_t row_bytes = (size_t)prm.KVH * D * ESZ;            // token stride in a block
+  const size_t blk_bytes = row_bytes << prm.bs_log2;
+  const size_t lane_off = (size_t)kvh * D * ESZ + (size_t)c * 16 + (size_t)r * row_bytes;
+  const char* kbase = static_cast<const char*>(prm.k_cache) + lane_off;
+  const char* vbase = static_cast<const char*>(prm.v_cache) + lane_off;
+  const int32_t* tbl = prm.tables + (size_t)b * prm.W;
+
+  // Tile state: U K-vectors and U V-vectors per lane, double buffered so that
+  // the next tile's loads are in flight while this tile is folded.
+  u32x4 kA[U], vA[U], kB[U], vB[U];
+  int okA = 0, okB = 0;
+
+  auto load_tile = [&](int tile, u32x4 (&kr)[U], u32x4 (&vr)[U]) -> int {
+    const int phys = tbl[tile >> prm.bs_log2];
+    if ((unsigned)phys >= (unsigned)prm.NB) return 0;   // entry outside the pool: no tokens
+    const size_t off = (size_t)phys * blk_bytes + (size_t)(tile & prm.bs_mask) * row_bytes;
+#pragma unroll
+    for (int u = 0; u < U; ++u) kr[u] = load16(kbase + off + (size_t)u * RPW * row_bytes);
+#pragma unroll
+    for (int u = 0; u < U; ++u) vr[u] = load16(vbase + off + (size_t)u * RPW * row_bytes);
+    return 1;
+  };
+
+  auto fold_tile = [&](int tile, int ok, const u32x4 (&kr)[U], const u32x4 (&vr)[U]) {
+    const int nvalid = ok ? min(TT, t_end - tile) : 0;   // valid tokens of this tile
+    const bool full = nvalid == TT;
+    float s[U][GC];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int g = 0; g < GC; ++g) s[u][g] = row_sum<LPT>(E::dot(qv[g], kr[u])) * prm.scale_log2;
+      if (!full) {
+        const bool valid = (u * RPW + r) < nvalid;
+#pragma unroll
+        for (int g = 0; g < GC; ++g) s[u][g] = valid ? s[u][g] : -INFINITY;
+      }
+    }
+    float mu[GC];
+#pragma unroll
+    for (int g = 0; g < GC; ++g) {
+      float mt = s[0][g];
+#pragma unroll
+      for (int u = 1; u < U; ++u) mt = fmaxf(mt, s[u][g]);
+      const float m_new = fmaxf(m[g], mt);
+      mu[g] = (m_new == -INFINITY) ? 0.0f : m_new;     // a row with no token yet
+      const float corr = exp2_fast(m[g] - mu[g]);
+      m[g] = m_new;
+      l[g] *= corr;
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) acc[g][e] *= corr;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float vf[EPV];
+      E::widen(vr[u], vf);
+      if (!full) {
+        const bool valid = (u * RPW + r) < nvalid;
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) vf[e] = valid ? vf[e] : 0.0f;
+      }
+#pragma unroll
+      for (int g = 0; g < GC; ++g) {
+        const float pr = exp2_fast(s[u][g] - mu[g]);
+        l[g] += pr;
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) acc[g][e] = fmaf(pr, vf[e], acc[g][e]);
+      }
+    }
+  };
+
+  int tile = t_begin;
+  if (tile < t_end) okA = load_tile(tile, kA, vA);
+  while (tile < t_end) {
+    const int t1 = tile + TT;
+    if (t1 < t_end) okB = load_tile(t1, kB, vB);
+    fold_tile(tile, okA, kA, vA);
+    if (t1 >= t_end) break;
+    const int t2 = t1 + TT;
+    if (t2 < t_end) okA = load_tile(t2, kA, vA);
+    fold_tile(t1, okB, kB, vB);
+    tile = t2;
+  }
+
+  // Combine the RPW row states of the wavefront.
+  const bool single = nparts <= 1;
+#pragma unroll
+  for (int g = 0; g < GC; ++g) {
+    const float M = rows_max<LPT>(m[g]);
+    const float f = (m[g] == -INFINITY) ? 0.0f : exp2_fast(m[g] - M);
+    const float L = rows_sum<LPT>(l[g] * f);
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) acc[g][e] = rows_sum<LPT>(acc[g][e] * f);
+    if (r == 0) {
+      const size_t bh = (size_t)b * prm.H + h0 + g;
+      if (single) {
+        const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+        float o[EPV];
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) o[e] = acc[g][e] * inv;
+        E::store(prm.out, bh * D + (size_t)c * EPV, o);
+      } else {
+        const size_t slot = bh * prm.maxP + p;
+        float* dst = prm.ws_acc + slot * D + (size_t)c * EPV;
+#pragma unroll
+        for (int e = 0; e < EPV; e += 4)
+          *reinterpret_cast<float4*>(dst + e) = make_float4(acc[g][e], acc[g][e + 1], acc[g][e + 2], acc[g][e + 3]);
+        if (c == 0) *reinterpret_cast<float2*>(prm.ws_ml + slot * 2) = make_float2(M, L);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// K3: partition merge
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) x = fmaxf(x, __shfl_xor(x, off));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) x += __shfl_xor(x, off);
+  return x;
+}
+
+template <typename E, int D>
+__global__ __launch_bounds__(64) void decode_merge_kernel(const DecodeParams prm) {
+  extern __shared__ float wsh[];   // one weight per partition
+  const int h = blockIdx.x;
+  const int b = blockIdx.y;
+  int n = prm.ctx[b];
+  n = n < 0 ? 0 : (n > prm.max_tokens ? prm.max_tokens : n);
+  const int nparts = (n + prm.P - 1) / prm.P;
+  if (nparts <= 1) return;                 // written by the partial kernel
+  const int lane = threadIdx.x;
+  const size_t bh = (size_t)b * prm.H + h;
+  const float* ml = prm.ws_ml + bh * prm.maxP * 2;
+  const float* acc = prm.ws_acc + bh * prm.maxP * D;
+
+  float M = -INFINITY;
+  for (int i = lane; i < nparts; i += 64) M = fmaxf(M, ml[2 * i]);
+  M = wave_max(M);
+  float L = 0.0f;
+  for (int i = lane; i < nparts; i += 64) {
+    const float mi = ml[2 * i];
+    const float w = (mi == -INFINITY) ? 0.0f : exp2_fast(mi - M);
+    wsh[i] = w;
+    L += w * ml[2 * i + 1];
+  }
+  L = wave_sum(L);
+  __syncthreads();
+  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+
+  constexpr int EPV = E::EPV;
+  // lane handles EPV consecutive outputs: D / EPV lanes are active
+  if (lane * EPV < D) {
+    float o[EPV];
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) o[e] = 0.0f;
+    const float* a = acc + (size_t)lane * EPV;
+    int i = 0;
+    for (; i + 4 <= nparts; i += 4) {
+      float4 x0[EPV / 4], x1[EPV / 4], x2[EPV / 4], x3[EPV / 4];
+#pragma unroll
+      for (int e = 0; e < EPV / 4; ++e) {
+        x0[e] = *reinterpret_cast<const float4*>(a + (size_t)(i + 0) * D + 4 * e);
+        x1[e] = *reinterpret_cast<const float4*>(a + (size_t)(i + 1) * D + 4 * e);
+        x2[e] = *reinterpret_cast<const float4*>(a + (size_t)(i + 2) * D + 4 * e);
+        x3[e] = *reinterpret_cast<const float4*>(a + (size_t)(i + 3) * D + 4 * e);
+      }
+      const float w0 = wsh[i], w1 = wsh[i + 1], w2 = wsh[i + 2], w3 = wsh[i + 3];
+#pragma unroll
+      for (int e = 0; e < EPV / 4; ++e) {
+        o[4 * e + 0] += w0 * x0[e].x + w1 * x1[e].x + w2 * x2[e].x + w3 * x3[e].x;
+        o[4 * e + 1] += w0 * x0[e].y + w1 * x1[e].y + w2 * x2[e].y + w3 * x3[e].y;
+        o[4 * e + 2] += w0 * x0[e].z + w1 * x1[e].z + w2 * x2[e].z + w3 * x3[e].z;
+        o[4 * e + 3] += w0 * x0[e].w + w1 * x1[e].w + w2 * x2[e].w + w3 * x3[e].w;
+      }
+    }
+    for (; i < nparts; ++i) {
+      const float w = wsh[i];
+#pragma unroll
+      for (int e = 0; e < EPV / 4; ++e) {
+        const float4 x = *reinterpret_cast<const float4*>(a + (size_t)i * D + 4 * e);
+        o[4 * e + 0] += w * x.x;
+        o[4 * e + 1] += w * x.y;
+        o[4 * e + 2] += w * x.z;
+        o[4 * e + 3] += w * x.w;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) o[e] *= inv;
+    E::store(prm.out, bh * D + (size_t)lane * EPV, o);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+template <typename E, int D, int GC, int U>
+static hipError_t launch_partial_u(const DecodeParams& prm, hipStream_t stream) {
+  dim3 grid(prm.maxP, prm.KVH * prm.nchunks, prm.B);
+  hipLaunchKernelGGL((decode_partial_kernel<E, D, GC, U>), grid, dim3(64), 0, stream, prm);
+  return hipGetLastError();
+}
+
+template <typename E, int D, int GC>
+static hipError_t launch_partial_gc(const DecodeParams& prm, int U, hipStream_t stream) {
+  constexpr int RPW = 64 / (D / E::EPV);
+  switch (U) {
+    case 4: return launch_partial_u<E, D, GC, 4>(prm, stream);
+    case 2:
+      if constexpr (RPW >= 4) return launch_partial_u<E, D, GC, 2>(prm, stream);
+      break;
+    case 1:
+      if constexpr (RPW >= 8) return launch_partial_u<E, D, GC, 1>(prm, stream);
+      break;
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename E, int D>
+static hipError_t launch_partial_d(const DecodeParams& prm, const DecodePlan& plan, hipStream_t s) {
+  switch (plan.heads_per_unit) {
+    case 1: return launch_partial_gc<E, D, 1>(prm, plan.tile_unroll, s);
+    case 2: return launch_partial_gc<E, D, 2>(prm, plan.tile_unroll, s);
+    case 4: return launch_partial_gc<E, D, 4>(prm, plan.tile_unroll, s);
+    case 8: return launch_partial_gc<E, D, 8>(prm, plan.tile_unroll, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename E>
+static hipError_t launch_partial_e(const DecodeParams& prm, int32_t D, const DecodePlan& plan,
+                                   hipStream_t s) {
+  switch (D) {
+    case 64: return launch_partial_d<E, 64>(prm, plan, s);
+    case 128: return launch_partial_d<E, 128>(prm, plan, s);
+    case 256: return launch_partial_d<E, 256>(prm, plan, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_partials(const DecodeParams& prm, int32_t dtype, int32_t D,
+                                  const DecodePlan& plan, hipStream_t stream) {
+  return dtype == 0 ? launch_partial_e<F32>(prm, D, plan, stream)
+                    : launch_partial_e<BF16>(prm, D, plan, stream);
+}
+
+template <typename E>
+static hipError_t launch_merge_e(const DecodeParams& prm, int32_t D, hipStream_t stream) {
+  const dim3 grid(prm.H, prm.B);
+  const size_t lds = (size_t)prm.maxP * sizeof(float);
+  switch (D) {
+    case 64: hipLaunchKernelGGL((decode_merge_kernel<E, 64>), grid, dim3(64), lds, stream, prm); break;
+    case 128: hipLaunchKernelGGL((decode_merge_kernel<E, 128>), grid, dim3(64), lds, stream, prm); break;
+    case 256: hipLaunchKernelGGL((decode_merge_kernel<E, 256>), grid, dim3(64), lds, stream, prm); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_merge(const DecodeParams& prm, int32_t dtype, int32_t D,
+                               hipStream_t stream) {
+  return dtype == 0 ? launch_merge_e<F32>(prm, D, stream) : launch_merge_e<BF16>(prm, D, stream);
+}
+
+}  // namespace pa

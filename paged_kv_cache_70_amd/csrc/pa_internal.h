@@ -1,0 +1,52 @@
+// Internal interface between the C-ABI entry points (pa_api.hip) and the
+// kernel launchers (pa_write.hip, pa_decode.hip).  Not installed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pa {
+
+// Everything the decode kernels need, passed by value as the kernel argument.
+struct DecodeParams {
+  void* out;               // [B, H, D] of the element type
+  float* ws_acc;           // [B, H, maxP, D] fp32 partial accumulators
+  float* ws_ml;            // [B, H, maxP, 2]  fp32 partial (max, sum), max in log2 units
+  const void* q;           // [B, H, D]
+  const void* k_cache;     // [NB, bs, KVH, D]
+  const void* v_cache;
+  const int32_t* tables;   // [B, W]
+  const int32_t* ctx;      // [B]
+  float scale_log2;        // scale * log2(e): scores are kept in base-2 exponent units
+  int32_t B, H, KVH, W, NB;
+  int32_t bs_log2, bs_mask;
+  int32_t P;               // tokens per partition, multiple of bs
+  int32_t maxP;            // partitions reserved per (b, h) in the workspace
+  int32_t nchunks;         // head chunks per kv head (G / heads-per-unit)
+  int32_t max_tokens;      // W * bs: context lengths are clamped to this
+};
+
+// Launch-shape choices made on the host (pure functions of the sizes).
+struct DecodePlan {
+  int32_t heads_per_unit;  // query heads sharing one K/V stream in one wavefront
+  int32_t nchunks;         // G / heads_per_unit
+  int32_t P;               // partition length in tokens
+  int32_t maxP;            // ceil(W * bs / P)
+  int32_t tile_unroll;     // 16-byte loads per K (and per V) per tile and lane
+};
+
+bool dtype_ok(int32_t dtype);
+int32_t elem_bytes(int32_t dtype);
+
+hipError_t launch_write_kv(void* k_cache, void* v_cache, const void* k, const void* v,
+                           const int64_t* slots, int32_t T, int32_t row_bytes,
+                           int64_t num_slots, hipStream_t stream);
+
+hipError_t launch_decode_partials(const DecodeParams& prm, int32_t dtype, int32_t D,
+                                  const DecodePlan& plan, hipStream_t stream);
+
+hipError_t launch_decode_merge(const DecodeParams& prm, int32_t dtype, int32_t D,
+                               hipStream_t stream);
+
+}  // namespace pa

@@ -1,0 +1,268 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle, on an MI355X.
+
+Write: bit-exact over the whole cache.  Decode: within max-abs 1e-5 (fp32) or
+2e-2 + 1e-2 |ref| (bf16) of the unrounded fp64 oracle, element by element.
+Small cases compare every output; the five full-size workloads compare the
+write over the whole cache and the decode on sampled sequences, in the same
+launch configuration the benchmark times (automatic partition size).
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import paged_kv_cache_70_amd as pk
+from synth import CONFIG_ORDER, CONFIGS, SENTINEL, make_custom, make_workload
+from tests.gpu_util import assert_matches_oracle, stored_np
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU (run with -m 'not gpu' on a CPU-only machine)")
+    pk.load_library()          # fails loudly if the HIP library is not built
+    yield
+
+
+def _say(msg):
+    print(f"[gpu-parity] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def _bits(a):
+    """Bit patterns of stored values (NaN-safe equality)."""
+    return a.view(np.uint32) if a.dtype == np.float32 else a
+
+
+def _same_bits(t, ref):
+    return np.array_equal(_bits(stored_np(t)), _bits(ref))
+
+
+def _oracle_write(w):
+    kc, vc = stored_np(w.k_cache).copy(), stored_np(w.v_cache).copy()
+    O.write_kv(kc, vc, stored_np(w.k_new), stored_np(w.v_new), stored_np(w.slot_mapping))
+    return kc, vc
+
+
+def _run_write_decode(w, partition_size=0):
+    """GPU write (in place on clones) then GPU decode; returns caches and out."""
+    kc, vc = w.k_cache.clone(), w.v_cache.clone()
+    pk.write_kv(kc, vc, w.k_new, w.v_new, w.slot_mapping)
+    out = pk.decode(w.q, kc, vc, w.block_tables, w.context_lens, w.scale,
+                    partition_size=partition_size)
+    torch.cuda.synchronize()
+    return kc, vc, out
+
+
+# ---------------------------------------------------------------------------
+# write
+# ---------------------------------------------------------------------------
+
+def test_write_padding_example_shape():
+    """The page's write example (slots [4, 5, -1, 1], padding row of sentinels)
+    on a geometry the kernels support (bs 8, D 64): bit-exact vs the oracle,
+    no sentinel anywhere, the last slot untouched."""
+    _say("write padding example")
+    dev = torch.device("cuda")
+    kc = torch.zeros(3, 8, 1, 64, device=dev)
+    vc = torch.zeros_like(kc)
+    k = torch.tensor([10.0, 20.0, 30.0, 40.0], device=dev).view(4, 1, 1).repeat(1, 1, 64)
+    v = k * 0.1
+    slots = torch.tensor([4, 5, -1, 1], dtype=torch.int64, device=dev)
+    k[2] = SENTINEL
+    v[2] = SENTINEL
+    ko, vo = stored_np(kc).copy(), stored_np(vc).copy()
+    O.write_kv(ko, vo, stored_np(k), stored_np(v), stored_np(slots))
+    assert pk.write_kv(kc, vc, k, v, slots) is None
+    torch.cuda.synchronize()
+    assert np.array_equal(stored_np(kc).view(np.uint32), ko.view(np.uint32))
+    assert np.array_equal(stored_np(vc).view(np.uint32), vo.view(np.uint32))
+    assert int((kc == SENTINEL).sum()) == 0 and int((vc == SENTINEL).sum()) == 0
+    assert float(kc[0, 4, 0, 0]) == 10.0 and float(kc[0, 1, 0, 0]) == 40.0
+    assert int((kc[-1, -1] != 0).sum()) == 0
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("D,KVH", [(64, 1), (128, 3), (256, 2)])
+def test_write_random_geometry(dtype, D, KVH):
+    """Random caches (not zeros), interleaved padding, shuffled slots: the whole
+    cache after the write equals the oracle's bit for bit."""
+    _say(f"write random {dtype} D={D} KVH={KVH}")
+    w = make_custom(num_seqs=5, num_heads=KVH * 2, num_kv_heads=KVH, head_dim=D, block_size=8,
+                    dtype=dtype, lens=[1, 8, 9, 30, 17], pad_tokens=3, seed=D + KVH, device="cuda")
+    kc, vc = w.k_cache.clone(), w.v_cache.clone()
+    pk.write_kv(kc, vc, w.k_new, w.v_new, w.slot_mapping)
+    torch.cuda.synchronize()
+    ko, vo = _oracle_write(w)
+    assert _same_bits(kc, ko) and _same_bits(vc, vo)
+
+
+def test_write_zero_tokens_is_noop():
+    w = make_custom(num_seqs=1, num_heads=2, num_kv_heads=1, head_dim=64, block_size=8,
+                    lens=[3], seed=1, device="cuda")
+    kc = w.k_cache.clone()
+    pk.write_kv(kc, w.v_cache.clone(), w.k_new[:0], w.v_new[:0], w.slot_mapping[:0])
+    torch.cuda.synchronize()
+    assert torch.equal(kc, w.k_cache)
+
+
+# ---------------------------------------------------------------------------
+# decode, small cases (every output compared)
+# ---------------------------------------------------------------------------
+
+def test_tiny_f32_config_all_partitions():
+    """The tiny fp32 workload (n = 1 and a multiple of 16 included, 99999 tails),
+    write then decode, at the automatic and at forced small partition sizes."""
+    w = make_workload(CONFIGS["tiny_f32"], "cuda")
+    ko, vo = _oracle_write(w)
+    ref = O.decode(stored_np(w.q), ko, vo, stored_np(w.block_tables), stored_np(w.context_lens),
+                   w.scale, "f32")
+    for P in (0, 16, 32, 64, 128):
+        _say(f"tiny_f32 P={P}")
+        kc, vc, out = _run_write_decode(w, P)
+        assert _same_bits(kc, ko) and _same_bits(vc, vo)
+        assert_matches_oracle(out, ref, "f32", f"tiny_f32 P={P}")
+
+
+_SHAPES = [
+    # dtype, D, bs, KVH, G
+    ("f32", 64, 16, 2, 4),
+    ("f32", 64, 8, 1, 8),
+    ("f32", 128, 32, 2, 2),
+    ("f32", 256, 8, 1, 3),
+    ("bf16", 64, 8, 2, 4),
+    ("bf16", 64, 16, 1, 1),
+    ("bf16", 64, 64, 2, 8),
+    ("bf16", 128, 16, 8, 4),
+    ("bf16", 128, 8, 2, 6),
+    ("bf16", 128, 32, 8, 8),
+    ("bf16", 128, 64, 1, 16),
+    ("bf16", 256, 16, 4, 4),
+    ("bf16", 256, 32, 2, 5),
+]
+
+
+@pytest.mark.parametrize("dtype,D,bs,KVH,G", _SHAPES, ids=lambda x: str(x))
+def test_random_shapes_poisoned(dtype, D, bs, KVH, G):
+    """Random lengths (1, multiples of bs, others), shuffled blocks, every row no
+    sequence reads filled with NaN, table tails pointing at NaN blocks; several
+    partition sizes so that both the one-partition and the merge paths run."""
+    lens = [1, bs, 3 * bs, 5 * bs + 3, 2 * bs - 1, 37, 300]
+    w = make_custom(num_seqs=len(lens), num_heads=KVH * G, num_kv_heads=KVH, head_dim=D,
+                    block_size=bs, dtype=dtype, lens=lens, tail="poison", poison=True,
+                    pad_tokens=2, seed=D * 7 + bs + G, device="cuda")
+    ko, vo = _oracle_write(w)
+    ref = O.decode(stored_np(w.q), ko, vo, stored_np(w.block_tables), stored_np(w.context_lens),
+                   w.scale, dtype)
+    assert np.all(np.isfinite(ref))
+    for P in sorted({0, bs, 2 * bs, 4 * bs, 64 if 64 % bs == 0 else bs}):
+        _say(f"random {dtype} D={D} bs={bs} KVH={KVH} G={G} P={P}")
+        kc, vc, out = _run_write_decode(w, P)
+        assert _same_bits(kc, ko) and _same_bits(vc, vo)
+        assert_matches_oracle(out, ref, dtype, f"{dtype} D{D} bs{bs} KVH{KVH} G{G} P{P}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_single_token_returns_v_row_exactly(dtype):
+    """A one-token context returns that token's V row bit-exactly, whatever q is
+    (the page's worked example, sequence 1)."""
+    _say(f"n=1 exact {dtype}")
+    w = make_custom(num_seqs=3, num_heads=8, num_kv_heads=2, head_dim=128, block_size=16,
+                    dtype=dtype, lens=[1, 1, 1], seed=3, device="cuda")
+    kc, vc, out = _run_write_decode(w)
+    tbl = w.block_tables.long().cpu()
+    for b in range(3):
+        for h in range(8):
+            row = vc[int(tbl[b, 0]), 0, h // 4]
+            assert torch.equal(out[b, h].view(torch.int16 if dtype == "bf16" else torch.int32),
+                               row.view(torch.int16 if dtype == "bf16" else torch.int32))
+
+
+def test_zero_length_gives_zeros():
+    """Reading for n = 0 (the pages imply n >= 1): the output is zeros."""
+    _say("n=0")
+    w = make_custom(num_seqs=3, num_heads=4, num_kv_heads=2, head_dim=64, block_size=8,
+                    dtype="bf16", lens=[5, 1, 20], seed=4, device="cuda")
+    lens = w.context_lens.clone()
+    lens[1] = 0
+    out = torch.full_like(w.q, 7.0)
+    for P in (0, 8):
+        pk.decode(w.q, w.k_cache, w.v_cache, w.block_tables, lens, w.scale, out=out, partition_size=P)
+        torch.cuda.synchronize()
+        assert int((out[1] != 0).sum()) == 0
+        ref = O.decode(stored_np(w.q), stored_np(w.k_cache), stored_np(w.v_cache),
+                       stored_np(w.block_tables), stored_np(lens), w.scale, "bf16")
+        assert_matches_oracle(out, ref, "bf16", f"n=0 P={P}")
+
+
+def test_split_entry_points_equal_decode():
+    """pa_decode_partials followed by pa_decode_merge gives pa_decode's bits."""
+    _say("split entry points")
+    w = make_custom(num_seqs=4, num_heads=16, num_kv_heads=4, head_dim=128, block_size=16,
+                    dtype="bf16", lens=[700, 5, 129, 1000], seed=6, device="cuda")
+    P = 64
+    a = pk.decode(w.q, w.k_cache, w.v_cache, w.block_tables, w.context_lens, w.scale, partition_size=P)
+    ws = torch.empty(pk.workspace_bytes(4, 16, w.block_tables.shape[1], w.k_cache, P),
+                     dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(w.q)
+    pk.decode_partials(w.q, w.k_cache, w.v_cache, w.block_tables, w.context_lens, w.scale, out=b,
+                       workspace=ws, partition_size=P)
+    pk.decode_merge(w.q, w.k_cache, w.block_tables, w.context_lens, out=b, workspace=ws,
+                    partition_size=P)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_out_of_order_and_aliased_tables():
+    """An out-of-order table (as in [3, 1]) and two tables aliasing the same
+    physical blocks give the dense result for each sequence."""
+    _say("aliased tables")
+    w = make_custom(num_seqs=2, num_heads=4, num_kv_heads=1, head_dim=64, block_size=8,
+                    dtype="f32", lens=[16, 16], seed=8, device="cuda")
+    t = w.block_tables.clone()
+    t[1, :2] = torch.flip(t[0, :2], [0])      # seq 1 reads seq 0's blocks in reverse order
+    out = pk.decode(w.q, w.k_cache, w.v_cache, t, w.context_lens, w.scale)
+    torch.cuda.synchronize()
+    ref = O.decode(stored_np(w.q), stored_np(w.k_cache), stored_np(w.v_cache), stored_np(t),
+                   stored_np(w.context_lens), w.scale, "f32")
+    assert_matches_oracle(out, ref, "f32", "aliased")
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads: whole-cache write, sampled decode
+# ---------------------------------------------------------------------------
+
+def _sample(lens, k, seed):
+    lens = np.asarray(lens)
+    order = np.argsort(lens)
+    pick = {int(order[0]), int(order[-1])}
+    rng = np.random.default_rng(seed)
+    rest = [i for i in range(len(lens)) if i not in pick]
+    pick.update(int(x) for x in rng.choice(rest, size=min(k - len(pick), len(rest)), replace=False))
+    return sorted(pick)
+
+
+@pytest.mark.parametrize("name", CONFIG_ORDER[1:])
+def test_full_size_config(name):
+    cfg = CONFIGS[name]
+    _say(f"full {name}: generate")
+    w = make_workload(cfg, "cuda")
+    _say(f"full {name}: write + decode on GPU")
+    kc, vc, out = _run_write_decode(w)
+    _say(f"full {name}: oracle write")
+    ko, vo = _oracle_write(w)
+    assert _same_bits(kc, ko), "k_cache differs from the oracle's write"
+    assert _same_bits(vc, vo), "v_cache differs from the oracle's write"
+    lens = stored_np(w.context_lens)
+    sel = _sample(lens, 3 if name == "long_ctx_bf16" else 8, seed=cfg.seed)
+    _say(f"full {name}: oracle decode of sequences {sel} (lengths {lens[sel].tolist()})")
+    ref = O.decode(stored_np(w.q)[sel], ko, vo, stored_np(w.block_tables)[sel], lens[sel],
+                   w.scale, cfg.dtype)
+    assert_matches_oracle(out[sel], ref, cfg.dtype, name)
+    assert bool(torch.isfinite(out.float()).all())

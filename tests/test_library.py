@@ -1,0 +1,98 @@
+"""The C-ABI library loads and exports every symbol the header declares; the
+host-side argument checks and planning queries behave as documented.  No
+kernel is launched (CPU only)."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import paged_kv_cache_70_amd as pk
+from paged_kv_cache_70_amd.api import CacheDesc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "paged_kv.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = pk.load_library()
+    names = _declared()
+    assert {"pa_write_kv", "pa_decode", "pa_decode_partials", "pa_decode_merge",
+            "pa_decode_workspace_bytes", "pa_decode_partition_size", "pa_status_string",
+            "pa_abi_version"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert pk.abi_version() >> 16 == 1
+
+
+def test_status_strings():
+    for code in range(0, -8, -1):
+        s = pk.status_string(code)
+        assert s and s != "unknown status"
+    assert pk.status_string(-99) == "unknown status"
+
+
+def _desc(**kw):
+    d = dict(num_blocks=100, block_size=16, num_kv_heads=8, head_dim=128, dtype=1)
+    d.update(kw)
+    return CacheDesc(**d)
+
+
+def test_argument_checks_without_launch():
+    lib = pk.load_library()
+    d = _desc()
+    # null pointers and bad shapes are rejected before anything is enqueued
+    assert lib.pa_write_kv(None, None, None, None, None, 4, ctypes.byref(d), None) == -1
+    assert lib.pa_write_kv(None, None, None, None, None, 0, ctypes.byref(d), None) == 0   # T = 0: no-op
+    assert lib.pa_write_kv(None, None, None, None, None, -1, ctypes.byref(d), None) == -2
+    assert lib.pa_write_kv(None, None, None, None, None, 4, None, None) == -1
+    for bad, code in ((dict(head_dim=96), -3), (dict(block_size=12), -3), (dict(block_size=128), -3),
+                      (dict(dtype=7), -3), (dict(num_blocks=0), -2), (dict(num_kv_heads=0), -2)):
+        assert lib.pa_write_kv(None, None, None, None, None, 4, ctypes.byref(_desc(**bad)), None) == code
+    args = lambda H, W, desc, P=0, ws=None, wsb=0: (
+        None, None, None, None, None, None, 1.0, 4, H, W, ctypes.byref(desc), P, ws, wsb, None)
+    assert lib.pa_decode(*args(30, 8, d)) == -2            # H % KVH != 0
+    assert lib.pa_decode(*args(32, 0, d)) == -2            # W = 0
+    assert lib.pa_decode(*args(32, 8, d, P=24)) == -3      # partition not a multiple of bs
+    assert lib.pa_decode(*args(32, 8, d)) == -1            # null tensors
+    # misaligned pointers
+    fake = ctypes.c_void_p(0x1008)
+    a = list(args(32, 8, d))
+    a[0:6] = [fake] * 6
+    assert lib.pa_decode(*a) == -5
+
+
+def test_workspace_and_partition_queries():
+    lib = pk.load_library()
+    d = _desc()
+    # Llama-3-8B shape: 64 sequences, 32 heads, 256-entry tables of 16 tokens
+    P = lib.pa_decode_partition_size(64, 32, 256, ctypes.byref(d))
+    assert P > 0 and P % 16 == 0
+    maxP = -(-256 * 16 // P)
+    ws = lib.pa_decode_workspace_bytes(64, 32, 256, ctypes.byref(d), 0)
+    assert ws == (64 * 32 * maxP * (128 + 2) * 4 if maxP > 1 else 0)
+    # explicit partition sizes
+    assert lib.pa_decode_workspace_bytes(2, 8, 4, ctypes.byref(d), 64) == 0       # one partition
+    assert lib.pa_decode_workspace_bytes(2, 8, 4, ctypes.byref(d), 16) == 2 * 8 * 4 * 130 * 4
+    assert lib.pa_decode_workspace_bytes(2, 8, 4, ctypes.byref(d), 24) == 0       # invalid
+    # long contexts get more than one partition, small ones may not
+    assert lib.pa_decode_partition_size(8, 32, 8192, ctypes.byref(d)) < 8192 * 16
+    # a workspace smaller than required is rejected before launch
+    fake = ctypes.c_void_p(0x1000)
+    st = lib.pa_decode(fake, fake, fake, fake, fake, fake, 1.0, 2, 8, 4, ctypes.byref(d), 16,
+                       fake, 100, None)
+    assert st == -4
+
+
+def test_binding_rejects_host_and_noncontiguous_tensors():
+    kc = torch.zeros(4, 16, 2, 64)
+    with pytest.raises(ValueError):
+        pk.write_kv(kc, kc.clone(), torch.zeros(1, 2, 64), torch.zeros(1, 2, 64),
+                    torch.zeros(1, dtype=torch.int64))
