@@ -7,9 +7,11 @@ Default workload: Llama-3-8B attention shape in bf16 (B=64, H=32, KVH=8,
 D=128, block size 16, context lengths U[1, 4096], shuffled blocks, 64 written
 tokens).  Inputs are seeded synthetic tensors already resident in HBM.
 
-By default a 1 GiB buffer is overwritten before every step (outside the
-step's timing events) so that the 256 MB last-level cache does not serve KV
-rows from the previous step; ``--hot`` skips that.
+By default a 1 GiB buffer is read before every step (outside the step's
+timing events) so that the 256 MB last-level cache holds none of the KV rows
+of the previous step.  The flush reads rather than writes: a written buffer
+would leave dirty lines whose write-back would share the timed step's
+bandwidth.  ``--hot`` skips the flush.
 
 Prints ONE JSON line.  `value` = KV bytes the decode must read (sum over
 sequences of n_b * 2 * KVH * D * elem) / mean step time, in GB/s (10^9 B/s).
@@ -126,7 +128,8 @@ def main():
     ws = torch.empty(max(16, pk.workspace_bytes(B, H, W, w.k_cache, P)), dtype=torch.uint8, device=dev)
     out = torch.empty_like(w.q)
     kc, vc = w.k_cache, w.v_cache
-    flush = None if args.hot else torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    flush = None if args.hot else torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    flush_sink = torch.zeros((), dtype=torch.float32, device=dev)
 
     def step(ev=None):
         if ev:
@@ -143,9 +146,12 @@ def main():
         if ev:
             ev[3].record()
 
-    for _ in range(args.warmup):
+    def do_flush():
         if flush is not None:
-            flush.fill_(1)
+            torch.sum(flush, dim=0, out=flush_sink)
+
+    for _ in range(args.warmup):
+        do_flush()
         step()
     torch.cuda.synchronize()
 
@@ -153,8 +159,7 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        if flush is not None:
-            flush.fill_(i & 0xFF)
+        do_flush()
         step(events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0

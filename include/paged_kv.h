@@ -57,7 +57,8 @@ typedef enum pa_status {
   PA_ERR_NULL = -1,         /* a required pointer is NULL */
   PA_ERR_SHAPE = -2,        /* a size is negative/zero where it must be positive, or H % KVH != 0 */
   PA_ERR_UNSUPPORTED = -3,  /* head_dim not in {64,128,256}, block_size not in {8,16,32,64}, unknown dtype,
-                               or a partition size that is not a positive multiple of block_size */
+                               or a partition size that is not a positive multiple of block_size
+                               or spans more than 64 blocks */
   PA_ERR_WORKSPACE = -4,    /* workspace NULL or smaller than pa_decode_workspace_bytes() */
   PA_ERR_ALIGN = -5,        /* a tensor pointer is not 16-byte aligned */
   PA_ERR_LAUNCH = -6,       /* the HIP runtime rejected a kernel launch */
@@ -133,7 +134,7 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads,
  *   max_blocks_per_seq  table width W > 0
  *   desc                host, cache geometry
  *   partition_size      tokens per split-KV partition: 0 = automatic, else a
- *                       positive multiple of block_size
+ *                       positive multiple of block_size, at most 64 * block_size
  *   workspace           device, >= pa_decode_workspace_bytes(...) bytes, no
  *                       initial contents required; may be NULL only when
  *                       workspace_bytes is 0 and the requirement is 0

@@ -40,12 +40,25 @@ static int32_t heads_per_unit(int32_t G) {
   return 1;
 }
 
-// 16-byte loads per K per lane per tile: up to 4, and a tile (rows-per-load x
-// loads) never crosses a block boundary.
-static int32_t tile_unroll(const pa_cache_desc* d) {
+// Rows of D elements one 16-byte-per-lane load instruction covers.
+static int32_t rows_per_wave(const pa_cache_desc* d) {
   const int32_t epv = 16 / elem_bytes(d->dtype);
-  const int32_t rpw = 64 / (d->head_dim / epv);
-  int32_t u = d->block_size / rpw;
+  return 64 / (d->head_dim / epv);
+}
+
+// kv heads per wavefront: as many of a token's (adjacent) kv heads as one
+// load instruction covers, so each instruction reads contiguous runs.
+static int32_t kv_per_wave(const pa_cache_desc* d) {
+  int32_t kg = rows_per_wave(d);
+  while (d->num_kv_heads % kg) kg >>= 1;
+  return kg;
+}
+
+// 16-byte loads per K per lane per tile: up to 4, and a tile (tokens per
+// load x loads) never crosses a block boundary.
+static int32_t tile_unroll(const pa_cache_desc* d) {
+  const int32_t tokens_per_load = rows_per_wave(d) / kv_per_wave(d);
+  const int32_t u = d->block_size / tokens_per_load;
   return u >= 4 ? 4 : u;
 }
 
@@ -55,13 +68,16 @@ static int32_t tile_unroll(const pa_cache_desc* d) {
 // (sequences x kv heads x head chunks x partitions of the longest possible
 // context) at or below kTargetUnits.
 static constexpr int64_t kTargetUnits = 8192;
+// A partition's block-table entries are held one per lane of a wavefront.
+static constexpr int32_t kMaxBlocksPerPartition = 64;
 static int32_t auto_partition(int32_t B, int32_t H, int32_t W, const pa_cache_desc* d) {
   const int32_t G = H / d->num_kv_heads;
-  const int64_t rows = (int64_t)B * d->num_kv_heads * (G / heads_per_unit(G));
+  const int64_t rows = (int64_t)B * (d->num_kv_heads / kv_per_wave(d)) * (G / heads_per_unit(G));
   const int64_t max_len = (int64_t)W * d->block_size;
   int64_t P = 256;
   if (P % d->block_size) P = d->block_size;
-  while (P < max_len && rows * ((max_len + P - 1) / P) > kTargetUnits) P *= 2;
+  const int64_t P_max = (int64_t)kMaxBlocksPerPartition * d->block_size;
+  while (P < max_len && P < P_max && rows * ((max_len + P - 1) / P) > kTargetUnits) P *= 2;
   return (int32_t)P;
 }
 
@@ -76,7 +92,8 @@ static int check_decode_sizes(int32_t B, int32_t H, int32_t W, const pa_cache_de
   if (st) return st;
   if (B <= 0 || H <= 0 || W <= 0) return PA_ERR_SHAPE;
   if (H % d->num_kv_heads) return PA_ERR_SHAPE;
-  if (partition_size < 0 || (partition_size && partition_size % d->block_size))
+  if (partition_size < 0 || (partition_size && partition_size % d->block_size) ||
+      partition_size > kMaxBlocksPerPartition * d->block_size)
     return PA_ERR_UNSUPPORTED;
   const int64_t max_len = (int64_t)W * d->block_size;
   if (max_len > INT_MAX / 2) return PA_ERR_TOO_LARGE;
@@ -86,9 +103,11 @@ static int check_decode_sizes(int32_t B, int32_t H, int32_t W, const pa_cache_de
   p.nchunks = G / p.heads_per_unit;
   p.P = partition_size ? partition_size : auto_partition(B, H, W, d);
   const int64_t maxP = (max_len + p.P - 1) / p.P;
-  // grid.y = KVH * nchunks and grid.z = B are limited to 65535; the merge
+  // grid.y = partitions and grid.z = B are limited to 65535; the merge
   // kernel keeps one fp32 weight per partition in LDS (at most 64 KiB).
-  if ((int64_t)d->num_kv_heads * p.nchunks > 65535 || B > 65535 || H > 65535 || maxP > 16384)
+  p.kv_per_wave = kv_per_wave(d);
+  if ((int64_t)(d->num_kv_heads / p.kv_per_wave) * p.nchunks > INT_MAX || B > 65535 || H > 65535 ||
+      maxP > 16384)
     return PA_ERR_TOO_LARGE;
   p.maxP = (int32_t)maxP;
   p.tile_unroll = tile_unroll(d);

@@ -30,6 +30,8 @@
 // block, whatever they hold (NaN included), cannot reach the output.
 #include <math.h>
 
+#include <type_traits>
+
 #include "pa_internal.h"
 
 namespace pa {
@@ -127,6 +129,34 @@ __device__ __forceinline__ float row_sum(float x) {
   return x;
 }
 
+// row_sum for N independent values, one reduction step across all of them at
+// a time, so consecutive DPP operations never depend on each other.
+template <int LPT, int N>
+__device__ __forceinline__ void row_sum_all(float* x) {
+  static_assert(LPT == 4 || LPT == 8 || LPT == 16 || LPT == 32 || LPT == 64, "row width");
+  if constexpr (LPT >= 16) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] += dpp<0x128>(x[i]);
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] += dpp<0x124>(x[i]);
+  } else if constexpr (LPT == 8) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] += dpp<0x141>(x[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < N; ++i) x[i] += dpp<0x4E>(x[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) x[i] += dpp<0xB1>(x[i]);
+  if constexpr (LPT >= 32) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] += __shfl_xor(x[i], 16);
+  }
+  if constexpr (LPT >= 64) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] += __shfl_xor(x[i], 32);
+  }
+}
+
 // Combine over the RPW rows of the wavefront (lanes LPT apart).
 template <int LPT>
 __device__ __forceinline__ float rows_max(float x) {
@@ -143,6 +173,9 @@ __device__ __forceinline__ float rows_sum(float x) {
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Word 3 of a buffer resource for gfx9-family targets (raw, untyped loads).
+constexpr int kRsrcWord3 = 0x00020000;
+
 __device__ __forceinline__ u32x4 load16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
@@ -150,20 +183,22 @@ __device__ __forceinline__ u32x4 load16(const void* p) {
 // ---------------------------------------------------------------------------
 // K2: split-KV partial kernel
 // ---------------------------------------------------------------------------
-template <typename E, int D, int GC, int U>
+template <typename E, int D, int GC, int U, int KG>
 __global__ __launch_bounds__(64) void decode_partial_kernel(const DecodeParams prm) {
   constexpr int EPV = E::EPV;
-  constexpr int LPT = D / EPV;       // lanes per token row
-  constexpr int RPW = 64 / LPT;      // token rows per load instruction
-  constexpr int TT = RPW * U;        // tokens per tile
+  constexpr int LPT = D / EPV;       // lanes per (token, kv head) row of D elements
+  constexpr int RPW = 64 / LPT;      // rows per load instruction
+  static_assert(KG >= 1 && RPW % KG == 0, "kv heads per wavefront");
+  constexpr int TR = RPW / KG;       // tokens per load instruction
+  constexpr int TT = TR * U;         // tokens per tile
   constexpr int ESZ = 16 / EPV;      // bytes per element
 
-  const int p = blockIdx.x;
+  // Grid: x = (kv-head group, head chunk) fastest, so the groups covering one
+  // block's token rows are dispatched together; y = partition; z = sequence.
+  const int p = blockIdx.y;
   const int b = blockIdx.z;
-  const int kvh = blockIdx.y / prm.nchunks;
-  const int chunk = blockIdx.y - kvh * prm.nchunks;
-  const int G = prm.H / prm.KVH;
-  const int h0 = kvh * G + chunk * GC;
+  const int kvg = blockIdx.x / prm.nchunks;
+  const int chunk = blockIdx.x - kvg * prm.nchunks;
 
   int n = prm.ctx[b];
   n = n < 0 ? 0 : (n > prm.max_tokens ? prm.max_tokens : n);
@@ -175,6 +210,13 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(const DecodeParams p
   const int lane = threadIdx.x;
   const int r = lane / LPT;          // row of this lane within a load
   const int c = lane - r * LPT;      // 16-byte piece of the D-row
+  // Row r covers kv head kvg * KG + r % KG of token r / KG: the KG heads of
+  // one token are adjacent in memory, so a load instruction reads TR runs of
+  // KG * D contiguous elements.
+  const int kvh = kvg * KG + r % KG;
+  const int tr = r / KG;
+  const int G = prm.H / prm.KVH;
+  const int h0 = kvh * G + chunk * GC;
 
   // This lane's slice of the GC queries.
   u32x4 qv[GC];
@@ -194,42 +236,66 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(const DecodeParams p
     for (int e = 0; e < EPV; ++e) acc[g][e] = 0.0f;
   }
 
-  const size_t row_bytes = (size_t)prm.KVH * D * ESZ;            // token stride in a block
-  const size_t blk_bytes = row_bytes << prm.bs_log2;
-  const size_t lane_off = (size_t)kvh * D * ESZ + (size_t)c * 16 + (size_t)r * row_bytes;
-  const char* kbase = static_cast<const char*>(prm.k_cache) + lane_off;
-  const char* vbase = static_cast<const char*>(prm.v_cache) + lane_off;
+  const uint32_t row_bytes = (uint32_t)prm.KVH * D * ESZ;         // token stride in a block
+  const size_t blk_bytes = (size_t)row_bytes << prm.bs_log2;
+  const uint32_t tile_bytes = row_bytes * TT;
+  // Per-lane byte offset inside a tile: fixed for the whole unit, so the loads
+  // need no per-tile vector address arithmetic.
+  const uint32_t lane_off = (uint32_t)kvh * D * ESZ + (uint32_t)c * 16 + (uint32_t)tr * row_bytes;
+  const char* kc = static_cast<const char*>(prm.k_cache);
+  const char* vc = static_cast<const char*>(prm.v_cache);
   const int32_t* tbl = prm.tables + (size_t)b * prm.W;
 
-  // Tile state: U K-vectors and U V-vectors per lane, double buffered so that
-  // the next tile's loads are in flight while this tile is folded.
-  u32x4 kA[U], vA[U], kB[U], vB[U];
-  int okA = 0, okB = 0;
+  // Block-table entries of this partition, one per lane (a partition spans at
+  // most 64 blocks): each tile takes its physical block id with v_readlane, so
+  // the tile loop issues no scalar loads and no conditional vector loads.
+  // Only entries below ceil(n / bs) are read.
+  const int j_first = t_begin >> prm.bs_log2;
+  const int j_end = (t_end + prm.bs_mask) >> prm.bs_log2;       // one past the last entry used
+  const int tbl_v = (j_first + lane < j_end) ? tbl[j_first + lane] : 0;
 
-  auto load_tile = [&](int tile, u32x4 (&kr)[U], u32x4 (&vr)[U]) -> int {
-    const int phys = tbl[tile >> prm.bs_log2];
-    if ((unsigned)phys >= (unsigned)prm.NB) return 0;   // entry outside the pool: no tokens
-    const size_t off = (size_t)phys * blk_bytes + (size_t)(tile & prm.bs_mask) * row_bytes;
+  // Tile state: U K-vectors and U V-vectors per lane, double buffered so that
+  // the next tile's loads are in flight while this tile is folded.  A tile is
+  // read through a buffer resource based at its first row (built in scalar
+  // registers); a block outside the pool gets an empty resource, whose loads
+  // return zeros without touching memory.
+  u32x4 kA[U], vA[U], kB[U], vB[U];
+
+  auto load_tile = [&](int tile, u32x4 (&kr)[U], u32x4 (&vr)[U]) -> bool {
+    const int phys = __builtin_amdgcn_readlane(tbl_v, (tile >> prm.bs_log2) - j_first);
+    const bool ok = (unsigned)phys < (unsigned)prm.NB;
+    const size_t off = (size_t)(ok ? phys : 0) * blk_bytes + (size_t)(tile & prm.bs_mask) * row_bytes;
+    const int nrec = ok ? (int)tile_bytes : 0;
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(kc + off), (short)0, nrec, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vc + off), (short)0, nrec, kRsrcWord3);
 #pragma unroll
-    for (int u = 0; u < U; ++u) kr[u] = load16(kbase + off + (size_t)u * RPW * row_bytes);
+    for (int u = 0; u < U; ++u) kr[u] = __builtin_amdgcn_raw_buffer_load_b128(rk, lane_off, u * TR * row_bytes, 0);
 #pragma unroll
-    for (int u = 0; u < U; ++u) vr[u] = load16(vbase + off + (size_t)u * RPW * row_bytes);
-    return 1;
+    for (int u = 0; u < U; ++u) vr[u] = __builtin_amdgcn_raw_buffer_load_b128(rv, lane_off, u * TR * row_bytes, 0);
+    // Keep the scheduler from hoisting the previous tile's arithmetic (which
+    // must wait for its own loads) above these loads.
+    __builtin_amdgcn_sched_barrier(0);
+    return ok;
   };
 
-  auto fold_tile = [&](int tile, int ok, const u32x4 (&kr)[U], const u32x4 (&vr)[U]) {
-    const int nvalid = ok ? min(TT, t_end - tile) : 0;   // valid tokens of this tile
-    const bool full = nvalid == TT;
+  // Fold one tile into the running state.  A full tile has every row valid
+  // (unless its block is outside the pool: then ok is false and its scores
+  // are -inf, its V rows zero).  The MASKED variant handles the tile holding
+  // the sequence end: rows past nvalid get a -inf score and a zero V row, by
+  // selection.
+  auto fold_tile = [&](auto masked, bool ok, int nvalid, const u32x4 (&kr)[U], const u32x4 (&vr)[U]) {
+    constexpr bool MASKED = decltype(masked)::value;
     float s[U][GC];
 #pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int g = 0; g < GC; ++g) s[u][g] = E::dot(qv[g], kr[u]);
+    row_sum_all<LPT, U * GC>(&s[0][0]);
+#pragma unroll
     for (int u = 0; u < U; ++u) {
+      const bool valid = ok && (!MASKED || (u * TR + tr) < nvalid);
 #pragma unroll
-      for (int g = 0; g < GC; ++g) s[u][g] = row_sum<LPT>(E::dot(qv[g], kr[u])) * prm.scale_log2;
-      if (!full) {
-        const bool valid = (u * RPW + r) < nvalid;
-#pragma unroll
-        for (int g = 0; g < GC; ++g) s[u][g] = valid ? s[u][g] : -INFINITY;
-      }
+      for (int g = 0; g < GC; ++g) s[u][g] = valid ? s[u][g] * prm.scale_log2 : -INFINITY;
     }
     float mu[GC];
 #pragma unroll
@@ -238,7 +304,7 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(const DecodeParams p
 #pragma unroll
       for (int u = 1; u < U; ++u) mt = fmaxf(mt, s[u][g]);
       const float m_new = fmaxf(m[g], mt);
-      mu[g] = (m_new == -INFINITY) ? 0.0f : m_new;     // a row with no token yet
+      mu[g] = (m_new == -INFINITY) ? 0.0f : m_new;   // a row with no token yet
       const float corr = exp2_fast(m[g] - mu[g]);
       m[g] = m_new;
       l[g] *= corr;
@@ -249,8 +315,8 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(const DecodeParams p
     for (int u = 0; u < U; ++u) {
       float vf[EPV];
       E::widen(vr[u], vf);
-      if (!full) {
-        const bool valid = (u * RPW + r) < nvalid;
+      if constexpr (MASKED) {
+        const bool valid = (u * TR + tr) < nvalid;
 #pragma unroll
         for (int e = 0; e < EPV; ++e) vf[e] = valid ? vf[e] : 0.0f;
       }
@@ -264,29 +330,44 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(const DecodeParams p
     }
   };
 
-  int tile = t_begin;
-  if (tile < t_end) okA = load_tile(tile, kA, vA);
-  while (tile < t_end) {
-    const int t1 = tile + TT;
-    if (t1 < t_end) okB = load_tile(t1, kB, vB);
-    fold_tile(tile, okA, kA, vA);
-    if (t1 >= t_end) break;
-    const int t2 = t1 + TT;
-    if (t2 < t_end) okA = load_tile(t2, kA, vA);
-    fold_tile(t1, okB, kB, vB);
-    tile = t2;
+  // Full tiles in a loop of pairs (A/B buffers swap roles every half, with a
+  // single loop exit so that each buffer keeps its registers), then the odd
+  // full tile and the one partial tile (sequence end), if any.
+  const int ntok = t_end - t_begin;
+  const int nfull = ntok > 0 ? ntok / TT : 0;
+  const int rem = ntok > 0 ? ntok - nfull * TT : 0;
+  const int ntiles = nfull + (rem ? 1 : 0);
+  if (ntiles > 0) {
+    // tile i starts at t_begin + i * TT; past the last tile the last one is
+    // fetched again (cache hit) so that every step issues its loads.
+    auto tile_at = [&](int i) { return t_begin + min(i, ntiles - 1) * TT; };
+    bool okA = load_tile(tile_at(0), kA, vA), okB;
+    const int npairs = nfull >> 1;
+    for (int ip = 0; ip < npairs; ++ip) {
+      okB = load_tile(tile_at(2 * ip + 1), kB, vB);
+      fold_tile(std::false_type{}, okA, TT, kA, vA);
+      okA = load_tile(tile_at(2 * ip + 2), kA, vA);
+      fold_tile(std::false_type{}, okB, TT, kB, vB);
+    }
+    if (nfull & 1) {
+      okB = load_tile(tile_at(nfull), kB, vB);
+      fold_tile(std::false_type{}, okA, TT, kA, vA);
+      if (rem) fold_tile(std::true_type{}, okB, rem, kB, vB);
+    } else if (rem) {
+      fold_tile(std::true_type{}, okA, rem, kA, vA);
+    }
   }
 
-  // Combine the RPW row states of the wavefront.
+  // Combine the TR row states of each kv head (rows LPT * KG lanes apart).
   const bool single = nparts <= 1;
 #pragma unroll
   for (int g = 0; g < GC; ++g) {
-    const float M = rows_max<LPT>(m[g]);
+    const float M = rows_max<LPT * KG>(m[g]);
     const float f = (m[g] == -INFINITY) ? 0.0f : exp2_fast(m[g] - M);
-    const float L = rows_sum<LPT>(l[g] * f);
+    const float L = rows_sum<LPT * KG>(l[g] * f);
 #pragma unroll
-    for (int e = 0; e < EPV; ++e) acc[g][e] = rows_sum<LPT>(acc[g][e] * f);
-    if (r == 0) {
+    for (int e = 0; e < EPV; ++e) acc[g][e] = rows_sum<LPT * KG>(acc[g][e] * f);
+    if (tr == 0) {
       const size_t bh = (size_t)b * prm.H + h0 + g;
       if (single) {
         const float inv = L > 0.0f ? 1.0f / L : 0.0f;
@@ -394,24 +475,42 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const DecodeParams prm
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-template <typename E, int D, int GC, int U>
+template <typename E, int D, int GC, int U, int KG>
 static hipError_t launch_partial_u(const DecodeParams& prm, hipStream_t stream) {
-  dim3 grid(prm.maxP, prm.KVH * prm.nchunks, prm.B);
-  hipLaunchKernelGGL((decode_partial_kernel<E, D, GC, U>), grid, dim3(64), 0, stream, prm);
+  dim3 grid((prm.KVH / KG) * prm.nchunks, prm.maxP, prm.B);
+  hipLaunchKernelGGL((decode_partial_kernel<E, D, GC, U, KG>), grid, dim3(64), 0, stream, prm);
   return hipGetLastError();
 }
 
-template <typename E, int D, int GC>
-static hipError_t launch_partial_gc(const DecodeParams& prm, int U, hipStream_t stream) {
+// (KG, U) pairs: KG kv heads per wavefront (a power of two dividing RPW),
+// U loads per tile with TR * U <= block size.
+template <typename E, int D, int GC, int KG>
+static hipError_t launch_partial_kg(const DecodeParams& prm, int U, hipStream_t stream) {
   constexpr int RPW = 64 / (D / E::EPV);
-  switch (U) {
-    case 4: return launch_partial_u<E, D, GC, 4>(prm, stream);
-    case 2:
-      if constexpr (RPW >= 4) return launch_partial_u<E, D, GC, 2>(prm, stream);
-      break;
-    case 1:
-      if constexpr (RPW >= 8) return launch_partial_u<E, D, GC, 1>(prm, stream);
-      break;
+  if constexpr (RPW % KG != 0) {
+    return hipErrorInvalidValue;
+  } else {
+    constexpr int TR = RPW / KG;
+    switch (U) {
+      case 4: return launch_partial_u<E, D, GC, 4, KG>(prm, stream);
+      case 2:
+        if constexpr (TR >= 4) return launch_partial_u<E, D, GC, 2, KG>(prm, stream);
+        break;
+      case 1:
+        if constexpr (TR >= 8) return launch_partial_u<E, D, GC, 1, KG>(prm, stream);
+        break;
+    }
+    return hipErrorInvalidValue;
+  }
+}
+
+template <typename E, int D, int GC>
+static hipError_t launch_partial_gc(const DecodeParams& prm, const DecodePlan& plan, hipStream_t s) {
+  switch (plan.kv_per_wave) {
+    case 1: return launch_partial_kg<E, D, GC, 1>(prm, plan.tile_unroll, s);
+    case 2: return launch_partial_kg<E, D, GC, 2>(prm, plan.tile_unroll, s);
+    case 4: return launch_partial_kg<E, D, GC, 4>(prm, plan.tile_unroll, s);
+    case 8: return launch_partial_kg<E, D, GC, 8>(prm, plan.tile_unroll, s);
   }
   return hipErrorInvalidValue;
 }
@@ -419,10 +518,10 @@ static hipError_t launch_partial_gc(const DecodeParams& prm, int U, hipStream_t 
 template <typename E, int D>
 static hipError_t launch_partial_d(const DecodeParams& prm, const DecodePlan& plan, hipStream_t s) {
   switch (plan.heads_per_unit) {
-    case 1: return launch_partial_gc<E, D, 1>(prm, plan.tile_unroll, s);
-    case 2: return launch_partial_gc<E, D, 2>(prm, plan.tile_unroll, s);
-    case 4: return launch_partial_gc<E, D, 4>(prm, plan.tile_unroll, s);
-    case 8: return launch_partial_gc<E, D, 8>(prm, plan.tile_unroll, s);
+    case 1: return launch_partial_gc<E, D, 1>(prm, plan, s);
+    case 2: return launch_partial_gc<E, D, 2>(prm, plan, s);
+    case 4: return launch_partial_gc<E, D, 4>(prm, plan, s);
+    case 8: return launch_partial_gc<E, D, 8>(prm, plan, s);
   }
   return hipErrorInvalidValue;
 }

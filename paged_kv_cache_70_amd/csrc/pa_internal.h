@@ -33,6 +33,7 @@ struct DecodePlan {
   int32_t nchunks;         // G / heads_per_unit
   int32_t P;               // partition length in tokens
   int32_t maxP;            // ceil(W * bs / P)
+  int32_t kv_per_wave;     // kv heads whose rows one load instruction covers (KG)
   int32_t tile_unroll;     // 16-byte loads per K (and per V) per tile and lane
 };
 
