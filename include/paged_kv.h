@@ -106,9 +106,10 @@ int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_heads,
 
 /*
  * pa_decode_workspace_bytes — size of the fp32 workspace pa_decode needs for
- * the per-partition partial results (max, sum, accumulator per head) of the
- * split-KV path.  partition_size 0 selects pa_decode_partition_size().
- * Returns 0 for invalid arguments.
+ * the per-partition partial results (max, sum, accumulator per query head) of
+ * the split-KV path; 0 when no sequence can span two partitions.
+ * partition_size 0 selects pa_decode_partition_size().  Returns 0 for invalid
+ * arguments.
  */
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads,
                                  int32_t max_blocks_per_seq, const pa_cache_desc* desc,
@@ -136,9 +137,13 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads,
  *   partition_size      tokens per split-KV partition: 0 = automatic, else a
  *                       positive multiple of block_size, at most 64 * block_size
  *   workspace           device, >= pa_decode_workspace_bytes(...) bytes, no
- *                       initial contents required; may be NULL only when
- *                       workspace_bytes is 0 and the requirement is 0
+ *                       initial contents required; may be NULL only when the
+ *                       requirement is 0.  Calls that share a workspace must
+ *                       not run concurrently.
  *   stream              hipStream_t
+ *
+ * bf16 caches run on the matrix cores (16-token tiles, up to 16 query heads of
+ * a kv head per product); fp32 caches on the vector ALUs.
  */
 int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
               const int32_t* block_tables, const int32_t* context_lens, float scale,
@@ -147,10 +152,12 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * pa_decode_partials — first half of pa_decode (same arguments): every
- * (sequence, kv head, partition) folds its tokens with an online softmax.
- * Sequences that fit in one partition (and n == 0) get their final output
- * written to `out`; the others leave fp32 partial results in `workspace`.
+ * pa_decode_partials — first half of a two-pass decode (same arguments as
+ * pa_decode): every (sequence, kv head, partition) folds its tokens with an
+ * online softmax.  Sequences that fit in one partition (and n == 0) get their
+ * final output written to `out`; the others leave fp32 partial results in
+ * `workspace` for pa_decode_merge (or for a merge of partitions computed
+ * elsewhere).
  */
 int pa_decode_partials(void* out, const void* q, const void* k_cache, const void* v_cache,
                        const int32_t* block_tables, const int32_t* context_lens, float scale,

@@ -14,6 +14,7 @@ from .api import (  # noqa: F401
     decode_partials,
     library_path,
     load_library,
+    new_workspace,
     partition_size,
     status_string,
     workspace_bytes,

@@ -32,6 +32,7 @@ __all__ = [
     "decode_merge",
     "partition_size",
     "workspace_bytes",
+    "new_workspace",
     "status_string",
     "abi_version",
 ]
@@ -166,6 +167,13 @@ def workspace_bytes(num_seqs: int, num_heads: int, max_blocks_per_seq: int, k_ca
     desc = cache_desc(k_cache)
     return int(load_library().pa_decode_workspace_bytes(num_seqs, num_heads, max_blocks_per_seq,
                                                         ctypes.byref(desc), partition_size))
+
+
+def new_workspace(num_seqs: int, num_heads: int, max_blocks_per_seq: int, k_cache: torch.Tensor,
+                  partition_size: int = 0) -> torch.Tensor:
+    """A decode workspace of the size pa_decode_workspace_bytes() gives."""
+    need = workspace_bytes(num_seqs, num_heads, max_blocks_per_seq, k_cache, partition_size)
+    return torch.empty(max(need, 16), dtype=torch.uint8, device=k_cache.device)
 
 
 def _decode_args(q, k_cache, v_cache, block_tables, context_lens, out, workspace, partition_size):

@@ -63,22 +63,37 @@ static int32_t tile_unroll(const pa_cache_desc* d) {
 }
 
 // Tokens per split-KV partition chosen without looking at the (device-side)
-// context lengths: the smallest power-of-two multiple of the block size, at
-// least 256 tokens, that keeps the worst-case number of work units
-// (sequences x kv heads x head chunks x partitions of the longest possible
-// context) at or below kTargetUnits.
-static constexpr int64_t kTargetUnits = 8192;
+// context lengths: 256 tokens (rounded to a whole number of blocks), doubled
+// while the worst-case number of work units (sequences x kv-head units x
+// partitions of the longest possible context) exceeds the target.  Units of
+// a few hundred tokens keep the hardware dispatcher's balancing fine-grained
+// while the partial results stay a few percent of the KV bytes.
+static constexpr int64_t kTargetUnitsMfma = 65536;
+static constexpr int64_t kTargetUnitsValu = 8192;
 // A partition's block-table entries are held one per lane of a wavefront.
 static constexpr int32_t kMaxBlocksPerPartition = 64;
-static int32_t auto_partition(int32_t B, int32_t H, int32_t W, const pa_cache_desc* d) {
-  const int32_t G = H / d->num_kv_heads;
-  const int64_t rows = (int64_t)B * (d->num_kv_heads / kv_per_wave(d)) * (G / heads_per_unit(G));
+static int32_t auto_partition(int32_t B, int32_t W, const pa_cache_desc* d, const DecodePlan& plan) {
+  const int32_t kv_units = plan.use_mfma ? d->num_kv_heads : d->num_kv_heads / kv_per_wave(d);
+  const int64_t rows = (int64_t)B * kv_units * plan.nchunks;
+  const int64_t target = plan.use_mfma ? kTargetUnitsMfma : kTargetUnitsValu;
   const int64_t max_len = (int64_t)W * d->block_size;
   int64_t P = 256;
   if (P % d->block_size) P = d->block_size;
   const int64_t P_max = (int64_t)kMaxBlocksPerPartition * d->block_size;
-  while (P < max_len && P < P_max && rows * ((max_len + P - 1) / P) > kTargetUnits) P *= 2;
+  while (P < max_len && P < P_max && rows * ((max_len + P - 1) / P) > target) P *= 2;
   return (int32_t)P;
+}
+
+// Wavefronts per workgroup: a unit's tiles are shared by NW wavefronts (merged
+// through LDS) when the worst-case unit count alone would leave the chip
+// short of wavefronts.
+static constexpr int64_t kTargetWaves = 8192;
+static int32_t waves_per_unit(int32_t B, const pa_cache_desc* d, const DecodePlan& p) {
+  const int64_t units = (int64_t)B * (d->num_kv_heads / p.kv_per_wave) * p.nchunks * p.maxP;
+  int32_t nw = 1;
+  const int32_t nw_max = p.heads_per_unit <= 4 ? 4 : 2;
+  while (nw < nw_max && units * nw < kTargetWaves) nw *= 2;
+  return nw;
 }
 
 struct Checked {
@@ -99,9 +114,17 @@ static int check_decode_sizes(int32_t B, int32_t H, int32_t W, const pa_cache_de
   if (max_len > INT_MAX / 2) return PA_ERR_TOO_LARGE;
   DecodePlan p;
   const int32_t G = H / d->num_kv_heads;
-  p.heads_per_unit = heads_per_unit(G);
-  p.nchunks = G / p.heads_per_unit;
-  p.P = partition_size ? partition_size : auto_partition(B, H, W, d);
+  p.use_mfma = d->dtype == PA_BF16;
+  if (p.use_mfma) {
+    // matrix-core kernel: one kv head per unit, its query heads as up to 16
+    // product columns
+    p.heads_per_unit = G < 16 ? G : 16;
+    p.nchunks = (G + 15) / 16;
+  } else {
+    p.heads_per_unit = heads_per_unit(G);
+    p.nchunks = G / p.heads_per_unit;
+  }
+  p.P = partition_size ? partition_size : auto_partition(B, W, d, p);
   const int64_t maxP = (max_len + p.P - 1) / p.P;
   // grid.y = partitions and grid.z = B are limited to 65535; the merge
   // kernel keeps one fp32 weight per partition in LDS (at most 64 KiB).
@@ -110,6 +133,7 @@ static int check_decode_sizes(int32_t B, int32_t H, int32_t W, const pa_cache_de
       maxP > 16384)
     return PA_ERR_TOO_LARGE;
   p.maxP = (int32_t)maxP;
+  p.waves_per_unit = p.use_mfma ? 1 : waves_per_unit(B, d, p);
   p.tile_unroll = tile_unroll(d);
   out->plan = p;
   const int64_t slots = (int64_t)B * H * maxP;
@@ -130,15 +154,20 @@ static int decode_params(void* out, const void* q, const void* k_cache, const vo
   }
   DecodeParams& p = *prm;
   p.out = out;
+  // workspace: [acc: B*H*maxP*D fp32][ml: B*H*maxP*2 fp32]
   const size_t acc_bytes = (size_t)B * H * ck.plan.maxP * d->head_dim * sizeof(float);
-  p.ws_acc = ck.ws_bytes ? static_cast<float*>(workspace) : nullptr;
-  p.ws_ml = ck.ws_bytes ? reinterpret_cast<float*>(static_cast<char*>(workspace) + acc_bytes) : nullptr;
+  char* ws = static_cast<char*>(workspace);
+  p.ws_acc = ck.ws_bytes ? reinterpret_cast<float*>(ws) : nullptr;
+  p.ws_ml = ck.ws_bytes ? reinterpret_cast<float*>(ws + acc_bytes) : nullptr;
   p.q = q;
   p.k_cache = k_cache;
   p.v_cache = v_cache;
   p.tables = block_tables;
   p.ctx = context_lens;
-  p.scale_log2 = scale * 1.4426950408889634f;   // log2(e)
+  // The kernels take a positive base-2 scale; the sign goes into q.
+  const float s2 = scale * 1.4426950408889634f;   // log2(e)
+  p.q_mode = s2 > 0.0f ? 0 : (s2 < 0.0f ? 1 : 2);
+  p.scale_log2 = s2 > 0.0f ? s2 : (s2 < 0.0f ? -s2 : 1.0f);
   p.B = B;
   p.H = H;
   p.KVH = d->num_kv_heads;
@@ -226,8 +255,12 @@ static int decode_common(bool partials, bool merge, void* out, const void* q,
                      num_heads, max_blocks_per_seq, desc, workspace, workspace_bytes, ck, &prm);
   if (st) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (partials && launch_decode_partials(prm, desc->dtype, desc->head_dim, ck.plan, s) != hipSuccess)
-    return PA_ERR_LAUNCH;
+  if (partials) {
+    const hipError_t e = ck.plan.use_mfma
+                             ? launch_decode_partials_mfma(prm, desc->head_dim, s)
+                             : launch_decode_partials(prm, desc->dtype, desc->head_dim, ck.plan, s);
+    if (e != hipSuccess) return PA_ERR_LAUNCH;
+  }
   if (merge && ck.plan.maxP > 1 &&
       launch_decode_merge(prm, desc->dtype, desc->head_dim, s) != hipSuccess)
     return PA_ERR_LAUNCH;

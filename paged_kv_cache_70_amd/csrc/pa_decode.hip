@@ -44,6 +44,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 // ---------------------------------------------------------------------------
 struct F32 {
   static constexpr int EPV = 4;
+  static constexpr uint32_t kSignMask = 0x80000000u;   // sign bit of each 32-bit word
   // partial dot product of this lane's 4 q values with 4 k values
   __device__ static __forceinline__ float dot(const u32x4& q, const u32x4& k) {
     float s = __uint_as_float(q[0]) * __uint_as_float(k[0]);
@@ -66,6 +67,7 @@ struct F32 {
 
 struct BF16 {
   static constexpr int EPV = 8;
+  static constexpr uint32_t kSignMask = 0x80008000u;   // sign bits of both bf16 halves
   // bf16 x bf16 products are exact in fp32; v_dot2 adds two of them per step.
   __device__ static __forceinline__ float dot(const u32x4& q, const u32x4& k) {
     float s = 0.0f;
@@ -183,8 +185,15 @@ __device__ __forceinline__ u32x4 load16(const void* p) {
 // ---------------------------------------------------------------------------
 // K2: split-KV partial kernel
 // ---------------------------------------------------------------------------
-template <typename E, int D, int GC, int U, int KG>
-__global__ __launch_bounds__(64) void decode_partial_kernel(const DecodeParams prm) {
+// The running softmax state of a row is kept against a reference maximum m
+// (base-2 units) that is raised only when a score exceeds it by more than
+// kRescaleSlack: every term 2^(s - m) stays below 2^kRescaleSlack, the
+// accumulators hold sum 2^(s - m) v and sum 2^(s - m), and the final ratio is
+// the same softmax.  Raising m rescales the accumulators by 2^(m_old - m_new).
+constexpr float kRescaleSlack = 8.0f;
+
+template <typename E, int D, int GC, int U, int KG, int NW>
+__global__ __launch_bounds__(64 * NW) void decode_partial_kernel(const DecodeParams prm) {
   constexpr int EPV = E::EPV;
   constexpr int LPT = D / EPV;       // lanes per (token, kv head) row of D elements
   constexpr int RPW = 64 / LPT;      // rows per load instruction
@@ -192,9 +201,11 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(const DecodeParams p
   constexpr int TR = RPW / KG;       // tokens per load instruction
   constexpr int TT = TR * U;         // tokens per tile
   constexpr int ESZ = 16 / EPV;      // bytes per element
+  constexpr int NSTATE = GC * (EPV + 2);
 
   // Grid: x = (kv-head group, head chunk) fastest, so the groups covering one
   // block's token rows are dispatched together; y = partition; z = sequence.
+  // The NW wavefronts of a workgroup share the unit and take its tiles in turn.
   const int p = blockIdx.y;
   const int b = blockIdx.z;
   const int kvg = blockIdx.x / prm.nchunks;
@@ -203,11 +214,12 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(const DecodeParams p
   int n = prm.ctx[b];
   n = n < 0 ? 0 : (n > prm.max_tokens ? prm.max_tokens : n);
   const int nparts = (n + prm.P - 1) / prm.P;
-  if (p >= (nparts > 0 ? nparts : 1)) return;
+  if (p >= (nparts > 0 ? nparts : 1)) return;           // uniform over the workgroup
   const int t_begin = p * prm.P;
   const int t_end = min(n, t_begin + prm.P);
 
-  const int lane = threadIdx.x;
+  const int wave = NW > 1 ? (int)(threadIdx.x >> 6) : 0;
+  const int lane = threadIdx.x & 63;
   const int r = lane / LPT;          // row of this lane within a load
   const int c = lane - r * LPT;      // 16-byte piece of the D-row
   // Row r covers kv head kvg * KG + r % KG of token r / KG: the KG heads of
@@ -218,19 +230,28 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(const DecodeParams p
   const int G = prm.H / prm.KVH;
   const int h0 = kvh * G + chunk * GC;
 
-  // This lane's slice of the GC queries.
+  // This lane's slice of the GC queries.  The host passes a positive scale:
+  // for a negative one the queries are negated here, for zero they are zeroed.
   u32x4 qv[GC];
   {
     const char* qb = static_cast<const char*>(prm.q) +
                      ((size_t)(b * prm.H + h0) * D + (size_t)c * EPV) * ESZ;
+    const uint32_t flip = prm.q_mode == 1 ? E::kSignMask : 0u;
+    const uint32_t keep = prm.q_mode == 2 ? 0u : 0xffffffffu;
 #pragma unroll
-    for (int g = 0; g < GC; ++g) qv[g] = load16(qb + (size_t)g * D * ESZ);
+    for (int g = 0; g < GC; ++g) {
+      qv[g] = load16(qb + (size_t)g * D * ESZ);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) qv[g][i] = (qv[g][i] ^ flip) & keep;
+    }
   }
+  const float cs = prm.scale_log2;   // > 0
 
-  float m[GC], l[GC], acc[GC][EPV];
+  float m[GC], mneg[GC], l[GC], acc[GC][EPV];
 #pragma unroll
   for (int g = 0; g < GC; ++g) {
     m[g] = -INFINITY;
+    mneg[g] = 0.0f;                  // -m, or 0 while m is -inf
     l[g] = 0.0f;
 #pragma unroll
     for (int e = 0; e < EPV; ++e) acc[g][e] = 0.0f;
@@ -285,7 +306,7 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(const DecodeParams p
   // selection.
   auto fold_tile = [&](auto masked, bool ok, int nvalid, const u32x4 (&kr)[U], const u32x4 (&vr)[U]) {
     constexpr bool MASKED = decltype(masked)::value;
-    float s[U][GC];
+    float s[U][GC];                  // q.k, then scaled to base-2 units
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
@@ -295,21 +316,33 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(const DecodeParams p
     for (int u = 0; u < U; ++u) {
       const bool valid = ok && (!MASKED || (u * TR + tr) < nvalid);
 #pragma unroll
-      for (int g = 0; g < GC; ++g) s[u][g] = valid ? s[u][g] * prm.scale_log2 : -INFINITY;
+      for (int g = 0; g < GC; ++g) s[u][g] = valid ? s[u][g] * cs : -INFINITY;
     }
-    float mu[GC];
+    // Raise the reference maxima only when some score outgrows them.  The
+    // maxima are taken over the same scaled scores the exponentials use, so a
+    // lone score gives exactly 2^0 = 1.
+    float mt[GC];
+    bool raise = false;
 #pragma unroll
     for (int g = 0; g < GC; ++g) {
-      float mt = s[0][g];
+      float x = s[0][g];
 #pragma unroll
-      for (int u = 1; u < U; ++u) mt = fmaxf(mt, s[u][g]);
-      const float m_new = fmaxf(m[g], mt);
-      mu[g] = (m_new == -INFINITY) ? 0.0f : m_new;   // a row with no token yet
-      const float corr = exp2_fast(m[g] - mu[g]);
-      m[g] = m_new;
-      l[g] *= corr;
+      for (int u = 1; u < U; ++u) x = fmaxf(x, s[u][g]);
+      mt[g] = x;
+      raise |= mt[g] > m[g] + kRescaleSlack;
+    }
+    if (__builtin_amdgcn_ballot_w64(raise)) {             // wavefront-uniform
 #pragma unroll
-      for (int e = 0; e < EPV; ++e) acc[g][e] *= corr;
+      for (int g = 0; g < GC; ++g) {
+        if (mt[g] > m[g]) {
+          const float corr = exp2_fast(m[g] - mt[g]);        // 0 while m is -inf
+          m[g] = mt[g];
+          mneg[g] = -mt[g];
+          l[g] *= corr;
+#pragma unroll
+          for (int e = 0; e < EPV; ++e) acc[g][e] *= corr;
+        }
+      }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -322,7 +355,7 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(const DecodeParams p
       }
 #pragma unroll
       for (int g = 0; g < GC; ++g) {
-        const float pr = exp2_fast(s[u][g] - mu[g]);
+        const float pr = exp2_fast(s[u][g] + mneg[g]);
         l[g] += pr;
 #pragma unroll
         for (int e = 0; e < EPV; ++e) acc[g][e] = fmaf(pr, vf[e], acc[g][e]);
@@ -330,47 +363,93 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(const DecodeParams p
     }
   };
 
-  // Full tiles in a loop of pairs (A/B buffers swap roles every half, with a
-  // single loop exit so that each buffer keeps its registers), then the odd
-  // full tile and the one partial tile (sequence end), if any.
+  // This wavefront's tiles are w, w + NW, w + 2 NW, ... of the unit: full
+  // tiles in a loop of pairs (A/B buffers swap roles every half, with a single
+  // loop exit so that each buffer keeps its registers), then the odd full tile
+  // and the unit's one partial tile (sequence end), if it is this wave's.
   const int ntok = t_end - t_begin;
   const int nfull = ntok > 0 ? ntok / TT : 0;
   const int rem = ntok > 0 ? ntok - nfull * TT : 0;
   const int ntiles = nfull + (rem ? 1 : 0);
-  if (ntiles > 0) {
-    // tile i starts at t_begin + i * TT; past the last tile the last one is
-    // fetched again (cache hit) so that every step issues its loads.
-    auto tile_at = [&](int i) { return t_begin + min(i, ntiles - 1) * TT; };
+  const int my_full = nfull > wave ? (nfull - wave + NW - 1) / NW : 0;
+  const int my_tiles = ntiles > wave ? (ntiles - wave + NW - 1) / NW : 0;
+  const bool my_rem = my_tiles > my_full;
+  if (my_tiles > 0) {
+    // j-th tile of this wave; past its last one the last one is fetched again
+    // (cache hit) so that every step issues its loads.
+    auto tile_at = [&](int j) { return t_begin + (wave + min(j, my_tiles - 1) * NW) * TT; };
     bool okA = load_tile(tile_at(0), kA, vA), okB;
-    const int npairs = nfull >> 1;
+    const int npairs = my_full >> 1;
     for (int ip = 0; ip < npairs; ++ip) {
       okB = load_tile(tile_at(2 * ip + 1), kB, vB);
       fold_tile(std::false_type{}, okA, TT, kA, vA);
       okA = load_tile(tile_at(2 * ip + 2), kA, vA);
       fold_tile(std::false_type{}, okB, TT, kB, vB);
     }
-    if (nfull & 1) {
-      okB = load_tile(tile_at(nfull), kB, vB);
+    if (my_full & 1) {
+      okB = load_tile(tile_at(my_full), kB, vB);
       fold_tile(std::false_type{}, okA, TT, kA, vA);
-      if (rem) fold_tile(std::true_type{}, okB, rem, kB, vB);
-    } else if (rem) {
+      if (my_rem) fold_tile(std::true_type{}, okB, rem, kB, vB);
+    } else if (my_rem) {
       fold_tile(std::true_type{}, okA, rem, kA, vA);
     }
   }
 
-  // Combine the TR row states of each kv head (rows LPT * KG lanes apart).
-  const bool single = nparts <= 1;
+  // Combine the TR row states of each kv head (rows LPT * KG lanes apart),
+  // then, with several wavefronts, the wavefronts' states through LDS.
+  float M[GC], L[GC];
 #pragma unroll
   for (int g = 0; g < GC; ++g) {
-    const float M = rows_max<LPT * KG>(m[g]);
-    const float f = (m[g] == -INFINITY) ? 0.0f : exp2_fast(m[g] - M);
-    const float L = rows_sum<LPT * KG>(l[g] * f);
+    M[g] = rows_max<LPT * KG>(m[g]);
+    const float f = (m[g] == -INFINITY) ? 0.0f : exp2_fast(m[g] - M[g]);
+    L[g] = rows_sum<LPT * KG>(l[g] * f);
 #pragma unroll
     for (int e = 0; e < EPV; ++e) acc[g][e] = rows_sum<LPT * KG>(acc[g][e] * f);
+  }
+  if constexpr (NW > 1) {
+    extern __shared__ float lds_state[];             // [NW][64 lanes][NSTATE]
+    float* mine = lds_state + ((size_t)wave * 64 + lane) * NSTATE;
+    if (wave > 0 && tr == 0) {
+#pragma unroll
+      for (int g = 0; g < GC; ++g) {
+        mine[g * (EPV + 2)] = M[g];
+        mine[g * (EPV + 2) + 1] = L[g];
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) mine[g * (EPV + 2) + 2 + e] = acc[g][e];
+      }
+    }
+    __syncthreads();
+    if (wave > 0) return;
     if (tr == 0) {
+#pragma unroll
+      for (int g = 0; g < GC; ++g) {
+        float Mx = M[g];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) Mx = fmaxf(Mx, lds_state[((size_t)w * 64 + lane) * NSTATE + g * (EPV + 2)]);
+        const float f0 = (M[g] == -INFINITY) ? 0.0f : exp2_fast(M[g] - Mx);
+        L[g] *= f0;
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) acc[g][e] *= f0;
+#pragma unroll
+        for (int w = 1; w < NW; ++w) {
+          const float* o = lds_state + ((size_t)w * 64 + lane) * NSTATE + g * (EPV + 2);
+          const float fw = (o[0] == -INFINITY) ? 0.0f : exp2_fast(o[0] - Mx);
+          L[g] = fmaf(o[1], fw, L[g]);
+#pragma unroll
+          for (int e = 0; e < EPV; ++e) acc[g][e] = fmaf(o[2 + e], fw, acc[g][e]);
+        }
+        M[g] = Mx;
+      }
+    }
+  }
+
+  const bool single = nparts <= 1;
+  if (tr == 0) {
+#pragma unroll
+    for (int g = 0; g < GC; ++g) {
       const size_t bh = (size_t)b * prm.H + h0 + g;
       if (single) {
-        const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+        const float inv = L[g] > 0.0f ? 1.0f / L[g] : 0.0f;
         float o[EPV];
 #pragma unroll
         for (int e = 0; e < EPV; ++e) o[e] = acc[g][e] * inv;
@@ -381,7 +460,7 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(const DecodeParams p
 #pragma unroll
         for (int e = 0; e < EPV; e += 4)
           *reinterpret_cast<float4*>(dst + e) = make_float4(acc[g][e], acc[g][e + 1], acc[g][e + 2], acc[g][e + 3]);
-        if (c == 0) *reinterpret_cast<float2*>(prm.ws_ml + slot * 2) = make_float2(M, L);
+        if (c == 0) *reinterpret_cast<float2*>(prm.ws_ml + slot * 2) = make_float2(M[g], L[g]);
       }
     }
   }
@@ -475,29 +554,42 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const DecodeParams prm
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-template <typename E, int D, int GC, int U, int KG>
-static hipError_t launch_partial_u(const DecodeParams& prm, hipStream_t stream) {
+template <typename E, int D, int GC, int U, int KG, int NW>
+static hipError_t launch_partial_nw(const DecodeParams& prm, hipStream_t stream) {
+  constexpr size_t kLds = NW > 1 ? (size_t)NW * 64 * GC * (E::EPV + 2) * sizeof(float) : 0;
   dim3 grid((prm.KVH / KG) * prm.nchunks, prm.maxP, prm.B);
-  hipLaunchKernelGGL((decode_partial_kernel<E, D, GC, U, KG>), grid, dim3(64), 0, stream, prm);
+  hipLaunchKernelGGL((decode_partial_kernel<E, D, GC, U, KG, NW>), grid, dim3(64 * NW), kLds, stream, prm);
   return hipGetLastError();
+}
+
+template <typename E, int D, int GC, int U, int KG>
+static hipError_t launch_partial_u(const DecodeParams& prm, int NW, hipStream_t stream) {
+  switch (NW) {
+    case 1: return launch_partial_nw<E, D, GC, U, KG, 1>(prm, stream);
+    case 2: return launch_partial_nw<E, D, GC, U, KG, 2>(prm, stream);
+    case 4:
+      if constexpr (GC <= 4) return launch_partial_nw<E, D, GC, U, KG, 4>(prm, stream);
+      break;
+  }
+  return hipErrorInvalidValue;
 }
 
 // (KG, U) pairs: KG kv heads per wavefront (a power of two dividing RPW),
 // U loads per tile with TR * U <= block size.
 template <typename E, int D, int GC, int KG>
-static hipError_t launch_partial_kg(const DecodeParams& prm, int U, hipStream_t stream) {
+static hipError_t launch_partial_kg(const DecodeParams& prm, const DecodePlan& plan, hipStream_t stream) {
   constexpr int RPW = 64 / (D / E::EPV);
   if constexpr (RPW % KG != 0) {
     return hipErrorInvalidValue;
   } else {
     constexpr int TR = RPW / KG;
-    switch (U) {
-      case 4: return launch_partial_u<E, D, GC, 4, KG>(prm, stream);
+    switch (plan.tile_unroll) {
+      case 4: return launch_partial_u<E, D, GC, 4, KG>(prm, plan.waves_per_unit, stream);
       case 2:
-        if constexpr (TR >= 4) return launch_partial_u<E, D, GC, 2, KG>(prm, stream);
+        if constexpr (TR >= 4) return launch_partial_u<E, D, GC, 2, KG>(prm, plan.waves_per_unit, stream);
         break;
       case 1:
-        if constexpr (TR >= 8) return launch_partial_u<E, D, GC, 1, KG>(prm, stream);
+        if constexpr (TR >= 8) return launch_partial_u<E, D, GC, 1, KG>(prm, plan.waves_per_unit, stream);
         break;
     }
     return hipErrorInvalidValue;
@@ -507,10 +599,10 @@ static hipError_t launch_partial_kg(const DecodeParams& prm, int U, hipStream_t 
 template <typename E, int D, int GC>
 static hipError_t launch_partial_gc(const DecodeParams& prm, const DecodePlan& plan, hipStream_t s) {
   switch (plan.kv_per_wave) {
-    case 1: return launch_partial_kg<E, D, GC, 1>(prm, plan.tile_unroll, s);
-    case 2: return launch_partial_kg<E, D, GC, 2>(prm, plan.tile_unroll, s);
-    case 4: return launch_partial_kg<E, D, GC, 4>(prm, plan.tile_unroll, s);
-    case 8: return launch_partial_kg<E, D, GC, 8>(prm, plan.tile_unroll, s);
+    case 1: return launch_partial_kg<E, D, GC, 1>(prm, plan, s);
+    case 2: return launch_partial_kg<E, D, GC, 2>(prm, plan, s);
+    case 4: return launch_partial_kg<E, D, GC, 4>(prm, plan, s);
+    case 8: return launch_partial_kg<E, D, GC, 8>(prm, plan, s);
   }
   return hipErrorInvalidValue;
 }

@@ -18,7 +18,8 @@ struct DecodeParams {
   const void* v_cache;
   const int32_t* tables;   // [B, W]
   const int32_t* ctx;      // [B]
-  float scale_log2;        // scale * log2(e): scores are kept in base-2 exponent units
+  float scale_log2;        // |scale| * log2(e) > 0: scores are kept in base-2 exponent units
+  int32_t q_mode;          // 0: q as given, 1: negate q (scale < 0), 2: zero q (scale == 0)
   int32_t B, H, KVH, W, NB;
   int32_t bs_log2, bs_mask;
   int32_t P;               // tokens per partition, multiple of bs
@@ -29,11 +30,13 @@ struct DecodeParams {
 
 // Launch-shape choices made on the host (pure functions of the sizes).
 struct DecodePlan {
+  int32_t use_mfma;        // bf16: matrix-core kernel (16-token tiles, up to 16 heads per unit)
   int32_t heads_per_unit;  // query heads sharing one K/V stream in one wavefront
   int32_t nchunks;         // G / heads_per_unit
   int32_t P;               // partition length in tokens
   int32_t maxP;            // ceil(W * bs / P)
   int32_t kv_per_wave;     // kv heads whose rows one load instruction covers (KG)
+  int32_t waves_per_unit;  // wavefronts of a workgroup sharing one unit's tiles (NW)
   int32_t tile_unroll;     // 16-byte loads per K (and per V) per tile and lane
 };
 
@@ -46,6 +49,8 @@ hipError_t launch_write_kv(void* k_cache, void* v_cache, const void* k, const vo
 
 hipError_t launch_decode_partials(const DecodeParams& prm, int32_t dtype, int32_t D,
                                   const DecodePlan& plan, hipStream_t stream);
+
+hipError_t launch_decode_partials_mfma(const DecodeParams& prm, int32_t D, hipStream_t stream);
 
 hipError_t launch_decode_merge(const DecodeParams& prm, int32_t dtype, int32_t D,
                                hipStream_t stream);

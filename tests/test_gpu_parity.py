@@ -202,21 +202,49 @@ def test_zero_length_gives_zeros():
 
 
 def test_split_entry_points_equal_decode():
-    """pa_decode_partials followed by pa_decode_merge gives pa_decode's bits."""
+    """pa_decode_partials followed by pa_decode_merge gives pa_decode's result
+    (both match the oracle; they run the same kernels, so bits agree)."""
     _say("split entry points")
     w = make_custom(num_seqs=4, num_heads=16, num_kv_heads=4, head_dim=128, block_size=16,
                     dtype="bf16", lens=[700, 5, 129, 1000], seed=6, device="cuda")
     P = 64
     a = pk.decode(w.q, w.k_cache, w.v_cache, w.block_tables, w.context_lens, w.scale, partition_size=P)
-    ws = torch.empty(pk.workspace_bytes(4, 16, w.block_tables.shape[1], w.k_cache, P),
-                     dtype=torch.uint8, device="cuda")
+    ws = pk.new_workspace(4, 16, w.block_tables.shape[1], w.k_cache, P)
     b = torch.empty_like(w.q)
     pk.decode_partials(w.q, w.k_cache, w.v_cache, w.block_tables, w.context_lens, w.scale, out=b,
                        workspace=ws, partition_size=P)
     pk.decode_merge(w.q, w.k_cache, w.block_tables, w.context_lens, out=b, workspace=ws,
                     partition_size=P)
     torch.cuda.synchronize()
+    ref = O.decode(stored_np(w.q), stored_np(w.k_cache), stored_np(w.v_cache),
+                   stored_np(w.block_tables), stored_np(w.context_lens), w.scale, "bf16")
+    assert_matches_oracle(a, ref, "bf16", "decode")
+    assert_matches_oracle(b, ref, "bf16", "two-pass")
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_workspace_reused_across_calls_and_sizes():
+    """One workspace, with stale contents from earlier calls, serves repeated
+    calls and other geometries: results are identical call after call."""
+    _say("workspace reuse")
+    big = torch.full((8 << 20,), 0x7F, dtype=torch.uint8, device="cuda")   # stale garbage
+    for trial, (B, H, KVH, lens, P) in enumerate([
+            (4, 16, 4, [700, 5, 129, 1000], 32),
+            (6, 32, 8, [1, 300, 17, 64, 999, 250], 16),
+            (2, 8, 2, [4000, 33], 64)]):
+        w = make_custom(num_seqs=B, num_heads=H, num_kv_heads=KVH, head_dim=128, block_size=16,
+                        dtype="bf16", lens=lens, seed=20 + trial, device="cuda")
+        assert pk.workspace_bytes(B, H, w.block_tables.shape[1], w.k_cache, P) <= big.numel()
+        ref = O.decode(stored_np(w.q), stored_np(w.k_cache), stored_np(w.v_cache),
+                       stored_np(w.block_tables), stored_np(w.context_lens), w.scale, "bf16")
+        outs = []
+        for rep in range(3):
+            o = pk.decode(w.q, w.k_cache, w.v_cache, w.block_tables, w.context_lens, w.scale,
+                          workspace=big, partition_size=P)
+            torch.cuda.synchronize()
+            assert_matches_oracle(o, ref, "bf16", f"reuse trial {trial} rep {rep}")
+            outs.append(o.view(torch.int16).clone())
+        assert all(torch.equal(outs[0], x) for x in outs[1:])
 
 
 def test_out_of_order_and_aliased_tables():

@@ -25,8 +25,8 @@ def test_library_exports_every_declared_symbol():
     lib = pk.load_library()
     names = _declared()
     assert {"pa_write_kv", "pa_decode", "pa_decode_partials", "pa_decode_merge",
-            "pa_decode_workspace_bytes", "pa_decode_partition_size", "pa_status_string",
-            "pa_abi_version"} <= set(names)
+            "pa_decode_workspace_bytes", "pa_decode_partition_size",
+            "pa_status_string", "pa_abi_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
     assert pk.abi_version() >> 16 == 1
@@ -76,11 +76,13 @@ def test_workspace_and_partition_queries():
     P = lib.pa_decode_partition_size(64, 32, 256, ctypes.byref(d))
     assert P > 0 and P % 16 == 0
     maxP = -(-256 * 16 // P)
+    CTRL = 0
     ws = lib.pa_decode_workspace_bytes(64, 32, 256, ctypes.byref(d), 0)
-    assert ws == (64 * 32 * maxP * (128 + 2) * 4 if maxP > 1 else 0)
+    assert ws == (CTRL + 64 * 32 * maxP * (128 + 2) * 4 if maxP > 1 else 0)
     # explicit partition sizes
     assert lib.pa_decode_workspace_bytes(2, 8, 4, ctypes.byref(d), 64) == 0       # one partition
-    assert lib.pa_decode_workspace_bytes(2, 8, 4, ctypes.byref(d), 16) == 2 * 8 * 4 * 130 * 4
+    assert lib.pa_decode_workspace_bytes(2, 8, 4, ctypes.byref(d), 16) == CTRL + 2 * 8 * 4 * 130 * 4
+    assert lib.pa_decode_workspace_bytes(2, 8, 4, ctypes.byref(d), 16 * 65) == 0  # > 64 blocks
     assert lib.pa_decode_workspace_bytes(2, 8, 4, ctypes.byref(d), 24) == 0       # invalid
     # long contexts get more than one partition, small ones may not
     assert lib.pa_decode_partition_size(8, 32, 8192, ctypes.byref(d)) < 8192 * 16
