@@ -63,24 +63,27 @@ static int32_t tile_unroll(const pa_cache_desc* d) {
 }
 
 // Tokens per split-KV partition chosen without looking at the (device-side)
-// context lengths: 256 tokens (rounded to a whole number of blocks), doubled
-// while the worst-case number of work units (sequences x kv-head units x
-// partitions of the longest possible context) exceeds the target.  Units of
-// a few hundred tokens keep the hardware dispatcher's balancing fine-grained
-// while the partial results stay a few percent of the KV bytes.
-static constexpr int64_t kTargetUnitsMfma = 65536;
+// context lengths.  Matrix-core path: 256 tokens (a whole number of blocks),
+// doubled while the longest possible context would need more than
+// kMaxPartsPerSeq partitions, so that long contexts do not drown the merge in
+// partial results; a few hundred tokens per unit keep the hardware
+// dispatcher's balancing fine-grained.  Vector-ALU path: doubled while the
+// worst-case number of work units exceeds kTargetUnitsValu.
+static constexpr int64_t kMaxPartsPerSeq = 128;
 static constexpr int64_t kTargetUnitsValu = 8192;
 // A partition's block-table entries are held one per lane of a wavefront.
 static constexpr int32_t kMaxBlocksPerPartition = 64;
 static int32_t auto_partition(int32_t B, int32_t W, const pa_cache_desc* d, const DecodePlan& plan) {
-  const int32_t kv_units = plan.use_mfma ? d->num_kv_heads : d->num_kv_heads / kv_per_wave(d);
-  const int64_t rows = (int64_t)B * kv_units * plan.nchunks;
-  const int64_t target = plan.use_mfma ? kTargetUnitsMfma : kTargetUnitsValu;
   const int64_t max_len = (int64_t)W * d->block_size;
+  const int64_t P_max = (int64_t)kMaxBlocksPerPartition * d->block_size;
   int64_t P = 256;
   if (P % d->block_size) P = d->block_size;
-  const int64_t P_max = (int64_t)kMaxBlocksPerPartition * d->block_size;
-  while (P < max_len && P < P_max && rows * ((max_len + P - 1) / P) > target) P *= 2;
+  if (plan.use_mfma) {
+    while (P < P_max && max_len > P * kMaxPartsPerSeq) P *= 2;
+  } else {
+    const int64_t rows = (int64_t)B * (d->num_kv_heads / kv_per_wave(d)) * plan.nchunks;
+    while (P < max_len && P < P_max && rows * ((max_len + P - 1) / P) > kTargetUnitsValu) P *= 2;
+  }
   return (int32_t)P;
 }
 

@@ -482,7 +482,16 @@ __device__ __forceinline__ float wave_sum(float x) {
 
 template <typename E, int D>
 __global__ __launch_bounds__(64) void decode_merge_kernel(const DecodeParams prm) {
-  extern __shared__ float wsh[];   // one weight per partition
+  // One wavefront per (sequence, head).  A partial accumulator row is D fp32
+  // = D / 4 lanes x 16 B, so one load instruction brings PPI = 256 / D rows;
+  // lane (sub, dl) accumulates rows sub, sub + PPI, ... at d = dl .. dl + 3.
+  // The (max, sum) pairs are read one per lane, R partitions per round; the
+  // accumulator loads of a round are issued before its maxima are reduced.
+  constexpr int LPP = D / 4;
+  constexpr int PPI = 64 / LPP;
+  constexpr int KMAX = PPI * 16 <= 64 ? 16 : 64 / PPI;   // loads per lane per round
+  constexpr int R = PPI * KMAX;                          // partitions per round (<= 64)
+  typedef float f4 __attribute__((ext_vector_type(4)));
   const int h = blockIdx.x;
   const int b = blockIdx.y;
   int n = prm.ctx[b];
@@ -490,64 +499,58 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const DecodeParams prm
   const int nparts = (n + prm.P - 1) / prm.P;
   if (nparts <= 1) return;                 // written by the partial kernel
   const int lane = threadIdx.x;
+  const int sub = lane / LPP;
+  const int dl = (lane % LPP) * 4;
   const size_t bh = (size_t)b * prm.H + h;
   const float* ml = prm.ws_ml + bh * prm.maxP * 2;
   const float* acc = prm.ws_acc + bh * prm.maxP * D;
 
-  float M = -INFINITY;
-  for (int i = lane; i < nparts; i += 64) M = fmaxf(M, ml[2 * i]);
-  M = wave_max(M);
-  float L = 0.0f;
-  for (int i = lane; i < nparts; i += 64) {
-    const float mi = ml[2 * i];
-    const float w = (mi == -INFINITY) ? 0.0f : exp2_fast(mi - M);
-    wsh[i] = w;
-    L += w * ml[2 * i + 1];
+  float Mrun = -INFINITY, Lrun = 0.0f;     // running (max, sum) over rounds, wave-uniform
+  f4 o = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int r0 = 0; r0 < nparts; r0 += R) {
+    const int cnt = min(R, nparts - r0);
+    f4 a[KMAX];
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+      const int i = sub + PPI * k;
+      a[k] = i < cnt ? *reinterpret_cast<const f4*>(acc + (size_t)(r0 + i) * D + dl) : f4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    const float2 mlv = lane < cnt ? *reinterpret_cast<const float2*>(ml + (size_t)(r0 + lane) * 2)
+                                  : make_float2(-INFINITY, 0.0f);
+    const float M = fmaxf(Mrun, wave_max(mlv.x));
+    const float w = mlv.x == -INFINITY ? 0.0f : exp2_fast(mlv.x - M);
+    const float fo = Mrun == -INFINITY ? 0.0f : exp2_fast(Mrun - M);
+    Lrun = Lrun * fo + wave_sum(w * mlv.y);
+    o *= fo;
+    Mrun = M;
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) o += __shfl(w, sub + PPI * k) * a[k];
   }
-  L = wave_sum(L);
-  __syncthreads();
-  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-
-  constexpr int EPV = E::EPV;
-  // lane handles EPV consecutive outputs: D / EPV lanes are active
-  if (lane * EPV < D) {
-    float o[EPV];
+  // rows sub = 0 .. PPI-1 hold disjoint partition sets of the same d range
 #pragma unroll
-    for (int e = 0; e < EPV; ++e) o[e] = 0.0f;
-    const float* a = acc + (size_t)lane * EPV;
-    int i = 0;
-    for (; i + 4 <= nparts; i += 4) {
-      float4 x0[EPV / 4], x1[EPV / 4], x2[EPV / 4], x3[EPV / 4];
+  for (int off = LPP; off < 64; off <<= 1) {
 #pragma unroll
-      for (int e = 0; e < EPV / 4; ++e) {
-        x0[e] = *reinterpret_cast<const float4*>(a + (size_t)(i + 0) * D + 4 * e);
-        x1[e] = *reinterpret_cast<const float4*>(a + (size_t)(i + 1) * D + 4 * e);
-        x2[e] = *reinterpret_cast<const float4*>(a + (size_t)(i + 2) * D + 4 * e);
-        x3[e] = *reinterpret_cast<const float4*>(a + (size_t)(i + 3) * D + 4 * e);
-      }
-      const float w0 = wsh[i], w1 = wsh[i + 1], w2 = wsh[i + 2], w3 = wsh[i + 3];
+    for (int e = 0; e < 4; ++e) o[e] += __shfl_xor(o[e], off);
+  }
+  if (sub == 0) {
+    const float inv = Lrun > 0.0f ? 1.0f / Lrun : 0.0f;
+    float v[E::EPV];
+    // E::store writes EPV consecutive values; stage 4 at a time
+    if constexpr (E::EPV == 4) {
 #pragma unroll
-      for (int e = 0; e < EPV / 4; ++e) {
-        o[4 * e + 0] += w0 * x0[e].x + w1 * x1[e].x + w2 * x2[e].x + w3 * x3[e].x;
-        o[4 * e + 1] += w0 * x0[e].y + w1 * x1[e].y + w2 * x2[e].y + w3 * x3[e].y;
-        o[4 * e + 2] += w0 * x0[e].z + w1 * x1[e].z + w2 * x2[e].z + w3 * x3[e].z;
-        o[4 * e + 3] += w0 * x0[e].w + w1 * x1[e].w + w2 * x2[e].w + w3 * x3[e].w;
+      for (int e = 0; e < 4; ++e) v[e] = o[e] * inv;
+      E::store(prm.out, bh * D + dl, v);
+    } else {
+      // bf16: two lanes' 4 values form one 8-value store; pair lanes dl and dl + 4
+      float w4[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w4[e] = __shfl_down(o[e], 1) * inv;
+      if ((lane & 1) == 0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { v[e] = o[e] * inv; v[4 + e] = w4[e]; }
+        E::store(prm.out, bh * D + dl, v);
       }
     }
-    for (; i < nparts; ++i) {
-      const float w = wsh[i];
-#pragma unroll
-      for (int e = 0; e < EPV / 4; ++e) {
-        const float4 x = *reinterpret_cast<const float4*>(a + (size_t)i * D + 4 * e);
-        o[4 * e + 0] += w * x.x;
-        o[4 * e + 1] += w * x.y;
-        o[4 * e + 2] += w * x.z;
-        o[4 * e + 3] += w * x.w;
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < EPV; ++e) o[e] *= inv;
-    E::store(prm.out, bh * D + (size_t)lane * EPV, o);
   }
 }
 
@@ -638,7 +641,7 @@ hipError_t launch_decode_partials(const DecodeParams& prm, int32_t dtype, int32_
 template <typename E>
 static hipError_t launch_merge_e(const DecodeParams& prm, int32_t D, hipStream_t stream) {
   const dim3 grid(prm.H, prm.B);
-  const size_t lds = (size_t)prm.maxP * sizeof(float);
+  const size_t lds = 0;
   switch (D) {
     case 64: hipLaunchKernelGGL((decode_merge_kernel<E, 64>), grid, dim3(64), lds, stream, prm); break;
     case 128: hipLaunchKernelGGL((decode_merge_kernel<E, 128>), grid, dim3(64), lds, stream, prm); break;
