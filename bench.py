@@ -33,15 +33,17 @@ if ROOT not in sys.path:
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 METRIC = "paged decode KV-read GB/s (% of HBM peak) + µs/step; write_kv GB/s"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_partial_traffic.json")
-DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_70_amd", "csrc", "pa_decode.hip")
+CSRC = os.path.join(ROOT, "paged_kv_cache_70_amd", "csrc")
+# source file of the partial kernel each cache dtype runs
+DECODE_SRC = {"bf16": os.path.join(CSRC, "pa_decode_mfma.hip"), "f32": os.path.join(CSRC, "pa_decode.hip")}
 
 
-def _src_hash() -> str:
-    with open(DECODE_SRC, "rb") as f:
+def _src_hash(dtype: str) -> str:
+    with open(DECODE_SRC[dtype], "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def _traffic(workload: str):
+def _traffic(workload: str, dtype: str):
     """HBM bytes per partial-kernel launch from the committed rocprofv3 counter
     summary, if it was taken on this workload and this kernel source."""
     try:
@@ -49,9 +51,50 @@ def _traffic(workload: str):
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("source_sha256_16") != _src_hash() or t.get("workload") != workload:
+    if t.get("source_sha256_16") != _src_hash(dtype) or t.get("workload") != workload:
         return None
     return t.get("bytes_per_launch")
+
+
+PARTIAL_KERNELS = {"bf16": "decode_partial_mfma_kernel", "f32": "decode_partial_kernel"}
+CALIB_TAG = "MulFunctor"        # torch.mul(src, 2.0, out=dst): the calibration copy
+
+
+def _counter_rows(path: str, counter: str):
+    """(kernel name, value) of every dispatch in a rocprofv3 --pmc CSV."""
+    import csv
+    with open(path, newline="") as f:
+        return [(r["Kernel_Name"], float(r["Counter_Value"])) for r in csv.DictReader(f)
+                if r.get("Counter_Name") == counter]
+
+
+def traffic_from_counters(fetch_csv: str, write_csv: str, workload: str, dtype: str,
+                          calib_bytes: int, out_json: str) -> dict:
+    """HBM bytes per partial-kernel launch from two rocprofv3 --pmc runs of
+    this script (FETCH_SIZE, then WRITE_SIZE; both in KiB per dispatch), each
+    scaled by the same counter's reading for the calibration copy, which reads
+    and writes calib_bytes."""
+    kname = PARTIAL_KERNELS[dtype]
+    res = {"workload": workload, "kernel": kname, "source_sha256_16": _src_hash(dtype),
+           "calibration_copy_bytes": calib_bytes}
+    total = 0.0
+    for key, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = _counter_rows(path, key)
+        kern = [v * 1024 for n, v in rows if n.startswith(kname) or f" {kname}<" in n or f"::{kname}<" in n]
+        cal = [v * 1024 for n, v in rows if CALIB_TAG in n]
+        if not kern or not cal:
+            raise SystemExit(f"{path}: no {key} rows for {kname} ({len(kern)}) or the calibration copy ({len(cal)})")
+        k_mean, c_mean = sum(kern) / len(kern), sum(cal) / len(cal)
+        factor = calib_bytes / c_mean
+        res[key.lower()] = {"dispatches": len(kern), "raw_bytes_per_launch": round(k_mean),
+                            "calibration_raw_bytes": round(c_mean), "scale": round(factor, 5),
+                            "bytes_per_launch": round(k_mean * factor)}
+        total += k_mean * factor
+    res["bytes_per_launch"] = round(total)
+    with open(out_json, "w") as f:
+        json.dump(res, f, indent=1)
+        f.write("\n")
+    return res
 
 
 def _cpu_baseline(w, budget_s: float):
@@ -102,7 +145,21 @@ def main():
     ap.add_argument("--hot", action="store_true", help="do not flush the last-level cache between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="before the steps, run a plain fp32 copy of MIB MiB three times (the reference "
+                         "reading for HBM byte counters)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU run: turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, WRITE_SIZE) of a "
+                         "--copy-calibration run into profiles/decode_partial_traffic.json")
     args = ap.parse_args()
+
+    if args.traffic_from:
+        from synth import CONFIGS
+        cfg = CONFIGS[args.config]
+        r = traffic_from_counters(*args.traffic_from, cfg.name, cfg.dtype,
+                                  (args.copy_calibration or 256) << 20, TRAFFIC_FILE)
+        print(json.dumps(r))
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -150,6 +207,15 @@ def main():
 
     def ev():
         return torch.cuda.Event(enable_timing=True)
+
+    if args.copy_calibration:
+        src = torch.ones(args.copy_calibration << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            do_flush()
+            torch.mul(src, 2.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         do_flush()
@@ -206,7 +272,7 @@ def main():
     dec_us = k2_us + k3_us
     value = kv_bytes / (step_us * 1e-6) / 1e9
     achieved = kv_bytes / (k2_us * 1e-6) / 1e9
-    traffic = _traffic(cfg.name)
+    traffic = _traffic(cfg.name, cfg.dtype)
 
     res = {
         "metric": METRIC,
@@ -246,7 +312,7 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
-            "kernel": "decode_partial_mfma_kernel" if cfg.dtype == "bf16" else "decode_partial_kernel",
+            "kernel": PARTIAL_KERNELS[cfg.dtype],
         },
     }
     if not args.no_cpu_baseline:

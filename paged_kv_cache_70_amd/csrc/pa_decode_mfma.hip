@@ -72,7 +72,9 @@ __device__ __forceinline__ int swz(int t) {
 
 }  // namespace
 
-template <int D>
+// WholeTile: block_size >= 16, so every 16-token tile (tiles start at multiples
+// of 16 and partitions at multiples of the block size) lies inside one block.
+template <int D, bool WholeTile>
 __global__ __launch_bounds__(64) void decode_partial_mfma_kernel(const DecodeParams prm) {
   constexpr int ROWB = D * 2;        // bytes of one (token, kv head) row
   constexpr int PPR = ROWB / 16;     // 16-byte pieces per row
@@ -143,9 +145,9 @@ __global__ __launch_bounds__(64) void decode_partial_mfma_kernel(const DecodePar
   const int tbl_v = (j_first + lane < j_end) ? tbl[j_first + lane] : 0;
 
   // Loads: instruction u of a tile brings token rows u * TPI + lane / PPR,
-  // piece lane % PPR, of the kv head.  Its buffer resource starts at that
-  // instruction's first row and ends after the last valid row of the
-  // sequence, so rows past the end (and blocks outside the pool) read zeros.
+  // piece lane % PPR, of the kv head.  Its buffer resource starts at the
+  // first row it covers and ends after the last valid row of the sequence, so
+  // rows past the end (and blocks outside the pool) read zeros.
   const uint32_t lane_off = (uint32_t)(lane / PPR) * row_bytes + (uint32_t)(lane % PPR) * 16;
   // LDS byte address each lane writes for instruction u, and reads for the K
   // operand of product c / the V operand of product j.
@@ -164,19 +166,37 @@ __global__ __launch_bounds__(64) void decode_partial_mfma_kernel(const DecodePar
 
   auto load_tile = [&](int tile, u32x4m (&kr)[NI], u32x4m (&vr)[NI]) -> uint32_t {
     uint32_t ok = 0;
-#pragma unroll
-    for (int u = 0; u < NI; ++u) {
-      const int t0 = tile + u * TPI;                   // first token of this instruction
-      const int phys = __builtin_amdgcn_readlane(tbl_v, (t0 >> prm.bs_log2) - j_first);
-      const int nv = min(TPI, t_end - t0);             // valid rows of this instruction
+    if constexpr (WholeTile) {
+      // The 16 rows lie in one block: one resource per tile, instruction u at
+      // a scalar offset of u * TPI rows.
+      const int phys = __builtin_amdgcn_readlane(tbl_v, (tile >> prm.bs_log2) - j_first);
+      const int nv = min(16, t_end - tile);             // valid rows of the tile
       const bool good = (unsigned)phys < (unsigned)prm.NB && nv > 0;
-      const size_t off = (size_t)(good ? phys : 0) * blk_bytes + (size_t)(t0 & prm.bs_mask) * row_bytes;
+      const size_t off = (size_t)(good ? phys : 0) * blk_bytes + (size_t)(tile & prm.bs_mask) * row_bytes;
       const int nrec = good ? nv * (int)row_bytes : 0;
       const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(kc + off), (short)0, nrec, kRsrcWord3M);
       const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vc + off), (short)0, nrec, kRsrcWord3M);
-      kr[u] = __builtin_amdgcn_raw_buffer_load_b128(rk, lane_off, 0, 0);
-      vr[u] = __builtin_amdgcn_raw_buffer_load_b128(rv, lane_off, 0, 0);
-      if (good) ok |= ((1u << nv) - 1u) << (u * TPI);
+#pragma unroll
+      for (int u = 0; u < NI; ++u) kr[u] = __builtin_amdgcn_raw_buffer_load_b128(rk, lane_off, u * TPI * row_bytes, 0);
+#pragma unroll
+      for (int u = 0; u < NI; ++u) vr[u] = __builtin_amdgcn_raw_buffer_load_b128(rv, lane_off, u * TPI * row_bytes, 0);
+      if (good) ok = nv >= 16 ? 0xffffu : ((1u << nv) - 1u);
+    } else {
+      // Blocks shorter than a tile: one resource per instruction.
+#pragma unroll
+      for (int u = 0; u < NI; ++u) {
+        const int t0 = tile + u * TPI;                   // first token of this instruction
+        const int phys = __builtin_amdgcn_readlane(tbl_v, (t0 >> prm.bs_log2) - j_first);
+        const int nv = min(TPI, t_end - t0);             // valid rows of this instruction
+        const bool good = (unsigned)phys < (unsigned)prm.NB && nv > 0;
+        const size_t off = (size_t)(good ? phys : 0) * blk_bytes + (size_t)(t0 & prm.bs_mask) * row_bytes;
+        const int nrec = good ? nv * (int)row_bytes : 0;
+        const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(kc + off), (short)0, nrec, kRsrcWord3M);
+        const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vc + off), (short)0, nrec, kRsrcWord3M);
+        kr[u] = __builtin_amdgcn_raw_buffer_load_b128(rk, lane_off, 0, 0);
+        vr[u] = __builtin_amdgcn_raw_buffer_load_b128(rv, lane_off, 0, 0);
+        if (good) ok |= ((1u << nv) - 1u) << (u * TPI);
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
     return ok;
@@ -281,12 +301,19 @@ __global__ __launch_bounds__(64) void decode_partial_mfma_kernel(const DecodePar
 
 hipError_t launch_decode_partials_mfma(const DecodeParams& prm, int32_t D, hipStream_t stream) {
   const dim3 grid(prm.KVH * prm.nchunks, prm.maxP, prm.B);
+  const bool whole = prm.bs_log2 >= 4;
+#define PA_LAUNCH(DD)                                                                     \
+  if (whole)                                                                               \
+    hipLaunchKernelGGL((decode_partial_mfma_kernel<DD, true>), grid, dim3(64), 0, stream, prm); \
+  else                                                                                     \
+    hipLaunchKernelGGL((decode_partial_mfma_kernel<DD, false>), grid, dim3(64), 0, stream, prm)
   switch (D) {
-    case 64: hipLaunchKernelGGL(decode_partial_mfma_kernel<64>, grid, dim3(64), 0, stream, prm); break;
-    case 128: hipLaunchKernelGGL(decode_partial_mfma_kernel<128>, grid, dim3(64), 0, stream, prm); break;
-    case 256: hipLaunchKernelGGL(decode_partial_mfma_kernel<256>, grid, dim3(64), 0, stream, prm); break;
+    case 64: PA_LAUNCH(64); break;
+    case 128: PA_LAUNCH(128); break;
+    case 256: PA_LAUNCH(256); break;
     default: return hipErrorInvalidValue;
   }
+#undef PA_LAUNCH
   return hipGetLastError();
 }
 

@@ -1,0 +1,60 @@
+"""Host-side logic of bench.py (CPU only): the GPU-count guard and the
+conversion of rocprofv3 counter CSVs into HBM bytes per launch."""
+import csv
+import json
+import os
+import subprocess
+import sys
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+_FIELDS = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+
+
+def _csv(path, counter, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=_FIELDS)
+        w.writeheader()
+        for i, (name, kib) in enumerate(rows):
+            w.writerow({"Dispatch_Id": i, "Kernel_Name": name, "Counter_Name": counter, "Counter_Value": kib})
+
+
+def test_traffic_from_counters_scales_by_calibration(tmp_path):
+    calib = 256 << 20
+    kern = "void pa::decode_partial_mfma_kernel<128, true>(pa::DecodeParams)"
+    other = "void pa::decode_partial_kernel<float, 128, 1, 2, 4, 1>(pa::DecodeParams)"
+    copy = "void at::native::vectorized_elementwise_kernel<4, AUnaryFunctor<float, float, float, MulFunctor<float>>>"
+    # the counters read 10% high on the copy: the kernel's reading is scaled down by 1/1.1
+    _csv(tmp_path / "f.csv", "FETCH_SIZE",
+         [(copy, calib * 1.1 / 1024), (kern, 1100.0), (kern, 1100.0), (other, 5e6), (copy, calib * 1.1 / 1024)])
+    _csv(tmp_path / "w.csv", "WRITE_SIZE", [(copy, calib / 1024), (kern, 10.0), (kern, 30.0)])
+    out = tmp_path / "t.json"
+    r = bench.traffic_from_counters(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"),
+                                    "llama3_8b_bf16", "bf16", calib, str(out))
+    assert r["fetch_size"]["dispatches"] == 2
+    assert r["fetch_size"]["bytes_per_launch"] == 1000 * 1024
+    assert r["write_size"]["bytes_per_launch"] == 20 * 1024
+    assert r["bytes_per_launch"] == 1020 * 1024
+    assert json.loads(out.read_text()) == r
+    assert r["source_sha256_16"] == bench._src_hash("bf16")
+
+
+def test_traffic_file_ignored_when_stale(tmp_path, monkeypatch):
+    p = tmp_path / "t.json"
+    p.write_text(json.dumps({"workload": "llama3_8b_bf16", "source_sha256_16": "0" * 16,
+                             "bytes_per_launch": 5}))
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(p))
+    assert bench._traffic("llama3_8b_bf16", "bf16") is None
+    p.write_text(json.dumps({"workload": "llama3_8b_bf16", "source_sha256_16": bench._src_hash("bf16"),
+                             "bytes_per_launch": 5}))
+    assert bench._traffic("llama3_8b_bf16", "bf16") == 5
+    assert bench._traffic("big_batch_bf16", "bf16") is None
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
