@@ -41,6 +41,7 @@ typedef uint32_t u32x4m __attribute__((ext_vector_type(4)));
 
 constexpr int kRsrcWord3M = 0x00020000;   // raw untyped buffer access, gfx9 family
 constexpr float kSlackM = 8.0f;           // lazy-rescale slack (base-2 units)
+constexpr int kPersistentWavesPerCU = 8;  // resident workgroups (one wavefront each) per CU
 
 __device__ __forceinline__ float exp2m(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -72,25 +73,20 @@ __device__ __forceinline__ int swz(int t) {
 
 }  // namespace
 
-// WholeTile: block_size >= 16, so every 16-token tile (tiles start at multiples
-// of 16 and partitions at multiples of the block size) lies inside one block.
+// One work unit: partition p of sequence b, kv head kvh, query-head chunk
+// chunk (up to 16 heads of the kv head's group).  WholeTile: block_size >= 16,
+// so every 16-token tile (tiles start at multiples of 16 and partitions at
+// multiples of the block size) lies inside one block.
 template <int D, bool WholeTile>
-__global__ __launch_bounds__(64) void decode_partial_mfma_kernel(const DecodeParams prm) {
+__device__ __forceinline__ void mfma_unit(const DecodeParams& prm, int b, int p, int kvh, int chunk,
+                                          uint8_t* __restrict__ lds_k, uint8_t* __restrict__ lds_v) {
   constexpr int ROWB = D * 2;        // bytes of one (token, kv head) row
   constexpr int PPR = ROWB / 16;     // 16-byte pieces per row
   constexpr int TPI = 64 / PPR;      // token rows per load instruction
   constexpr int NI = 16 / TPI;       // load instructions per 16-token tile (K, and again V)
   constexpr int NQK = D / 32;        // QK products (32 d each)
   constexpr int NPV = D / 16;        // PV products (16 d columns each)
-  __shared__ __attribute__((aligned(16))) uint8_t lds_k[16 * ROWB];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_v[16 * ROWB];
 
-  // Grid: x = (kv head, chunk of up to 16 query heads) fastest, y = partition,
-  // z = sequence.
-  const int p = blockIdx.y;
-  const int b = blockIdx.z;
-  const int kvh = blockIdx.x / prm.nchunks;
-  const int chunk = blockIdx.x - kvh * prm.nchunks;
   const int G = prm.H / prm.KVH;
   const int h_base = kvh * G + chunk * 16;
   const int nh = min(16, G - chunk * 16);
@@ -299,22 +295,138 @@ __global__ __launch_bounds__(64) void decode_partial_mfma_kernel(const DecodePar
   }
 }
 
-hipError_t launch_decode_partials_mfma(const DecodeParams& prm, int32_t D, hipStream_t stream) {
+// Grid form (sequence counts beyond the persistent form's search): one
+// workgroup per unit.  Grid x = (kv head, head chunk) fastest, y = partition,
+// z = sequence; units past a sequence's last partition exit at once.
+template <int D, bool WholeTile>
+__global__ __launch_bounds__(64) void decode_partial_mfma_grid_kernel(const DecodeParams prm) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds_k[16 * 2 * D];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_v[16 * 2 * D];
+  const int kvh = blockIdx.x / prm.nchunks;
+  mfma_unit<D, WholeTile>(prm, blockIdx.z, blockIdx.y, kvh, blockIdx.x - kvh * prm.nchunks, lds_k, lds_v);
+}
+
+// Persistent form: as many workgroups as stay resident (a fixed number per
+// CU) walk a list of the units that exist, so that the chip holds its full
+// complement of wavefronts from the first tile to the drain, with no
+// workgroup dispatch between units and no empty units.
+//
+// The list: first every sequence's partitions before its last one (all full,
+// P tokens), sequence by sequence, then the last partition of each sequence;
+// each (sequence, partition) pair expands into kv heads x head chunks
+// consecutive units.  Round r of the walk hands units r*G .. r*G + G-1 to the
+// G workgroups, in forward order on even rounds and reverse order on odd
+// ones, so that a workgroup that drew a late (short) unit in one round draws
+// an early one in the next.  The list is rebuilt by every workgroup from the
+// context lengths (an exclusive scan into LDS), so all of them agree on it
+// without any communication.
+template <int D, bool WholeTile>
+__global__ __launch_bounds__(64) void decode_partial_mfma_kernel(const DecodeParams prm) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds_k[16 * 2 * D];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_v[16 * 2 * D];
+  extern __shared__ int32_t s_first[];          // [B]: list index of sequence b's first full pair
+  const int lane = threadIdx.x;
+  const int B = prm.B, P = prm.P;
+  auto nparts_of = [&](int b) {
+    int n = prm.ctx[b];
+    n = n < 0 ? 0 : (n > prm.max_tokens ? prm.max_tokens : n);
+    return (n + P - 1) / P;
+  };
+  int carry = 0;
+  for (int base = 0; base < B; base += 64) {
+    const int b = base + lane;
+    int f = 0;
+    if (b < B) {
+      const int np = nparts_of(b);
+      f = np > 1 ? np - 1 : 0;
+    }
+    int incl = f;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(incl, d);
+      if (lane >= d) incl += y;
+    }
+    if (b < B) s_first[b] = carry + incl - f;
+    carry += __builtin_amdgcn_readlane(incl, 63);
+  }
+  __syncthreads();
+  const uint32_t F = (uint32_t)carry;           // pairs of full partitions
+  const uint32_t upp = (uint32_t)(prm.KVH * prm.nchunks);
+  const uint32_t nunits = (F + (uint32_t)B) * upp;
+  const uint32_t G = gridDim.x;
+  const int stride = (B + 63) >> 6;             // sequences per lane in the first search level
+
+  uint32_t t = blockIdx.x;
+  for (uint32_t round = 1; t < nunits; ++round) {
+    const uint32_t pair = t / upp, sub = t - pair * upp;
+    int b, p;
+    if (pair < F) {
+      // b = the last sequence whose first list index is <= pair: one ballot
+      // over every stride-th sequence, then one inside the chosen stretch
+      const int i1 = lane * stride;
+      const uint64_t m1 = __ballot(i1 < B && (uint32_t)s_first[i1 < B ? i1 : 0] <= pair);
+      const int seg = __popcll(m1) - 1;
+      const int i2 = seg * stride + lane;
+      const uint64_t m2 = __ballot(lane < stride && i2 < B && (uint32_t)s_first[i2 < B ? i2 : 0] <= pair);
+      b = __builtin_amdgcn_readfirstlane(seg * stride + __popcll(m2) - 1);
+      p = (int)(pair - (uint32_t)s_first[b]);
+    } else {
+      b = (int)(pair - F);
+      const int np = nparts_of(b);
+      p = np > 0 ? np - 1 : 0;
+    }
+    const int kvh = (int)(sub / (uint32_t)prm.nchunks);
+    mfma_unit<D, WholeTile>(prm, b, p, kvh, (int)sub - kvh * prm.nchunks, lds_k, lds_v);
+    t = round * G + ((round & 1) ? G - 1 - blockIdx.x : blockIdx.x);
+  }
+}
+
+namespace {
+constexpr int kMaxPersistentSeqs = 4096;   // the pair search covers 64 x 64 sequences
+
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (!cus[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+template <int D, bool WholeTile>
+hipError_t launch_mfma(const DecodeParams& prm, hipStream_t stream) {
+  if (prm.B <= kMaxPersistentSeqs) {
+    const size_t lds = (size_t)prm.B * sizeof(int32_t);
+    int per_cu = 0;
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &per_cu, reinterpret_cast<const void*>(&decode_partial_mfma_kernel<D, WholeTile>), 64, lds);
+    const int cus = device_cus();
+    if (e == hipSuccess && per_cu > 0 && cus > 0) {
+      if (per_cu > kPersistentWavesPerCU) per_cu = kPersistentWavesPerCU;
+      const int64_t units_max = (int64_t)prm.B * prm.maxP * prm.KVH * prm.nchunks;
+      const int64_t wgs = (int64_t)per_cu * cus < units_max ? (int64_t)per_cu * cus : units_max;
+      hipLaunchKernelGGL((decode_partial_mfma_kernel<D, WholeTile>), dim3((uint32_t)wgs), dim3(64), lds, stream,
+                         prm);
+      return hipGetLastError();
+    }
+  }
   const dim3 grid(prm.KVH * prm.nchunks, prm.maxP, prm.B);
+  hipLaunchKernelGGL((decode_partial_mfma_grid_kernel<D, WholeTile>), grid, dim3(64), 0, stream, prm);
+  return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_decode_partials_mfma(const DecodeParams& prm, int32_t D, hipStream_t stream) {
   const bool whole = prm.bs_log2 >= 4;
-#define PA_LAUNCH(DD)                                                                     \
-  if (whole)                                                                               \
-    hipLaunchKernelGGL((decode_partial_mfma_kernel<DD, true>), grid, dim3(64), 0, stream, prm); \
-  else                                                                                     \
-    hipLaunchKernelGGL((decode_partial_mfma_kernel<DD, false>), grid, dim3(64), 0, stream, prm)
   switch (D) {
-    case 64: PA_LAUNCH(64); break;
-    case 128: PA_LAUNCH(128); break;
-    case 256: PA_LAUNCH(256); break;
+    case 64: return whole ? launch_mfma<64, true>(prm, stream) : launch_mfma<64, false>(prm, stream);
+    case 128: return whole ? launch_mfma<128, true>(prm, stream) : launch_mfma<128, false>(prm, stream);
+    case 256: return whole ? launch_mfma<256, true>(prm, stream) : launch_mfma<256, false>(prm, stream);
     default: return hipErrorInvalidValue;
   }
-#undef PA_LAUNCH
-  return hipGetLastError();
 }
 
 }  // namespace pa

@@ -247,6 +247,26 @@ def test_workspace_reused_across_calls_and_sizes():
         assert all(torch.equal(outs[0], x) for x in outs[1:])
 
 
+@pytest.mark.parametrize("B", [1000, 4100])
+def test_many_sequences(B):
+    """Many sequences of mixed lengths, every 7th with n = 0: up to 4096
+    sequences the partial kernel runs as resident workgroups walking the list
+    of existing (sequence, partition) pairs, found by a two-level search over
+    the sequences; beyond that as one workgroup per unit."""
+    _say(f"many sequences B={B}")
+    lens = np.random.default_rng(B).integers(1, 200, size=B).tolist()
+    w = make_custom(num_seqs=B, num_heads=8, num_kv_heads=2, head_dim=64, block_size=16,
+                    dtype="bf16", lens=lens, seed=B % 97, device="cuda")
+    ctx = w.context_lens.clone()
+    ctx[::7] = 0
+    ref = O.decode(stored_np(w.q), stored_np(w.k_cache), stored_np(w.v_cache),
+                   stored_np(w.block_tables), stored_np(ctx), w.scale, "bf16")
+    for P in (0, 32, 64):
+        out = pk.decode(w.q, w.k_cache, w.v_cache, w.block_tables, ctx, w.scale, partition_size=P)
+        torch.cuda.synchronize()
+        assert_matches_oracle(out, ref, "bf16", f"B={B} P={P}")
+
+
 def test_out_of_order_and_aliased_tables():
     """An out-of-order table (as in [3, 1]) and two tables aliasing the same
     physical blocks give the dense result for each sequence."""
