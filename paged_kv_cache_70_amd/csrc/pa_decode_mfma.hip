@@ -34,14 +34,13 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4m __attribute__((ext_vector_type(4)));
 
 constexpr int kRsrcWord3M = 0x00020000;   // raw untyped buffer access, gfx9 family
 constexpr float kSlackM = 8.0f;           // lazy-rescale slack (base-2 units)
-constexpr int kPersistentWavesPerCU = 8;  // resident workgroups (one wavefront each) per CU
+constexpr int kBuckets = 64;              // length classes of the last-partition ordering
 
 __device__ __forceinline__ float exp2m(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -71,293 +70,453 @@ __device__ __forceinline__ int swz(int t) {
     return t >> 1;
 }
 
-}  // namespace
+template <int D>
+struct Geo {
+  static constexpr int ROWB = D * 2;        // bytes of one (token, kv head) row
+  static constexpr int PPR = ROWB / 16;     // 16-byte pieces per row
+  static constexpr int TPI = 64 / PPR;      // token rows per load instruction
+  static constexpr int NI = 16 / TPI;       // load instructions per 16-token tile (K, and again V)
+  static constexpr int NQK = D / 32;        // QK products (32 d each)
+  static constexpr int NPV = D / 16;        // PV products (16 d columns each)
+};
 
-// One work unit: partition p of sequence b, kv head kvh, query-head chunk
-// chunk (up to 16 heads of the kv head's group).  WholeTile: block_size >= 16,
-// so every 16-token tile (tiles start at multiples of 16 and partitions at
-// multiples of the block size) lies inside one block.
-template <int D, bool WholeTile>
-__device__ __forceinline__ void mfma_unit(const DecodeParams& prm, int b, int p, int kvh, int chunk,
-                                          uint8_t* __restrict__ lds_k, uint8_t* __restrict__ lds_v) {
-  constexpr int ROWB = D * 2;        // bytes of one (token, kv head) row
-  constexpr int PPR = ROWB / 16;     // 16-byte pieces per row
-  constexpr int TPI = 64 / PPR;      // token rows per load instruction
-  constexpr int NI = 16 / TPI;       // load instructions per 16-token tile (K, and again V)
-  constexpr int NQK = D / 32;        // QK products (32 d each)
-  constexpr int NPV = D / 16;        // PV products (16 d columns each)
+// One work unit: partition p of sequence b (n tokens, np partitions), kv head
+// kvh, query-head chunk chunk (up to 16 heads of the kv head's group), tokens
+// [t_begin, t_end) in ntiles 16-token tiles (at least one: an empty unit
+// folds one fully masked tile and writes zeros).  Wave-uniform.
+struct Unit {
+  int b, p, kvh, chunk, np;
+  int t_begin, t_end, ntiles;
+};
 
+__device__ __forceinline__ Unit make_unit(const DecodeParams& prm, int b, int p, int n, int kvh, int chunk) {
+  Unit u;
+  u.b = b;
+  u.p = p;
+  u.kvh = kvh;
+  u.chunk = chunk;
+  u.np = (n + prm.P - 1) / prm.P;
+  u.t_begin = p * prm.P;
+  u.t_end = min(n, u.t_begin + prm.P);
+  const int ntok = u.t_end - u.t_begin;
+  u.ntiles = ntok > 0 ? (ntok + 15) >> 4 : 1;
+  return u;
+}
+
+// The neighbour sequence of b (the previous one, or sequence 1 for sequence
+// 0): sequences that share a prefix usually sit next to each other in a
+// batch (samples of one prompt), or all share it (a common system prompt).
+__device__ __forceinline__ int neighbour(const DecodeParams& prm, int b) {
+  return b > 0 ? b - 1 : (prm.B > 1 ? 1 : -1);
+}
+
+__device__ __forceinline__ int clamp_len(const DecodeParams& prm, int n) {
+  return n < 0 ? 0 : (n > prm.max_tokens ? prm.max_tokens : n);
+}
+
+// The kv head's column of the caches.
+template <int D>
+__device__ __forceinline__ const char* kv_col(const void* cache, int kvh) {
+  return static_cast<const char*>(cache) + (size_t)kvh * Geo<D>::ROWB;
+}
+
+// Raw Q^T operands of a unit: lane holds q[head col][32 c + 8 grp .. + 8] of
+// its column's head (head 0 of the chunk for padding columns, masked later).
+template <int D>
+__device__ __forceinline__ void load_q(const DecodeParams& prm, const Unit& u, int lane,
+                                       u32x4m (&qr)[Geo<D>::NQK]) {
   const int G = prm.H / prm.KVH;
-  const int h_base = kvh * G + chunk * 16;
-  const int nh = min(16, G - chunk * 16);
-
-  int n = prm.ctx[b];
-  n = n < 0 ? 0 : (n > prm.max_tokens ? prm.max_tokens : n);
-  const int nparts = (n + prm.P - 1) / prm.P;
-  if (p >= (nparts > 0 ? nparts : 1)) return;
-  const int t_begin = p * prm.P;
-  const int t_end = min(n, t_begin + prm.P);
-
-  const int lane = threadIdx.x;
-  const int col = lane & 15;         // query head (column) of this lane
-  const int grp = lane >> 4;         // 16-lane group
-  const bool head_ok = col < nh;
-
-  // Q^T operands: lane holds q[head col][32 c + 8 grp .. + 8] (zero for padding
-  // columns).  A negative scale is applied as negated q, a zero scale as zero q.
-  bf16x8 qop[NQK];
-  {
-    const uint32_t flip = prm.q_mode == 1 ? 0x80008000u : 0u;
-    const uint32_t keep = (prm.q_mode == 2 || !head_ok) ? 0u : 0xffffffffu;
-    const uint8_t* qrow = static_cast<const uint8_t*>(prm.q) +
-                          ((size_t)(b * prm.H + h_base + (head_ok ? col : 0)) * D) * 2;
+  const int nh = min(16, G - u.chunk * 16);
+  const int col = lane & 15, grp = lane >> 4;
+  const int h = u.kvh * G + u.chunk * 16 + (col < nh ? col : 0);
+  const uint8_t* qrow = static_cast<const uint8_t*>(prm.q) + ((size_t)(u.b * prm.H + h) * D) * 2;
 #pragma unroll
-    for (int c = 0; c < NQK; ++c) {
-      u32x4m w = *reinterpret_cast<const u32x4m*>(qrow + (32 * c + 8 * grp) * 2);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t x = w[i];
-        w[i] = (x ^ flip) & keep;
-      }
-      qop[c] = __builtin_bit_cast(bf16x8, w);
-    }
-  }
-  const float cs = prm.scale_log2;
+  for (int c = 0; c < Geo<D>::NQK; ++c)
+    qr[c] = *reinterpret_cast<const u32x4m*>(qrow + (32 * c + 8 * grp) * 2);
+}
 
-  // Softmax state of column col (uniform over the four groups), this lane's
-  // share of the running sum, and O^T accumulators.
-  float m = -INFINITY, mneg = 0.0f, lsum = 0.0f;
-  f32x4 o[NPV];
+// Q^T operands from the raw loads: zero for padding columns; a negative scale
+// is applied as negated q, a zero scale as zero q.
+template <int D>
+__device__ __forceinline__ void q_operands(const DecodeParams& prm, const Unit& u, int lane,
+                                           const u32x4m (&qr)[Geo<D>::NQK], bf16x8 (&qop)[Geo<D>::NQK]) {
+  const int G = prm.H / prm.KVH;
+  const bool head_ok = (lane & 15) < min(16, G - u.chunk * 16);
+  const uint32_t flip = prm.q_mode == 1 ? 0x80008000u : 0u;
+  const uint32_t keep = (prm.q_mode == 2 || !head_ok) ? 0u : 0xffffffffu;
 #pragma unroll
-  for (int j = 0; j < NPV; ++j) o[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-
-  const uint32_t row_bytes = (uint32_t)prm.KVH * ROWB;
-  const size_t blk_bytes = (size_t)row_bytes << prm.bs_log2;
-  const char* kc = static_cast<const char*>(prm.k_cache) + (size_t)kvh * ROWB;
-  const char* vc = static_cast<const char*>(prm.v_cache) + (size_t)kvh * ROWB;
-  const int32_t* tbl = prm.tables + (size_t)b * prm.W;
-  const int j_first = t_begin >> prm.bs_log2;
-  const int j_end = (t_end + prm.bs_mask) >> prm.bs_log2;
-  const int tbl_v = (j_first + lane < j_end) ? tbl[j_first + lane] : 0;
-
-  // Loads: instruction u of a tile brings token rows u * TPI + lane / PPR,
-  // piece lane % PPR, of the kv head.  Its buffer resource starts at the
-  // first row it covers and ends after the last valid row of the sequence, so
-  // rows past the end (and blocks outside the pool) read zeros.
-  const uint32_t lane_off = (uint32_t)(lane / PPR) * row_bytes + (uint32_t)(lane % PPR) * 16;
-  // LDS byte address each lane writes for instruction u, and reads for the K
-  // operand of product c / the V operand of product j.
-  int wr_addr[NI];
-#pragma unroll
-  for (int u = 0; u < NI; ++u) {
-    const int t = u * TPI + lane / PPR, pc = lane % PPR;
-    wr_addr[u] = (t * PPR + (pc ^ swz<PPR>(t))) * 16;
-  }
-  const int tk = col;                                // K operand row (token) of this lane
-  const int tv = 4 * grp + ((lane & 15) >> 2);       // V rows read by this lane (tr layout)
-  const int dv = 4 * (lane & 3);                     // d offset within a 16-column chunk
-
-  u32x4m kA[NI], vA[NI], kB[NI], vB[NI];
-  uint32_t okA = 0, okB = 0;                         // per-row validity mask of the tile (bit r)
-
-  auto load_tile = [&](int tile, u32x4m (&kr)[NI], u32x4m (&vr)[NI]) -> uint32_t {
-    uint32_t ok = 0;
-    if constexpr (WholeTile) {
-      // The 16 rows lie in one block: one resource per tile, instruction u at
-      // a scalar offset of u * TPI rows.
-      const int phys = __builtin_amdgcn_readlane(tbl_v, (tile >> prm.bs_log2) - j_first);
-      const int nv = min(16, t_end - tile);             // valid rows of the tile
-      const bool good = (unsigned)phys < (unsigned)prm.NB && nv > 0;
-      const size_t off = (size_t)(good ? phys : 0) * blk_bytes + (size_t)(tile & prm.bs_mask) * row_bytes;
-      const int nrec = good ? nv * (int)row_bytes : 0;
-      const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(kc + off), (short)0, nrec, kRsrcWord3M);
-      const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vc + off), (short)0, nrec, kRsrcWord3M);
-#pragma unroll
-      for (int u = 0; u < NI; ++u) kr[u] = __builtin_amdgcn_raw_buffer_load_b128(rk, lane_off, u * TPI * row_bytes, 0);
-#pragma unroll
-      for (int u = 0; u < NI; ++u) vr[u] = __builtin_amdgcn_raw_buffer_load_b128(rv, lane_off, u * TPI * row_bytes, 0);
-      if (good) ok = nv >= 16 ? 0xffffu : ((1u << nv) - 1u);
-    } else {
-      // Blocks shorter than a tile: one resource per instruction.
-#pragma unroll
-      for (int u = 0; u < NI; ++u) {
-        const int t0 = tile + u * TPI;                   // first token of this instruction
-        const int phys = __builtin_amdgcn_readlane(tbl_v, (t0 >> prm.bs_log2) - j_first);
-        const int nv = min(TPI, t_end - t0);             // valid rows of this instruction
-        const bool good = (unsigned)phys < (unsigned)prm.NB && nv > 0;
-        const size_t off = (size_t)(good ? phys : 0) * blk_bytes + (size_t)(t0 & prm.bs_mask) * row_bytes;
-        const int nrec = good ? nv * (int)row_bytes : 0;
-        const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(kc + off), (short)0, nrec, kRsrcWord3M);
-        const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vc + off), (short)0, nrec, kRsrcWord3M);
-        kr[u] = __builtin_amdgcn_raw_buffer_load_b128(rk, lane_off, 0, 0);
-        vr[u] = __builtin_amdgcn_raw_buffer_load_b128(rv, lane_off, 0, 0);
-        if (good) ok |= ((1u << nv) - 1u) << (u * TPI);
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    return ok;
-  };
-
-  auto fold_tile = [&](uint32_t ok, const u32x4m (&kr)[NI], const u32x4m (&vr)[NI]) {
-    // Stage the tile in LDS (the previous tile's reads were issued earlier by
-    // this wavefront, and LDS serves one wavefront's accesses in order).
-#pragma unroll
-    for (int u = 0; u < NI; ++u) {
-      *reinterpret_cast<u32x4m*>(lds_k + wr_addr[u]) = kr[u];
-      *reinterpret_cast<u32x4m*>(lds_v + wr_addr[u]) = vr[u];
-    }
-    // S = K_tile . Q^T: lane holds S[token 4 grp + i][head col].
-    f32x4 s = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int c = 0; c < NQK; ++c) {
-      const int pc = 4 * c + grp;
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(lds_k + (tk * PPR + (pc ^ swz<PPR>(tk))) * 16);
-      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[c], s, 0, 0, 0);
-    }
-    float sc[4];
+  for (int c = 0; c < Geo<D>::NQK; ++c) {
+    u32x4m w = qr[c];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const bool valid = (ok >> (4 * grp + i)) & 1u;
-      sc[i] = valid ? s[i] * cs : -INFINITY;
+      const uint32_t x = w[i];
+      w[i] = (x ^ flip) & keep;
     }
-    float mt = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-    mt = groups_max(mt);
-    if (__builtin_amdgcn_ballot_w64(mt > m + kSlackM)) {   // wavefront-uniform, rare
-      if (mt > m) {
-        const float corr = exp2m(m - mt);                  // 0 while m is -inf
-        m = mt;
-        mneg = -mt;
-        lsum *= corr;
-#pragma unroll
-        for (int j = 0; j < NPV; ++j) o[j] *= corr;
-      }
-    }
-    float pr[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      pr[i] = exp2m(sc[i] + mneg);
-      lsum += pr[i];
-    }
-    bf16x4 pb;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) pb[i] = (__bf16)pr[i];
-    // O^T += V_tile^T . P^T, one 16-column d chunk per product.
-#pragma unroll
-    for (int j = 0; j < NPV; ++j) {
-      const int d = 16 * j + dv;
-      const int pc = d >> 3;
-      const int addr = (tv * PPR + (pc ^ swz<PPR>(tv))) * 16 + (d & 7) * 2;
-      const s16x4 vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) s16x4*)(lds_v + addr));
-      o[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, vt), pb, o[j], 0, 0, 0);
-    }
-  };
-
-  const int ntok = t_end - t_begin;
-  const int ntiles = ntok > 0 ? (ntok + 15) / 16 : 0;
-  if (ntiles > 0) {
-    auto tile_at = [&](int i) { return t_begin + min(i, ntiles - 1) * 16; };
-    okA = load_tile(tile_at(0), kA, vA);
-    const int npairs = ntiles >> 1;
-    for (int ip = 0; ip < npairs; ++ip) {
-      okB = load_tile(tile_at(2 * ip + 1), kB, vB);
-      fold_tile(okA, kA, vA);
-      okA = load_tile(tile_at(2 * ip + 2), kA, vA);
-      fold_tile(okB, kB, vB);
-    }
-    if (ntiles & 1) fold_tile(okA, kA, vA);
-  }
-
-  // Column col's totals.
-  const float L = groups_sum(lsum);
-  const size_t bh = (size_t)b * prm.H + h_base + col;
-  auto store_out = [&](const f32x4 (&acc)[NPV], float inv) {
-    uint16_t* outp = static_cast<uint16_t*>(prm.out) + bh * D;
-#pragma unroll
-    for (int j = 0; j < NPV; ++j) {
-      bf16x4 w;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) w[i] = (__bf16)(acc[j][i] * inv);
-      *reinterpret_cast<bf16x4*>(outp + 16 * j + 4 * grp) = w;
-    }
-  };
-  if (nparts <= 1) {
-    if (head_ok) store_out(o, L > 0.0f ? 1.0f / L : 0.0f);
-    return;
-  }
-  // Partial results (fp32) for the merge kernel.
-  if (head_ok) {
-    const size_t slot = bh * prm.maxP + p;
-    float* dst = prm.ws_acc + slot * D;
-#pragma unroll
-    for (int j = 0; j < NPV; ++j) *reinterpret_cast<f32x4*>(dst + 16 * j + 4 * grp) = o[j];
-    if (grp == 0) *reinterpret_cast<float2*>(prm.ws_ml + slot * 2) = make_float2(m, L);
+    qop[c] = __builtin_bit_cast(bf16x8, w);
   }
 }
 
-// Grid form (sequence counts beyond the persistent form's search): one
+template <int A>
+struct CachePolicy {
+  static constexpr int aux = A;
+};
+constexpr int kAuxNT = 2;   // buffer-load cache policy bit "nt": non-temporal (streaming) access
+
+// Loads of the 16-token tile starting at token `tile` of a partition ending
+// at t_end: instruction u brings token rows u * TPI + lane / PPR, piece
+// lane % PPR, of the kv head (kc, vc: the kv head's column of the caches).
+// ph0 is the physical block holding the tile's first token, ph1 (blocks of 8
+// tokens only) the next one.  A buffer resource starts at the first row it
+// covers and ends after the last valid row of the partition, so rows past the
+// end (and blocks outside the pool, and every row of a dead load) read zeros.
+// AUX is the loads' cache policy: kAuxNT when the rows are read once in this
+// call, 0 (default) when other sequences are likely to read the same blocks
+// (a shared prefix).
+// Returns the tile's row validity mask (bit r: row r holds a token).
+// WholeTile: block_size >= 16, so a tile (tiles start at multiples of 16,
+// partitions at multiples of the block size) lies inside one block;
+// otherwise the block size is 8 and a tile spans two blocks.
+template <int D, bool WholeTile, int AUX>
+__device__ __forceinline__ uint32_t load_tile(const DecodeParams& prm, const char* kc, const char* vc, int t_end,
+                                              int tile, bool live, int ph0, int ph1, uint32_t lane_off,
+                                              u32x4m (&kr)[Geo<D>::NI], u32x4m (&vr)[Geo<D>::NI]) {
+  constexpr int TPI = Geo<D>::TPI, NI = Geo<D>::NI;
+  const uint32_t row_bytes = (uint32_t)prm.KVH * Geo<D>::ROWB;
+  const size_t blk_bytes = (size_t)row_bytes << prm.bs_log2;
+  uint32_t ok = 0;
+  if constexpr (WholeTile) {
+    const int nv = min(16, t_end - tile);               // valid rows of the tile
+    const bool good = live && (unsigned)ph0 < (unsigned)prm.NB && nv > 0;
+    const size_t off = (size_t)(good ? ph0 : 0) * blk_bytes + (size_t)(tile & prm.bs_mask) * row_bytes;
+    const int nrec = good ? nv * (int)row_bytes : 0;
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(kc + off), (short)0, nrec, kRsrcWord3M);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vc + off), (short)0, nrec, kRsrcWord3M);
+#pragma unroll
+    for (int u = 0; u < NI; ++u) kr[u] = __builtin_amdgcn_raw_buffer_load_b128(rk, lane_off, u * TPI * row_bytes, AUX);
+#pragma unroll
+    for (int u = 0; u < NI; ++u) vr[u] = __builtin_amdgcn_raw_buffer_load_b128(rv, lane_off, u * TPI * row_bytes, AUX);
+    if (good) ok = nv >= 16 ? 0xffffu : ((1u << nv) - 1u);
+  } else {
+    // One resource per instruction; instructions 0 .. NI/2-1 read block ph0
+    // (tokens tile .. tile+7), the others block ph1.
+#pragma unroll
+    for (int u = 0; u < NI; ++u) {
+      const int t0 = tile + u * TPI;                   // first token of this instruction
+      const int phys = u * TPI >= 8 ? ph1 : ph0;
+      const int nv = min(TPI, t_end - t0);             // valid rows of this instruction
+      const bool good = live && (unsigned)phys < (unsigned)prm.NB && nv > 0;
+      const size_t off = (size_t)(good ? phys : 0) * blk_bytes + (size_t)(t0 & prm.bs_mask) * row_bytes;
+      const int nrec = good ? nv * (int)row_bytes : 0;
+      const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(kc + off), (short)0, nrec, kRsrcWord3M);
+      const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vc + off), (short)0, nrec, kRsrcWord3M);
+      kr[u] = __builtin_amdgcn_raw_buffer_load_b128(rk, lane_off, 0, AUX);
+      vr[u] = __builtin_amdgcn_raw_buffer_load_b128(rv, lane_off, 0, AUX);
+      if (good) ok |= ((1u << nv) - 1u) << (u * TPI);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  return ok;
+}
+
+// Online-softmax state of one unit: column col's reference maximum m (base-2
+// units, uniform over the four groups) and -m, this lane's share of the
+// running sum, and the O^T accumulators.
+template <int D>
+struct Fold {
+  float m, mneg, lsum;
+  f32x4 o[Geo<D>::NPV];
+  __device__ __forceinline__ void reset() {
+    m = -INFINITY;
+    mneg = 0.0f;
+    lsum = 0.0f;
+#pragma unroll
+    for (int j = 0; j < Geo<D>::NPV; ++j) o[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+};
+
+// Per-lane LDS addresses: where the tile's loads are written, and where the
+// K operand (row tk) and the transposed V operand (rows tv.., d offset dv)
+// are read.
+template <int D>
+struct LdsMap {
+  int wr[Geo<D>::NI];
+  int tk, tv, dv;
+  __device__ __forceinline__ explicit LdsMap(int lane) {
+    constexpr int PPR = Geo<D>::PPR, TPI = Geo<D>::TPI;
+#pragma unroll
+    for (int u = 0; u < Geo<D>::NI; ++u) {
+      const int t = u * TPI + lane / PPR, pc = lane % PPR;
+      wr[u] = (t * PPR + (pc ^ swz<PPR>(t))) * 16;
+    }
+    tk = lane & 15;
+    tv = 4 * (lane >> 4) + ((lane & 15) >> 2);
+    dv = 4 * (lane & 3);
+  }
+};
+
+// Folds one loaded tile into the unit's state.
+template <int D>
+__device__ __forceinline__ void fold_tile(uint32_t ok, const u32x4m (&kr)[Geo<D>::NI],
+                                          const u32x4m (&vr)[Geo<D>::NI], const bf16x8 (&qop)[Geo<D>::NQK],
+                                          float cs, const LdsMap<D>& map, int lane, Fold<D>& st,
+                                          uint8_t* __restrict__ lds_k, uint8_t* __restrict__ lds_v) {
+  constexpr int PPR = Geo<D>::PPR, NI = Geo<D>::NI, NQK = Geo<D>::NQK, NPV = Geo<D>::NPV;
+  const int grp = lane >> 4;
+  // Stage the tile in LDS (the previous tile's reads were issued earlier by
+  // this wavefront, and LDS serves one wavefront's accesses in order).
+#pragma unroll
+  for (int u = 0; u < NI; ++u) {
+    *reinterpret_cast<u32x4m*>(lds_k + map.wr[u]) = kr[u];
+    *reinterpret_cast<u32x4m*>(lds_v + map.wr[u]) = vr[u];
+  }
+  // S = K_tile . Q^T: lane holds S[token 4 grp + i][head col].
+  f32x4 s = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int c = 0; c < NQK; ++c) {
+    const int pc = 4 * c + grp;
+    const bf16x8 a = *reinterpret_cast<const bf16x8*>(lds_k + (map.tk * PPR + (pc ^ swz<PPR>(map.tk))) * 16);
+    s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[c], s, 0, 0, 0);
+  }
+  float sc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bool valid = (ok >> (4 * grp + i)) & 1u;
+    sc[i] = valid ? s[i] * cs : -INFINITY;
+  }
+  float mt = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+  mt = groups_max(mt);
+  if (__builtin_amdgcn_ballot_w64(mt > st.m + kSlackM)) {   // wavefront-uniform, rare
+    if (mt > st.m) {
+      const float corr = exp2m(st.m - mt);                  // 0 while m is -inf
+      st.m = mt;
+      st.mneg = -mt;
+      st.lsum *= corr;
+#pragma unroll
+      for (int j = 0; j < NPV; ++j) st.o[j] *= corr;
+    }
+  }
+  float pr[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    pr[i] = exp2m(sc[i] + st.mneg);
+    st.lsum += pr[i];
+  }
+  bf16x4 pb;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) pb[i] = (__bf16)pr[i];
+  // O^T += V_tile^T . P^T, one 16-column d chunk per product.
+#pragma unroll
+  for (int j = 0; j < NPV; ++j) {
+    const int d = 16 * j + map.dv;
+    const int pc = d >> 3;
+    const int addr = (map.tv * PPR + (pc ^ swz<PPR>(map.tv))) * 16 + (d & 7) * 2;
+    const s16x4 vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(lds_v + addr));
+    st.o[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, vt), pb, st.o[j], 0, 0, 0);
+  }
+}
+
+// Writes a finished unit: the final bf16 output of a one-partition sequence,
+// else the fp32 partial (acc, m, l) of partition p for the merge kernel.
+template <int D>
+__device__ __forceinline__ void store_unit(const DecodeParams& prm, const Unit& u, int lane, const Fold<D>& st) {
+  constexpr int NPV = Geo<D>::NPV;
+  const int G = prm.H / prm.KVH;
+  const int col = lane & 15, grp = lane >> 4;
+  const bool head_ok = col < min(16, G - u.chunk * 16);
+  const float L = groups_sum(st.lsum);
+  const size_t bh = (size_t)u.b * prm.H + u.kvh * G + u.chunk * 16 + col;
+  // (structured branches only: an early return under the per-lane head_ok
+  // would make the compiler treat the caller's later state as divergent)
+  if (u.np <= 1) {
+    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+    uint16_t* outp = static_cast<uint16_t*>(prm.out) + bh * D;
+    if (head_ok) {
+#pragma unroll
+      for (int j = 0; j < NPV; ++j) {
+        bf16x4 w;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = (__bf16)(st.o[j][i] * inv);
+        *reinterpret_cast<bf16x4*>(outp + 16 * j + 4 * grp) = w;
+      }
+    }
+  } else {
+    const size_t slot = bh * prm.maxP + u.p;
+    float* dst = prm.ws_acc + slot * D;
+    if (head_ok) {
+#pragma unroll
+      for (int j = 0; j < NPV; ++j) *reinterpret_cast<f32x4*>(dst + 16 * j + 4 * grp) = st.o[j];
+      if (grp == 0) *reinterpret_cast<float2*>(prm.ws_ml + slot * 2) = make_float2(st.m, L);
+    }
+  }
+}
+
+}  // namespace
+
+// Grid form (sequence counts beyond the persistent form's list): one
 // workgroup per unit.  Grid x = (kv head, head chunk) fastest, y = partition,
 // z = sequence; units past a sequence's last partition exit at once.
 template <int D, bool WholeTile>
 __global__ __launch_bounds__(64) void decode_partial_mfma_grid_kernel(const DecodeParams prm) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds_k[16 * 2 * D];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_v[16 * 2 * D];
+  using Gm = Geo<D>;
+  __shared__ __attribute__((aligned(16))) uint8_t lds_k[16 * Gm::ROWB];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_v[16 * Gm::ROWB];
+  const int lane = threadIdx.x;
+  const int b = blockIdx.z, p = blockIdx.y;
   const int kvh = blockIdx.x / prm.nchunks;
-  mfma_unit<D, WholeTile>(prm, blockIdx.z, blockIdx.y, kvh, blockIdx.x - kvh * prm.nchunks, lds_k, lds_v);
+  const int n = clamp_len(prm, prm.ctx[b]);
+  const Unit u = make_unit(prm, b, p, n, kvh, blockIdx.x - kvh * prm.nchunks);
+  if (p >= (u.np > 0 ? u.np : 1)) return;
+  // lane l: table entry j_first + l of the partition (0 past its blocks)
+  const int j_first = u.t_begin >> prm.bs_log2;
+  const int j_end = (u.t_end + prm.bs_mask) >> prm.bs_log2;
+  const int tbl = (j_first + lane < j_end) ? prm.tables[(size_t)b * prm.W + j_first + lane] : 0;
+  // the partition's first block is also the neighbour's block at that table
+  // position: a shared prefix, read with the default cache policy
+  const int nbr = neighbour(prm, b);
+  const int nbr_blocks = nbr >= 0 ? (clamp_len(prm, prm.ctx[nbr]) + prm.bs_mask) >> prm.bs_log2 : 0;
+  const bool shared = j_first < j_end && j_first < nbr_blocks &&
+                      prm.tables[(size_t)nbr * prm.W + j_first] == prm.tables[(size_t)b * prm.W + j_first];
+  const char* kc = kv_col<D>(prm.k_cache, kvh);
+  const char* vc = kv_col<D>(prm.v_cache, kvh);
+  u32x4m qr[Gm::NQK];
+  load_q<D>(prm, u, lane, qr);
+  bf16x8 qop[Gm::NQK];
+  q_operands<D>(prm, u, lane, qr, qop);
+  const LdsMap<D> map(lane);
+  const uint32_t lane_off = (uint32_t)(lane / Gm::PPR) * (uint32_t)(prm.KVH * Gm::ROWB) + (uint32_t)(lane % Gm::PPR) * 16;
+  Fold<D> st;
+  st.reset();
+  auto run = [&](auto pol) {
+    constexpr int A = decltype(pol)::aux;
+    u32x4m kA[Gm::NI], vA[Gm::NI], kB[Gm::NI], vB[Gm::NI];
+    auto load_at = [&](int i, u32x4m (&kr)[Gm::NI], u32x4m (&vr)[Gm::NI]) {
+      const int tile = u.t_begin + min(i, u.ntiles - 1) * 16;
+      const int j = (tile >> prm.bs_log2) - j_first;
+      const int ph0 = __builtin_amdgcn_readlane(tbl, j & 63);
+      const int ph1 = WholeTile ? ph0 : __builtin_amdgcn_readlane(tbl, (j + 1) & 63);
+      return load_tile<D, WholeTile, A>(prm, kc, vc, u.t_end, tile, true, ph0, ph1, lane_off, kr, vr);
+    };
+    uint32_t okA = load_at(0, kA, vA), okB;
+    for (int ip = 0; ip < (u.ntiles >> 1); ++ip) {
+      okB = load_at(2 * ip + 1, kB, vB);
+      fold_tile<D>(okA, kA, vA, qop, prm.scale_log2, map, lane, st, lds_k, lds_v);
+      okA = load_at(2 * ip + 2, kA, vA);
+      fold_tile<D>(okB, kB, vB, qop, prm.scale_log2, map, lane, st, lds_k, lds_v);
+    }
+    if (u.ntiles & 1) fold_tile<D>(okA, kA, vA, qop, prm.scale_log2, map, lane, st, lds_k, lds_v);
+  };
+  if (shared)
+    run(CachePolicy<0>{});
+  else
+    run(CachePolicy<kAuxNT>{});
+  store_unit<D>(prm, u, lane, st);
 }
 
-// Persistent form: as many workgroups as stay resident (a fixed number per
-// CU) walk a list of the units that exist, so that the chip holds its full
-// complement of wavefronts from the first tile to the drain, with no
-// workgroup dispatch between units and no empty units.
+// Persistent form: one workgroup of NW wavefronts per CU; each wavefront folds
+// a sequence of units as one continuous stream of tiles: the loads of a
+// unit's first tile (and its q) are issued while the previous unit's last
+// tile is folded, so no unit starts with an empty pipeline.
 //
-// The list: first every sequence's partitions before its last one (all full,
-// P tokens), sequence by sequence, then the last partition of each sequence;
-// each (sequence, partition) pair expands into kv heads x head chunks
-// consecutive units.  Round r of the walk hands units r*G .. r*G + G-1 to the
-// G workgroups, in forward order on even rounds and reverse order on odd
-// ones, so that a workgroup that drew a late (short) unit in one round draws
-// an early one in the next.  The list is rebuilt by every workgroup from the
-// context lengths (an exclusive scan into LDS), so all of them agree on it
-// without any communication.
-template <int D, bool WholeTile>
-__global__ __launch_bounds__(64) void decode_partial_mfma_kernel(const DecodeParams prm) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds_k[16 * 2 * D];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_v[16 * 2 * D];
-  extern __shared__ int32_t s_first[];          // [B]: list index of sequence b's first full pair
-  const int lane = threadIdx.x;
+// The unit list (built in LDS by the workgroup's first wavefront from the
+// context lengths, so that all workgroups agree on it without
+// communication): first every sequence's partitions before its last one (all
+// full, P tokens), sequence by sequence, then the last partition of each
+// sequence in decreasing length (counting sort over kBuckets length
+// classes), so that the shortest units come last; each (sequence, partition)
+// pair expands into kv heads x head chunks consecutive units.
+//
+// Workgroup c of NC owns units c, c + NC, c + 2 NC, ... (an equal share of
+// every size class).  Inside the workgroup the units are handed out in that
+// order through an LDS counter as wavefronts finish their previous one:
+// wavefronts sharing a CU stream at very different rates, and this lets the
+// faster ones take more units, so that all of a CU's wavefronts finish
+// together.
+template <int D, bool WholeTile, int NW>
+__global__ __launch_bounds__(64 * NW) void decode_partial_mfma_kernel(const DecodeParams prm) {
+  using Gm = Geo<D>;
+  constexpr int NBUF = 2;   // tiles in flight per wavefront (3 measured no faster)
+  __shared__ __attribute__((aligned(16))) uint8_t lds_tiles[NW][2][16 * Gm::ROWB];
+  __shared__ int32_t s_cnt[kBuckets];
+  __shared__ uint32_t s_next;         // next unit (in the workgroup's share) to hand out
+  __shared__ int32_t s_shared;        // some sequence starts with its neighbour's first block
+  extern __shared__ int32_t s_list[];
   const int B = prm.B, P = prm.P;
-  auto nparts_of = [&](int b) {
-    int n = prm.ctx[b];
-    n = n < 0 ? 0 : (n > prm.max_tokens ? prm.max_tokens : n);
-    return (n + P - 1) / P;
+  int32_t* s_first = s_list;          // [B] list index of sequence b's first full pair
+  int32_t* s_len = s_list + B;        // [B] clamped context length
+  int32_t* s_last = s_list + 2 * B;   // [B] sequences in last-pair order
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t NC = gridDim.x, wg = blockIdx.x;
+  uint8_t* lds_k = lds_tiles[wave][0];
+  uint8_t* lds_v = lds_tiles[wave][1];
+
+  // ---- the unit list (first wavefront) ----
+  const int tmax = (P + 15) >> 4;     // tiles of a full partition
+  auto last_class = [&](int n) {      // 0 = longest last partition
+    const int np = (n + P - 1) / P;
+    const int lt = (n - (np > 1 ? (np - 1) * P : 0) + 15) >> 4;
+    return (kBuckets - 1) - lt * (kBuckets - 1) / tmax;
   };
-  int carry = 0;
-  for (int base = 0; base < B; base += 64) {
-    const int b = base + lane;
-    int f = 0;
-    if (b < B) {
-      const int np = nparts_of(b);
-      f = np > 1 ? np - 1 : 0;
-    }
-    int incl = f;
+  if (wave == 0) {
+    s_cnt[lane] = 0;
+    if (lane == 0) s_next = NW;
+    int carry = 0;
+    bool shared = false;
+    for (int base = 0; base < B; base += 64) {
+      const int b = base + lane;
+      const int n = b < B ? clamp_len(prm, prm.ctx[b]) : 0;
+      {
+        // entry 0 of every table row exists; it is compared only when both
+        // sequences use it
+        const int nb = b < B ? neighbour(prm, b) : -1;
+        const int nn = nb >= 0 ? clamp_len(prm, prm.ctx[nb]) : 0;
+        const int e0 = b < B ? prm.tables[(size_t)b * prm.W] : -1;
+        const int e1 = nb >= 0 ? prm.tables[(size_t)nb * prm.W] : -2;
+        shared |= __ballot(n > 0 && nn > 0 && e0 == e1) != 0;
+      }
+      const int np = (n + P - 1) / P;
+      const int f = (b < B && np > 1) ? np - 1 : 0;
+      int incl = f;
 #pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int y = __shfl_up(incl, d);
-      if (lane >= d) incl += y;
+      for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(incl, d);
+        if (lane >= d) incl += y;
+      }
+      if (b < B) {
+        s_first[b] = carry + incl - f;
+        s_len[b] = n;
+        atomicAdd(&s_cnt[last_class(n)], 1);
+      }
+      carry += __builtin_amdgcn_readlane(incl, 63);
     }
-    if (b < B) s_first[b] = carry + incl - f;
-    carry += __builtin_amdgcn_readlane(incl, 63);
+    {
+      const int c = s_cnt[lane];
+      int incl = c;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(incl, d);
+        if (lane >= d) incl += y;
+      }
+      s_cnt[lane] = incl - c;
+    }
+    for (int base = 0; base < B; base += 64) {
+      const int b = base + lane;
+      if (b < B) s_last[atomicAdd(&s_cnt[last_class(s_len[b])], 1)] = b;
+    }
+    if (lane == 0) {
+      s_shared = shared ? 1 : 0;
+      s_cnt[0] = carry;               // pairs of full partitions (the bucket bases are no longer needed)
+    }
   }
   __syncthreads();
-  const uint32_t F = (uint32_t)carry;           // pairs of full partitions
+
+  const uint32_t F = (uint32_t)__builtin_amdgcn_readfirstlane(s_cnt[0]);   // pairs of full partitions
   const uint32_t upp = (uint32_t)(prm.KVH * prm.nchunks);
   const uint32_t nunits = (F + (uint32_t)B) * upp;
-  const uint32_t G = gridDim.x;
-  const int stride = (B + 63) >> 6;             // sequences per lane in the first search level
+  const int stride = (B + 63) >> 6;                   // sequences per lane in the first search level
 
-  uint32_t t = blockIdx.x;
-  for (uint32_t round = 1; t < nunits; ++round) {
+  auto describe = [&](uint32_t t) -> Unit {
     const uint32_t pair = t / upp, sub = t - pair * upp;
     int b, p;
     if (pair < F) {
@@ -369,20 +528,167 @@ __global__ __launch_bounds__(64) void decode_partial_mfma_kernel(const DecodePar
       const int i2 = seg * stride + lane;
       const uint64_t m2 = __ballot(lane < stride && i2 < B && (uint32_t)s_first[i2 < B ? i2 : 0] <= pair);
       b = __builtin_amdgcn_readfirstlane(seg * stride + __popcll(m2) - 1);
-      p = (int)(pair - (uint32_t)s_first[b]);
+      p = (int)(pair - (uint32_t)__builtin_amdgcn_readfirstlane(s_first[b]));
     } else {
-      b = (int)(pair - F);
-      const int np = nparts_of(b);
+      b = __builtin_amdgcn_readfirstlane(s_last[pair - F]);
+      p = -1;
+    }
+    const int n = __builtin_amdgcn_readfirstlane(s_len[b]);
+    if (p < 0) {
+      const int np = (n + P - 1) / P;
       p = np > 0 ? np - 1 : 0;
     }
     const int kvh = (int)(sub / (uint32_t)prm.nchunks);
-    mfma_unit<D, WholeTile>(prm, b, p, kvh, (int)sub - kvh * prm.nchunks, lds_k, lds_v);
-    t = round * G + ((round & 1) ? G - 1 - blockIdx.x : blockIdx.x);
+    return make_unit(prm, b, p, n, kvh, (int)sub - kvh * prm.nchunks);
+  };
+
+  auto walk = [&](auto pol) {
+    constexpr int A = decltype(pol)::aux;
+    const LdsMap<D> map(lane);
+    const uint32_t lane_off = (uint32_t)(lane / Gm::PPR) * (uint32_t)(prm.KVH * Gm::ROWB) + (uint32_t)(lane % Gm::PPR) * 16;
+    const float cs = prm.scale_log2;
+    // Block-table entries are read with scalar loads (uniform addresses), one
+    // tile ahead of the buffer loads that use them.
+    typedef const __attribute__((address_space(4))) int32_t ctab_t;
+    ctab_t* ctab = (ctab_t*)prm.tables;
+
+    // State flags of the walk, kept in one word (separate bool variables
+    // updated on different paths get merged by the compiler into stores
+    // through a selected address, which keeps them in scratch memory):
+    //   kNOk     N exists
+    //   kNTaken  the producer has moved on to N
+    //   kDead    the producer has no further unit
+    //   kPending the producer waits for the unit after N
+    //   kAlive   the walk goes on
+    enum : uint32_t { kNOk = 1, kNTaken = 2, kDead = 4, kPending = 8, kAlive = 16 };
+    uint32_t fl = kAlive;
+    auto has = [&](uint32_t f) { return (fl & f) != 0; };
+
+    // C: the unit being folded; N: the next one.
+    Unit C = describe(wg + (uint32_t)wave * NC);
+    Unit N = C;
+    auto next_unit = [&]() {
+      uint32_t k = 0;
+      if (lane == 0) k = atomicAdd(&s_next, 1u);
+      k = __builtin_amdgcn_readlane(k, 0);
+      const uint32_t un = wg + k * NC;
+      fl = un < nunits ? (fl | kNOk) : (fl & ~kNOk);
+      if (un < nunits) N = describe(un);
+    };
+    next_unit();
+
+    u32x4m qr[Gm::NQK], qn[Gm::NQK];
+    load_q<D>(prm, C, lane, qr);
+    bf16x8 qop[Gm::NQK];
+    q_operands<D>(prm, C, lane, qr, qop);
+    Fold<D> st;
+    st.reset();
+    int c_tile = 0;            // tiles of C folded
+    // Producer cursor: the next tile to load is tile l_tile of unit L (C, or
+    // N once taken, whose q then goes to qn), with block ids ph0/ph1
+    // requested by scalar loads when the cursor moved there (dead: there is
+    // no further unit).
+    Unit L = C;
+    int l_tile = 0, ph0 = -1, ph1 = -1;
+
+    auto request_blocks = [&]() {
+      const int tile = L.t_begin + 16 * l_tile;
+      const int j = tile >> prm.bs_log2;
+      ph0 = -1;
+      ph1 = -1;
+      if (tile < L.t_end) ph0 = ctab[(size_t)L.b * prm.W + j];
+      if (!WholeTile && tile + 8 < L.t_end) ph1 = ctab[(size_t)L.b * prm.W + j + 1];
+    };
+    // Loads the next tile of the stream into (kr, vr); returns whether it is
+    // a real tile (false: the stream is dead, or waits for a unit the
+    // consumer has not handed out yet).
+    auto produce = [&](u32x4m (&kr)[Gm::NI], u32x4m (&vr)[Gm::NI], uint32_t& ok) -> bool {
+      // L exhausted: move on to N (its q first, so that it is older than the
+      // tile loads the fold of N's first tile waits for), or wait for the
+      // consumer to hand N out, or stop.  (Flags are assigned outright: a
+      // store chosen between two flags would keep them in scratch memory.)
+      const bool exhausted = !has(kDead | kPending) && l_tile >= L.ntiles;
+      if (exhausted) fl |= !has(kNOk) ? kDead : (has(kNTaken) ? kPending : kNTaken);
+      if (exhausted && has(kNOk) && (fl & kPending) == 0) {
+        L = N;
+        l_tile = 0;
+        load_q<D>(prm, N, lane, qn);
+        request_blocks();
+      }
+      const bool live = (fl & (kDead | kPending | kAlive)) == kAlive;
+      ok = load_tile<D, WholeTile, A>(prm, kv_col<D>(prm.k_cache, L.kvh), kv_col<D>(prm.v_cache, L.kvh),
+                                      L.t_end, L.t_begin + 16 * l_tile, live, ph0, ph1, lane_off, kr, vr);
+      if (live) {
+        ++l_tile;
+        if (l_tile < L.ntiles) request_blocks();
+      }
+      return live;
+    };
+    // Folds one tile of C; at C's last tile, writes C and moves to N, or
+    // ends the walk (alive = false) when there is no further unit.
+    auto consume = [&](bool real, uint32_t ok, const u32x4m (&kr)[Gm::NI], const u32x4m (&vr)[Gm::NI]) {
+      if (!real || !has(kAlive)) return;
+      fold_tile<D>(ok, kr, vr, qop, cs, map, lane, st, lds_k, lds_v);
+      if (++c_tile < C.ntiles) return;
+      store_unit<D>(prm, C, lane, st);
+      if (!has(kNOk)) {
+        fl &= ~kAlive;
+        return;
+      }
+      // the tiles of a unit are loaded after all of the previous unit's, so
+      // the producer has taken N by now
+      C = N;
+      q_operands<D>(prm, C, lane, qn, qop);
+      st.reset();
+      c_tile = 0;
+      fl &= ~(kNTaken | kPending);   // a waiting producer moves on at its next load
+      next_unit();
+    };
+
+    // NBUF tiles in flight: the producer runs NBUF-1 tiles ahead of the
+    // folds, in a rotation of register buffers.
+    request_blocks();
+    u32x4m kA[Gm::NI], vA[Gm::NI], kB[Gm::NI], vB[Gm::NI];
+    uint32_t okA, okB;
+    bool rA = produce(kA, vA, okA), rB;
+    // One exit, at the end of the loop body (an exit after every fold would
+    // give the compiler paths that skip loads, and stricter load waits).
+    if constexpr (NBUF == 2) {
+      do {
+        rB = produce(kB, vB, okB);
+        consume(rA, okA, kA, vA);
+        rA = produce(kA, vA, okA);
+        consume(rB, okB, kB, vB);
+      } while (has(kAlive));
+    } else {
+      u32x4m kC[Gm::NI], vC[Gm::NI];
+      uint32_t okC;
+      bool rC;
+      rB = produce(kB, vB, okB);
+      do {
+        rC = produce(kC, vC, okC);
+        consume(rA, okA, kA, vA);
+        rA = produce(kA, vA, okA);
+        consume(rB, okB, kB, vB);
+        rB = produce(kB, vB, okB);
+        consume(rC, okC, kC, vC);
+      } while (has(kAlive));
+    }
+  };
+  // Blocks shared between sequences (a common prefix) are likely to be read
+  // again by other workgroups: keep the default cache policy for them.
+  // Otherwise every K/V row is read once, and the loads are non-temporal.
+  if (wg + (uint32_t)wave * NC < nunits) {
+    if (__builtin_amdgcn_readfirstlane(s_shared))
+      walk(CachePolicy<0>{});
+    else
+      walk(CachePolicy<kAuxNT>{});
   }
 }
 
 namespace {
 constexpr int kMaxPersistentSeqs = 4096;   // the pair search covers 64 x 64 sequences
+constexpr size_t kMinLdsPerCU = 82 * 1024; // more than half of a CU's 160 KiB of LDS
 
 int device_cus() {
   static int cus[64] = {0};
@@ -398,20 +704,18 @@ int device_cus() {
 
 template <int D, bool WholeTile>
 hipError_t launch_mfma(const DecodeParams& prm, hipStream_t stream) {
-  if (prm.B <= kMaxPersistentSeqs) {
-    const size_t lds = (size_t)prm.B * sizeof(int32_t);
-    int per_cu = 0;
-    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &per_cu, reinterpret_cast<const void*>(&decode_partial_mfma_kernel<D, WholeTile>), 64, lds);
-    const int cus = device_cus();
-    if (e == hipSuccess && per_cu > 0 && cus > 0) {
-      if (per_cu > kPersistentWavesPerCU) per_cu = kPersistentWavesPerCU;
-      const int64_t units_max = (int64_t)prm.B * prm.maxP * prm.KVH * prm.nchunks;
-      const int64_t wgs = (int64_t)per_cu * cus < units_max ? (int64_t)per_cu * cus : units_max;
-      hipLaunchKernelGGL((decode_partial_mfma_kernel<D, WholeTile>), dim3((uint32_t)wgs), dim3(64), lds, stream,
-                         prm);
-      return hipGetLastError();
-    }
+  // Wavefronts per CU: two per SIMD while a wavefront needs at most half a
+  // SIMD's registers (head_dim <= 128), else one.
+  constexpr int NW = D <= 128 ? 8 : 4;
+  const int cus = device_cus();
+  if (prm.B <= kMaxPersistentSeqs && cus > 0) {
+    // the list, padded so that a second workgroup never fits on the same CU
+    size_t lds = (size_t)prm.B * 3 * sizeof(int32_t);
+    const size_t fixed = sizeof(uint8_t) * NW * 2 * 16 * 2 * D + 64 * 4 + 8;
+    if (lds + fixed < kMinLdsPerCU) lds = kMinLdsPerCU - fixed;
+    hipLaunchKernelGGL((decode_partial_mfma_kernel<D, WholeTile, NW>), dim3((uint32_t)cus), dim3(64 * NW), lds,
+                       stream, prm);
+    return hipGetLastError();
   }
   const dim3 grid(prm.KVH * prm.nchunks, prm.maxP, prm.B);
   hipLaunchKernelGGL((decode_partial_mfma_grid_kernel<D, WholeTile>), grid, dim3(64), 0, stream, prm);
