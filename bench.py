@@ -13,6 +13,11 @@ of the previous step.  The flush reads rather than writes: a written buffer
 would leave dirty lines whose write-back would share the timed step's
 bandwidth.  ``--hot`` skips the flush.
 
+The timed step is the three kernels (write, partials, merge) launched one
+after another on one stream.  The same step captured in a HIP graph and
+replayed is timed too (`graph_step_us`): on this stack a replay takes longer
+than the three launches.
+
 Prints ONE JSON line.  `value` = KV bytes the decode must read (sum over
 sequences of n_b * 2 * KVH * D * elem) / mean step time, in GB/s (10^9 B/s).
 """
@@ -146,6 +151,7 @@ def main():
     ap.add_argument("--partition", type=int, default=0, help="tokens per split-KV partition (0 = library's choice)")
     ap.add_argument("--hot", action="store_true", help="do not flush the last-level cache between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="skip the graph-replay timing")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="before the steps, run a plain fp32 copy of MIB MiB three times (the reference "
@@ -261,6 +267,38 @@ def main():
     k3 = [e[2].elapsed_time(e[3]) * 1e3 for e in kev]
     mean = lambda x: sum(x) / len(x)
 
+    # The same step captured once in a HIP graph (the library enqueues only
+    # kernels: no host synchronisation, allocation or memset) and replayed;
+    # the flush stays outside.  Reported beside the step, not as the step.
+    gst = []
+    if not args.no_graph:
+        graph = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap):
+            write()
+            partials()
+            merge()                     # warm the capture stream once
+        torch.cuda.current_stream().wait_stream(cap)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph):
+            write()
+            partials()
+            merge()
+        torch.cuda.synchronize()
+        for _ in range(args.warmup):
+            do_flush()
+            graph.replay()
+        gev = [(ev(), ev()) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            do_flush()
+            gev[i][0].record()
+            graph.replay()
+            gev[i][1].record()
+        torch.cuda.synchronize()
+        gst = [a.elapsed_time(b) * 1e3 for a, b in gev]
+
     def pct(x, q):
         s = sorted(x)
         return s[min(len(s) - 1, int(q * len(s)))]
@@ -270,7 +308,8 @@ def main():
     row = cfg.num_kv_heads * D * elem
     n_valid = int((w.slot_mapping >= 0).sum())
     write_bytes = n_valid * row * 2 * 2 + 8 * w.slot_mapping.numel()
-    step_us, wr_us, k2_us, k3_us = mean(st), mean(wr), mean(k2), mean(k3)
+    step_us = mean(st)
+    wr_us, k2_us, k3_us = mean(wr), mean(k2), mean(k3)
     dec_us = k2_us + k3_us
     value = kv_bytes / (step_us * 1e-6) / 1e9
     achieved = kv_bytes / (k2_us * 1e-6) / 1e9
@@ -300,13 +339,15 @@ def main():
         "decode_kv_GBps": round(kv_bytes / (dec_us * 1e-6) / 1e9, 1),
         "partial_kernel_us": round(k2_us, 2),
         "merge_kernel_us": round(k3_us, 2),
-        "step_us_p10_p50_p90": [round(pct(st, 0.1), 2), round(pct(st, 0.5), 2), round(pct(st, 0.9), 2)],
+        "step_us_p10_p50_p90": [round(pct(st, q), 2) for q in (0.1, 0.5, 0.9)],
+        "graph_step_us": round(mean(gst), 2) if gst else None,
         "write_us": round(wr_us, 2),
         "write_GBps": round(write_bytes / (wr_us * 1e-6) / 1e9, 2),
         "kv_bytes_per_step": kv_bytes,
         "wall_ms_per_step_incl_flush": round(wall / args.steps * 1e3, 4),
-        "timing": "step = events around write + partial + merge kernels; per-kernel times from a "
-                  "second pass with events around each kernel (each includes ~1-3 us of event/launch gap)",
+        "timing": "step = events around the write, partial and merge kernels launched one after another "
+                  "(graph_step_us: the same step replayed from a HIP graph); per-kernel times from a second "
+                  "pass with events around each kernel (each includes ~1-3 us of event/launch gap)",
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 1),

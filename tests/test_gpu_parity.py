@@ -314,3 +314,54 @@ def test_full_size_config(name):
                    w.scale, cfg.dtype)
     assert_matches_oracle(out[sel], ref, cfg.dtype, name)
     assert bool(torch.isfinite(out.float()).all())
+
+
+def test_graph_replay_of_write_and_decode():
+    """The write and both decode kernels captured in one HIP graph and
+    replayed: every replay, with eager work on the stream between replays,
+    gives the eager result (the library enqueues kernels only)."""
+    _say("graph replay")
+    w = make_custom(num_seqs=6, num_heads=16, num_kv_heads=4, head_dim=128, block_size=16,
+                    dtype="bf16", lens=[1, 40, 300, 1100, 2500, 17], seed=77, device="cuda")
+    B, H, W = w.q.shape[0], w.q.shape[1], w.block_tables.shape[1]
+    P = 256
+    kc, vc = w.k_cache.clone(), w.v_cache.clone()
+    # the new rows are written at each sequence's last position
+    k_new = torch.randn(B, 4, 128, device="cuda").to(torch.bfloat16)
+    v_new = torch.randn(B, 4, 128, device="cuda").to(torch.bfloat16)
+    lens = w.context_lens.cpu().tolist()
+    tbl = w.block_tables.cpu()
+    slots = torch.tensor([int(tbl[b, (n - 1) // 16]) * 16 + (n - 1) % 16 for b, n in enumerate(lens)],
+                         dtype=torch.int64, device="cuda")
+    ws = pk.new_workspace(B, H, W, kc, P)
+    out = torch.empty_like(w.q)
+
+    def step():
+        pk.write_kv(kc, vc, k_new, v_new, slots)
+        pk.decode(w.q, kc, vc, w.block_tables, w.context_lens, w.scale, out=out, workspace=ws,
+                  partition_size=P)
+
+    ko, vo = stored_np(kc).copy(), stored_np(vc).copy()
+    O.write_kv(ko, vo, stored_np(k_new), stored_np(v_new), stored_np(slots))
+    ref = O.decode(stored_np(w.q), ko, vo, stored_np(w.block_tables), stored_np(w.context_lens),
+                   w.scale, "bf16")
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        step()
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+    eager = out.clone()
+    assert_matches_oracle(eager, ref, "bf16", "eager step")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    junk = torch.empty(1 << 24, device="cuda")
+    for rep in range(4):
+        out.fill_(float("nan"))
+        junk.normal_()                              # unrelated eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {rep}"
+        assert np.array_equal(stored_np(kc), ko) and np.array_equal(stored_np(vc), vo)
