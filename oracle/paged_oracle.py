@@ -17,6 +17,10 @@ Sources (titles of the pages, with the section each function follows):
        inference-learning-path.pages.dev, sections 直接答案 and 代码 (the
        online-softmax fold over the block table).
 
+``prefill`` (several new queries per sequence) is the varlen version [P1]
+asks for in 面试官追问 & 对照源码 without defining it; it takes the plainest
+reading that [P1] 细节 supports (see its docstring).
+
 Every function here is pinned by ``tests/test_oracle_pins.py`` against values
 the pages print, closed forms, invariants and brute force; none is "parity
 unpinned".
@@ -37,6 +41,8 @@ __all__ = [
     "gather_context",
     "decode",
     "decode_online_fold",
+    "query_positions",
+    "prefill",
     "OracleError",
 ]
 
@@ -240,4 +246,70 @@ def decode_online_fold(q, k_cache, v_cache, block_tables, context_lens, scale,
                     pos += 1
             if n:
                 out[b, h] = [a / l for a in acc]
+    return out
+
+
+# ---------------------------------------------------------------------------
+# prefill: many new queries per sequence ([P1] 面试官追问 asks for the varlen
+# prefill version; [P1] 细节 gives the reason decode has no causal mask)
+# ---------------------------------------------------------------------------
+
+def query_positions(n: int, num_queries: int) -> np.ndarray:
+    """Positions of a sequence's new queries: they are its last num_queries
+    tokens (already written into the cache, as the newest token is in decode,
+    [P1] 细节), so query i sits at position n - num_queries + i."""
+    if num_queries < 0 or num_queries > n:
+        raise OracleError(f"{num_queries} new queries do not fit a context of {n} tokens")
+    return np.arange(n - num_queries, n, dtype=np.int64)
+
+
+def prefill(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
+            block_tables: np.ndarray, context_lens: np.ndarray,
+            query_start_loc: np.ndarray, scale: float, dtype: str) -> np.ndarray:
+    """Paged attention of a packed (varlen) batch of new queries, in float64.
+
+    Reading of the pages (they pose the question and stop there):
+      * q is [T, H, D]: sequence b owns rows query_start_loc[b] ..
+        query_start_loc[b+1] - 1 (query_start_loc[0] = 0, non-decreasing,
+        query_start_loc[B] = T), L_b of them;
+      * context_lens[b] = n_b counts every token of the sequence, the L_b new
+        ones included (their K/V rows are written before the call, as decode's
+        newest token is), and query i of the sequence is token n_b - L_b + i;
+      * decode needs no causal mask only because its one query is the newest
+        token ([P1] 细节); with several, query at position p attends to the
+        tokens 0..p of the gathered context and to nothing after it;
+      * everything else is decode's definition: the same gather (table order,
+        ceil(n/bs) entries, cut to n rows), the GQA map h // (H/KVH), the scale
+        on the scores before the softmax.
+    L_b = 1 for every b is exactly decode.  Returns the unrounded float64
+    output [T, H, D]; rows of no sequence (none, given the preconditions) stay 0.
+    """
+    T, H, D = q.shape
+    KVH = k_cache.shape[2]
+    if k_cache.shape[3] != D:
+        raise OracleError("head_dim of q and cache differ")
+    if H % KVH:
+        raise OracleError("num_heads must be a multiple of num_kv_heads")
+    qs = np.asarray(query_start_loc, dtype=np.int64)
+    B = len(context_lens)
+    if len(qs) != B + 1 or qs[0] != 0 or qs[-1] != T or np.any(np.diff(qs) < 0):
+        raise OracleError("query_start_loc must run from 0 to T without decreasing")
+    qf = stored_to_f64(q, dtype)
+    out = np.zeros((T, H, D), dtype=np.float64)
+    for b in range(B):
+        n = int(context_lens[b])
+        s0, s1 = int(qs[b]), int(qs[b + 1])
+        pos = query_positions(n, s1 - s0)
+        if s1 == s0:
+            continue
+        Kb = stored_to_f64(gather_context(k_cache, block_tables[b], n), dtype)   # [n, KVH, D]
+        Vb = stored_to_f64(gather_context(v_cache, block_tables[b], n), dtype)
+        visible = np.arange(n)[None, :] <= pos[:, None]                          # [L, n] causal mask
+        for h in range(H):
+            kvh = kv_head_of(h, H, KVH)
+            s = scale * (qf[s0:s1, h, :] @ Kb[:, kvh, :].T)                     # [L, n], scaled first
+            s = np.where(visible, s, -np.inf)
+            e = np.exp(s - s.max(axis=1, keepdims=True))
+            p = e / e.sum(axis=1, keepdims=True)
+            out[s0:s1, h] = p @ Vb[:, kvh, :]
     return out

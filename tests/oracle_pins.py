@@ -363,6 +363,142 @@ def pin_n_zero_and_errors(O):
         O.write_kv(kc.copy(), kc.copy(), np.ones((2, 1, 2), np.float32), np.ones((2, 1, 2), np.float32), np.array([1, 1]))
 
 
+# ---------------------------------------------------------------------------
+# prefill pins (the varlen version [P1] 面试官追问 asks for; [P1] 细节: decode
+# needs no causal mask because its single query is the newest token)
+# ---------------------------------------------------------------------------
+
+def _prefill_case(rng, lens, qlens, KVH, G, D, bs, tail_value=55555):
+    """Random paged case: per-sequence contiguous K/V placed in a shuffled
+    pool, packed queries [T, H, D] and query_start_loc."""
+    Ks = [rng.standard_normal((n, KVH, D)).astype(np.float32).astype(np.float64) for n in lens]
+    Vs = [rng.standard_normal((n, KVH, D)).astype(np.float32).astype(np.float64) for n in lens]
+    kc, vc, tables, cl = _paged_from_dense(rng, Ks, Vs, bs, extra_blocks=2, tail_value=tail_value)
+    T = int(sum(qlens))
+    q = rng.standard_normal((T, KVH * G, D)).astype(np.float32)
+    qs = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int64)
+    return Ks, Vs, kc, vc, tables, cl, q, qs
+
+
+def pin_prefill_brute_force(O):
+    """Causal attention of each new query over the tokens up to its own
+    position, with the key/value rows found by walking the table token by
+    token (block table[j // bs], offset j % bs) and scalar Python loops; fp64
+    agreement to 1e-12.  Lengths cover 1, multiples of bs and others; query
+    counts cover 0, 1, all of the context and a part of it."""
+    rng = np.random.default_rng(31)
+    for trial in range(8):
+        bs = int(rng.choice([1, 2, 3, 4]))
+        KVH = int(rng.choice([1, 2]))
+        G = int(rng.choice([1, 2, 3]))
+        D = int(rng.choice([1, 3, 4]))
+        lens = [1, bs * int(rng.integers(1, 4)), int(rng.integers(2, 11)), int(rng.integers(1, 9))]
+        qlens = [1, lens[1], int(rng.integers(1, lens[2])), 0]
+        Ks, Vs, kc, vc, tables, cl, q, qs = _prefill_case(rng, lens, qlens, KVH, G, D, bs)
+        scale = float(rng.uniform(0.2, 1.3))
+        out = O.prefill(q, kc, vc, tables, cl, qs, scale, "f32")
+        H = KVH * G
+        for b, n in enumerate(lens):
+            for i in range(qlens[b]):
+                p = n - qlens[b] + i
+                row = int(qs[b]) + i
+                for h in range(H):
+                    c = h // G
+                    keys, vals = [], []
+                    for j in range(p + 1):
+                        blk = int(tables[b][j // bs])
+                        keys.append([float(x) for x in kc[blk, j % bs, c]])
+                        vals.append([float(x) for x in vc[blk, j % bs, c]])
+                    ref = _dense_attention_loops([float(x) for x in q[row, h]], keys, vals, scale)
+                    assert np.allclose(out[row, h], ref, atol=1e-12, rtol=1e-12), (trial, b, i, h)
+
+
+def pin_prefill_one_query_is_decode(O):
+    """With one new query per sequence the query is the newest token and sees
+    the whole context: prefill reduces to decode ([P1] 细节), which the
+    decode pins fix.  Agreement to 1e-13."""
+    rng = np.random.default_rng(32)
+    lens = [1, 5, 8, 13]
+    Ks, Vs, kc, vc, tables, cl, q, qs = _prefill_case(rng, lens, [1, 1, 1, 1], KVH=2, G=2, D=4, bs=4)
+    a = O.prefill(q, kc, vc, tables, cl, qs, 0.7, "f32")
+    b = O.decode(q, kc, vc, tables, cl, 0.7, "f32")
+    assert np.allclose(a, b, atol=1e-13, rtol=1e-13)
+
+
+def pin_prefill_zero_keys_running_mean(O):
+    """Closed form: with every key zero all visible scores are equal, so the
+    softmax is uniform and query at position p returns the mean of V rows
+    0..p.  A mask that is off by one, aligned to the first token instead of
+    the last, or missing changes the mean."""
+    rng = np.random.default_rng(33)
+    lens, qlens = [7, 9], [7, 4]
+    Ks, Vs, kc, vc, tables, cl, q, qs = _prefill_case(rng, lens, qlens, KVH=1, G=2, D=3, bs=2)
+    kc = np.zeros_like(kc)
+    out = O.prefill(q, kc, vc, tables, cl, qs, 1.0, "f32")
+    for b, n in enumerate(lens):
+        for i in range(qlens[b]):
+            p = n - qlens[b] + i
+            want = Vs[b][: p + 1, 0].mean(axis=0)
+            for h in range(2):
+                assert np.allclose(out[qs[b] + i, h], want, atol=1e-14), (b, i, h)
+
+
+def pin_prefill_first_token_is_v0(O):
+    """A fresh prefill (all n tokens new): the first query sees only token 0,
+    so its output is exactly V[0] (weight 1), whatever q and K hold."""
+    rng = np.random.default_rng(34)
+    Ks, Vs, kc, vc, tables, cl, q, qs = _prefill_case(rng, [6], [6], KVH=2, G=1, D=4, bs=4)
+    q = (q * 50).astype(np.float32)
+    out = O.prefill(q, kc, vc, tables, cl, qs, 1.0, "f32")
+    for h in range(2):
+        assert np.array_equal(out[0, h], Vs[0][0, h])
+
+
+def pin_prefill_chunk_invariance(O):
+    """Chunked prefill: the same tokens' queries computed in two calls (the
+    first c tokens with context c, then the rest with context n) give what one
+    call over all n gives; position, not chunking, decides what a query sees."""
+    rng = np.random.default_rng(35)
+    n, c = 11, 4
+    Ks, Vs, kc, vc, tables, cl, q, qs = _prefill_case(rng, [n], [n], KVH=1, G=3, D=5, bs=3)
+    whole = O.prefill(q, kc, vc, tables, cl, qs, 0.9, "f32")
+    first = O.prefill(q[:c], kc, vc, tables, np.array([c]), np.array([0, c]), 0.9, "f32")
+    rest = O.prefill(q[c:], kc, vc, tables, np.array([n]), np.array([0, n - c]), 0.9, "f32")
+    assert np.allclose(np.concatenate([first, rest]), whole, atol=1e-13, rtol=1e-13)
+
+
+def pin_prefill_sdpa_fp64(O):
+    """Library routine: torch's scaled_dot_product_attention in float64 on the
+    dense per-sequence K/V, with an explicit boolean mask (query row i may
+    see keys 0 .. n - L + i) and the kv heads expanded by repeat_interleave."""
+    import torch.nn.functional as F
+    rng = np.random.default_rng(36)
+    lens, qlens = [12, 5, 9], [5, 5, 1]
+    KVH, G, D = 2, 4, 8
+    Ks, Vs, kc, vc, tables, cl, q, qs = _prefill_case(rng, lens, qlens, KVH, G, D, bs=4)
+    out = O.prefill(q, kc, vc, tables, cl, qs, 0.35, "f32")
+    for b, n in enumerate(lens):
+        L = qlens[b]
+        qt = torch.from_numpy(q[qs[b]:qs[b + 1]].astype(np.float64)).transpose(0, 1)       # [H, L, D]
+        kt = torch.from_numpy(Ks[b]).transpose(0, 1).repeat_interleave(G, dim=0)          # [H, n, D]
+        vt = torch.from_numpy(Vs[b]).transpose(0, 1).repeat_interleave(G, dim=0)
+        mask = torch.arange(n)[None, :] <= (n - L + torch.arange(L))[:, None]
+        ref = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask, scale=0.35)
+        assert np.allclose(out[qs[b]:qs[b + 1]], ref.transpose(0, 1).numpy(), atol=1e-12, rtol=1e-12), b
+
+
+def pin_prefill_errors(O):
+    """Preconditions: more new queries than context tokens, or a
+    query_start_loc that does not run from 0 to T, are errors."""
+    import pytest
+    kc = np.ones((2, 2, 1, 2), dtype=np.float32)
+    q = np.ones((3, 1, 2), dtype=np.float32)
+    with pytest.raises(O.OracleError):
+        O.prefill(q, kc, kc, np.array([[0]]), np.array([2]), np.array([0, 3]), 1.0, "f32")
+    with pytest.raises(O.OracleError):
+        O.prefill(q, kc, kc, np.array([[0, 1]]), np.array([4]), np.array([1, 3]), 1.0, "f32")
+
+
 ALL_PINS = [
     pin_bf16_widening,
     pin_m1_write_example,
@@ -378,4 +514,11 @@ ALL_PINS = [
     pin_fold_matches_direct,
     pin_scale_before_softmax,
     pin_n_zero_and_errors,
+    pin_prefill_brute_force,
+    pin_prefill_one_query_is_decode,
+    pin_prefill_zero_keys_running_mean,
+    pin_prefill_first_token_is_v0,
+    pin_prefill_chunk_invariance,
+    pin_prefill_sdpa_fp64,
+    pin_prefill_errors,
 ]

@@ -41,8 +41,8 @@ MUTANTS = {
                             "            out[b, h] = scale * (p @ Vb[:, kvh, :])\n    return out"),
     "scale_twice": ("            s = scale * (Kb[:, kvh, :] @ qf[b, h])",
                     "            s = scale * scale * (Kb[:, kvh, :] @ qf[b, h])"),
-    "kv_swapped_in_decode": ("        Kb = stored_to_f64(gather_context(k_cache,",
-                             "        Kb = stored_to_f64(gather_context(v_cache,"),
+    "kv_swapped_in_decode": ("        Kb = stored_to_f64(gather_context(k_cache, block_tables[b], n), dtype)  #",
+                             "        Kb = stored_to_f64(gather_context(v_cache, block_tables[b], n), dtype)  #"),
     "no_max_shift_normalisation": ("            p = e / e.sum()", "            p = e / e.max()"),
     "q_head_index": ("            s = scale * (Kb[:, kvh, :] @ qf[b, h])",
                      "            s = scale * (Kb[:, kvh, :] @ qf[b, kvh])"),
@@ -54,6 +54,21 @@ MUTANTS = {
                            "                    c = 1.0"),
     "fold_sum_unscaled": ("                    l = l * c + p", "                    l = l + p"),
     "fold_off_by_one": ("                    if pos >= n:", "                    if pos > n:"),
+    # prefill (causal varlen)
+    "prefill_mask_excludes_self": ("        visible = np.arange(n)[None, :] <= pos[:, None]",
+                                   "        visible = np.arange(n)[None, :] < pos[:, None]"),
+    "prefill_no_mask": ("            s = np.where(visible, s, -np.inf)\n", ""),
+    "prefill_top_left_alignment": ("    return np.arange(n - num_queries, n, dtype=np.int64)",
+                                   "    return np.arange(0, num_queries, dtype=np.int64)"),
+    "prefill_query_rows_shifted": ("            s = scale * (qf[s0:s1, h, :] @ Kb[:, kvh, :].T)",
+                                   "            s = scale * (qf[s0 + (s1 - s0 > 1):s1 + (s1 - s0 > 1), h, :] @ Kb[:, kvh, :].T)"),
+    "prefill_kv_head_mod": ("        for h in range(H):\n            kvh = kv_head_of(h, H, KVH)\n            s = scale * (qf[s0:s1",
+                            "        for h in range(H):\n            kvh = h % KVH\n            s = scale * (qf[s0:s1"),
+    "prefill_scale_dropped": ("            s = scale * (qf[s0:s1, h, :] @ Kb[:, kvh, :].T)",
+                              "            s = (qf[s0:s1, h, :] @ Kb[:, kvh, :].T)"),
+    "prefill_softmax_over_queries": ("            p = e / e.sum(axis=1, keepdims=True)",
+                                     "            p = e / e.sum(axis=0, keepdims=True)"),
+    "prefill_v_from_k": ("            out[s0:s1, h] = p @ Vb[:, kvh, :]", "            out[s0:s1, h] = p @ Kb[:, kvh, :]"),
 }
 
 
