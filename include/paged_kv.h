@@ -1,6 +1,6 @@
 /*
- * paged_kv.h — C ABI of the paged KV-cache write and paged decode attention
- * for AMD Instinct MI355X (gfx950).
+ * paged_kv.h — C ABI of the paged KV-cache write, paged decode attention and
+ * paged (varlen, causal) prefill attention for AMD Instinct MI355X (gfx950).
  *
  * The operations are the ones defined on the page "P09 · Paged KV 写入 +
  * decode attention（参考实现）" (kuanzhou.online), sections 题面速览 and
@@ -176,6 +176,46 @@ int pa_decode_merge(void* out, const int32_t* context_lens,
                     int32_t num_seqs, int32_t num_heads, int32_t max_blocks_per_seq,
                     const pa_cache_desc* desc, int32_t partition_size,
                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pa_prefill — paged attention of a packed (varlen) batch of new query tokens,
+ * causal within each sequence (prefill, or one chunk of a chunked prefill).
+ * "P09 · Paged KV 写入 + decode attention" (kuanzhou.online) asks for this
+ * varlen prefill in 面试官追问 & 对照源码 without defining it; this is the
+ * reading its 细节 supports (decode needs no causal mask only because its one
+ * query is the newest token):
+ *   sequence b owns q rows query_start_loc[b] .. query_start_loc[b+1] - 1
+ *   (L_b of them); they are its last L_b tokens, whose K/V rows are already in
+ *   the cache (pa_write_kv first), so query i is token p = n_b - L_b + i with
+ *   n_b = context_lens[b]; it attends to tokens 0 .. p of the sequence,
+ *   gathered through block_tables exactly as pa_decode does:
+ *   out[row, h] = softmax_{j <= p}(scale * q[row, h] . K_b[j, kvh]) . V_b[:, kvh],
+ *   kvh = h / (H / KVH); fp32 scores and softmax, out rounded to bf16.
+ * With L_b = 1 for every b this is pa_decode.
+ *
+ *   out               device, [num_tokens, H, D] bf16 (written; rows of no
+ *                     sequence are left untouched)
+ *   q                 device, [num_tokens, H, D] bf16
+ *   k_cache, v_cache  device, [NB, bs, KVH, D] bf16
+ *   block_tables      device, [B, max_blocks_per_seq] int32; row b's first
+ *                     ceil(n_b / bs) entries are read
+ *   context_lens      device, [B] int32, n_b (new tokens included)
+ *   query_start_loc   device, [B + 1] int32, non-decreasing from 0 to num_tokens
+ *   scale             multiplies q.k before the softmax
+ *   num_tokens        T >= 0 (T == 0 enqueues nothing)
+ *   max_query_len     host, >= every L_b (work is sized from it; queries of a
+ *                     sequence beyond it are not computed); 0 enqueues nothing
+ *   desc              host, cache geometry; dtype must be PA_BF16
+ *                     (PA_ERR_UNSUPPORTED otherwise)
+ * Device-side preconditions as for pa_decode, plus L_b <= n_b (queries at
+ * negative positions, if any, get zeros) and query_start_loc as stated
+ * (entries are clamped to [0, num_tokens]).  No workspace is needed.
+ */
+int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
+               const int32_t* block_tables, const int32_t* context_lens,
+               const int32_t* query_start_loc, float scale, int32_t num_seqs, int32_t num_heads,
+               int32_t max_blocks_per_seq, int32_t num_tokens, int32_t max_query_len,
+               const pa_cache_desc* desc, void* stream);
 
 /* Static, NUL-terminated name of a pa_status code ("unknown status" otherwise). */
 const char* pa_status_string(int status);

@@ -1,4 +1,4 @@
-"""Paged KV-cache write and paged decode attention for AMD MI355X (gfx950).
+"""Paged KV-cache write, paged decode and paged prefill attention for AMD MI355X (gfx950).
 
 The compute path is the HIP library ``libpaged_kv.so`` (C ABI in
 ``include/paged_kv.h``); :mod:`paged_kv_cache_70_amd.api` marshals torch
@@ -16,6 +16,7 @@ from .api import (  # noqa: F401
     load_library,
     new_workspace,
     partition_size,
+    prefill,
     status_string,
     workspace_bytes,
     write_kv,

@@ -10,6 +10,7 @@ Functions keep the names of the C entry points without the ``pa_`` prefix:
     write_kv(k_cache, v_cache, k, v, slot_mapping)          -> None (in place)
     decode(q, k_cache, v_cache, block_tables, context_lens, scale, ...) -> out
     decode_partials(...), decode_merge(...)                  the two halves of decode
+    prefill(q, k_cache, v_cache, block_tables, context_lens, query_start_loc, scale, ...) -> out
     partition_size(...), workspace_bytes(...)                host-side planning queries
 """
 from __future__ import annotations
@@ -30,6 +31,7 @@ __all__ = [
     "decode",
     "decode_partials",
     "decode_merge",
+    "prefill",
     "partition_size",
     "workspace_bytes",
     "new_workspace",
@@ -82,6 +84,7 @@ def load_library() -> ctypes.CDLL:
         "pa_decode": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, f32, i32, i32, i32, pdesc, i32, vp, sz, vp]),
         "pa_decode_partials": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, f32, i32, i32, i32, pdesc, i32, vp, sz, vp]),
         "pa_decode_merge": (ctypes.c_int, [vp, vp, i32, i32, i32, pdesc, i32, vp, sz, vp]),
+        "pa_prefill": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, vp, f32, i32, i32, i32, i32, i32, pdesc, vp]),
         "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "pa_abi_version": (i32, []),
     }
@@ -240,4 +243,39 @@ def decode_merge(q_like: torch.Tensor, k_cache: torch.Tensor, block_tables: torc
                              ctypes.byref(desc), int(partition_size), _dev(workspace, "workspace"),
                              workspace.numel() * workspace.element_size(), _stream(out))
     _check("pa_decode_merge", st)
+    return out
+
+
+def prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_tables: torch.Tensor,
+            context_lens: torch.Tensor, query_start_loc: torch.Tensor, scale: float, *,
+            max_query_len: Optional[int] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Paged causal attention of a packed batch of new queries; returns ``out``
+    [T, H, D] in q's dtype.  Sequence b's queries are rows
+    query_start_loc[b] .. query_start_loc[b+1] - 1, its last tokens.
+    ``max_query_len`` (>= every sequence's query count) sizes the launch; when
+    omitted it is read back from ``query_start_loc`` (a device-to-host copy)."""
+    lib = load_library()
+    desc = cache_desc(k_cache)
+    if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
+        raise ValueError("k_cache and v_cache must match")
+    if q.dim() != 3 or q.dtype != k_cache.dtype or q.shape[2] != desc.head_dim:
+        raise ValueError("q must be [num_tokens, num_heads, head_dim] of the cache dtype")
+    T, H, _ = q.shape
+    if block_tables.dim() != 2:
+        raise ValueError("block_tables must be [num_seqs, max_blocks_per_seq]")
+    B, W = block_tables.shape
+    if tuple(context_lens.shape) != (B,) or tuple(query_start_loc.shape) != (B + 1,):
+        raise ValueError("context_lens must be [num_seqs] and query_start_loc [num_seqs + 1]")
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must be like q")
+    if max_query_len is None:
+        max_query_len = int((query_start_loc[1:] - query_start_loc[:-1]).max()) if B else 0
+    st = lib.pa_prefill(_dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                        _dev(block_tables, "block_tables", torch.int32),
+                        _dev(context_lens, "context_lens", torch.int32),
+                        _dev(query_start_loc, "query_start_loc", torch.int32), float(scale), B, H, W, T,
+                        int(max_query_len), ctypes.byref(desc), _stream(q))
+    _check("pa_prefill", st)
     return out

@@ -15,7 +15,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libpaged_kv.so")
-SOURCES = ["pa_api.hip", "pa_write.hip", "pa_decode.hip", "pa_decode_mfma.hip"]
+SOURCES = ["pa_api.hip", "pa_write.hip", "pa_decode.hip", "pa_decode_mfma.hip", "pa_prefill.hip"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep the compiler from forming v_pk_{add,mul,fma}_f32.

@@ -185,13 +185,23 @@ static int decode_params(void* out, const void* q, const void* k_cache, const vo
   return PA_OK;
 }
 
+// Prefill launch shape: query heads per workgroup (the largest of 4, 2, 1
+// dividing G) and query tokens per workgroup (4 wavefronts x 32 queries, 16
+// for head_dim 256, shared by hg heads).
+static int32_t prefill_heads_per_group(int32_t G) {
+  return G % 4 == 0 ? 4 : (G % 2 == 0 ? 2 : 1);
+}
+static int32_t prefill_query_tile(int32_t D, int32_t hg) {
+  return (D >= 256 ? 16 : 32) * 4 / hg;
+}
+
 }  // namespace pa
 
 using namespace pa;
 
 extern "C" {
 
-int32_t pa_abi_version(void) { return (1 << 16) | 0; }
+int32_t pa_abi_version(void) { return (1 << 16) | 1; }
 
 const char* pa_status_string(int status) {
   switch (status) {
@@ -297,6 +307,56 @@ int pa_decode_merge(void* out, const int32_t* context_lens, int32_t num_seqs, in
   return decode_common(false, true, out, nullptr, nullptr, nullptr, nullptr, context_lens, 1.0f,
                        num_seqs, num_heads, max_blocks_per_seq, desc, partition_size, workspace,
                        workspace_bytes, stream);
+}
+
+int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
+               const int32_t* block_tables, const int32_t* context_lens,
+               const int32_t* query_start_loc, float scale, int32_t num_seqs, int32_t num_heads,
+               int32_t max_blocks_per_seq, int32_t num_tokens, int32_t max_query_len,
+               const pa_cache_desc* desc, void* stream) {
+  int st = check_desc(desc);
+  if (st) return st;
+  const int32_t B = num_seqs, H = num_heads, W = max_blocks_per_seq;
+  if (B <= 0 || H <= 0 || W <= 0 || num_tokens < 0 || max_query_len < 0) return PA_ERR_SHAPE;
+  if (H % desc->num_kv_heads) return PA_ERR_SHAPE;
+  if (desc->dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
+  const int64_t max_len = (int64_t)W * desc->block_size;
+  if (max_len > INT_MAX / 2) return PA_ERR_TOO_LARGE;
+  if (num_tokens == 0 || max_query_len == 0) return PA_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start_loc)
+    return PA_ERR_NULL;
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_ALIGN;
+  PrefillParams p;
+  const int32_t G = H / desc->num_kv_heads;
+  p.hg = prefill_heads_per_group(G);
+  p.nchunks = G / p.hg;
+  p.tq = prefill_query_tile(desc->head_dim, p.hg);
+  const int32_t Lmax = max_query_len < num_tokens ? max_query_len : num_tokens;
+  p.qtiles = (Lmax + p.tq - 1) / p.tq;
+  const int64_t units = (int64_t)B * desc->num_kv_heads * p.nchunks * p.qtiles;
+  if (units > INT_MAX) return PA_ERR_TOO_LARGE;
+  p.out = out;
+  p.q = q;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.tables = block_tables;
+  p.ctx = context_lens;
+  p.qstart = query_start_loc;
+  const float s2 = scale * 1.4426950408889634f;   // log2(e)
+  p.q_mode = s2 > 0.0f ? 0 : (s2 < 0.0f ? 1 : 2);
+  p.scale_log2 = s2 > 0.0f ? s2 : (s2 < 0.0f ? -s2 : 1.0f);
+  p.B = B;
+  p.H = H;
+  p.KVH = desc->num_kv_heads;
+  p.W = W;
+  p.NB = desc->num_blocks;
+  p.T = num_tokens;
+  p.bs_log2 = ilog2(desc->block_size);
+  p.bs_mask = desc->block_size - 1;
+  p.max_tokens = (int32_t)max_len;
+  return launch_prefill_mfma(p, desc->head_dim, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? PA_OK
+             : PA_ERR_LAUNCH;
 }
 
 }  // extern "C"

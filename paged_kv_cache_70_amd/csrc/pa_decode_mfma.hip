@@ -26,59 +26,13 @@
 // the unrounded fp32 values).
 #include <math.h>
 
-#include "pa_internal.h"
+#include "pa_mfma_tile.h"
 
 namespace pa {
 
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4m __attribute__((ext_vector_type(4)));
-
-constexpr int kRsrcWord3M = 0x00020000;   // raw untyped buffer access, gfx9 family
-constexpr float kSlackM = 8.0f;           // lazy-rescale slack (base-2 units)
 constexpr int kBuckets = 64;              // length classes of the last-partition ordering
-
-__device__ __forceinline__ float exp2m(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// max / sum over the four 16-lane groups (lanes xor 16, xor 32)
-__device__ __forceinline__ float groups_max(float x) {
-  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-__device__ __forceinline__ float groups_sum(float x) {
-  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-
-// LDS slot swizzle: 16-byte piece pc of token row t is stored at piece
-// pc ^ sw(t) of the row.  sw is a permutation of the 16 rows' residues so that
-// the K operand reads (16 rows, one piece each) and the transposed V reads
-// (4 rows, two adjacent pieces each) fall in distinct bank groups.
-template <int PPR>
-__device__ __forceinline__ int swz(int t) {
-  if constexpr (PPR >= 16)
-    return ((t & 7) << 1) | (t >> 3);
-  else
-    return t >> 1;
-}
-
-template <int D>
-struct Geo {
-  static constexpr int ROWB = D * 2;        // bytes of one (token, kv head) row
-  static constexpr int PPR = ROWB / 16;     // 16-byte pieces per row
-  static constexpr int TPI = 64 / PPR;      // token rows per load instruction
-  static constexpr int NI = 16 / TPI;       // load instructions per 16-token tile (K, and again V)
-  static constexpr int NQK = D / 32;        // QK products (32 d each)
-  static constexpr int NPV = D / 16;        // PV products (16 d columns each)
-};
 
 // One work unit: partition p of sequence b (n tokens, np partitions), kv head
 // kvh, query-head chunk chunk (up to 16 heads of the kv head's group), tokens
@@ -112,12 +66,6 @@ __device__ __forceinline__ int neighbour(const DecodeParams& prm, int b) {
 
 __device__ __forceinline__ int clamp_len(const DecodeParams& prm, int n) {
   return n < 0 ? 0 : (n > prm.max_tokens ? prm.max_tokens : n);
-}
-
-// The kv head's column of the caches.
-template <int D>
-__device__ __forceinline__ const char* kv_col(const void* cache, int kvh) {
-  return static_cast<const char*>(cache) + (size_t)kvh * Geo<D>::ROWB;
 }
 
 // Raw Q^T operands of a unit: lane holds q[head col][32 c + 8 grp .. + 8] of
@@ -156,68 +104,6 @@ __device__ __forceinline__ void q_operands(const DecodeParams& prm, const Unit& 
   }
 }
 
-template <int A>
-struct CachePolicy {
-  static constexpr int aux = A;
-};
-constexpr int kAuxNT = 2;   // buffer-load cache policy bit "nt": non-temporal (streaming) access
-
-// Loads of the 16-token tile starting at token `tile` of a partition ending
-// at t_end: instruction u brings token rows u * TPI + lane / PPR, piece
-// lane % PPR, of the kv head (kc, vc: the kv head's column of the caches).
-// ph0 is the physical block holding the tile's first token, ph1 (blocks of 8
-// tokens only) the next one.  A buffer resource starts at the first row it
-// covers and ends after the last valid row of the partition, so rows past the
-// end (and blocks outside the pool, and every row of a dead load) read zeros.
-// AUX is the loads' cache policy: kAuxNT when the rows are read once in this
-// call, 0 (default) when other sequences are likely to read the same blocks
-// (a shared prefix).
-// Returns the tile's row validity mask (bit r: row r holds a token).
-// WholeTile: block_size >= 16, so a tile (tiles start at multiples of 16,
-// partitions at multiples of the block size) lies inside one block;
-// otherwise the block size is 8 and a tile spans two blocks.
-template <int D, bool WholeTile, int AUX>
-__device__ __forceinline__ uint32_t load_tile(const DecodeParams& prm, const char* kc, const char* vc, int t_end,
-                                              int tile, bool live, int ph0, int ph1, uint32_t lane_off,
-                                              u32x4m (&kr)[Geo<D>::NI], u32x4m (&vr)[Geo<D>::NI]) {
-  constexpr int TPI = Geo<D>::TPI, NI = Geo<D>::NI;
-  const uint32_t row_bytes = (uint32_t)prm.KVH * Geo<D>::ROWB;
-  const size_t blk_bytes = (size_t)row_bytes << prm.bs_log2;
-  uint32_t ok = 0;
-  if constexpr (WholeTile) {
-    const int nv = min(16, t_end - tile);               // valid rows of the tile
-    const bool good = live && (unsigned)ph0 < (unsigned)prm.NB && nv > 0;
-    const size_t off = (size_t)(good ? ph0 : 0) * blk_bytes + (size_t)(tile & prm.bs_mask) * row_bytes;
-    const int nrec = good ? nv * (int)row_bytes : 0;
-    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(kc + off), (short)0, nrec, kRsrcWord3M);
-    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vc + off), (short)0, nrec, kRsrcWord3M);
-#pragma unroll
-    for (int u = 0; u < NI; ++u) kr[u] = __builtin_amdgcn_raw_buffer_load_b128(rk, lane_off, u * TPI * row_bytes, AUX);
-#pragma unroll
-    for (int u = 0; u < NI; ++u) vr[u] = __builtin_amdgcn_raw_buffer_load_b128(rv, lane_off, u * TPI * row_bytes, AUX);
-    if (good) ok = nv >= 16 ? 0xffffu : ((1u << nv) - 1u);
-  } else {
-    // One resource per instruction; instructions 0 .. NI/2-1 read block ph0
-    // (tokens tile .. tile+7), the others block ph1.
-#pragma unroll
-    for (int u = 0; u < NI; ++u) {
-      const int t0 = tile + u * TPI;                   // first token of this instruction
-      const int phys = u * TPI >= 8 ? ph1 : ph0;
-      const int nv = min(TPI, t_end - t0);             // valid rows of this instruction
-      const bool good = live && (unsigned)phys < (unsigned)prm.NB && nv > 0;
-      const size_t off = (size_t)(good ? phys : 0) * blk_bytes + (size_t)(t0 & prm.bs_mask) * row_bytes;
-      const int nrec = good ? nv * (int)row_bytes : 0;
-      const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(kc + off), (short)0, nrec, kRsrcWord3M);
-      const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vc + off), (short)0, nrec, kRsrcWord3M);
-      kr[u] = __builtin_amdgcn_raw_buffer_load_b128(rk, lane_off, 0, AUX);
-      vr[u] = __builtin_amdgcn_raw_buffer_load_b128(rv, lane_off, 0, AUX);
-      if (good) ok |= ((1u << nv) - 1u) << (u * TPI);
-    }
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  return ok;
-}
-
 // Online-softmax state of one unit: column col's reference maximum m (base-2
 // units, uniform over the four groups) and -m, this lane's share of the
 // running sum, and the O^T accumulators.
@@ -231,26 +117,6 @@ struct Fold {
     lsum = 0.0f;
 #pragma unroll
     for (int j = 0; j < Geo<D>::NPV; ++j) o[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  }
-};
-
-// Per-lane LDS addresses: where the tile's loads are written, and where the
-// K operand (row tk) and the transposed V operand (rows tv.., d offset dv)
-// are read.
-template <int D>
-struct LdsMap {
-  int wr[Geo<D>::NI];
-  int tk, tv, dv;
-  __device__ __forceinline__ explicit LdsMap(int lane) {
-    constexpr int PPR = Geo<D>::PPR, TPI = Geo<D>::TPI;
-#pragma unroll
-    for (int u = 0; u < Geo<D>::NI; ++u) {
-      const int t = u * TPI + lane / PPR, pc = lane % PPR;
-      wr[u] = (t * PPR + (pc ^ swz<PPR>(t))) * 16;
-    }
-    tk = lane & 15;
-    tv = 4 * (lane >> 4) + ((lane & 15) >> 2);
-    dv = 4 * (lane & 3);
   }
 };
 

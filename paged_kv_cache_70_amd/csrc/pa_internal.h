@@ -40,6 +40,27 @@ struct DecodePlan {
   int32_t tile_unroll;     // 16-byte loads per K (and per V) per tile and lane
 };
 
+// Paged prefill (bf16, matrix cores): a packed batch of new queries per
+// sequence, causal over the sequence's paged K/V.
+struct PrefillParams {
+  void* out;               // [T, H, D] bf16
+  const void* q;           // [T, H, D] bf16
+  const void* k_cache;     // [NB, bs, KVH, D] bf16
+  const void* v_cache;
+  const int32_t* tables;   // [B, W]
+  const int32_t* ctx;      // [B] tokens of each sequence, its new ones included
+  const int32_t* qstart;   // [B + 1] first q row of each sequence
+  float scale_log2;        // |scale| * log2(e) > 0
+  int32_t q_mode;          // 0: q as given, 1: negate q (scale < 0), 2: zero q (scale == 0)
+  int32_t B, H, KVH, W, NB, T;
+  int32_t bs_log2, bs_mask;
+  int32_t max_tokens;      // W * bs: context lengths are clamped to this
+  int32_t hg;              // query heads per workgroup (4, 2 or 1, dividing G)
+  int32_t nchunks;         // G / hg
+  int32_t tq;              // query tokens per workgroup (128 / hg)
+  int32_t qtiles;          // query tiles per (sequence, kv head, chunk) at the longest query run
+};
+
 bool dtype_ok(int32_t dtype);
 int32_t elem_bytes(int32_t dtype);
 
@@ -51,6 +72,8 @@ hipError_t launch_decode_partials(const DecodeParams& prm, int32_t dtype, int32_
                                   const DecodePlan& plan, hipStream_t stream);
 
 hipError_t launch_decode_partials_mfma(const DecodeParams& prm, int32_t D, hipStream_t stream);
+
+hipError_t launch_prefill_mfma(const PrefillParams& prm, int32_t D, hipStream_t stream);
 
 hipError_t launch_decode_merge(const DecodeParams& prm, int32_t dtype, int32_t D,
                                hipStream_t stream);

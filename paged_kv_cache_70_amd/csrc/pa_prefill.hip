@@ -1,0 +1,329 @@
+// Paged prefill attention for gfx950, bf16 caches: a packed (varlen) batch of
+// new query tokens per sequence, each attending causally over its sequence's
+// paged K/V.
+//
+// Operation: the varlen prefill that "P09 · Paged KV 写入 + decode attention"
+// (kuanzhou.online) asks for in 面试官追问 & 对照源码, read with that page's
+// 细节: decode needs no causal mask only because its single query is the
+// newest token; with L new queries (the last L of the sequence's n tokens,
+// already in the cache), the query at position p sees tokens 0 .. p.  Gather,
+// GQA map and scale are decode's (题面速览 and the decode shape trace).
+//
+// Work decomposition: one workgroup of 4 wavefronts per (sequence, kv head,
+// chunk of hg query heads of its group, tile of tq query tokens), hg * tq =
+// 128 query rows, 32 per wavefront (one head, 32 consecutive tokens; 64 and
+// 16 for head_dim 256).  Keys are
+// walked in 64-token tiles: each wavefront loads one 16-token subtile of K and
+// V through the block table (the same 16-byte buffer loads as decode) and
+// writes it to a double-buffered LDS tile; after one barrier all four
+// wavefronts read the whole tile as matrix operands:
+//   S^T  = K_tile (64 x D) . Q^T (D x 32)        v_mfma_f32_16x16x32_bf16
+//   O^T += V_tile^T (D x 64) . P^T (64 x 32)      v_mfma_f32_16x16x32_bf16
+// The PV product contracts over 32 keys as [keys 0-15 of a pair of 16-key
+// blocks, keys 16-31] in the order lane group g holds them in the S^T
+// accumulators (keys 4g .. 4g+3 of each block): any order of the contraction
+// index is correct as long as both operands use it, so the probabilities go
+// from the accumulators into the B operand without leaving their lane, and
+// the A operand is two transposing LDS reads (ds_read_b64_tr_b16) of the two
+// blocks.  The online softmax (running max and sum per query column) is the
+// decode kernel's, in base-2 units.
+//
+// Causality costs no extra pass: the key loop of a workgroup ends at its last
+// query's position, tiles entirely visible to a wavefront's 32 queries skip
+// the mask, and tiles after a wavefront's last query skip its products.
+#include <math.h>
+
+#include "pa_mfma_tile.h"
+
+namespace pa {
+
+namespace {
+
+constexpr int kWaves = 4;          // wavefronts per workgroup
+constexpr int kKeyTile = 64;       // keys staged per step (one 16-row subtile per wavefront)
+constexpr int kNKB = kKeyTile / 16;
+constexpr int kXcds = 8;           // accelerator complex dies: workgroup i runs on die i % 8
+
+// Workgroups are dealt round-robin to the dies, each with its own L2.  Give
+// die x a contiguous range of logical units instead, so the query tiles of one
+// (sequence, kv head), which re-read the same K/V, share one L2.
+__device__ __forceinline__ int xcd_order(int id, int n) {
+  const int die = id % kXcds, k = id / kXcds;
+  const int per = n / kXcds, rem = n % kXcds;
+  return die < rem ? die * (per + 1) + k : rem * (per + 1) + (die - rem) * per + k;
+}
+
+// 16-query column blocks per wavefront: 2 (32 queries), 1 for D = 256, where
+// two blocks' accumulators and operands would not fit the register file.
+template <int D>
+constexpr int query_blocks() { return D >= 256 ? 1 : 2; }
+
+// Online-softmax state of one wavefront's QB x 16 query columns: reference
+// maximum (base-2 units, uniform over the four lane groups of a column) and
+// its negation, this lane's share of the running sum, and the O^T
+// accumulators (lane: query column lane % 16 of block qb, d = 16 j + 4 (lane
+// / 16) + i).
+template <int D, int QB = query_blocks<D>()>
+struct PState {
+  float m[QB], mneg[QB], lsum[QB];
+  f32x4 o[D / 16][QB];
+};
+
+// Folds one staged 64-key tile (keys t0 ..) into the state.  Masked: apply
+// the causal mask key <= qpos and the tile's row validity bits okw (bit r: key
+// t0 + r was loaded from a block inside the pool).
+template <int D, bool Masked, int kQB = query_blocks<D>()>
+__device__ __forceinline__ void fold_keys(const uint8_t* __restrict__ lk, const uint8_t* __restrict__ lv,
+                                          uint64_t okw, int t0, const int (&qpos)[kQB],
+                                          const bf16x8 (&qop)[kQB][Geo<D>::NQK], float cs,
+                                          const LdsMap<D>& map, int lane, PState<D>& st) {
+  constexpr int ROWB = Geo<D>::ROWB, PPR = Geo<D>::PPR, NQK = Geo<D>::NQK, NDJ = D / 16;
+  const int grp = lane >> 4;
+  // S^T = K . Q^T: s[kb][qb] lane holds keys 16 kb + 4 grp + i of query column (lane % 16) of block qb.
+  f32x4 s[kNKB][kQB];
+#pragma unroll
+  for (int kb = 0; kb < kNKB; ++kb) {
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) s[kb][qb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    const uint8_t* rowk = lk + (16 * kb + map.tk) * ROWB;
+#pragma unroll
+    for (int c = 0; c < NQK; ++c) {
+      const int pc = 4 * c + grp;
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(rowk + (pc ^ swz<PPR>(map.tk)) * 16);
+#pragma unroll
+      for (int qb = 0; qb < kQB; ++qb) s[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[qb][c], s[kb][qb], 0, 0, 0);
+    }
+  }
+  bf16x8 pb[kNKB / 2][kQB];
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb) {
+    float mt = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < kNKB; ++kb) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float v = s[kb][qb][i] * cs;
+        if constexpr (Masked) {
+          const int r = 16 * kb + 4 * grp + i;
+          const bool ok = ((okw >> r) & 1u) && t0 + r <= qpos[qb];
+          v = ok ? v : -INFINITY;
+        }
+        s[kb][qb][i] = v;
+        mt = fmaxf(mt, v);
+      }
+    }
+    mt = groups_max(mt);
+    if (__builtin_amdgcn_ballot_w64(mt > st.m[qb] + kSlackM)) {   // wavefront-uniform, rare after the first tiles
+      if (mt > st.m[qb]) {
+        const float corr = exp2m(st.m[qb] - mt);                    // 0 while m is -inf
+        st.m[qb] = mt;
+        st.mneg[qb] = -mt;
+        st.lsum[qb] *= corr;
+#pragma unroll
+        for (int j = 0; j < NDJ; ++j) st.o[j][qb] *= corr;
+      }
+    }
+#pragma unroll
+    for (int kk = 0; kk < kNKB / 2; ++kk) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p = exp2m(s[2 * kk + h][qb][i] + st.mneg[qb]);
+          st.lsum[qb] += p;
+          pb[kk][qb][4 * h + i] = (__bf16)p;
+        }
+      }
+    }
+  }
+  // O^T += V^T . P^T over key pairs of 16-row blocks (2 kk, 2 kk + 1).
+#pragma unroll
+  for (int j = 0; j < NDJ; ++j) {
+    const int d = 16 * j + map.dv;
+    const int pc = d >> 3;
+    const int off = (map.tv * PPR + (pc ^ swz<PPR>(map.tv))) * 16 + (d & 7) * 2;
+#pragma unroll
+    for (int kk = 0; kk < kNKB / 2; ++kk) {
+      const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4*)(lv + (32 * kk) * ROWB + off));
+      const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4*)(lv + (32 * kk + 16) * ROWB + off));
+      const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+      for (int qb = 0; qb < kQB; ++qb) st.o[j][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[kk][qb], st.o[j][qb], 0, 0, 0);
+    }
+  }
+}
+
+}  // namespace
+
+// One workgroup per (sequence, kv head, head chunk, query tile); the
+// logical unit order is sequence, kv head, chunk, then query tiles from the
+// last (most keys) to the first.  Units past a sequence's query tiles exit.
+template <int D, bool WholeTile>
+__global__ __launch_bounds__(256) void prefill_mfma_kernel(const PrefillParams prm) {
+  using Gm = Geo<D>;
+  constexpr int ROWB = Gm::ROWB, PPR = Gm::PPR, NI = Gm::NI, NQK = Gm::NQK, NDJ = D / 16;
+  constexpr int kQB = query_blocks<D>(), QW = 16 * kQB;   // query columns per wavefront
+  constexpr int TILEB = kKeyTile * ROWB;
+  __shared__ __attribute__((aligned(16))) uint8_t lds_kv[2][2][TILEB];   // [buffer][K, V][64 key rows]
+  __shared__ uint32_t lds_ok[2][kNKB];                                  // row validity of each subtile
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int grp = lane >> 4, col = lane & 15;
+
+  int u = xcd_order(blockIdx.x, gridDim.x);
+  const int x = u % prm.qtiles;
+  u /= prm.qtiles;
+  const int chunk = u % prm.nchunks;
+  u /= prm.nchunks;
+  const int kvh = u % prm.KVH;
+  const int b = u / prm.KVH;
+
+  int n = prm.ctx[b];
+  n = n < 0 ? 0 : (n > prm.max_tokens ? prm.max_tokens : n);
+  int q0 = prm.qstart[b], q1 = prm.qstart[b + 1];
+  q0 = q0 < 0 ? 0 : (q0 > prm.T ? prm.T : q0);
+  q1 = q1 < q0 ? q0 : (q1 > prm.T ? prm.T : q1);
+  const int nq = q1 - q0;
+  const int ntq = (nq + prm.tq - 1) / prm.tq;
+  if (x >= ntq) return;
+  const int tok0 = (ntq - 1 - x) * prm.tq;            // first query (index within the sequence's new ones)
+  const int tok_end = min(nq, tok0 + prm.tq);
+  const int pbase = n - nq;                           // position of new query 0 (< 0 only if nq > n)
+  const int kend = min(max(pbase + tok_end, 0), n);   // keys the workgroup's last query sees
+  const int ntiles = (kend + kKeyTile - 1) / kKeyTile;
+
+  const int G = prm.H / prm.KVH;
+  const int h = kvh * G + chunk * prm.hg + wave % prm.hg;
+  const int wtok0 = tok0 + (wave / prm.hg) * QW;
+  const int w_valid = min(QW, tok_end - wtok0);        // this wavefront's queries (<= 0: none)
+  const int wpos_lo = pbase + wtok0;
+  const int wpos_hi = pbase + wtok0 + w_valid - 1;
+
+  // Q^T operands: lane holds q[token wtok0 + 16 qb + col][h][32 c + 8 grp .. + 8];
+  // a negative scale is applied as negated q, a zero scale as zero q.
+  bf16x8 qop[kQB][NQK];
+  int qpos[kQB];
+  {
+    const uint32_t flip = prm.q_mode == 1 ? 0x80008000u : 0u;
+    const uint32_t keep = prm.q_mode == 2 ? 0u : 0xffffffffu;
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) {
+      const int tok = wtok0 + 16 * qb + col;
+      qpos[qb] = pbase + tok;
+      const size_t row = (size_t)q0 + (tok < nq ? tok : 0);
+      const uint8_t* qrow = static_cast<const uint8_t*>(prm.q) + (row * prm.H + h) * (size_t)D * 2;
+#pragma unroll
+      for (int c = 0; c < NQK; ++c) {
+        u32x4m w = *reinterpret_cast<const u32x4m*>(qrow + (32 * c + 8 * grp) * 2);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = (w[i] ^ flip) & keep;
+        qop[qb][c] = __builtin_bit_cast(bf16x8, w);
+      }
+    }
+  }
+
+  const char* kc = kv_col<D>(prm.k_cache, kvh);
+  const char* vc = kv_col<D>(prm.v_cache, kvh);
+  const uint32_t lane_off = (uint32_t)(lane / PPR) * (uint32_t)(prm.KVH * ROWB) + (uint32_t)(lane % PPR) * 16;
+  typedef const __attribute__((address_space(4))) int32_t ctab_t;
+  ctab_t* trow = (ctab_t*)(prm.tables + (size_t)b * prm.W);
+
+  // This wavefront's 16-key subtile of key tile `it`: table entries are read
+  // only for blocks holding keys below kend (entries < ceil(n / bs)).
+  auto issue = [&](int it, u32x4m (&kr)[NI], u32x4m (&vr)[NI]) -> uint32_t {
+    const int t = it * kKeyTile + wave * 16;
+    const int j = t >> prm.bs_log2;
+    const bool live = t < kend;
+    int ph0 = 0, ph1 = 0;
+    if (live) ph0 = trow[j];
+    if (!WholeTile && t + 8 < kend) ph1 = trow[j + 1];
+    return load_tile<D, WholeTile, 0>(prm, kc, vc, kend, t, live, ph0, ph1, lane_off, kr, vr);
+  };
+  const LdsMap<D> map(lane);
+  auto stage = [&](int buf, uint32_t ok, const u32x4m (&kr)[NI], const u32x4m (&vr)[NI]) {
+    uint8_t* lk = lds_kv[buf][0] + wave * 16 * ROWB;
+    uint8_t* lv = lds_kv[buf][1] + wave * 16 * ROWB;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      *reinterpret_cast<u32x4m*>(lk + map.wr[i]) = kr[i];
+      *reinterpret_cast<u32x4m*>(lv + map.wr[i]) = vr[i];
+    }
+    if (lane == 0) lds_ok[buf][wave] = ok;
+  };
+
+  PState<D> st;
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb) {
+    st.m[qb] = -INFINITY;
+    st.mneg[qb] = 0.0f;
+    st.lsum[qb] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NDJ; ++j) st.o[j][qb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+
+  u32x4m kr[NI], vr[NI];
+  if (ntiles > 0) {
+    const uint32_t ok = issue(0, kr, vr);
+    stage(0, ok, kr, vr);
+  }
+  __syncthreads();
+  for (int it = 0; it < ntiles; ++it) {
+    const int buf = it & 1;
+    const bool more = it + 1 < ntiles;
+    uint32_t ok_next = 0;
+    if (more) ok_next = issue(it + 1, kr, vr);
+    const int t0 = it * kKeyTile;
+    if (w_valid > 0 && t0 <= wpos_hi) {
+      uint64_t okw = 0;
+#pragma unroll
+      for (int kb = 0; kb < kNKB; ++kb) okw |= (uint64_t)(lds_ok[buf][kb] & 0xffffu) << (16 * kb);
+      okw = __builtin_amdgcn_readfirstlane((uint32_t)okw) | ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(okw >> 32)) << 32);
+      if (okw == ~0ull && t0 + kKeyTile - 1 <= wpos_lo)
+        fold_keys<D, false>(lds_kv[buf][0], lds_kv[buf][1], okw, t0, qpos, qop, prm.scale_log2, map, lane, st);
+      else
+        fold_keys<D, true>(lds_kv[buf][0], lds_kv[buf][1], okw, t0, qpos, qop, prm.scale_log2, map, lane, st);
+    }
+    if (more) stage(buf ^ 1, ok_next, kr, vr);
+    __syncthreads();
+  }
+
+  // out[row][h][16 j + 4 grp + i] = O^T / l for this lane's query columns.
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb) {
+    const float L = groups_sum(st.lsum[qb]);
+    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+    const int tok = wtok0 + 16 * qb + col;
+    if (tok < tok_end) {
+      uint16_t* outp = static_cast<uint16_t*>(prm.out) + (((size_t)q0 + tok) * prm.H + h) * D;
+#pragma unroll
+      for (int j = 0; j < NDJ; ++j) {
+        bf16x4 w;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = (__bf16)(st.o[j][qb][i] * inv);
+        *reinterpret_cast<bf16x4*>(outp + 16 * j + 4 * grp) = w;
+      }
+    }
+  }
+}
+
+template <int D, bool WholeTile>
+static hipError_t launch_prefill_d(const PrefillParams& prm, int64_t units, hipStream_t stream) {
+  hipLaunchKernelGGL((prefill_mfma_kernel<D, WholeTile>), dim3((unsigned)units), dim3(kWaves * 64), 0, stream, prm);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_mfma(const PrefillParams& prm, int32_t D, hipStream_t stream) {
+  const int64_t units = (int64_t)prm.B * prm.KVH * prm.nchunks * prm.qtiles;
+  const bool whole = prm.bs_log2 >= 4;
+  switch (D) {
+    case 64: return whole ? launch_prefill_d<64, true>(prm, units, stream) : launch_prefill_d<64, false>(prm, units, stream);
+    case 128: return whole ? launch_prefill_d<128, true>(prm, units, stream) : launch_prefill_d<128, false>(prm, units, stream);
+    case 256: return whole ? launch_prefill_d<256, true>(prm, units, stream) : launch_prefill_d<256, false>(prm, units, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pa

@@ -1,0 +1,152 @@
+"""Parity of the HIP paged prefill (through the C ABI) with the CPU oracle.
+
+A prefill step writes the new tokens' K/V rows (pa_write_kv) and then attends
+with their queries (pa_prefill).  The write is compared bit for bit; the
+attention within 2e-2 + 1e-2 |ref| (bf16) of the unrounded fp64 oracle,
+element by element.  Small cases cover every launch shape (heads per
+workgroup 4, 2, 1 and several head chunks; head_dim 64, 128, 256; block
+sizes 8, 16, 32) and ragged query counts (0, 1, tile multiples and
+remainders, a whole fresh prefill); the Llama-3-8B-shape chunked prefill is
+compared on sampled sequences in the launch configuration the benchmark
+times.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import paged_kv_cache_70_amd as pk
+from synth import PREFILL_CONFIGS, make_prefill, make_prefill_custom
+from tests.gpu_util import assert_matches_oracle, stored_np
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU (run with -m 'not gpu' on a CPU-only machine)")
+    pk.load_library()
+    yield
+
+
+def _say(msg):
+    print(f"[gpu-prefill] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def _gpu_step(w):
+    kc, vc = w.k_cache.clone(), w.v_cache.clone()
+    pk.write_kv(kc, vc, w.k_new, w.v_new, w.slot_mapping)
+    out = pk.prefill(w.q, kc, vc, w.block_tables, w.context_lens, w.query_start_loc, w.scale,
+                     max_query_len=w.max_query_len)
+    torch.cuda.synchronize()
+    return kc, vc, out
+
+
+def _oracle_caches(w):
+    kc, vc = stored_np(w.k_cache).copy(), stored_np(w.v_cache).copy()
+    O.write_kv(kc, vc, stored_np(w.k_new), stored_np(w.v_new), stored_np(w.slot_mapping))
+    return kc, vc
+
+
+def _check(w, what):
+    kc, vc, out = _gpu_step(w)
+    ko, vo = _oracle_caches(w)
+    assert np.array_equal(stored_np(kc), ko) and np.array_equal(stored_np(vc), vo), f"{what}: write"
+    ref = O.prefill(stored_np(w.q), ko, vo, stored_np(w.block_tables), stored_np(w.context_lens),
+                    stored_np(w.query_start_loc), w.scale, w.cfg.dtype)
+    err = assert_matches_oracle(out, ref, w.cfg.dtype, what)
+    _say(f"{what}: max err {err:.2e}")
+
+
+# (H, KVH, D, bs, cached, new): the query counts straddle the query tiles
+# (32 tokens per wavefront, 32/64/128 per workgroup for 4/2/1 heads per
+# workgroup, 16 per wavefront for D = 256) and the 64-key tiles.
+CASES = [
+    (8, 2, 128, 16, [0, 5, 100, 0, 300], [1, 40, 33, 64, 129]),        # G=4: 4 heads per workgroup
+    (8, 4, 128, 16, [17, 0, 64], [70, 65, 1]),                        # G=2: 2 heads, 64-token tiles
+    (4, 4, 128, 16, [0, 31, 200], [130, 97, 0]),                       # G=1: 128-token tiles, an empty query run
+    (6, 2, 128, 16, [3, 0], [45, 77]),                                # G=3: one head per workgroup
+    (16, 2, 128, 16, [50, 0], [40, 96]),                              # G=8: two head chunks
+    (8, 2, 64, 16, [0, 129, 7], [96, 31, 65]),                        # D=64
+    (8, 2, 256, 16, [0, 40, 128], [50, 17, 16]),                      # D=256: 16 queries per wavefront
+    (8, 2, 128, 8, [0, 9, 33], [57, 24, 8]),                          # block size 8: a 16-row subtile spans 2 blocks
+    (8, 2, 128, 32, [1, 0, 95], [64, 100, 33]),                       # block size 32
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"H{c[0]}_KVH{c[1]}_D{c[2]}_bs{c[3]}")
+def test_prefill_small(case):
+    H, KVH, D, bs, cached, new = case
+    w = make_prefill_custom(num_heads=H, num_kv_heads=KVH, head_dim=D, block_size=bs, cached=cached,
+                            new=new, seed=len(cached) * 7 + D + bs, device="cuda", poison=True)
+    _check(w, f"H{H} KVH{KVH} D{D} bs{bs} cached {cached} new {new}")
+
+
+def test_prefill_fresh_and_single_token():
+    """Whole fresh prefills (cached 0) and one-token contexts."""
+    w = make_prefill_custom(num_heads=8, num_kv_heads=2, head_dim=128, block_size=16,
+                            cached=[0, 0, 0, 0], new=[1, 2, 200, 16], seed=91, device="cuda", poison=True)
+    _check(w, "fresh prefills")
+
+
+def test_prefill_one_query_equals_decode():
+    """One new query per sequence is decode: the two HIP paths agree within
+    their rounding (both are also held to the oracle)."""
+    w = make_prefill_custom(num_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+                            cached=[0, 15, 300, 1023, 2000], new=[1, 1, 1, 1, 1], seed=92, device="cuda")
+    kc, vc, out = _gpu_step(w)
+    dec = pk.decode(w.q, kc, vc, w.block_tables, w.context_lens, w.scale)
+    torch.cuda.synchronize()
+    diff = (out.float() - dec.float()).abs().max().item()
+    assert diff <= 2e-2, diff
+
+
+def test_prefill_scale_signs():
+    """Negative and zero scales (q negated / zeroed inside the kernel)."""
+    for scale in (-0.2, 0.0):
+        w = make_prefill_custom(num_heads=8, num_kv_heads=2, head_dim=128, block_size=16,
+                                cached=[10, 0], new=[40, 70], seed=93, device="cuda")
+        w.scale = scale
+        _check(w, f"scale {scale}")
+
+
+def test_prefill_full_size_sampled():
+    """Llama-3-8B-shape chunked prefill (8 sequences, U[0,4096] cached tokens,
+    chunks of U[512,2048]) in the benchmark's launch: every output of the
+    shortest and the longest sequence against the oracle, which computes
+    those two sequences only (sequences are independent)."""
+    cfg = PREFILL_CONFIGS["prefill_8b_bf16"]
+    w = make_prefill(cfg, "cuda")
+    _say(f"prefill_8b_bf16: T={w.q.shape[0]}, cached {w.cached}, new {w.new}")
+    kc, vc, out = _gpu_step(w)
+    ko, vo = _oracle_caches(w)
+    assert np.array_equal(stored_np(kc), ko) and np.array_equal(stored_np(vc), vo), "write"
+    lens = [c + x for c, x in zip(w.cached, w.new)]
+    qsl = stored_np(w.query_start_loc)
+    for b in (int(np.argmin(lens)), int(np.argmax(lens))):
+        s0, s1 = int(qsl[b]), int(qsl[b + 1])
+        ref = O.prefill(stored_np(w.q[s0:s1]), ko, vo, stored_np(w.block_tables[b:b + 1]),
+                        stored_np(w.context_lens[b:b + 1]), np.array([0, s1 - s0]), w.scale, "bf16")
+        err = assert_matches_oracle(out[s0:s1], ref, "bf16", f"prefill_8b_bf16 seq {b}")
+        _say(f"prefill_8b_bf16 seq {b} (n={lens[b]}, new={w.new[b]}): max err {err:.2e}")
+
+
+def test_prefill_rejects_f32_and_accepts_empty():
+    kc = torch.zeros((4, 16, 2, 64), dtype=torch.float32, device="cuda")
+    q = torch.zeros((3, 4, 64), dtype=torch.float32, device="cuda")
+    bt = torch.zeros((1, 1), dtype=torch.int32, device="cuda")
+    cl = torch.tensor([3], dtype=torch.int32, device="cuda")
+    qs = torch.tensor([0, 3], dtype=torch.int32, device="cuda")
+    with pytest.raises(pk.PaError):
+        pk.prefill(q, kc, kc, bt, cl, qs, 1.0, max_query_len=3)
+    kb = kc.to(torch.bfloat16)
+    qe = torch.zeros((0, 4, 64), dtype=torch.bfloat16, device="cuda")
+    out = pk.prefill(qe, kb, kb, bt, cl, torch.tensor([0, 0], dtype=torch.int32, device="cuda"), 1.0,
+                     max_query_len=0)
+    assert out.shape == (0, 4, 64)

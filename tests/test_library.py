@@ -24,7 +24,7 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     lib = pk.load_library()
     names = _declared()
-    assert {"pa_write_kv", "pa_decode", "pa_decode_partials", "pa_decode_merge",
+    assert {"pa_write_kv", "pa_decode", "pa_decode_partials", "pa_decode_merge", "pa_prefill",
             "pa_decode_workspace_bytes", "pa_decode_partition_size",
             "pa_status_string", "pa_abi_version"} <= set(names)
     for n in names:
@@ -98,3 +98,22 @@ def test_binding_rejects_host_and_noncontiguous_tensors():
     with pytest.raises(ValueError):
         pk.write_kv(kc, kc.clone(), torch.zeros(1, 2, 64), torch.zeros(1, 2, 64),
                     torch.zeros(1, dtype=torch.int64))
+
+
+def test_prefill_host_checks():
+    """pa_prefill's argument checks run on the host and return before any
+    device work: unsupported dtype, bad sizes, empty batches, null pointers."""
+    import ctypes
+    lib = pk.load_library()
+    bf16 = pk.CacheDesc(64, 16, 2, 128, 1)
+    f32 = pk.CacheDesc(64, 16, 2, 128, 0)
+    call = lambda desc, B=2, H=8, W=4, T=10, L=5, ptr=None: lib.pa_prefill(
+        ptr, ptr, ptr, ptr, ptr, ptr, ptr, 0.1, B, H, W, T, L, ctypes.byref(desc), None)
+    assert call(f32) == -3                       # PA_ERR_UNSUPPORTED: prefill is bf16 only
+    assert call(bf16, H=7) == -2                 # H % KVH != 0
+    assert call(bf16, B=0) == -2
+    assert call(bf16, T=-1) == -2
+    assert call(bf16, T=0) == 0                  # nothing to do
+    assert call(bf16, L=0) == 0
+    assert call(bf16) == -1                      # null pointers with work to do
+    assert call(pk.CacheDesc(64, 12, 2, 128, 1)) == -3   # block size not a power of two
