@@ -20,6 +20,14 @@ than the three launches.
 
 Prints ONE JSON line.  `value` = KV bytes the decode must read (sum over
 sequences of n_b * 2 * KVH * D * elem) / mean step time, in GB/s (10^9 B/s).
+
+``--config prefill_8b_bf16`` times the paged prefill instead: one step =
+pa_write_kv of every sequence's new chunk, then pa_prefill (causal attention
+of the chunk's queries over the sequence's paged K/V), on the Llama-3-8B
+shape with 8 sequences of U[0, 4096] cached tokens and U[512, 2048]-token
+chunks.  `value` = algorithmic flops (4 * D * H per causally visible
+(query, key) pair) / mean step time, in TFLOP/s; the roofline is the bf16
+matrix-core peak.
 """
 from __future__ import annotations
 
@@ -36,7 +44,9 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores, published
 METRIC = "paged decode KV-read GB/s (% of HBM peak) + µs/step; write_kv GB/s"
+PREFILL_METRIC = "paged prefill TFLOP/s (% of bf16 MFMA peak) + µs/step"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_partial_traffic.json")
 CSRC = os.path.join(ROOT, "paged_kv_cache_70_amd", "csrc")
 # source file of the partial kernel each cache dtype runs
@@ -142,6 +152,145 @@ def _cpu_baseline(w, budget_s: float):
     }
 
 
+def _cpu_baseline_prefill(w, budget_s: float):
+    """The oracle (fp64 NumPy, untuned) on a bounded sample of the prefill
+    workload: whole sequences in a fixed shuffled order while less than
+    budget_s of CPU work has been done, scaled to TFLOP/s of the same
+    algorithmic flops."""
+    import numpy as np
+    import oracle as O
+    from tests.gpu_util import stored_np
+
+    cfg = w.cfg
+    kc, vc = stored_np(w.k_cache).copy(), stored_np(w.v_cache).copy()
+    O.write_kv(kc, vc, stored_np(w.k_new), stored_np(w.v_new), stored_np(w.slot_mapping))
+    q, tbl, lens, qsl = stored_np(w.q), stored_np(w.block_tables), stored_np(w.context_lens), stored_np(w.query_start_loc)
+    order = np.random.default_rng(0).permutation(len(lens))
+    done, flops, t = 0, 0, 0.0
+    while t < budget_s and done < 4 * len(lens):
+        b = int(order[done % len(order)])
+        s0, s1 = int(qsl[b]), int(qsl[b + 1])
+        t0 = time.perf_counter()
+        O.prefill(q[s0:s1], kc, vc, tbl[b:b + 1], lens[b:b + 1], np.array([0, s1 - s0]), w.scale, cfg.dtype)
+        t += time.perf_counter() - t0
+        L, n = s1 - s0, int(lens[b])
+        flops += 4 * cfg.head_dim * cfg.num_heads * (L * (n - L) + L * (L + 1) // 2)
+        done += 1
+    threads = 1
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([1] + [int(i.get("num_threads", 1)) for i in threadpool_info()])
+    except Exception:  # noqa: BLE001
+        pass
+    return {
+        "value": round(flops / t / 1e12, 5),
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{done} single-sequence prefills of the {len(lens)} sequences ({flops / 1e9:.1f} GFLOP) "
+                  f"in {t:.1f} s, fp64 NumPy; host has {len(os.sched_getaffinity(0))} usable cores",
+    }
+
+
+def run_prefill(args, cfg):
+    """Chunked-prefill step: write the chunks' K/V, then paged causal attention."""
+    import torch
+
+    import paged_kv_cache_70_amd as pk
+    from synth import make_prefill
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = make_prefill(cfg, dev)
+    T, H, D = w.q.shape
+    kc, vc = w.k_cache, w.v_cache
+    out = torch.empty_like(w.q)
+    flush = None if args.hot else torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    flush_sink = torch.zeros((), dtype=torch.float32, device=dev)
+
+    def write():
+        pk.write_kv(kc, vc, w.k_new, w.v_new, w.slot_mapping)
+
+    def attend():
+        pk.prefill(w.q, kc, vc, w.block_tables, w.context_lens, w.query_start_loc, w.scale,
+                   max_query_len=w.max_query_len, out=out)
+
+    def do_flush():
+        if flush is not None:
+            torch.sum(flush, dim=0, out=flush_sink)
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    for _ in range(args.warmup):
+        do_flush()
+        write()
+        attend()
+    torch.cuda.synchronize()
+    events = [(ev(), ev(), ev()) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        do_flush()
+        e = events[i]
+        e[0].record()
+        write()
+        e[1].record()
+        attend()
+        e[2].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    st = [e[0].elapsed_time(e[2]) * 1e3 for e in events]
+    wr = [e[0].elapsed_time(e[1]) * 1e3 for e in events]
+    ak = [e[1].elapsed_time(e[2]) * 1e3 for e in events]
+    mean = lambda x: sum(x) / len(x)
+    flops = w.flops()
+    step_us, wr_us, ak_us = mean(st), mean(wr), mean(ak)
+    value = flops / (step_us * 1e-6) / 1e12
+    achieved = flops / (ak_us * 1e-6) / 1e12
+    row = cfg.num_kv_heads * D * 2
+    write_bytes = T * row * 2 * 2 + 8 * T
+    res = {
+        "metric": PREFILL_METRIC,
+        "value": round(value, 1),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_us / 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded N(0,1) values, shuffled physical blocks)",
+        "config": {
+            "workload": cfg.name, "num_seqs": cfg.num_seqs, "num_heads": H, "num_kv_heads": cfg.num_kv_heads,
+            "head_dim": D, "block_size": cfg.block_size, "cached_tokens": w.cached, "new_tokens": w.new,
+            "query_tokens": T, "cache_flush_between_steps": flush is not None,
+        },
+        "flops_per_step": flops,
+        "prefill_kernel_us": round(ak_us, 2),
+        "write_us": round(wr_us, 2),
+        "write_GBps": round(write_bytes / (wr_us * 1e-6) / 1e9, 2),
+        "step_us_p10_p50_p90": [round(sorted(st)[min(len(st) - 1, int(q * len(st)))], 2) for q in (0.1, 0.5, 0.9)],
+        "wall_ms_per_step_incl_flush": round(wall / args.steps * 1e3, 4),
+        "timing": "step = events around the write and prefill kernels launched one after another; the "
+                  "prefill kernel's share from the middle event",
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 1),
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": None,
+            "kernel": "prefill_mfma_kernel",
+        },
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = _cpu_baseline_prefill(w, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -183,6 +332,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     pk.load_library()
+    from synth import PREFILL_CONFIGS
+    if args.config in PREFILL_CONFIGS:
+        return run_prefill(args, PREFILL_CONFIGS[args.config])
     cfg = CONFIGS[args.config]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

@@ -209,7 +209,10 @@ int pa_decode_merge(void* out, const int32_t* context_lens,
  *                     (PA_ERR_UNSUPPORTED otherwise)
  * Device-side preconditions as for pa_decode, plus L_b <= n_b (queries at
  * negative positions, if any, get zeros) and query_start_loc as stated
- * (entries are clamped to [0, num_tokens]).  No workspace is needed.
+ * (entries are clamped to [0, num_tokens]).  Memory safety holds when they
+ * are violated, but unlike pa_decode a table entry outside the pool is not
+ * masked out: its rows read as zeros and take part in the softmax.  No
+ * workspace is needed.
  */
 int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
                const int32_t* block_tables, const int32_t* context_lens,

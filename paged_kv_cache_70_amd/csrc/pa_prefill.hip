@@ -42,17 +42,6 @@ namespace {
 constexpr int kWaves = 4;          // wavefronts per workgroup
 constexpr int kKeyTile = 64;       // keys staged per step (one 16-row subtile per wavefront)
 constexpr int kNKB = kKeyTile / 16;
-constexpr int kXcds = 8;           // accelerator complex dies: workgroup i runs on die i % 8
-
-// Workgroups are dealt round-robin to the dies, each with its own L2.  Give
-// die x a contiguous range of logical units instead, so the query tiles of one
-// (sequence, kv head), which re-read the same K/V, share one L2.
-__device__ __forceinline__ int xcd_order(int id, int n) {
-  const int die = id % kXcds, k = id / kXcds;
-  const int per = n / kXcds, rem = n % kXcds;
-  return die < rem ? die * (per + 1) + k : rem * (per + 1) + (die - rem) * per + k;
-}
-
 // 16-query column blocks per wavefront: 2 (32 queries), 1 for D = 256, where
 // two blocks' accumulators and operands would not fit the register file.
 template <int D>
@@ -69,59 +58,86 @@ struct PState {
   f32x4 o[D / 16][QB];
 };
 
-// Folds one staged 64-key tile (keys t0 ..) into the state.  Masked: apply
-// the causal mask key <= qpos and the tile's row validity bits okw (bit r: key
-// t0 + r was loaded from a block inside the pool).
-template <int D, bool Masked, int kQB = query_blocks<D>()>
+// Folds one staged 64-key tile (keys t0 ..) into the state; masked
+// (wavefront-uniform): apply the causal mask key <= qpos.  Operand reads run
+// one group ahead of the products that use them (K: one 16-key block, V: one
+// 16-column d block), pinned in that order by scheduling barriers, so LDS
+// latency hides behind the previous group's products.
+template <int D, int kQB = query_blocks<D>()>
 __device__ __forceinline__ void fold_keys(const uint8_t* __restrict__ lk, const uint8_t* __restrict__ lv,
-                                          uint64_t okw, int t0, const int (&qpos)[kQB],
+                                          bool masked, int t0, const int (&qpos)[kQB],
                                           const bf16x8 (&qop)[kQB][Geo<D>::NQK], float cs,
                                           const LdsMap<D>& map, int lane, PState<D>& st) {
   constexpr int ROWB = Geo<D>::ROWB, PPR = Geo<D>::PPR, NQK = Geo<D>::NQK, NDJ = D / 16;
   const int grp = lane >> 4;
-  // S^T = K . Q^T: s[kb][qb] lane holds keys 16 kb + 4 grp + i of query column (lane % 16) of block qb.
-  f32x4 s[kNKB][kQB];
-#pragma unroll
-  for (int kb = 0; kb < kNKB; ++kb) {
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) s[kb][qb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  auto read_k = [&](int kb, bf16x8 (&a)[NQK]) {
     const uint8_t* rowk = lk + (16 * kb + map.tk) * ROWB;
 #pragma unroll
-    for (int c = 0; c < NQK; ++c) {
-      const int pc = 4 * c + grp;
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(rowk + (pc ^ swz<PPR>(map.tk)) * 16);
+    for (int c = 0; c < NQK; ++c)
+      a[c] = *reinterpret_cast<const bf16x8*>(rowk + ((4 * c + grp) ^ swz<PPR>(map.tk)) * 16);
+  };
+  // V^T operand of d block j for key pair kk: two transposing reads (keys
+  // 32 kk + 4 grp + i and 32 kk + 16 + 4 grp + i of d column 16 j + lane % 16).
+  auto read_v = [&](int j, bf16x8 (&a)[kNKB / 2]) {
+    const int d = 16 * j + map.dv;
+    const int off = (map.tv * PPR + ((d >> 3) ^ swz<PPR>(map.tv))) * 16 + (d & 7) * 2;
 #pragma unroll
-      for (int qb = 0; qb < kQB; ++qb) s[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[qb][c], s[kb][qb], 0, 0, 0);
+    for (int kk = 0; kk < kNKB / 2; ++kk) {
+      const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4*)(lv + (32 * kk) * ROWB + off));
+      const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4*)(lv + (32 * kk + 16) * ROWB + off));
+      a[kk] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
     }
+  };
+  // S^T = K . Q^T: s[kb][qb] lane holds keys 16 kb + 4 grp + i of query column (lane % 16) of block qb.
+  f32x4 s[kNKB][kQB];
+  bf16x8 ka[2][NQK];
+  read_k(0, ka[0]);
+#pragma unroll
+  for (int kb = 0; kb < kNKB; ++kb) {
+    if (kb + 1 < kNKB) read_k(kb + 1, ka[(kb + 1) & 1]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) s[kb][qb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int c = 0; c < NQK; ++c)
+#pragma unroll
+      for (int qb = 0; qb < kQB; ++qb)
+        s[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kb & 1][c], qop[qb][c], s[kb][qb], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // the first two V groups load while the softmax runs
+  bf16x8 va[2][kNKB / 2];
+  read_v(0, va[0]);
+  if (NDJ > 1) read_v(1, va[1]);
+  __builtin_amdgcn_sched_barrier(0);
+  if (masked) {
+#pragma unroll
+    for (int kb = 0; kb < kNKB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int qb = 0; qb < kQB; ++qb)
+          if (t0 + 16 * kb + 4 * grp + i > qpos[qb]) s[kb][qb][i] = -INFINITY;
   }
   bf16x8 pb[kNKB / 2][kQB];
 #pragma unroll
   for (int qb = 0; qb < kQB; ++qb) {
     float mt = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < kNKB; ++kb) {
+    for (int kb = 0; kb < kNKB; ++kb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float v = s[kb][qb][i] * cs;
-        if constexpr (Masked) {
-          const int r = 16 * kb + 4 * grp + i;
-          const bool ok = ((okw >> r) & 1u) && t0 + r <= qpos[qb];
-          v = ok ? v : -INFINITY;
-        }
-        s[kb][qb][i] = v;
-        mt = fmaxf(mt, v);
-      }
-    }
-    mt = groups_max(mt);
+      for (int i = 0; i < 4; ++i) mt = fmaxf(mt, s[kb][qb][i]);
+    mt = groups_max(mt) * cs;                                       // cs > 0: max of the scaled scores
     if (__builtin_amdgcn_ballot_w64(mt > st.m[qb] + kSlackM)) {   // wavefront-uniform, rare after the first tiles
-      if (mt > st.m[qb]) {
-        const float corr = exp2m(st.m[qb] - mt);                    // 0 while m is -inf
-        st.m[qb] = mt;
-        st.mneg[qb] = -mt;
-        st.lsum[qb] *= corr;
+      const float mnew = fmaxf(st.m[qb], mt);
+      const float corr = mnew > st.m[qb] ? exp2m(st.m[qb] - mnew) : 1.0f;   // 0 while m is -inf
+      st.m[qb] = mnew;
+      st.mneg[qb] = mnew == -INFINITY ? 0.0f : -mnew;
+      st.lsum[qb] *= corr;
 #pragma unroll
-        for (int j = 0; j < NDJ; ++j) st.o[j][qb] *= corr;
-      }
+      for (int j = 0; j < NDJ; ++j) st.o[j][qb] *= corr;
     }
 #pragma unroll
     for (int kk = 0; kk < kNKB / 2; ++kk) {
@@ -129,53 +145,51 @@ __device__ __forceinline__ void fold_keys(const uint8_t* __restrict__ lk, const 
       for (int h = 0; h < 2; ++h) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float p = exp2m(s[2 * kk + h][qb][i] + st.mneg[qb]);
+          const float p = exp2m(__builtin_fmaf(s[2 * kk + h][qb][i], cs, st.mneg[qb]));
           st.lsum[qb] += p;
           pb[kk][qb][4 * h + i] = (__bf16)p;
         }
       }
     }
   }
-  // O^T += V^T . P^T over key pairs of 16-row blocks (2 kk, 2 kk + 1).
+  __builtin_amdgcn_sched_barrier(0);
+  // O^T += V^T . P^T, d block by d block, reads two blocks ahead.
 #pragma unroll
   for (int j = 0; j < NDJ; ++j) {
-    const int d = 16 * j + map.dv;
-    const int pc = d >> 3;
-    const int off = (map.tv * PPR + (pc ^ swz<PPR>(map.tv))) * 16 + (d & 7) * 2;
 #pragma unroll
-    for (int kk = 0; kk < kNKB / 2; ++kk) {
-      const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) s16x4*)(lv + (32 * kk) * ROWB + off));
-      const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) s16x4*)(lv + (32 * kk + 16) * ROWB + off));
-      const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+    for (int kk = 0; kk < kNKB / 2; ++kk)
 #pragma unroll
-      for (int qb = 0; qb < kQB; ++qb) st.o[j][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[kk][qb], st.o[j][qb], 0, 0, 0);
-    }
+      for (int qb = 0; qb < kQB; ++qb)
+        st.o[j][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[j & 1][kk], pb[kk][qb], st.o[j][qb], 0, 0, 0);
+    if (j + 2 < NDJ) read_v(j + 2, va[j & 1]);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
 }  // namespace
 
-// One workgroup per (sequence, kv head, head chunk, query tile); the
-// logical unit order is sequence, kv head, chunk, then query tiles from the
-// last (most keys) to the first.  Units past a sequence's query tiles exit.
+// One workgroup per (sequence, kv head, head chunk, query tile).  Grid order:
+// query tiles counted from each sequence's end outermost, so the tiles with
+// the most keys of every sequence are dispatched first (a longest-first
+// schedule across the chip); units past a sequence's query tiles exit.
 template <int D, bool WholeTile>
-__global__ __launch_bounds__(256) void prefill_mfma_kernel(const PrefillParams prm) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 1 : 2)))
+void prefill_mfma_kernel(const PrefillParams prm) {
   using Gm = Geo<D>;
   constexpr int ROWB = Gm::ROWB, PPR = Gm::PPR, NI = Gm::NI, NQK = Gm::NQK, NDJ = D / 16;
   constexpr int kQB = query_blocks<D>(), QW = 16 * kQB;   // query columns per wavefront
   constexpr int TILEB = kKeyTile * ROWB;
   __shared__ __attribute__((aligned(16))) uint8_t lds_kv[2][2][TILEB];   // [buffer][K, V][64 key rows]
-  __shared__ uint32_t lds_ok[2][kNKB];                                  // row validity of each subtile
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int grp = lane >> 4, col = lane & 15;
 
-  int u = xcd_order(blockIdx.x, gridDim.x);
-  const int x = u % prm.qtiles;
-  u /= prm.qtiles;
+  // unit order: query tile counted from each sequence's end (outermost, so
+  // the tiles with the most keys start first), sequence, kv head, chunk
+  const int per_x = prm.B * prm.KVH * prm.nchunks;
+  const int x = blockIdx.x / per_x;
+  int u = blockIdx.x - x * per_x;
   const int chunk = u % prm.nchunks;
   u /= prm.nchunks;
   const int kvh = u % prm.KVH;
@@ -232,18 +246,19 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(const PrefillParams p
   ctab_t* trow = (ctab_t*)(prm.tables + (size_t)b * prm.W);
 
   // This wavefront's 16-key subtile of key tile `it`: table entries are read
-  // only for blocks holding keys below kend (entries < ceil(n / bs)).
-  auto issue = [&](int it, u32x4m (&kr)[NI], u32x4m (&vr)[NI]) -> uint32_t {
+  // only for blocks holding keys below kend (entries < ceil(n / bs)); rows at
+  // or past kend, and rows of a block outside the pool, read as zeros.
+  auto issue = [&](int it, u32x4m (&kr)[NI], u32x4m (&vr)[NI]) {
     const int t = it * kKeyTile + wave * 16;
     const int j = t >> prm.bs_log2;
     const bool live = t < kend;
     int ph0 = 0, ph1 = 0;
     if (live) ph0 = trow[j];
     if (!WholeTile && t + 8 < kend) ph1 = trow[j + 1];
-    return load_tile<D, WholeTile, 0>(prm, kc, vc, kend, t, live, ph0, ph1, lane_off, kr, vr);
+    (void)load_tile<D, WholeTile, 0>(prm, kc, vc, kend, t, live, ph0, ph1, lane_off, kr, vr);
   };
   const LdsMap<D> map(lane);
-  auto stage = [&](int buf, uint32_t ok, const u32x4m (&kr)[NI], const u32x4m (&vr)[NI]) {
+  auto stage = [&](int buf, const u32x4m (&kr)[NI], const u32x4m (&vr)[NI]) {
     uint8_t* lk = lds_kv[buf][0] + wave * 16 * ROWB;
     uint8_t* lv = lds_kv[buf][1] + wave * 16 * ROWB;
 #pragma unroll
@@ -251,7 +266,6 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(const PrefillParams p
       *reinterpret_cast<u32x4m*>(lk + map.wr[i]) = kr[i];
       *reinterpret_cast<u32x4m*>(lv + map.wr[i]) = vr[i];
     }
-    if (lane == 0) lds_ok[buf][wave] = ok;
   };
 
   PState<D> st;
@@ -266,27 +280,20 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(const PrefillParams p
 
   u32x4m kr[NI], vr[NI];
   if (ntiles > 0) {
-    const uint32_t ok = issue(0, kr, vr);
-    stage(0, ok, kr, vr);
+    issue(0, kr, vr);
+    stage(0, kr, vr);
   }
   __syncthreads();
   for (int it = 0; it < ntiles; ++it) {
     const int buf = it & 1;
     const bool more = it + 1 < ntiles;
-    uint32_t ok_next = 0;
-    if (more) ok_next = issue(it + 1, kr, vr);
+    if (more) issue(it + 1, kr, vr);
     const int t0 = it * kKeyTile;
     if (w_valid > 0 && t0 <= wpos_hi) {
-      uint64_t okw = 0;
-#pragma unroll
-      for (int kb = 0; kb < kNKB; ++kb) okw |= (uint64_t)(lds_ok[buf][kb] & 0xffffu) << (16 * kb);
-      okw = __builtin_amdgcn_readfirstlane((uint32_t)okw) | ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(okw >> 32)) << 32);
-      if (okw == ~0ull && t0 + kKeyTile - 1 <= wpos_lo)
-        fold_keys<D, false>(lds_kv[buf][0], lds_kv[buf][1], okw, t0, qpos, qop, prm.scale_log2, map, lane, st);
-      else
-        fold_keys<D, true>(lds_kv[buf][0], lds_kv[buf][1], okw, t0, qpos, qop, prm.scale_log2, map, lane, st);
+      const bool masked = t0 + kKeyTile - 1 > wpos_lo;
+      fold_keys<D>(lds_kv[buf][0], lds_kv[buf][1], masked, t0, qpos, qop, prm.scale_log2, map, lane, st);
     }
-    if (more) stage(buf ^ 1, ok_next, kr, vr);
+    if (more) stage(buf ^ 1, kr, vr);
     __syncthreads();
   }
 
