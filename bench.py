@@ -205,6 +205,7 @@ def run_prefill(args, cfg):
     T, H, D = w.q.shape
     kc, vc = w.k_cache, w.v_cache
     out = torch.empty_like(w.q)
+    ws = pk.prefill_workspace(cfg.num_seqs, H, T, kc)
     flush = None if args.hot else torch.ones(1 << 28, dtype=torch.float32, device=dev)
     flush_sink = torch.zeros((), dtype=torch.float32, device=dev)
 
@@ -213,7 +214,7 @@ def run_prefill(args, cfg):
 
     def attend():
         pk.prefill(w.q, kc, vc, w.block_tables, w.context_lens, w.query_start_loc, w.scale,
-                   max_query_len=w.max_query_len, out=out)
+                   out=out, workspace=ws)
 
     def do_flush():
         if flush is not None:

@@ -178,6 +178,15 @@ int pa_decode_merge(void* out, const int32_t* context_lens,
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * pa_prefill_workspace_bytes — size of the device workspace pa_prefill needs
+ * (its work plan: 16 bytes plus 4 per (sequence, query tile) pair, bounded by
+ * num_tokens / tile + num_seqs).  Depends only on its arguments.  Returns 0
+ * for invalid arguments (including a non-bf16 cache).
+ */
+size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t num_tokens,
+                                  const pa_cache_desc* desc);
+
+/*
  * pa_prefill — paged attention of a packed (varlen) batch of new query tokens,
  * causal within each sequence (prefill, or one chunk of a chunked prefill).
  * "P09 · Paged KV 写入 + decode attention" (kuanzhou.online) asks for this
@@ -203,22 +212,24 @@ int pa_decode_merge(void* out, const int32_t* context_lens,
  *   query_start_loc   device, [B + 1] int32, non-decreasing from 0 to num_tokens
  *   scale             multiplies q.k before the softmax
  *   num_tokens        T >= 0 (T == 0 enqueues nothing)
- *   max_query_len     host, >= every L_b (work is sized from it; queries of a
- *                     sequence beyond it are not computed); 0 enqueues nothing
  *   desc              host, cache geometry; dtype must be PA_BF16
  *                     (PA_ERR_UNSUPPORTED otherwise)
+ *   workspace         device, >= pa_prefill_workspace_bytes(...) bytes, no
+ *                     initial contents required.  Calls that share a
+ *                     workspace must not run concurrently.
+ * Enqueues a one-workgroup planning kernel (the work list, heaviest first)
+ * and the attention kernel, whose workgroups draw work from that list.
  * Device-side preconditions as for pa_decode, plus L_b <= n_b (queries at
  * negative positions, if any, get zeros) and query_start_loc as stated
  * (entries are clamped to [0, num_tokens]).  Memory safety holds when they
  * are violated, but unlike pa_decode a table entry outside the pool is not
- * masked out: its rows read as zeros and take part in the softmax.  No
- * workspace is needed.
+ * masked out: its rows read as zeros and take part in the softmax.
  */
 int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
                const int32_t* block_tables, const int32_t* context_lens,
                const int32_t* query_start_loc, float scale, int32_t num_seqs, int32_t num_heads,
-               int32_t max_blocks_per_seq, int32_t num_tokens, int32_t max_query_len,
-               const pa_cache_desc* desc, void* stream);
+               int32_t max_blocks_per_seq, int32_t num_tokens, const pa_cache_desc* desc,
+               void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static, NUL-terminated name of a pa_status code ("unknown status" otherwise). */
 const char* pa_status_string(int status);

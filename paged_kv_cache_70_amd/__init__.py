@@ -17,6 +17,7 @@ from .api import (  # noqa: F401
     new_workspace,
     partition_size,
     prefill,
+    prefill_workspace,
     status_string,
     workspace_bytes,
     write_kv,

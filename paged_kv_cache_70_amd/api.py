@@ -32,6 +32,7 @@ __all__ = [
     "decode_partials",
     "decode_merge",
     "prefill",
+    "prefill_workspace",
     "partition_size",
     "workspace_bytes",
     "new_workspace",
@@ -84,7 +85,8 @@ def load_library() -> ctypes.CDLL:
         "pa_decode": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, f32, i32, i32, i32, pdesc, i32, vp, sz, vp]),
         "pa_decode_partials": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, f32, i32, i32, i32, pdesc, i32, vp, sz, vp]),
         "pa_decode_merge": (ctypes.c_int, [vp, vp, i32, i32, i32, pdesc, i32, vp, sz, vp]),
-        "pa_prefill": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, vp, f32, i32, i32, i32, i32, i32, pdesc, vp]),
+        "pa_prefill": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, vp, f32, i32, i32, i32, i32, pdesc, vp, sz, vp]),
+        "pa_prefill_workspace_bytes": (sz, [i32, i32, i32, pdesc]),
         "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "pa_abi_version": (i32, []),
     }
@@ -246,14 +248,19 @@ def decode_merge(q_like: torch.Tensor, k_cache: torch.Tensor, block_tables: torc
     return out
 
 
+def prefill_workspace(num_seqs: int, num_heads: int, num_tokens: int, k_cache: torch.Tensor) -> torch.Tensor:
+    """A prefill workspace of the size pa_prefill_workspace_bytes() gives."""
+    need = int(load_library().pa_prefill_workspace_bytes(num_seqs, num_heads, num_tokens,
+                                                         ctypes.byref(cache_desc(k_cache))))
+    return torch.empty(max(need, 16), dtype=torch.uint8, device=k_cache.device)
+
+
 def prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_tables: torch.Tensor,
             context_lens: torch.Tensor, query_start_loc: torch.Tensor, scale: float, *,
-            max_query_len: Optional[int] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+            out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Paged causal attention of a packed batch of new queries; returns ``out``
     [T, H, D] in q's dtype.  Sequence b's queries are rows
-    query_start_loc[b] .. query_start_loc[b+1] - 1, its last tokens.
-    ``max_query_len`` (>= every sequence's query count) sizes the launch; when
-    omitted it is read back from ``query_start_loc`` (a device-to-host copy)."""
+    query_start_loc[b] .. query_start_loc[b+1] - 1, its last tokens."""
     lib = load_library()
     desc = cache_desc(k_cache)
     if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
@@ -270,12 +277,13 @@ def prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block
         out = torch.empty_like(q)
     elif out.shape != q.shape or out.dtype != q.dtype:
         raise ValueError("out must be like q")
-    if max_query_len is None:
-        max_query_len = int((query_start_loc[1:] - query_start_loc[:-1]).max()) if B else 0
+    if workspace is None:
+        workspace = prefill_workspace(B, H, T, k_cache) if desc.dtype == PA_BF16 else out
     st = lib.pa_prefill(_dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
                         _dev(block_tables, "block_tables", torch.int32),
                         _dev(context_lens, "context_lens", torch.int32),
                         _dev(query_start_loc, "query_start_loc", torch.int32), float(scale), B, H, W, T,
-                        int(max_query_len), ctypes.byref(desc), _stream(q))
+                        ctypes.byref(desc), _dev(workspace, "workspace"),
+                        workspace.numel() * workspace.element_size(), _stream(q))
     _check("pa_prefill", st)
     return out

@@ -9,6 +9,18 @@
 namespace pa {
 
 bool dtype_ok(int32_t dtype) { return dtype == PA_F32 || dtype == PA_BF16; }
+
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (!cus[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
 int32_t elem_bytes(int32_t dtype) { return dtype == PA_F32 ? 4 : 2; }
 
 static bool pow2_in(int32_t x, int32_t lo, int32_t hi) {
@@ -309,32 +321,66 @@ int pa_decode_merge(void* out, const int32_t* context_lens, int32_t num_seqs, in
                        workspace_bytes, stream);
 }
 
+// Prefill launch geometry shared by the workspace query and the call.
+struct PrefillShape {
+  int32_t hg, nchunks, tq;
+  int64_t max_tiles;
+  size_t ws_bytes;
+};
+
+static int prefill_shape(int32_t B, int32_t H, int32_t T, const pa_cache_desc* d, PrefillShape* out) {
+  int st = check_desc(d);
+  if (st) return st;
+  if (B <= 0 || H <= 0 || T < 0) return PA_ERR_SHAPE;
+  if (H % d->num_kv_heads) return PA_ERR_SHAPE;
+  if (d->dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
+  PrefillShape p;
+  const int32_t G = H / d->num_kv_heads;
+  p.hg = prefill_heads_per_group(G);
+  p.nchunks = G / p.hg;
+  p.tq = prefill_query_tile(d->head_dim, p.hg);
+  // (sequence, query tile) pairs: sum_b ceil(L_b / tq) <= ceil(T / tq) + B;
+  // a plan entry packs the sequence and the tile into 16 bits each
+  p.max_tiles = ((int64_t)T + p.tq - 1) / p.tq + B;
+  if (B > 65536 || ((int64_t)T + p.tq - 1) / p.tq > 65536 ||
+      p.max_tiles * d->num_kv_heads * p.nchunks > INT_MAX)
+    return PA_ERR_TOO_LARGE;
+  p.ws_bytes = 16 + (size_t)p.max_tiles * sizeof(uint32_t);
+  *out = p;
+  return PA_OK;
+}
+
+size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t num_tokens,
+                                  const pa_cache_desc* desc) {
+  PrefillShape p;
+  return prefill_shape(num_seqs, num_heads, num_tokens, desc, &p) ? 0 : p.ws_bytes;
+}
+
 int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
                const int32_t* block_tables, const int32_t* context_lens,
                const int32_t* query_start_loc, float scale, int32_t num_seqs, int32_t num_heads,
-               int32_t max_blocks_per_seq, int32_t num_tokens, int32_t max_query_len,
-               const pa_cache_desc* desc, void* stream) {
-  int st = check_desc(desc);
-  if (st) return st;
+               int32_t max_blocks_per_seq, int32_t num_tokens, const pa_cache_desc* desc,
+               void* workspace, size_t workspace_bytes, void* stream) {
   const int32_t B = num_seqs, H = num_heads, W = max_blocks_per_seq;
-  if (B <= 0 || H <= 0 || W <= 0 || num_tokens < 0 || max_query_len < 0) return PA_ERR_SHAPE;
-  if (H % desc->num_kv_heads) return PA_ERR_SHAPE;
-  if (desc->dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
+  PrefillShape shp;
+  int st = prefill_shape(B, H, num_tokens, desc, &shp);
+  if (st) return st;
+  if (W <= 0) return PA_ERR_SHAPE;
   const int64_t max_len = (int64_t)W * desc->block_size;
   if (max_len > INT_MAX / 2) return PA_ERR_TOO_LARGE;
-  if (num_tokens == 0 || max_query_len == 0) return PA_OK;
+  if (num_tokens == 0) return PA_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start_loc)
     return PA_ERR_NULL;
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_ALIGN;
+  if (!workspace || workspace_bytes < shp.ws_bytes) return PA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return PA_ERR_ALIGN;
   PrefillParams p;
-  const int32_t G = H / desc->num_kv_heads;
-  p.hg = prefill_heads_per_group(G);
-  p.nchunks = G / p.hg;
-  p.tq = prefill_query_tile(desc->head_dim, p.hg);
-  const int32_t Lmax = max_query_len < num_tokens ? max_query_len : num_tokens;
-  p.qtiles = (Lmax + p.tq - 1) / p.tq;
-  const int64_t units = (int64_t)B * desc->num_kv_heads * p.nchunks * p.qtiles;
-  if (units > INT_MAX) return PA_ERR_TOO_LARGE;
+  p.hg = shp.hg;
+  p.nchunks = shp.nchunks;
+  p.tq = shp.tq;
+  p.max_tiles = (int32_t)shp.max_tiles;
+  p.tickets = static_cast<int32_t*>(workspace);
+  p.plan = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + 16);
   p.out = out;
   p.q = q;
   p.k_cache = k_cache;

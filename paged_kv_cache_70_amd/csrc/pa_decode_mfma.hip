@@ -556,18 +556,6 @@ namespace {
 constexpr int kMaxPersistentSeqs = 4096;   // the pair search covers 64 x 64 sequences
 constexpr size_t kMinLdsPerCU = 82 * 1024; // more than half of a CU's 160 KiB of LDS
 
-int device_cus() {
-  static int cus[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (!cus[dev]) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    cus[dev] = n;
-  }
-  return cus[dev];
-}
-
 template <int D, bool WholeTile>
 hipError_t launch_mfma(const DecodeParams& prm, hipStream_t stream) {
   // Wavefronts per CU: two per SIMD while a wavefront needs at most half a

@@ -58,10 +58,13 @@ struct PrefillParams {
   int32_t hg;              // query heads per workgroup (4, 2 or 1, dividing G)
   int32_t nchunks;         // G / hg
   int32_t tq;              // query tokens per workgroup (128 / hg)
-  int32_t qtiles;          // query tiles per (sequence, kv head, chunk) at the longest query run
+  int32_t max_tiles;       // bound on the (sequence, query tile) pairs: T / tq + B
+  uint32_t* plan;          // workspace: [max_tiles] (sequence << 16 | query tile), heaviest first
+  int32_t* tickets;        // workspace: [0] next unit, [1] number of plan entries
 };
 
 bool dtype_ok(int32_t dtype);
+int device_cus();        // compute units of the current device (0 if the runtime cannot tell)
 int32_t elem_bytes(int32_t dtype);
 
 hipError_t launch_write_kv(void* k_cache, void* v_cache, const void* k, const void* v,

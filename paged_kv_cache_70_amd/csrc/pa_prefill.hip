@@ -168,10 +168,106 @@ __device__ __forceinline__ void fold_keys(const uint8_t* __restrict__ lk, const 
 
 }  // namespace
 
-// One workgroup per (sequence, kv head, head chunk, query tile).  Grid order:
-// query tiles counted from each sequence's end outermost, so the tiles with
-// the most keys of every sequence are dispatched first (a longest-first
-// schedule across the chip); units past a sequence's query tiles exit.
+// Query range and context length of sequence b, clamped so that any input
+// stays in bounds: rows [q0, q0 + nq) of q, n keys.
+struct SeqRange {
+  int q0, nq, n;
+};
+
+__device__ __forceinline__ SeqRange seq_range(const PrefillParams& prm, int b) {
+  SeqRange r;
+  int n = prm.ctx[b];
+  r.n = n < 0 ? 0 : (n > prm.max_tokens ? prm.max_tokens : n);
+  int q0 = prm.qstart[b], q1 = prm.qstart[b + 1];
+  q0 = q0 < 0 ? 0 : (q0 > prm.T ? prm.T : q0);
+  q1 = q1 < q0 ? q0 : (q1 > prm.T ? prm.T : q1);
+  r.q0 = q0;
+  r.nq = q1 - q0;
+  return r;
+}
+
+// Keys that query tile qt of a sequence needs: up to its last query's position.
+__device__ __forceinline__ int tile_keys(const SeqRange& r, int qt, int tq) {
+  const int tok_end = min(r.nq, (qt + 1) * tq);
+  return min(max(r.n - r.nq + tok_end, 0), r.n);
+}
+
+constexpr int kPlanThreads = 1024;
+constexpr int kCostClasses = 2048;   // cost = 64-key tiles of a query tile, capped
+static_assert(kCostClasses == 2 * kPlanThreads, "each plan thread scans two classes");
+
+// Plans one call: lists every (sequence, query tile) pair, heaviest first (a
+// counting sort on its number of 64-key tiles), into the workspace, and zeroes
+// the ticket counter the workgroups of the main kernel draw units from.  One
+// workgroup; at most max_tiles pairs are listed whatever the inputs hold.
+__global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(const PrefillParams prm) {
+  __shared__ int hist[kCostClasses];
+  __shared__ int wave_sums[kPlanThreads / 64];
+  __shared__ int budget;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int c = tid; c < kCostClasses; c += kPlanThreads) hist[c] = 0;
+  if (tid == 0) budget = prm.max_tiles;
+  __syncthreads();
+  auto cost = [&](const SeqRange& r, int qt) {
+    return min(kCostClasses - 1, (tile_keys(r, qt, prm.tq) + kKeyTile - 1) / kKeyTile);
+  };
+  // One wavefront per sequence, lanes over its query tiles.  The budget caps
+  // the listed pairs at max_tiles (reached only if query_start_loc breaks its
+  // preconditions).
+  constexpr int kWavesPlan = kPlanThreads / 64;
+  auto allowed = [&](int ntq) {
+    int left = 0;
+    if (lane == 0) left = atomicSub(&budget, ntq);
+    left = __builtin_amdgcn_readfirstlane(left);
+    return min(ntq, max(left, 0));
+  };
+  // pass 1: histogram of costs
+  for (int b = wave; b < prm.B; b += kWavesPlan) {
+    const SeqRange r = seq_range(prm, b);
+    const int ntq = allowed((r.nq + prm.tq - 1) / prm.tq);
+    for (int qt = lane; qt < ntq; qt += 64) atomicAdd(&hist[cost(r, qt)], 1);
+  }
+  __syncthreads();
+  // exclusive scan in decreasing cost: thread t owns classes C-1-2t, C-2-2t
+  const int c0 = kCostClasses - 1 - 2 * tid, c1 = c0 - 1;
+  const int h0 = hist[c0], h1 = hist[c1];
+  int incl = h0 + h1;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += y;
+  }
+  if (lane == 63) wave_sums[wave] = incl;
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < wave; ++w) before += wave_sums[w];
+  const int excl = before + incl - h0 - h1;
+  __syncthreads();
+  hist[c0] = excl;            // hist now holds each class's next write position
+  hist[c1] = excl + h0;
+  if (tid == kPlanThreads - 1) {
+    prm.tickets[0] = 0;
+    prm.tickets[1] = before + incl;
+    budget = prm.max_tiles;
+  }
+  __syncthreads();
+  // pass 2: place every pair (the same sequences get the same budget only
+  // when nothing was capped; positions past max_tiles are dropped)
+  for (int b = wave; b < prm.B; b += kWavesPlan) {
+    const SeqRange r = seq_range(prm, b);
+    const int ntq = allowed((r.nq + prm.tq - 1) / prm.tq);
+    for (int qt = lane; qt < ntq; qt += 64) {
+      const int pos = atomicAdd(&hist[cost(r, qt)], 1);
+      if (pos < prm.max_tiles) prm.plan[pos] = ((uint32_t)b << 16) | (uint32_t)qt;
+    }
+  }
+}
+
+// Persistent: a few workgroups per CU, each drawing units (a planned
+// (sequence, query tile) pair times one (kv head, head chunk)) from the ticket
+// counter until none is left, heaviest first, so the chip stays full however
+// unequal the units are.  A unit is 4 wavefronts: hg query heads of one kv
+// head x tq query tokens, 32 rows per wavefront (16 for D = 256).
 template <int D, bool WholeTile>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 1 : 2)))
 void prefill_mfma_kernel(const PrefillParams prm) {
@@ -180,155 +276,164 @@ void prefill_mfma_kernel(const PrefillParams prm) {
   constexpr int kQB = query_blocks<D>(), QW = 16 * kQB;   // query columns per wavefront
   constexpr int TILEB = kKeyTile * ROWB;
   __shared__ __attribute__((aligned(16))) uint8_t lds_kv[2][2][TILEB];   // [buffer][K, V][64 key rows]
+  __shared__ int s_ticket;
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int grp = lane >> 4, col = lane & 15;
-
-  // unit order: query tile counted from each sequence's end (outermost, so
-  // the tiles with the most keys start first), sequence, kv head, chunk
-  const int per_x = prm.B * prm.KVH * prm.nchunks;
-  const int x = blockIdx.x / per_x;
-  int u = blockIdx.x - x * per_x;
-  const int chunk = u % prm.nchunks;
-  u /= prm.nchunks;
-  const int kvh = u % prm.KVH;
-  const int b = u / prm.KVH;
-
-  int n = prm.ctx[b];
-  n = n < 0 ? 0 : (n > prm.max_tokens ? prm.max_tokens : n);
-  int q0 = prm.qstart[b], q1 = prm.qstart[b + 1];
-  q0 = q0 < 0 ? 0 : (q0 > prm.T ? prm.T : q0);
-  q1 = q1 < q0 ? q0 : (q1 > prm.T ? prm.T : q1);
-  const int nq = q1 - q0;
-  const int ntq = (nq + prm.tq - 1) / prm.tq;
-  if (x >= ntq) return;
-  const int tok0 = (ntq - 1 - x) * prm.tq;            // first query (index within the sequence's new ones)
-  const int tok_end = min(nq, tok0 + prm.tq);
-  const int pbase = n - nq;                           // position of new query 0 (< 0 only if nq > n)
-  const int kend = min(max(pbase + tok_end, 0), n);   // keys the workgroup's last query sees
-  const int ntiles = (kend + kKeyTile - 1) / kKeyTile;
-
+  const int KU = prm.KVH * prm.nchunks;
+  const int units = min(prm.tickets[1], prm.max_tiles) * KU;
+  const LdsMap<D> map(lane);
+  const uint32_t lane_off = (uint32_t)(lane / PPR) * (uint32_t)(prm.KVH * ROWB) + (uint32_t)(lane % PPR) * 16;
   const int G = prm.H / prm.KVH;
-  const int h = kvh * G + chunk * prm.hg + wave % prm.hg;
-  const int wtok0 = tok0 + (wave / prm.hg) * QW;
-  const int w_valid = min(QW, tok_end - wtok0);        // this wavefront's queries (<= 0: none)
-  const int wpos_lo = pbase + wtok0;
-  const int wpos_hi = pbase + wtok0 + w_valid - 1;
+  typedef const __attribute__((address_space(4))) int32_t ctab_t;
 
-  // Q^T operands: lane holds q[token wtok0 + 16 qb + col][h][32 c + 8 grp .. + 8];
-  // a negative scale is applied as negated q, a zero scale as zero q.
-  bf16x8 qop[kQB][NQK];
-  int qpos[kQB];
-  {
-    const uint32_t flip = prm.q_mode == 1 ? 0x80008000u : 0u;
-    const uint32_t keep = prm.q_mode == 2 ? 0u : 0xffffffffu;
+  for (;;) {
+    if (threadIdx.x == 0) s_ticket = atomicAdd(&prm.tickets[0], 1);
+    __syncthreads();
+    const int ticket = __builtin_amdgcn_readfirstlane(s_ticket);
+    __syncthreads();
+    if (ticket >= units) break;
+    const uint32_t entry = prm.plan[ticket / KU];
+    const int rest = ticket % KU;
+    const int chunk = rest % prm.nchunks;
+    const int kvh = rest / prm.nchunks;
+    const int b = min((int)(entry >> 16), prm.B - 1);
+    const int qt = (int)(entry & 0xffffu);
+
+    const SeqRange sr = seq_range(prm, b);
+    const int q0 = sr.q0, nq = sr.nq, n = sr.n;
+    const int tok0 = qt * prm.tq;                       // first query (index within the sequence's new ones)
+    const int tok_end = min(nq, tok0 + prm.tq);
+    const int pbase = n - nq;                           // position of new query 0 (< 0 only if nq > n)
+    const int kend = tile_keys(sr, qt, prm.tq);         // keys the unit's last query sees
+    const int ntiles = tok0 < nq ? (kend + kKeyTile - 1) / kKeyTile : 0;
+
+    const int h = kvh * G + chunk * prm.hg + wave % prm.hg;
+    const int wtok0 = tok0 + (wave / prm.hg) * QW;
+    const int w_valid = min(QW, tok_end - wtok0);        // this wavefront's queries (<= 0: none)
+    const int wpos_lo = pbase + wtok0;
+    const int wpos_hi = pbase + wtok0 + w_valid - 1;
+
+    // Q^T operands: lane holds q[token wtok0 + 16 qb + col][h][32 c + 8 grp .. + 8];
+    // a negative scale is applied as negated q, a zero scale as zero q.
+    bf16x8 qop[kQB][NQK];
+    int qpos[kQB];
+    {
+      const uint32_t flip = prm.q_mode == 1 ? 0x80008000u : 0u;
+      const uint32_t keep = prm.q_mode == 2 ? 0u : 0xffffffffu;
 #pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
-      const int tok = wtok0 + 16 * qb + col;
-      qpos[qb] = pbase + tok;
-      const size_t row = (size_t)q0 + (tok < nq ? tok : 0);
-      const uint8_t* qrow = static_cast<const uint8_t*>(prm.q) + (row * prm.H + h) * (size_t)D * 2;
+      for (int qb = 0; qb < kQB; ++qb) {
+        const int tok = wtok0 + 16 * qb + col;
+        qpos[qb] = pbase + tok;
+        const size_t row = (size_t)q0 + (tok < nq ? tok : 0);
+        const uint8_t* qrow = static_cast<const uint8_t*>(prm.q) + (row * prm.H + h) * (size_t)D * 2;
 #pragma unroll
-      for (int c = 0; c < NQK; ++c) {
-        u32x4m w = *reinterpret_cast<const u32x4m*>(qrow + (32 * c + 8 * grp) * 2);
+        for (int c = 0; c < NQK; ++c) {
+          u32x4m w = *reinterpret_cast<const u32x4m*>(qrow + (32 * c + 8 * grp) * 2);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) w[i] = (w[i] ^ flip) & keep;
-        qop[qb][c] = __builtin_bit_cast(bf16x8, w);
+          for (int i = 0; i < 4; ++i) w[i] = (w[i] ^ flip) & keep;
+          qop[qb][c] = __builtin_bit_cast(bf16x8, w);
+        }
       }
     }
-  }
 
-  const char* kc = kv_col<D>(prm.k_cache, kvh);
-  const char* vc = kv_col<D>(prm.v_cache, kvh);
-  const uint32_t lane_off = (uint32_t)(lane / PPR) * (uint32_t)(prm.KVH * ROWB) + (uint32_t)(lane % PPR) * 16;
-  typedef const __attribute__((address_space(4))) int32_t ctab_t;
-  ctab_t* trow = (ctab_t*)(prm.tables + (size_t)b * prm.W);
+    const char* kc = kv_col<D>(prm.k_cache, kvh);
+    const char* vc = kv_col<D>(prm.v_cache, kvh);
+    ctab_t* trow = (ctab_t*)(prm.tables + (size_t)b * prm.W);
 
-  // This wavefront's 16-key subtile of key tile `it`: table entries are read
-  // only for blocks holding keys below kend (entries < ceil(n / bs)); rows at
-  // or past kend, and rows of a block outside the pool, read as zeros.
-  auto issue = [&](int it, u32x4m (&kr)[NI], u32x4m (&vr)[NI]) {
-    const int t = it * kKeyTile + wave * 16;
-    const int j = t >> prm.bs_log2;
-    const bool live = t < kend;
-    int ph0 = 0, ph1 = 0;
-    if (live) ph0 = trow[j];
-    if (!WholeTile && t + 8 < kend) ph1 = trow[j + 1];
-    (void)load_tile<D, WholeTile, 0>(prm, kc, vc, kend, t, live, ph0, ph1, lane_off, kr, vr);
-  };
-  const LdsMap<D> map(lane);
-  auto stage = [&](int buf, const u32x4m (&kr)[NI], const u32x4m (&vr)[NI]) {
-    uint8_t* lk = lds_kv[buf][0] + wave * 16 * ROWB;
-    uint8_t* lv = lds_kv[buf][1] + wave * 16 * ROWB;
+    // This wavefront's 16-key subtile of key tile `it`: table entries are read
+    // only for blocks holding keys below kend (entries < ceil(n / bs)); rows at
+    // or past kend, and rows of a block outside the pool, read as zeros.
+    auto issue = [&](int it, u32x4m (&kr)[NI], u32x4m (&vr)[NI]) {
+      const int t = it * kKeyTile + wave * 16;
+      const int j = t >> prm.bs_log2;
+      const bool live = t < kend;
+      int ph0 = 0, ph1 = 0;
+      if (live) ph0 = trow[j];
+      if (!WholeTile && t + 8 < kend) ph1 = trow[j + 1];
+      (void)load_tile<D, WholeTile, 0>(prm, kc, vc, kend, t, live, ph0, ph1, lane_off, kr, vr);
+    };
+    auto stage = [&](int buf, const u32x4m (&kr)[NI], const u32x4m (&vr)[NI]) {
+      uint8_t* lk = lds_kv[buf][0] + wave * 16 * ROWB;
+      uint8_t* lv = lds_kv[buf][1] + wave * 16 * ROWB;
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      *reinterpret_cast<u32x4m*>(lk + map.wr[i]) = kr[i];
-      *reinterpret_cast<u32x4m*>(lv + map.wr[i]) = vr[i];
+      for (int i = 0; i < NI; ++i) {
+        *reinterpret_cast<u32x4m*>(lk + map.wr[i]) = kr[i];
+        *reinterpret_cast<u32x4m*>(lv + map.wr[i]) = vr[i];
+      }
+    };
+
+    PState<D> st;
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) {
+      st.m[qb] = -INFINITY;
+      st.mneg[qb] = 0.0f;
+      st.lsum[qb] = 0.0f;
+#pragma unroll
+      for (int j = 0; j < NDJ; ++j) st.o[j][qb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     }
-  };
 
-  PState<D> st;
-#pragma unroll
-  for (int qb = 0; qb < kQB; ++qb) {
-    st.m[qb] = -INFINITY;
-    st.mneg[qb] = 0.0f;
-    st.lsum[qb] = 0.0f;
-#pragma unroll
-    for (int j = 0; j < NDJ; ++j) st.o[j][qb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  }
-
-  u32x4m kr[NI], vr[NI];
-  if (ntiles > 0) {
-    issue(0, kr, vr);
-    stage(0, kr, vr);
-  }
-  __syncthreads();
-  for (int it = 0; it < ntiles; ++it) {
-    const int buf = it & 1;
-    const bool more = it + 1 < ntiles;
-    if (more) issue(it + 1, kr, vr);
-    const int t0 = it * kKeyTile;
-    if (w_valid > 0 && t0 <= wpos_hi) {
-      const bool masked = t0 + kKeyTile - 1 > wpos_lo;
-      fold_keys<D>(lds_kv[buf][0], lds_kv[buf][1], masked, t0, qpos, qop, prm.scale_log2, map, lane, st);
+    // Key tiles, double-buffered in LDS; the previous unit's last reads ended
+    // before its last barrier.
+    u32x4m kr[NI], vr[NI];
+    if (ntiles > 0) {
+      issue(0, kr, vr);
+      stage(0, kr, vr);
     }
-    if (more) stage(buf ^ 1, kr, vr);
     __syncthreads();
-  }
+    for (int it = 0; it < ntiles; ++it) {
+      const int buf = it & 1;
+      const bool more = it + 1 < ntiles;
+      if (more) issue(it + 1, kr, vr);
+      const int t0 = it * kKeyTile;
+      if (w_valid > 0 && t0 <= wpos_hi) {
+        const bool masked = t0 + kKeyTile - 1 > wpos_lo;
+        fold_keys<D>(lds_kv[buf][0], lds_kv[buf][1], masked, t0, qpos, qop, prm.scale_log2, map, lane, st);
+      }
+      if (more) stage(buf ^ 1, kr, vr);
+      __syncthreads();
+    }
 
-  // out[row][h][16 j + 4 grp + i] = O^T / l for this lane's query columns.
+    // out[row][h][16 j + 4 grp + i] = O^T / l for this lane's query columns.
 #pragma unroll
-  for (int qb = 0; qb < kQB; ++qb) {
-    const float L = groups_sum(st.lsum[qb]);
-    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-    const int tok = wtok0 + 16 * qb + col;
-    if (tok < tok_end) {
-      uint16_t* outp = static_cast<uint16_t*>(prm.out) + (((size_t)q0 + tok) * prm.H + h) * D;
+    for (int qb = 0; qb < kQB; ++qb) {
+      const float L = groups_sum(st.lsum[qb]);
+      const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+      const int tok = wtok0 + 16 * qb + col;
+      if (tok < tok_end) {
+        uint16_t* outp = static_cast<uint16_t*>(prm.out) + (((size_t)q0 + tok) * prm.H + h) * D;
 #pragma unroll
-      for (int j = 0; j < NDJ; ++j) {
-        bf16x4 w;
+        for (int j = 0; j < NDJ; ++j) {
+          bf16x4 w;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) w[i] = (__bf16)(st.o[j][qb][i] * inv);
-        *reinterpret_cast<bf16x4*>(outp + 16 * j + 4 * grp) = w;
+          for (int i = 0; i < 4; ++i) w[i] = (__bf16)(st.o[j][qb][i] * inv);
+          *reinterpret_cast<bf16x4*>(outp + 16 * j + 4 * grp) = w;
+        }
       }
     }
   }
 }
 
 template <int D, bool WholeTile>
-static hipError_t launch_prefill_d(const PrefillParams& prm, int64_t units, hipStream_t stream) {
-  hipLaunchKernelGGL((prefill_mfma_kernel<D, WholeTile>), dim3((unsigned)units), dim3(kWaves * 64), 0, stream, prm);
+static hipError_t launch_prefill_d(const PrefillParams& prm, hipStream_t stream) {
+  // resident workgroups per CU: LDS (2 x 2 x 64 rows of D bf16) and registers
+  constexpr int kPerCU = D >= 256 ? 1 : (D >= 128 ? 2 : 3);
+  const int cus = device_cus();
+  const int64_t units = (int64_t)prm.max_tiles * prm.KVH * prm.nchunks;
+  int64_t grid = (int64_t)(cus > 0 ? cus : 256) * kPerCU;
+  if (grid > units) grid = units;
+  hipLaunchKernelGGL(prefill_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, prm);
+  hipLaunchKernelGGL((prefill_mfma_kernel<D, WholeTile>), dim3((unsigned)grid), dim3(kWaves * 64), 0, stream, prm);
   return hipGetLastError();
 }
 
 hipError_t launch_prefill_mfma(const PrefillParams& prm, int32_t D, hipStream_t stream) {
-  const int64_t units = (int64_t)prm.B * prm.KVH * prm.nchunks * prm.qtiles;
   const bool whole = prm.bs_log2 >= 4;
   switch (D) {
-    case 64: return whole ? launch_prefill_d<64, true>(prm, units, stream) : launch_prefill_d<64, false>(prm, units, stream);
-    case 128: return whole ? launch_prefill_d<128, true>(prm, units, stream) : launch_prefill_d<128, false>(prm, units, stream);
-    case 256: return whole ? launch_prefill_d<256, true>(prm, units, stream) : launch_prefill_d<256, false>(prm, units, stream);
+    case 64: return whole ? launch_prefill_d<64, true>(prm, stream) : launch_prefill_d<64, false>(prm, stream);
+    case 128: return whole ? launch_prefill_d<128, true>(prm, stream) : launch_prefill_d<128, false>(prm, stream);
+    case 256: return whole ? launch_prefill_d<256, true>(prm, stream) : launch_prefill_d<256, false>(prm, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -42,8 +42,7 @@ def _say(msg):
 def _gpu_step(w):
     kc, vc = w.k_cache.clone(), w.v_cache.clone()
     pk.write_kv(kc, vc, w.k_new, w.v_new, w.slot_mapping)
-    out = pk.prefill(w.q, kc, vc, w.block_tables, w.context_lens, w.query_start_loc, w.scale,
-                     max_query_len=w.max_query_len)
+    out = pk.prefill(w.q, kc, vc, w.block_tables, w.context_lens, w.query_start_loc, w.scale)
     torch.cuda.synchronize()
     return kc, vc, out
 
@@ -144,9 +143,31 @@ def test_prefill_rejects_f32_and_accepts_empty():
     cl = torch.tensor([3], dtype=torch.int32, device="cuda")
     qs = torch.tensor([0, 3], dtype=torch.int32, device="cuda")
     with pytest.raises(pk.PaError):
-        pk.prefill(q, kc, kc, bt, cl, qs, 1.0, max_query_len=3)
+        pk.prefill(q, kc, kc, bt, cl, qs, 1.0)
     kb = kc.to(torch.bfloat16)
     qe = torch.zeros((0, 4, 64), dtype=torch.bfloat16, device="cuda")
-    out = pk.prefill(qe, kb, kb, bt, cl, torch.tensor([0, 0], dtype=torch.int32, device="cuda"), 1.0,
-                     max_query_len=0)
+    out = pk.prefill(qe, kb, kb, bt, cl, torch.tensor([0, 0], dtype=torch.int32, device="cuda"), 1.0)
     assert out.shape == (0, 4, 64)
+
+
+def test_prefill_workspace_reuse_and_sparse_batches():
+    """One workspace across calls of different shapes (the planning kernel
+    resets the work counter each call), and a batch where most sequences have
+    no or one new query (decode-like members of a mixed batch)."""
+    cached = [0, 7, 300, 20, 1000, 0, 64, 5] * 6
+    new = [0, 1, 0, 1, 130, 33, 0, 1] * 6
+    w1 = make_prefill_custom(num_heads=8, num_kv_heads=2, head_dim=128, block_size=16, cached=cached,
+                             new=new, seed=94, device="cuda")
+    w2 = make_prefill_custom(num_heads=8, num_kv_heads=2, head_dim=128, block_size=16, cached=[10, 0],
+                             new=[60, 97], seed=95, device="cuda")
+    ws = pk.prefill_workspace(len(cached), 8, w1.q.shape[0], w1.k_cache)
+    for w, what in ((w1, "sparse batch"), (w2, "second shape, same workspace"), (w1, "sparse batch again")):
+        kc, vc = w.k_cache.clone(), w.v_cache.clone()
+        pk.write_kv(kc, vc, w.k_new, w.v_new, w.slot_mapping)
+        out = pk.prefill(w.q, kc, vc, w.block_tables, w.context_lens, w.query_start_loc, w.scale, workspace=ws)
+        torch.cuda.synchronize()
+        ko, vo = _oracle_caches(w)
+        ref = O.prefill(stored_np(w.q), ko, vo, stored_np(w.block_tables), stored_np(w.context_lens),
+                        stored_np(w.query_start_loc), w.scale, "bf16")
+        err = assert_matches_oracle(out, ref, "bf16", what)
+        _say(f"{what}: max err {err:.2e}")

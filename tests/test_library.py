@@ -102,18 +102,28 @@ def test_binding_rejects_host_and_noncontiguous_tensors():
 
 def test_prefill_host_checks():
     """pa_prefill's argument checks run on the host and return before any
-    device work: unsupported dtype, bad sizes, empty batches, null pointers."""
+    device work: unsupported dtype, bad sizes, empty batches, null pointers,
+    a missing workspace; and the workspace size query."""
     import ctypes
     lib = pk.load_library()
     bf16 = pk.CacheDesc(64, 16, 2, 128, 1)
     f32 = pk.CacheDesc(64, 16, 2, 128, 0)
-    call = lambda desc, B=2, H=8, W=4, T=10, L=5, ptr=None: lib.pa_prefill(
-        ptr, ptr, ptr, ptr, ptr, ptr, ptr, 0.1, B, H, W, T, L, ctypes.byref(desc), None)
+    call = lambda desc, B=2, H=8, W=4, T=10, ptr=None, ws=None, wsb=0: lib.pa_prefill(
+        ptr, ptr, ptr, ptr, ptr, ptr, ptr, 0.1, B, H, W, T, ctypes.byref(desc), ws, wsb, None)
     assert call(f32) == -3                       # PA_ERR_UNSUPPORTED: prefill is bf16 only
     assert call(bf16, H=7) == -2                 # H % KVH != 0
     assert call(bf16, B=0) == -2
     assert call(bf16, T=-1) == -2
+    assert call(bf16, W=0) == -2
     assert call(bf16, T=0) == 0                  # nothing to do
-    assert call(bf16, L=0) == 0
     assert call(bf16) == -1                      # null pointers with work to do
     assert call(pk.CacheDesc(64, 12, 2, 128, 1)) == -3   # block size not a power of two
+    # non-null (never dereferenced) pointers: the missing or short workspace is reported
+    assert call(bf16, ptr=16) == -4
+    assert call(bf16, ptr=16, ws=16, wsb=27) == -4
+    # G = 4 -> 4 heads x 32 tokens per unit: ceil(10 / 32) + 2 = 3 plan entries
+    size = lambda B, H, T, d=bf16: lib.pa_prefill_workspace_bytes(B, H, T, ctypes.byref(d))
+    assert size(2, 8, 10) == 16 + 4 * 3
+    assert size(2, 4, 10) == 16 + 4 * (1 + 2)    # G = 2 -> 64-token tiles
+    assert size(3, 2, 300) == 16 + 4 * (3 + 3)   # G = 1 -> 128-token tiles
+    assert size(2, 8, 10, f32) == 0
