@@ -365,3 +365,63 @@ def test_graph_replay_of_write_and_decode():
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {rep}"
         assert np.array_equal(stored_np(kc), ko) and np.array_equal(stored_np(vc), vo)
+
+
+@pytest.mark.parametrize("cfg_name", ["tiny_f32", "llama3_8b_bf16"])
+def test_graph_step_padded_batch_new_inputs_each_replay(cfg_name):
+    """A decode step as a serving loop runs it: write + decode captured once
+    in a HIP graph over fixed buffers (a padded batch: slot -1 rows carry the
+    sentinel and must not be written), then replayed with new q, k, v and
+    slots copied into those buffers before each replay.  Every replay is held
+    to the oracle: the write bit for bit over the whole cache, the decode
+    within the tolerance."""
+    cfg = CONFIGS[cfg_name]
+    w = make_workload(cfg, "cuda")
+    _say(f"graph step {cfg_name}")
+    B, H, D = w.q.shape
+    W = w.block_tables.shape[1]
+    T = w.slot_mapping.numel()
+    kc, vc = w.k_cache.clone(), w.v_cache.clone()
+    ws = pk.new_workspace(B, H, W, kc)
+    q_buf, k_buf, v_buf = w.q.clone(), w.k_new.clone(), w.v_new.clone()
+    slot_buf = w.slot_mapping.clone()
+    out = torch.empty_like(w.q)
+
+    def step():
+        pk.write_kv(kc, vc, k_buf, v_buf, slot_buf)
+        pk.decode(q_buf, kc, vc, w.block_tables, w.context_lens, w.scale, out=out, workspace=ws)
+
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        step()                                       # warm the capture stream
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    gen = torch.Generator(device="cuda").manual_seed(321)
+    pad = slot_buf < 0
+    for rep in range(3):
+        # new inputs in place: fresh q, k, v rows; the valid slots permuted among themselves
+        q_buf.copy_(torch.randn(q_buf.shape, generator=gen, device="cuda").to(q_buf.dtype))
+        k_buf.copy_(torch.randn(k_buf.shape, generator=gen, device="cuda").to(k_buf.dtype))
+        v_buf.copy_(torch.randn(v_buf.shape, generator=gen, device="cuda").to(v_buf.dtype))
+        k_buf[pad] = SENTINEL
+        v_buf[pad] = SENTINEL
+        valid = torch.nonzero(~pad).flatten()
+        perm = valid[torch.randperm(valid.numel(), generator=gen, device="cuda")]
+        new_slots = slot_buf.clone()
+        new_slots[valid] = slot_buf[perm]
+        slot_buf.copy_(new_slots)
+        ko, vo = stored_np(kc).copy(), stored_np(vc).copy()
+        O.write_kv(ko, vo, stored_np(k_buf), stored_np(v_buf), stored_np(slot_buf))
+        ref = O.decode(stored_np(q_buf), ko, vo, stored_np(w.block_tables), stored_np(w.context_lens),
+                       w.scale, cfg.dtype)
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert _same_bits(kc, ko) and _same_bits(vc, vo), f"{cfg_name} replay {rep}: write"
+        err = assert_matches_oracle(out, ref, cfg.dtype, f"{cfg_name} replay {rep}")
+        _say(f"graph step {cfg_name} replay {rep} (T={T}, {int(pad.sum())} padding rows): max err {err:.2e}")
