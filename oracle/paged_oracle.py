@@ -17,6 +17,10 @@ Sources (titles of the pages, with the section each function follows):
        inference-learning-path.pages.dev, sections 直接答案 and 代码 (the
        online-softmax fold over the block table).
 
+The vLLM cache layout of [P2] 深入原理 (K as [NB, KVH, D/x, bs, x], V as
+[NB, KVH, D, bs]) is handled by plain re-indexing into [P1]'s layout and back
+(``pack_*`` / ``unpack_*``): it moves stored values, never changes them.
+
 ``prefill`` (several new queries per sequence) is the varlen version [P1]
 asks for in 面试官追问 & 对照源码 without defining it; it takes the plainest
 reading that [P1] 细节 supports (see its docstring).
@@ -43,6 +47,13 @@ __all__ = [
     "decode_online_fold",
     "query_positions",
     "prefill",
+    "vllm_pack_width",
+    "pack_k_vllm",
+    "pack_v_vllm",
+    "unpack_k_vllm",
+    "unpack_v_vllm",
+    "write_kv_vllm",
+    "decode_vllm",
     "OracleError",
 ]
 
@@ -313,3 +324,60 @@ def prefill(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
             p = e / e.sum(axis=1, keepdims=True)
             out[s0:s1, h] = p @ Vb[:, kvh, :]
     return out
+
+
+# ---------------------------------------------------------------------------
+# vLLM's cache layout ([P2] 深入原理: the K cache's extra dimension)
+# ---------------------------------------------------------------------------
+
+def vllm_pack_width(dtype: str) -> int:
+    """x = 16 bytes / element size: the innermost K dimension packs one
+    16-byte-aligned group of head_dim ([P2] 深入原理: 8 for 2-byte types)."""
+    return {"bf16": 8, "f32": 4}[dtype]
+
+
+def pack_k_vllm(k_cache: np.ndarray, dtype: str) -> np.ndarray:
+    """[NB, bs, KVH, D] -> [NB, KVH, D/x, bs, x]: element (blk, t, h, d) moves
+    to (blk, h, d // x, t, d % x)."""
+    NB, bs, KVH, D = k_cache.shape
+    x = vllm_pack_width(dtype)
+    if D % x:
+        raise OracleError("head_dim must be a multiple of the pack width")
+    return np.ascontiguousarray(k_cache.reshape(NB, bs, KVH, D // x, x).transpose(0, 2, 3, 1, 4))
+
+
+def unpack_k_vllm(k_packed: np.ndarray) -> np.ndarray:
+    """Inverse of pack_k_vllm: [NB, KVH, D/x, bs, x] -> [NB, bs, KVH, D]."""
+    NB, KVH, G, bs, x = k_packed.shape
+    return np.ascontiguousarray(k_packed.transpose(0, 3, 1, 2, 4).reshape(NB, bs, KVH, G * x))
+
+
+def pack_v_vllm(v_cache: np.ndarray) -> np.ndarray:
+    """[NB, bs, KVH, D] -> [NB, KVH, D, bs]: V is read along the token axis and
+    needs no packing ([P2] 深入原理)."""
+    return np.ascontiguousarray(v_cache.transpose(0, 2, 3, 1))
+
+
+def unpack_v_vllm(v_packed: np.ndarray) -> np.ndarray:
+    """Inverse of pack_v_vllm: [NB, KVH, D, bs] -> [NB, bs, KVH, D]."""
+    return np.ascontiguousarray(v_packed.transpose(0, 3, 1, 2))
+
+
+def write_kv_vllm(k_packed: np.ndarray, v_packed: np.ndarray, k: np.ndarray, v: np.ndarray,
+                  slot_mapping: np.ndarray) -> None:
+    """write_kv on caches in vLLM's layout, in place: the same scatter, done in
+    [P1]'s layout and re-indexed back (the layout moves values only)."""
+    x = k_packed.shape[4]
+    dtype = "bf16" if x == 8 else "f32"
+    kc, vc = unpack_k_vllm(k_packed), unpack_v_vllm(v_packed)
+    write_kv(kc, vc, k, v, slot_mapping)
+    k_packed[...] = pack_k_vllm(kc, dtype)
+    v_packed[...] = pack_v_vllm(vc)
+    return None
+
+
+def decode_vllm(q, k_packed, v_packed, block_tables, context_lens, scale, dtype: str) -> np.ndarray:
+    """decode on caches in vLLM's layout: paging and layout change where the
+    rows live, not what attention computes ([P2] 直接答案)."""
+    return decode(q, unpack_k_vllm(k_packed), unpack_v_vllm(v_packed), block_tables, context_lens,
+                  scale, dtype)

@@ -499,6 +499,67 @@ def pin_prefill_errors(O):
         O.prefill(q, kc, kc, np.array([[0, 1]]), np.array([4]), np.array([1, 3]), 1.0, "f32")
 
 
+# ---------------------------------------------------------------------------
+# vLLM cache layout pins ([P2] 深入原理)
+# ---------------------------------------------------------------------------
+
+def pin_vllm_layout_indexing(O):
+    """Element (blk, t, h, d) of [P1]'s layout sits at K[blk, h, d // x, t, d % x]
+    and V[blk, h, d, t] of vLLM's, with x = 8 for 2-byte elements and 4 for
+    4-byte ones (16 bytes per group); checked element by element with scalar
+    loops, and unpacking inverts packing."""
+    assert O.vllm_pack_width("bf16") == 8 and O.vllm_pack_width("f32") == 4
+    rng = np.random.default_rng(41)
+    for dtype, D in (("f32", 8), ("bf16", 16)):
+        NB, bs, KVH = 3, 4, 2
+        c = rng.standard_normal((NB, bs, KVH, D)).astype(np.float32)
+        if dtype == "bf16":
+            c = torch.from_numpy(c).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        x = 8 if dtype == "bf16" else 4
+        kp, vp = O.pack_k_vllm(c, dtype), O.pack_v_vllm(c)
+        assert kp.shape == (NB, KVH, D // x, bs, x) and vp.shape == (NB, KVH, D, bs)
+        for blk in range(NB):
+            for t in range(bs):
+                for h in range(KVH):
+                    for d in range(D):
+                        assert kp[blk, h, d // x, t, d % x] == c[blk, t, h, d]
+                        assert vp[blk, h, d, t] == c[blk, t, h, d]
+        assert np.array_equal(O.unpack_k_vllm(kp), c) and np.array_equal(O.unpack_v_vllm(vp), c)
+        # the K group of 8 (bf16) or 4 (fp32) elements is 16 contiguous bytes
+        assert kp.strides[-1] * x == 16 and kp.strides[-2] == 16
+
+
+def pin_vllm_layout_write_and_decode(O):
+    """The same write and decode on caches in vLLM's layout: the written values
+    land where the layout says (scalar loop over the written slots), and the
+    decode equals [P1]'s decode of the same values (it is attention either way,
+    [P2] 直接答案)."""
+    rng = np.random.default_rng(42)
+    NB, bs, KVH, D, H = 6, 4, 2, 8, 4
+    kc = rng.standard_normal((NB, bs, KVH, D)).astype(np.float32)
+    vc = rng.standard_normal((NB, bs, KVH, D)).astype(np.float32)
+    k = rng.standard_normal((3, KVH, D)).astype(np.float32)
+    v = rng.standard_normal((3, KVH, D)).astype(np.float32)
+    slots = np.array([5, -1, 22])
+    kp, vp = O.pack_k_vllm(kc, "f32"), O.pack_v_vllm(vc)
+    O.write_kv_vllm(kp, vp, k, v, slots)
+    for i, s in enumerate(slots):
+        if s < 0:
+            continue
+        blk, t = s // bs, s % bs
+        for h in range(KVH):
+            for d in range(D):
+                assert kp[blk, h, d // 4, t, d % 4] == k[i, h, d] and vp[blk, h, d, t] == v[i, h, d]
+    tables = np.array([[1, 5, 77], [0, 2, 3]])
+    lens = np.array([7, 12])
+    q = rng.standard_normal((2, H, D)).astype(np.float32)
+    a = O.decode_vllm(q, kp, vp, tables, lens, 0.4, "f32")
+    kw, vw = kc.copy(), vc.copy()
+    O.write_kv(kw, vw, k, v, slots)
+    b = O.decode(q, kw, vw, tables, lens, 0.4, "f32")
+    assert np.array_equal(a, b)
+
+
 ALL_PINS = [
     pin_bf16_widening,
     pin_m1_write_example,
@@ -521,4 +582,6 @@ ALL_PINS = [
     pin_prefill_chunk_invariance,
     pin_prefill_sdpa_fp64,
     pin_prefill_errors,
+    pin_vllm_layout_indexing,
+    pin_vllm_layout_write_and_decode,
 ]

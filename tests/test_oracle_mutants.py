@@ -68,6 +68,12 @@ MUTANTS = {
                               "            s = (qf[s0:s1, h, :] @ Kb[:, kvh, :].T)"),
     "prefill_softmax_over_queries": ("            p = e / e.sum(axis=1, keepdims=True)",
                                      "            p = e / e.sum(axis=0, keepdims=True)"),
+    # vLLM cache layout
+    "vllm_k_token_and_group_swapped": ("reshape(NB, bs, KVH, D // x, x).transpose(0, 2, 3, 1, 4)",
+                                       "reshape(NB, bs, KVH, D // x, x).transpose(0, 2, 1, 3, 4)"),
+    "vllm_pack_width_elements": ('    return {"bf16": 8, "f32": 4}[dtype]', '    return {"bf16": 8, "f32": 8}[dtype]'),
+    "vllm_v_not_transposed": ("    return np.ascontiguousarray(v_cache.transpose(0, 2, 3, 1))",
+                              "    return np.ascontiguousarray(v_cache.transpose(0, 2, 1, 3))"),
     "prefill_v_from_k": ("            out[s0:s1, h] = p @ Vb[:, kvh, :]", "            out[s0:s1, h] = p @ Kb[:, kvh, :]"),
 }
 
