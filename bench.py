@@ -300,6 +300,9 @@ def main():
     ap.add_argument("--config", default="llama3_8b_bf16")
     ap.add_argument("--partition", type=int, default=0, help="tokens per split-KV partition (0 = library's choice)")
     ap.add_argument("--hot", action="store_true", help="do not flush the last-level cache between steps")
+    ap.add_argument("--layout", choices=["p09", "vllm"], default="p09",
+                    help="cache layout: P09's [NB, bs, KVH, D] (default) or vLLM's packed K [NB, KVH, D/x, bs, x] "
+                         "with V [NB, KVH, D, bs] (decode configs, bf16)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="skip the graph-replay timing")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
@@ -342,10 +345,13 @@ def main():
     w = make_workload(cfg, dev)
     B, H, D = w.q.shape
     W = w.block_tables.shape[1]
-    P = args.partition or pk.partition_size(B, H, W, w.k_cache)
-    ws = pk.new_workspace(B, H, W, w.k_cache, P)
-    out = torch.empty_like(w.q)
     kc, vc = w.k_cache, w.v_cache
+    if args.layout == "vllm":
+        from synth import to_vllm_layout
+        kc, vc = to_vllm_layout(kc, vc)
+    P = args.partition or pk.partition_size(B, H, W, kc)
+    ws = pk.new_workspace(B, H, W, kc, P)
+    out = torch.empty_like(w.q)
     flush = None if args.hot else torch.ones(1 << 28, dtype=torch.float32, device=dev)
     flush_sink = torch.zeros((), dtype=torch.float32, device=dev)
 
@@ -466,7 +472,7 @@ def main():
     dec_us = k2_us + k3_us
     value = kv_bytes / (step_us * 1e-6) / 1e9
     achieved = kv_bytes / (k2_us * 1e-6) / 1e9
-    traffic = _traffic(cfg.name, cfg.dtype)
+    traffic = _traffic(cfg.name, cfg.dtype) if args.layout == "p09" else None
 
     res = {
         "metric": METRIC,
@@ -484,7 +490,7 @@ def main():
         "config": {
             "workload": cfg.name, "num_seqs": B, "num_heads": H, "num_kv_heads": cfg.num_kv_heads,
             "head_dim": D, "block_size": cfg.block_size, "context_lens": list(cfg.ctx),
-            "write_tokens": int(w.slot_mapping.numel()), "partition_size": P,
+            "write_tokens": int(w.slot_mapping.numel()), "partition_size": P, "cache_layout": args.layout,
             "cache_flush_between_steps": flush is not None,
         },
         "hbm_frac_step": round(value / HBM_PEAK_GBPS, 4),
@@ -508,7 +514,7 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
-            "kernel": PARTIAL_KERNELS[cfg.dtype],
+            "kernel": PARTIAL_KERNELS[cfg.dtype] if args.layout == "p09" else "decode_partial_vllm_kernel",
         },
     }
     if not args.no_cpu_baseline:

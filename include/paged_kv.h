@@ -56,7 +56,8 @@ typedef enum pa_status {
   PA_OK = 0,
   PA_ERR_NULL = -1,         /* a required pointer is NULL */
   PA_ERR_SHAPE = -2,        /* a size is negative/zero where it must be positive, or H % KVH != 0 */
-  PA_ERR_UNSUPPORTED = -3,  /* head_dim not in {64,128,256}, block_size not in {8,16,32,64}, unknown dtype,
+  PA_ERR_UNSUPPORTED = -3,  /* head_dim not in {64,128,256}, block_size not in {8,16,32,64}, unknown dtype
+                               or layout, a layout/dtype pair an entry point does not implement,
                                or a partition size that is not a positive multiple of block_size
                                or spans more than 64 blocks */
   PA_ERR_WORKSPACE = -4,    /* workspace NULL or smaller than pa_decode_workspace_bytes() */
@@ -65,6 +66,19 @@ typedef enum pa_status {
   PA_ERR_TOO_LARGE = -7     /* sizes overflow the kernels' 32-bit grid/index limits */
 } pa_status;
 
+/* Memory layout of the two caches. */
+typedef enum pa_layout {
+  /* "P09 · Paged KV 写入 + decode attention", 题面速览: both caches
+     [num_blocks, block_size, num_kv_heads, head_dim]. */
+  PA_LAYOUT_P09 = 0,
+  /* vLLM's, "PagedAttention kernel：paged KV cache 与 block table", 深入原理:
+     k_cache [num_blocks, num_kv_heads, head_dim / x, block_size, x] with x
+     elements = 16 bytes (8 for bf16, 4 for fp32), v_cache [num_blocks,
+     num_kv_heads, head_dim, block_size].  Supported by pa_write_kv (both
+     dtypes) and the decode entry points (bf16 only). */
+  PA_LAYOUT_VLLM = 1
+} pa_layout;
+
 /* Geometry of the paged cache (k_cache and v_cache share it). */
 typedef struct pa_cache_desc {
   int32_t num_blocks;    /* NB: physical blocks in the pool, > 0 */
@@ -72,6 +86,7 @@ typedef struct pa_cache_desc {
   int32_t num_kv_heads;  /* KVH, > 0 */
   int32_t head_dim;      /* D, one of 64, 128, 256 */
   int32_t dtype;         /* a pa_dtype */
+  int32_t layout;        /* a pa_layout */
 } pa_cache_desc;
 
 /*
@@ -82,7 +97,8 @@ typedef struct pa_cache_desc {
  * slots are padding (CUDA-graph padded batches use -1) and write nothing.
  * The copy is bit-exact.
  *
- *   k_cache, v_cache  device, [NB, bs, KVH, D] of desc->dtype, updated in place
+ *   k_cache, v_cache  device, in desc->layout ([NB, bs, KVH, D] for PA_LAYOUT_P09)
+ *                     of desc->dtype, updated in place
  *   k, v              device, [num_tokens, KVH, D] of desc->dtype
  *   slot_mapping      device, [num_tokens] int64 flat slot = block * bs + offset
  *   num_tokens        T >= 0; T == 0 enqueues nothing and returns PA_OK
@@ -126,7 +142,8 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads,
  *
  *   out                 device, [B, H, D] of desc->dtype (written)
  *   q                   device, [B, H, D] of desc->dtype
- *   k_cache, v_cache    device, [NB, bs, KVH, D] of desc->dtype
+ *   k_cache, v_cache    device, in desc->layout ([NB, bs, KVH, D] for PA_LAYOUT_P09)
+ *                       of desc->dtype (PA_LAYOUT_VLLM: bf16 only)
  *   block_tables        device, [B, max_blocks_per_seq] int32; only the first
  *                       ceil(context_lens[b] / bs) entries of row b are read
  *   context_lens        device, [B] int32, tokens of each sequence (0 gives zeros)
@@ -212,8 +229,8 @@ size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t n
  *   query_start_loc   device, [B + 1] int32, non-decreasing from 0 to num_tokens
  *   scale             multiplies q.k before the softmax
  *   num_tokens        T >= 0 (T == 0 enqueues nothing)
- *   desc              host, cache geometry; dtype must be PA_BF16
- *                     (PA_ERR_UNSUPPORTED otherwise)
+ *   desc              host, cache geometry; dtype must be PA_BF16 and layout
+ *                     PA_LAYOUT_P09 (PA_ERR_UNSUPPORTED otherwise)
  *   workspace         device, >= pa_prefill_workspace_bytes(...) bytes, no
  *                     initial contents required.  Calls that share a
  *                     workspace must not run concurrently.
@@ -234,7 +251,7 @@ int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cach
 /* Static, NUL-terminated name of a pa_status code ("unknown status" otherwise). */
 const char* pa_status_string(int status);
 
-/* ABI version of this header: (major << 16) | minor. */
+/* ABI version of this header: (major << 16) | minor (2.0: pa_cache_desc.layout). */
 int32_t pa_abi_version(void);
 
 #ifdef __cplusplus

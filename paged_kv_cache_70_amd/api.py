@@ -45,6 +45,7 @@ _LIB: Optional[ctypes.CDLL] = None
 
 PA_F32, PA_BF16 = 0, 1
 _DTYPES = {torch.float32: PA_F32, torch.bfloat16: PA_BF16}
+PA_LAYOUT_P09, PA_LAYOUT_VLLM = 0, 1
 
 
 class PaError(RuntimeError):
@@ -60,6 +61,7 @@ class CacheDesc(ctypes.Structure):
         ("num_kv_heads", ctypes.c_int32),
         ("head_dim", ctypes.c_int32),
         ("dtype", ctypes.c_int32),
+        ("layout", ctypes.c_int32),
     ]
 
 
@@ -107,12 +109,29 @@ def abi_version() -> int:
 
 
 def cache_desc(k_cache: torch.Tensor) -> CacheDesc:
-    if k_cache.dim() != 4:
-        raise ValueError("cache must be [num_blocks, block_size, num_kv_heads, head_dim]")
+    """Geometry of a K cache: [num_blocks, block_size, num_kv_heads, head_dim]
+    (the P09 layout), or 5-D [num_blocks, num_kv_heads, head_dim / x,
+    block_size, x] with x = 16 bytes of elements (vLLM's layout)."""
     if k_cache.dtype not in _DTYPES:
         raise TypeError(f"unsupported cache dtype {k_cache.dtype}")
-    NB, bs, KVH, D = k_cache.shape
-    return CacheDesc(NB, bs, KVH, D, _DTYPES[k_cache.dtype])
+    if k_cache.dim() == 4:
+        NB, bs, KVH, D = k_cache.shape
+        return CacheDesc(NB, bs, KVH, D, _DTYPES[k_cache.dtype], PA_LAYOUT_P09)
+    if k_cache.dim() == 5:
+        NB, KVH, G, bs, x = k_cache.shape
+        if x * k_cache.element_size() != 16:
+            raise ValueError("vLLM-layout K cache: the last dimension must hold 16 bytes")
+        return CacheDesc(NB, bs, KVH, G * x, _DTYPES[k_cache.dtype], PA_LAYOUT_VLLM)
+    raise ValueError("k_cache must be [NB, bs, KVH, D] or vLLM's [NB, KVH, D/x, bs, x]")
+
+
+def _check_v(k_cache: torch.Tensor, v_cache: torch.Tensor, desc: CacheDesc) -> None:
+    if desc.layout == PA_LAYOUT_VLLM:
+        want = (desc.num_blocks, desc.num_kv_heads, desc.head_dim, desc.block_size)
+    else:
+        want = tuple(k_cache.shape)
+    if tuple(v_cache.shape) != want or v_cache.dtype != k_cache.dtype:
+        raise ValueError(f"v_cache must be {list(want)} of {k_cache.dtype}")
 
 
 def _dev(t: torch.Tensor, name: str, dtype=None) -> int:
@@ -142,8 +161,7 @@ def write_kv(k_cache: torch.Tensor, v_cache: torch.Tensor, k: torch.Tensor, v: t
     """In place: cache[slot // bs, slot % bs] = k[i] (and v) for slot >= 0."""
     lib = load_library()
     desc = cache_desc(k_cache)
-    if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
-        raise ValueError("k_cache and v_cache must match")
+    _check_v(k_cache, v_cache, desc)
     T = slot_mapping.shape[0] if slot_mapping.dim() == 1 else -1
     if T < 0:
         raise ValueError("slot_mapping must be 1-D")
@@ -183,8 +201,7 @@ def new_workspace(num_seqs: int, num_heads: int, max_blocks_per_seq: int, k_cach
 
 def _decode_args(q, k_cache, v_cache, block_tables, context_lens, out, workspace, partition_size):
     desc = cache_desc(k_cache)
-    if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
-        raise ValueError("k_cache and v_cache must match")
+    _check_v(k_cache, v_cache, desc)
     if q.dim() != 3 or q.dtype != k_cache.dtype or q.shape[2] != desc.head_dim:
         raise ValueError("q must be [num_seqs, num_heads, head_dim] of the cache dtype")
     B, H, D = q.shape
@@ -263,8 +280,7 @@ def prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block
     query_start_loc[b] .. query_start_loc[b+1] - 1, its last tokens."""
     lib = load_library()
     desc = cache_desc(k_cache)
-    if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
-        raise ValueError("k_cache and v_cache must match")
+    _check_v(k_cache, v_cache, desc)
     if q.dim() != 3 or q.dtype != k_cache.dtype or q.shape[2] != desc.head_dim:
         raise ValueError("q must be [num_tokens, num_heads, head_dim] of the cache dtype")
     T, H, _ = q.shape

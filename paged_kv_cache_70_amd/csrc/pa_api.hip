@@ -39,6 +39,7 @@ static int check_desc(const pa_cache_desc* d) {
   if (!dtype_ok(d->dtype)) return PA_ERR_UNSUPPORTED;
   if (d->head_dim != 64 && d->head_dim != 128 && d->head_dim != 256) return PA_ERR_UNSUPPORTED;
   if (!pow2_in(d->block_size, 8, 64)) return PA_ERR_UNSUPPORTED;
+  if (d->layout != PA_LAYOUT_P09 && d->layout != PA_LAYOUT_VLLM) return PA_ERR_UNSUPPORTED;
   // byte offsets inside the pool are size_t; rows must fit 32-bit lane math
   const int64_t row = (int64_t)d->num_kv_heads * d->head_dim * elem_bytes(d->dtype);
   if (row > INT_MAX) return PA_ERR_TOO_LARGE;
@@ -122,6 +123,7 @@ static int check_decode_sizes(int32_t B, int32_t H, int32_t W, const pa_cache_de
   if (st) return st;
   if (B <= 0 || H <= 0 || W <= 0) return PA_ERR_SHAPE;
   if (H % d->num_kv_heads) return PA_ERR_SHAPE;
+  if (d->layout == PA_LAYOUT_VLLM && d->dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
   if (partition_size < 0 || (partition_size && partition_size % d->block_size) ||
       partition_size > kMaxBlocksPerPartition * d->block_size)
     return PA_ERR_UNSUPPORTED;
@@ -213,7 +215,7 @@ using namespace pa;
 
 extern "C" {
 
-int32_t pa_abi_version(void) { return (1 << 16) | 1; }
+int32_t pa_abi_version(void) { return (2 << 16) | 0; }
 
 const char* pa_status_string(int status) {
   switch (status) {
@@ -242,8 +244,12 @@ int pa_write_kv(void* k_cache, void* v_cache, const void* k, const void* v,
   const int64_t row_bytes = (int64_t)desc->num_kv_heads * desc->head_dim * elem_bytes(desc->dtype);
   if ((int64_t)num_tokens * (row_bytes / 16) > (int64_t)UINT_MAX - 256) return PA_ERR_TOO_LARGE;
   const int64_t num_slots = (int64_t)desc->num_blocks * desc->block_size;
-  hipError_t e = launch_write_kv(k_cache, v_cache, k, v, slot_mapping, num_tokens,
-                                 (int32_t)row_bytes, num_slots, static_cast<hipStream_t>(stream));
+  hipError_t e = desc->layout == PA_LAYOUT_VLLM
+                     ? launch_write_kv_vllm(k_cache, v_cache, k, v, slot_mapping, num_tokens, (int32_t)row_bytes,
+                                            elem_bytes(desc->dtype), ilog2(desc->block_size), num_slots,
+                                            static_cast<hipStream_t>(stream))
+                     : launch_write_kv(k_cache, v_cache, k, v, slot_mapping, num_tokens, (int32_t)row_bytes,
+                                       num_slots, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
@@ -281,9 +287,11 @@ static int decode_common(bool partials, bool merge, void* out, const void* q,
   if (st) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (partials) {
-    const hipError_t e = ck.plan.use_mfma
-                             ? launch_decode_partials_mfma(prm, desc->head_dim, s)
-                             : launch_decode_partials(prm, desc->dtype, desc->head_dim, ck.plan, s);
+    const hipError_t e = desc->layout == PA_LAYOUT_VLLM
+                             ? launch_decode_partials_vllm(prm, desc->head_dim, s)
+                             : ck.plan.use_mfma
+                                   ? launch_decode_partials_mfma(prm, desc->head_dim, s)
+                                   : launch_decode_partials(prm, desc->dtype, desc->head_dim, ck.plan, s);
     if (e != hipSuccess) return PA_ERR_LAUNCH;
   }
   if (merge && ck.plan.maxP > 1 &&
@@ -333,7 +341,7 @@ static int prefill_shape(int32_t B, int32_t H, int32_t T, const pa_cache_desc* d
   if (st) return st;
   if (B <= 0 || H <= 0 || T < 0) return PA_ERR_SHAPE;
   if (H % d->num_kv_heads) return PA_ERR_SHAPE;
-  if (d->dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
+  if (d->dtype != PA_BF16 || d->layout != PA_LAYOUT_P09) return PA_ERR_UNSUPPORTED;
   PrefillShape p;
   const int32_t G = H / d->num_kv_heads;
   p.hg = prefill_heads_per_group(G);

@@ -279,6 +279,224 @@ __global__ __launch_bounds__(64) void decode_partial_mfma_grid_kernel(const Deco
   store_unit<D>(prm, u, lane, st);
 }
 
+// vLLM's cache layout ("PagedAttention kernel：paged KV cache 与 block table",
+// 深入原理): K [NB, KVH, D/8, bs, 8], V [NB, KVH, D, bs].  There the operands of
+// a 16-token tile load straight from the block in operand order, with no LDS:
+//   K (A of S = K Q^T): lane l takes the 16-byte group 4 c + l / 16 of token
+//     row l % 16; the 16 lanes of a group read 256 contiguous bytes;
+//   V^T (A of O^T += V^T P^T, 16x16x16): lane l takes tokens 4 (l / 16) .. + 3
+//     of d row 16 j + l % 16, 8 contiguous bytes.
+// Rows past the partition's end, and blocks outside the pool, are not loaded
+// (zeros); V elements of rows past the end are zeroed, so stale values never
+// reach the products.
+namespace {
+
+typedef uint32_t u32x2m __attribute__((ext_vector_type(2)));
+
+template <int D>
+struct VllmTile {
+  u32x4m k[Geo<D>::NQK];
+  u32x2m v[Geo<D>::NPV];
+};
+
+// Loads the 16-token tile starting at token `tile` (block ph0; for block size
+// 8 the tile's second half is block ph1) of kv head kvh, valid rows
+// [0, t_end - tile).  Buffer loads, one resource per block over the kv head's
+// region of it (empty for a block outside the pool), so that nothing branches
+// around a load; a lane whose row lies in the other block of a split tile
+// reads past its resource's end (zeros).  V elements of rows past the end are
+// zeroed.  Returns the row validity mask.
+template <int D, bool WholeTile, int AUX = 0>
+__device__ __forceinline__ uint32_t load_tile_vllm(const DecodeParams& prm, int kvh, int t_end, int tile,
+                                                   int ph0, int ph1, int lane, VllmTile<D>& T) {
+  constexpr int NQK = Geo<D>::NQK, NPV = Geo<D>::NPV;
+  constexpr uint32_t kFar = 0x80000000u;   // a byte offset past every resource's end
+  const int bs_log2 = prm.bs_log2;
+  const int nv = min(16, t_end - tile);
+  const int r = lane & 15, g4 = lane >> 4;
+  const bool ok0 = (unsigned)ph0 < (unsigned)prm.NB, ok1 = (unsigned)ph1 < (unsigned)prm.NB;
+  const int k_region = (D / 8) << (bs_log2 + 4), v_region = D << (bs_log2 + 1);   // bytes per (block, kv head)
+  auto rsrc = [&](const void* cache, int blk, bool ok, int region) {
+    const char* base = static_cast<const char*>(cache) + (size_t)(ok ? blk : 0) * prm.KVH * region + (size_t)kvh * region;
+    return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, ok ? region : 0, kRsrcWord3M);
+  };
+  const int row0 = WholeTile ? (tile & prm.bs_mask) : 0;
+  // K: token row r of the tile
+  {
+    const int krow = WholeTile ? row0 + r : (r & 7);
+    const __amdgpu_buffer_rsrc_t k0 = rsrc(prm.k_cache, ph0, ok0, k_region);
+#pragma unroll
+    for (int c = 0; c < NQK; ++c) {
+      const uint32_t off = ((uint32_t)((4 * c + g4) << bs_log2) + krow) * 16;
+      if constexpr (WholeTile) {
+        T.k[c] = __builtin_amdgcn_raw_buffer_load_b128(k0, off, 0, AUX);
+      } else {
+        const __amdgpu_buffer_rsrc_t k1 = rsrc(prm.k_cache, ph1, ok1, k_region);
+        const u32x4m a = __builtin_amdgcn_raw_buffer_load_b128(k0, r < 8 ? off : kFar, 0, AUX);
+        const u32x4m b = __builtin_amdgcn_raw_buffer_load_b128(k1, r < 8 ? kFar : off, 0, AUX);
+        T.k[c] = a | b;
+      }
+    }
+  }
+  // V: tokens 4 g4 .. 4 g4 + 3 of d rows 16 j + r
+  {
+    const int vtok = WholeTile ? row0 + 4 * g4 : ((4 * g4) & 7);
+    const int vn = min(max(nv - 4 * g4, 0), 4);            // valid tokens of the lane's 4
+    const uint32_t keep_lo = vn >= 2 ? 0xffffffffu : (vn == 1 ? 0x0000ffffu : 0u);
+    const uint32_t keep_hi = vn >= 4 ? 0xffffffffu : (vn == 3 ? 0x0000ffffu : 0u);
+    const __amdgpu_buffer_rsrc_t v0 = rsrc(prm.v_cache, ph0, ok0, v_region);
+#pragma unroll
+    for (int j = 0; j < NPV; ++j) {
+      const uint32_t off = ((uint32_t)((16 * j + r) << bs_log2) + vtok) * 2;
+      u32x2m w;
+      if constexpr (WholeTile) {
+        w = __builtin_amdgcn_raw_buffer_load_b64(v0, off, 0, AUX);
+      } else {
+        const __amdgpu_buffer_rsrc_t v1 = rsrc(prm.v_cache, ph1, ok1, v_region);
+        const u32x2m a = __builtin_amdgcn_raw_buffer_load_b64(v0, g4 < 2 ? off : kFar, 0, AUX);
+        const u32x2m b = __builtin_amdgcn_raw_buffer_load_b64(v1, g4 < 2 ? kFar : off, 0, AUX);
+        w = a | b;
+      }
+      w[0] &= keep_lo;
+      w[1] &= keep_hi;
+      T.v[j] = w;
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  uint32_t ok;
+  if constexpr (WholeTile) {
+    ok = ok0 ? (nv >= 16 ? 0xffffu : (nv > 0 ? (1u << nv) - 1u : 0u)) : 0u;
+  } else {
+    const uint32_t lo = ok0 ? (nv >= 8 ? 0xffu : (nv > 0 ? (1u << nv) - 1u : 0u)) : 0u;
+    const uint32_t hi = ok1 && nv > 8 ? ((nv >= 16 ? 0xffu : (1u << (nv - 8)) - 1u) << 8) : 0u;
+    ok = lo | hi;
+  }
+  return ok;
+}
+
+// Folds a tile held in registers: S = K . Q^T, the same online softmax as the
+// LDS-staged tiles (scores masked by row validity, lazy rescale, bf16 P^T), and
+// O^T += V^T . P^T.
+template <int D>
+__device__ __forceinline__ void fold_tile_vllm(uint32_t ok, const VllmTile<D>& T, const bf16x8 (&qop)[Geo<D>::NQK],
+                                               float cs, int lane, Fold<D>& st) {
+  constexpr int NQK = Geo<D>::NQK, NPV = Geo<D>::NPV;
+  const int grp = lane >> 4;
+  f32x4 s = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int c = 0; c < NQK; ++c) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, T.k[c]), qop[c], s, 0, 0, 0);
+  float sc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) sc[i] = ((ok >> (4 * grp + i)) & 1u) ? s[i] * cs : -INFINITY;
+  float mt = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+  mt = groups_max(mt);
+  if (__builtin_amdgcn_ballot_w64(mt > st.m + kSlackM)) {
+    if (mt > st.m) {
+      const float corr = exp2m(st.m - mt);
+      st.m = mt;
+      st.mneg = -mt;
+      st.lsum *= corr;
+#pragma unroll
+      for (int j = 0; j < NPV; ++j) st.o[j] *= corr;
+    }
+  }
+  bf16x4 pb;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float p = exp2m(sc[i] + st.mneg);
+    st.lsum += p;
+    pb[i] = (__bf16)p;
+  }
+#pragma unroll
+  for (int j = 0; j < NPV; ++j)
+    st.o[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, T.v[j]), pb, st.o[j], 0, 0, 0);
+}
+
+}  // namespace
+
+// One wavefront per unit (kv head and head chunk fastest, partition,
+// sequence), tiles double-buffered in registers.
+template <int D, bool WholeTile>
+__global__ __launch_bounds__(64) void decode_partial_vllm_kernel(const DecodeParams prm) {
+  const int lane = threadIdx.x;
+  const int b = blockIdx.z, p = blockIdx.y;
+  const int kvh = blockIdx.x / prm.nchunks;
+  const int n = clamp_len(prm, prm.ctx[b]);
+  const Unit u = make_unit(prm, b, p, n, kvh, blockIdx.x - kvh * prm.nchunks);
+  if (p >= (u.np > 0 ? u.np : 1)) return;
+  const int j_first = u.t_begin >> prm.bs_log2;
+  const int j_end = (u.t_end + prm.bs_mask) >> prm.bs_log2;
+  const int tbl = (j_first + lane < j_end) ? prm.tables[(size_t)b * prm.W + j_first + lane] : -1;
+  u32x4m qr[Geo<D>::NQK];
+  load_q<D>(prm, u, lane, qr);
+  bf16x8 qop[Geo<D>::NQK];
+  q_operands<D>(prm, u, lane, qr, qop);
+  Fold<D> st;
+  st.reset();
+  VllmTile<D> A, Bt;
+  auto load_at = [&](int i, VllmTile<D>& T) {
+    const int tile = u.t_begin + min(i, u.ntiles - 1) * 16;
+    const int j = (tile >> prm.bs_log2) - j_first;
+    const int ph0 = __builtin_amdgcn_readlane(tbl, j & 63);
+    const int ph1 = WholeTile ? ph0 : __builtin_amdgcn_readlane(tbl, (j + 1) & 63);
+    return load_tile_vllm<D, WholeTile>(prm, kvh, u.t_end, tile, ph0, ph1, lane, T);
+  };
+  uint32_t okA = load_at(0, A), okB;
+  for (int ip = 0; ip < (u.ntiles >> 1); ++ip) {
+    okB = load_at(2 * ip + 1, Bt);
+    fold_tile_vllm<D>(okA, A, qop, prm.scale_log2, lane, st);
+    okA = load_at(2 * ip + 2, A);
+    fold_tile_vllm<D>(okB, Bt, qop, prm.scale_log2, lane, st);
+  }
+  if (u.ntiles & 1) fold_tile_vllm<D>(okA, A, qop, prm.scale_log2, lane, st);
+  store_unit<D>(prm, u, lane, st);
+}
+
+namespace {
+
+// What the persistent walk needs from a cache layout: a tile's registers, its
+// load and its fold.
+template <int D>
+struct P09Tile {
+  u32x4m k[Geo<D>::NI], v[Geo<D>::NI];
+};
+
+template <int D, bool WholeTile, bool Vllm>
+struct TileOps;
+
+template <int D, bool WholeTile>
+struct TileOps<D, WholeTile, false> {   // P09 layout: whole rows, staged through LDS
+  using Tile = P09Tile<D>;
+  template <int AUX>
+  static __device__ __forceinline__ uint32_t load(const DecodeParams& prm, int kvh, int t_end, int tile, bool live,
+                                                  int ph0, int ph1, int lane, uint32_t lane_off, Tile& T) {
+    return load_tile<D, WholeTile, AUX>(prm, kv_col<D>(prm.k_cache, kvh), kv_col<D>(prm.v_cache, kvh), t_end,
+                                        tile, live, ph0, ph1, lane_off, T.k, T.v);
+  }
+  static __device__ __forceinline__ void fold(uint32_t ok, const Tile& T, const bf16x8 (&qop)[Geo<D>::NQK],
+                                              float cs, const LdsMap<D>& map, int lane, Fold<D>& st,
+                                              uint8_t* lds_k, uint8_t* lds_v) {
+    fold_tile<D>(ok, T.k, T.v, qop, cs, map, lane, st, lds_k, lds_v);
+  }
+};
+
+template <int D, bool WholeTile>
+struct TileOps<D, WholeTile, true> {    // vLLM layout: operands straight from the blocks
+  using Tile = VllmTile<D>;
+  template <int AUX>
+  static __device__ __forceinline__ uint32_t load(const DecodeParams& prm, int kvh, int t_end, int tile, bool live,
+                                                  int ph0, int ph1, int lane, uint32_t, Tile& T) {
+    return load_tile_vllm<D, WholeTile, AUX>(prm, kvh, t_end, tile, live ? ph0 : -1, live ? ph1 : -1, lane, T);
+  }
+  static __device__ __forceinline__ void fold(uint32_t ok, const Tile& T, const bf16x8 (&qop)[Geo<D>::NQK],
+                                              float cs, const LdsMap<D>&, int lane, Fold<D>& st, uint8_t*,
+                                              uint8_t*) {
+    fold_tile_vllm<D>(ok, T, qop, cs, lane, st);
+  }
+};
+
+}  // namespace
+
 // Persistent form: one workgroup of NW wavefronts per CU; each wavefront folds
 // a sequence of units as one continuous stream of tiles: the loads of a
 // unit's first tile (and its q) are issued while the previous unit's last
@@ -298,9 +516,11 @@ __global__ __launch_bounds__(64) void decode_partial_mfma_grid_kernel(const Deco
 // wavefronts sharing a CU stream at very different rates, and this lets the
 // faster ones take more units, so that all of a CU's wavefronts finish
 // together.
-template <int D, bool WholeTile, int NW>
+template <int D, bool WholeTile, int NW, bool Vllm = false>
 __global__ __launch_bounds__(64 * NW) void decode_partial_mfma_kernel(const DecodeParams prm) {
   using Gm = Geo<D>;
+  using Ops = TileOps<D, WholeTile, Vllm>;
+  using Tile = typename Ops::Tile;
   constexpr int NBUF = 2;   // tiles in flight per wavefront (3 measured no faster)
   __shared__ __attribute__((aligned(16))) uint8_t lds_tiles[NW][2][16 * Gm::ROWB];
   __shared__ int32_t s_cnt[kBuckets];
@@ -468,7 +688,7 @@ __global__ __launch_bounds__(64 * NW) void decode_partial_mfma_kernel(const Deco
     // Loads the next tile of the stream into (kr, vr); returns whether it is
     // a real tile (false: the stream is dead, or waits for a unit the
     // consumer has not handed out yet).
-    auto produce = [&](u32x4m (&kr)[Gm::NI], u32x4m (&vr)[Gm::NI], uint32_t& ok) -> bool {
+    auto produce = [&](Tile& T, uint32_t& ok) -> bool {
       // L exhausted: move on to N (its q first, so that it is older than the
       // tile loads the fold of N's first tile waits for), or wait for the
       // consumer to hand N out, or stop.  (Flags are assigned outright: a
@@ -482,8 +702,7 @@ __global__ __launch_bounds__(64 * NW) void decode_partial_mfma_kernel(const Deco
         request_blocks();
       }
       const bool live = (fl & (kDead | kPending | kAlive)) == kAlive;
-      ok = load_tile<D, WholeTile, A>(prm, kv_col<D>(prm.k_cache, L.kvh), kv_col<D>(prm.v_cache, L.kvh),
-                                      L.t_end, L.t_begin + 16 * l_tile, live, ph0, ph1, lane_off, kr, vr);
+      ok = Ops::template load<A>(prm, L.kvh, L.t_end, L.t_begin + 16 * l_tile, live, ph0, ph1, lane, lane_off, T);
       if (live) {
         ++l_tile;
         if (l_tile < L.ntiles) request_blocks();
@@ -492,9 +711,9 @@ __global__ __launch_bounds__(64 * NW) void decode_partial_mfma_kernel(const Deco
     };
     // Folds one tile of C; at C's last tile, writes C and moves to N, or
     // ends the walk (alive = false) when there is no further unit.
-    auto consume = [&](bool real, uint32_t ok, const u32x4m (&kr)[Gm::NI], const u32x4m (&vr)[Gm::NI]) {
+    auto consume = [&](bool real, uint32_t ok, const Tile& T) {
       if (!real || !has(kAlive)) return;
-      fold_tile<D>(ok, kr, vr, qop, cs, map, lane, st, lds_k, lds_v);
+      Ops::fold(ok, T, qop, cs, map, lane, st, lds_k, lds_v);
       if (++c_tile < C.ntiles) return;
       store_unit<D>(prm, C, lane, st);
       if (!has(kNOk)) {
@@ -514,38 +733,41 @@ __global__ __launch_bounds__(64 * NW) void decode_partial_mfma_kernel(const Deco
     // NBUF tiles in flight: the producer runs NBUF-1 tiles ahead of the
     // folds, in a rotation of register buffers.
     request_blocks();
-    u32x4m kA[Gm::NI], vA[Gm::NI], kB[Gm::NI], vB[Gm::NI];
+    Tile tA, tB;
     uint32_t okA, okB;
-    bool rA = produce(kA, vA, okA), rB;
+    bool rA = produce(tA, okA), rB;
     // One exit, at the end of the loop body (an exit after every fold would
     // give the compiler paths that skip loads, and stricter load waits).
     if constexpr (NBUF == 2) {
       do {
-        rB = produce(kB, vB, okB);
-        consume(rA, okA, kA, vA);
-        rA = produce(kA, vA, okA);
-        consume(rB, okB, kB, vB);
+        rB = produce(tB, okB);
+        consume(rA, okA, tA);
+        rA = produce(tA, okA);
+        consume(rB, okB, tB);
       } while (has(kAlive));
     } else {
-      u32x4m kC[Gm::NI], vC[Gm::NI];
+      Tile tC;
       uint32_t okC;
       bool rC;
-      rB = produce(kB, vB, okB);
+      rB = produce(tB, okB);
       do {
-        rC = produce(kC, vC, okC);
-        consume(rA, okA, kA, vA);
-        rA = produce(kA, vA, okA);
-        consume(rB, okB, kB, vB);
-        rB = produce(kB, vB, okB);
-        consume(rC, okC, kC, vC);
+        rC = produce(tC, okC);
+        consume(rA, okA, tA);
+        rA = produce(tA, okA);
+        consume(rB, okB, tB);
+        rB = produce(tB, okB);
+        consume(rC, okC, tC);
       } while (has(kAlive));
     }
   };
   // Blocks shared between sequences (a common prefix) are likely to be read
   // again by other workgroups: keep the default cache policy for them.
-  // Otherwise every K/V row is read once, and the loads are non-temporal.
+  // Otherwise every K/V row is read once, and the loads are non-temporal --
+  // except in vLLM's layout with blocks of 32 or more tokens, where a 16-token
+  // tile reads half of every K group and V row of its block and the next tile
+  // reads the other half.
   if (wg + (uint32_t)wave * NC < nunits) {
-    if (__builtin_amdgcn_readfirstlane(s_shared))
+    if (__builtin_amdgcn_readfirstlane(s_shared) || (Vllm && prm.bs_log2 >= 5))
       walk(CachePolicy<0>{});
     else
       walk(CachePolicy<kAuxNT>{});
@@ -556,7 +778,7 @@ namespace {
 constexpr int kMaxPersistentSeqs = 4096;   // the pair search covers 64 x 64 sequences
 constexpr size_t kMinLdsPerCU = 82 * 1024; // more than half of a CU's 160 KiB of LDS
 
-template <int D, bool WholeTile>
+template <int D, bool WholeTile, bool Vllm>
 hipError_t launch_mfma(const DecodeParams& prm, hipStream_t stream) {
   // Wavefronts per CU: two per SIMD while a wavefront needs at most half a
   // SIMD's registers (head_dim <= 128), else one.
@@ -567,12 +789,15 @@ hipError_t launch_mfma(const DecodeParams& prm, hipStream_t stream) {
     size_t lds = (size_t)prm.B * 3 * sizeof(int32_t);
     const size_t fixed = sizeof(uint8_t) * NW * 2 * 16 * 2 * D + 64 * 4 + 8;
     if (lds + fixed < kMinLdsPerCU) lds = kMinLdsPerCU - fixed;
-    hipLaunchKernelGGL((decode_partial_mfma_kernel<D, WholeTile, NW>), dim3((uint32_t)cus), dim3(64 * NW), lds,
+    hipLaunchKernelGGL((decode_partial_mfma_kernel<D, WholeTile, NW, Vllm>), dim3((uint32_t)cus), dim3(64 * NW), lds,
                        stream, prm);
     return hipGetLastError();
   }
   const dim3 grid(prm.KVH * prm.nchunks, prm.maxP, prm.B);
-  hipLaunchKernelGGL((decode_partial_mfma_grid_kernel<D, WholeTile>), grid, dim3(64), 0, stream, prm);
+  if constexpr (Vllm)
+    hipLaunchKernelGGL((decode_partial_vllm_kernel<D, WholeTile>), grid, dim3(64), 0, stream, prm);
+  else
+    hipLaunchKernelGGL((decode_partial_mfma_grid_kernel<D, WholeTile>), grid, dim3(64), 0, stream, prm);
   return hipGetLastError();
 }
 }  // namespace
@@ -580,9 +805,19 @@ hipError_t launch_mfma(const DecodeParams& prm, hipStream_t stream) {
 hipError_t launch_decode_partials_mfma(const DecodeParams& prm, int32_t D, hipStream_t stream) {
   const bool whole = prm.bs_log2 >= 4;
   switch (D) {
-    case 64: return whole ? launch_mfma<64, true>(prm, stream) : launch_mfma<64, false>(prm, stream);
-    case 128: return whole ? launch_mfma<128, true>(prm, stream) : launch_mfma<128, false>(prm, stream);
-    case 256: return whole ? launch_mfma<256, true>(prm, stream) : launch_mfma<256, false>(prm, stream);
+    case 64: return whole ? launch_mfma<64, true, false>(prm, stream) : launch_mfma<64, false, false>(prm, stream);
+    case 128: return whole ? launch_mfma<128, true, false>(prm, stream) : launch_mfma<128, false, false>(prm, stream);
+    case 256: return whole ? launch_mfma<256, true, false>(prm, stream) : launch_mfma<256, false, false>(prm, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_decode_partials_vllm(const DecodeParams& prm, int32_t D, hipStream_t stream) {
+  const bool whole = prm.bs_log2 >= 4;
+  switch (D) {
+    case 64: return whole ? launch_mfma<64, true, true>(prm, stream) : launch_mfma<64, false, true>(prm, stream);
+    case 128: return whole ? launch_mfma<128, true, true>(prm, stream) : launch_mfma<128, false, true>(prm, stream);
+    case 256: return whole ? launch_mfma<256, true, true>(prm, stream) : launch_mfma<256, false, true>(prm, stream);
     default: return hipErrorInvalidValue;
   }
 }

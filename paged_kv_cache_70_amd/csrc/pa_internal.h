@@ -76,6 +76,12 @@ hipError_t launch_decode_partials(const DecodeParams& prm, int32_t dtype, int32_
 
 hipError_t launch_decode_partials_mfma(const DecodeParams& prm, int32_t D, hipStream_t stream);
 
+// Caches in vLLM's layout (K [NB, KVH, D/x, bs, x], V [NB, KVH, D, bs]).
+hipError_t launch_write_kv_vllm(void* k_cache, void* v_cache, const void* k, const void* v,
+                                const int64_t* slots, int32_t T, int32_t row_bytes, int32_t elem_bytes,
+                                int32_t bs_log2, int64_t num_slots, hipStream_t stream);
+hipError_t launch_decode_partials_vllm(const DecodeParams& prm, int32_t D, hipStream_t stream);
+
 hipError_t launch_prefill_mfma(const PrefillParams& prm, int32_t D, hipStream_t stream);
 
 hipError_t launch_decode_merge(const DecodeParams& prm, int32_t dtype, int32_t D,

@@ -35,6 +35,54 @@ __global__ __launch_bounds__(256) void write_kv_kernel(
   v_cache[dst] = vv;
 }
 
+// The same scatter into vLLM's cache layout ("PagedAttention kernel：paged KV
+// cache 与 block table", 深入原理): K [NB, KVH, D/x, bs, x] with x elements =
+// 16 bytes, V [NB, KVH, D, bs].  One thread per 16-byte group of x elements
+// (token, kv head, group g): the K group is one 16-byte store at
+// (block, head, g, offset); its x V elements go to x rows d = g x + e of
+// (block, head), each at column `offset` (stride bs elements).
+template <typename E>
+__global__ __launch_bounds__(256) void write_kv_vllm_kernel(
+    u32x4* __restrict__ k_cache, E* __restrict__ v_cache,
+    const u32x4* __restrict__ k, const E* __restrict__ v,
+    const int64_t* __restrict__ slots, uint32_t total_groups, uint32_t row_groups,
+    int32_t bs_log2, int64_t num_slots) {
+  constexpr uint32_t X = 16 / sizeof(E);
+  const uint32_t idx = blockIdx.x * 256u + threadIdx.x;
+  if (idx >= total_groups) return;
+  const uint32_t tok = idx / row_groups;
+  const uint32_t rem = idx - tok * row_groups;     // kv head * (D / x) + group
+  const int64_t s = slots[tok];
+  if (s < 0 || s >= num_slots) return;
+  const size_t blk = (size_t)(s >> bs_log2);
+  const size_t off = (size_t)(s & ((1 << bs_log2) - 1));
+  const size_t col = (blk * row_groups + rem) << bs_log2;   // (block, head, group) row of bs columns
+  k_cache[col + off] = k[idx];
+  const E* src = v + (size_t)idx * X;
+#pragma unroll
+  for (uint32_t e = 0; e < X; ++e) v_cache[((col * X) + ((size_t)e << bs_log2)) + off] = src[e];
+}
+
+hipError_t launch_write_kv_vllm(void* k_cache, void* v_cache, const void* k, const void* v,
+                                const int64_t* slots, int32_t T, int32_t row_bytes, int32_t elem_bytes,
+                                int32_t bs_log2, int64_t num_slots, hipStream_t stream) {
+  const uint32_t row_groups = (uint32_t)row_bytes / 16u;
+  const uint64_t total = (uint64_t)T * row_groups;
+  if (total == 0) return hipSuccess;
+  const uint32_t grid = (uint32_t)((total + 255u) / 256u);
+  if (elem_bytes == 2)
+    hipLaunchKernelGGL(write_kv_vllm_kernel<uint16_t>, dim3(grid), dim3(256), 0, stream,
+                       static_cast<u32x4*>(k_cache), static_cast<uint16_t*>(v_cache),
+                       static_cast<const u32x4*>(k), static_cast<const uint16_t*>(v), slots,
+                       (uint32_t)total, row_groups, bs_log2, num_slots);
+  else
+    hipLaunchKernelGGL(write_kv_vllm_kernel<uint32_t>, dim3(grid), dim3(256), 0, stream,
+                       static_cast<u32x4*>(k_cache), static_cast<uint32_t*>(v_cache),
+                       static_cast<const u32x4*>(k), static_cast<const uint32_t*>(v), slots,
+                       (uint32_t)total, row_groups, bs_log2, num_slots);
+  return hipGetLastError();
+}
+
 hipError_t launch_write_kv(void* k_cache, void* v_cache, const void* k, const void* v,
                            const int64_t* slots, int32_t T, int32_t row_bytes,
                            int64_t num_slots, hipStream_t stream) {

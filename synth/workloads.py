@@ -40,6 +40,7 @@ __all__ = [
     "bits_view",
     "SENTINEL",
     "TAIL_FILL",
+    "to_vllm_layout",
 ]
 
 SENTINEL = 9.0          # value carried by padding rows (slot = -1)
@@ -336,3 +337,13 @@ def make_custom(*, num_seqs: int, num_heads: int, num_kv_heads: int, head_dim: i
         ctx=("explicit", tuple(int(x) for x in lens)), num_blocks=num_blocks,
         tail=tail, pad_tokens=pad_tokens, shuffle_write=shuffle_write, seed=seed)
     return make_workload(cfg, device, poison=poison)
+
+
+def to_vllm_layout(k_cache: torch.Tensor, v_cache: torch.Tensor):
+    """The same stored values in vLLM's cache layout (K [NB, KVH, D/x, bs, x]
+    with x elements = 16 bytes, V [NB, KVH, D, bs]): a copy, values unchanged."""
+    NB, bs, KVH, D = k_cache.shape
+    x = 16 // k_cache.element_size()
+    k = k_cache.view(NB, bs, KVH, D // x, x).permute(0, 2, 3, 1, 4).contiguous()
+    v = v_cache.permute(0, 2, 3, 1).contiguous()
+    return k, v

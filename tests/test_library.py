@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
             "pa_status_string", "pa_abi_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert pk.abi_version() >> 16 == 1
+    assert pk.abi_version() >> 16 == 2
 
 
 def test_status_strings():
@@ -54,7 +54,8 @@ def test_argument_checks_without_launch():
     assert lib.pa_write_kv(None, None, None, None, None, -1, ctypes.byref(d), None) == -2
     assert lib.pa_write_kv(None, None, None, None, None, 4, None, None) == -1
     for bad, code in ((dict(head_dim=96), -3), (dict(block_size=12), -3), (dict(block_size=128), -3),
-                      (dict(dtype=7), -3), (dict(num_blocks=0), -2), (dict(num_kv_heads=0), -2)):
+                      (dict(dtype=7), -3), (dict(num_blocks=0), -2), (dict(num_kv_heads=0), -2),
+                      (dict(layout=2), -3), (dict(layout=-1), -3)):
         assert lib.pa_write_kv(None, None, None, None, None, 4, ctypes.byref(_desc(**bad)), None) == code
     args = lambda H, W, desc, P=0, ws=None, wsb=0: (
         None, None, None, None, None, None, 1.0, 4, H, W, ctypes.byref(desc), P, ws, wsb, None)
@@ -127,3 +128,14 @@ def test_prefill_host_checks():
     assert size(2, 4, 10) == 16 + 4 * (1 + 2)    # G = 2 -> 64-token tiles
     assert size(3, 2, 300) == 16 + 4 * (3 + 3)   # G = 1 -> 128-token tiles
     assert size(2, 8, 10, f32) == 0
+
+
+def test_layout_support_matrix():
+    """The vLLM cache layout: the write takes both dtypes, the decode bf16
+    only (fp32 is reported before any launch), the prefill neither."""
+    lib = pk.load_library()
+    vb, vf = _desc(layout=1), _desc(layout=1, dtype=0)
+    assert lib.pa_write_kv(None, None, None, None, None, 4, ctypes.byref(vf), None) == -1   # accepted, then null
+    assert lib.pa_decode_partition_size(4, 32, 64, ctypes.byref(vb)) > 0
+    assert lib.pa_decode_partition_size(4, 32, 64, ctypes.byref(vf)) == -3
+    assert lib.pa_prefill_workspace_bytes(4, 32, 100, ctypes.byref(vb)) == 0
