@@ -63,7 +63,9 @@ typedef enum pa_status {
   PA_ERR_WORKSPACE = -4,    /* workspace NULL or smaller than pa_decode_workspace_bytes() */
   PA_ERR_ALIGN = -5,        /* a tensor pointer is not 16-byte aligned */
   PA_ERR_LAUNCH = -6,       /* the HIP runtime rejected a kernel launch */
-  PA_ERR_TOO_LARGE = -7     /* sizes overflow the kernels' 32-bit grid/index limits */
+  PA_ERR_TOO_LARGE = -7,    /* sizes overflow the kernels' 32-bit grid/index limits */
+  PA_ERR_NO_BLOCKS = -8,    /* block manager: not enough free blocks (nothing was changed) */
+  PA_ERR_NO_SEQUENCE = -9   /* block manager: unknown sequence id */
 } pa_status;
 
 /* Memory layout of the two caches. */
@@ -247,6 +249,69 @@ int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cach
                const int32_t* query_start_loc, float scale, int32_t num_seqs, int32_t num_heads,
                int32_t max_blocks_per_seq, int32_t num_tokens, const pa_cache_desc* desc,
                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Host block manager with prefix sharing (CPU only; no device access).  It
+ * hands out the physical blocks whose ids fill block_tables, slot_mapping and
+ * context_lens for the calls above.  Sources: the third page's BlockManager
+ * (a pool of fixed-size blocks, each keeping its token ids and a hash of them
+ * chained with its prefix's hash, a hash -> block map, a queue of free ids,
+ * allocate reporting the cached prefix) and "PagedAttention kernel：paged KV
+ * cache 与 block table", 面试官追问 (sequences sharing a prompt prefix point
+ * at the same blocks for it).  Semantics where the pages stop:
+ *   - a full block is shared under the chained key h_i = FNV-1a-64 over the
+ *     8-byte little-endian words (h_{i-1}, t_0 .. t_{bs-1}), h_{-1} = all ones,
+ *     when the stored tokens are equal too; partial blocks are private; a
+ *     block is registered for sharing once it is full;
+ *   - a new sequence reuses cached blocks from its start up to the first
+ *     one that is not cached; every later block is new;
+ *   - blocks are reference-counted; at count 0 a block joins the back of the
+ *     free queue keeping its key (a later sequence can revive it); new blocks
+ *     come from the front (initially 0 .. NB-1), evicting a cached block there;
+ *   - an operation that cannot get its blocks returns PA_ERR_NO_BLOCKS and
+ *     changes nothing.
+ * Slot of position p of a sequence: table[p / bs] * bs + p % bs.
+ * Not thread-safe: use one manager per thread or lock around calls.
+ */
+typedef struct pa_block_manager pa_block_manager;
+
+/* A manager of num_blocks blocks of block_size tokens; NULL for non-positive
+ * sizes or if memory runs out.  Free it with pa_bm_destroy. */
+pa_block_manager* pa_bm_create(int32_t num_blocks, int32_t block_size);
+void pa_bm_destroy(pa_block_manager* bm);
+
+/* New sequence holding tokens[0 .. n).  *seq_id receives its id (0, 1, 2, ...
+ * in creation order); *cached_tokens (may be NULL) the number of leading
+ * tokens whose blocks were already cached (a multiple of block_size). */
+int pa_bm_add_sequence(pa_block_manager* bm, const int64_t* tokens, int32_t n, int64_t* seq_id,
+                       int32_t* cached_tokens);
+
+/* Appends one token; *slot receives its slot (for pa_write_kv). */
+int pa_bm_append(pa_block_manager* bm, int64_t seq_id, int64_t token, int64_t* slot);
+
+/* Releases a sequence's blocks (shared blocks stay with their other users). */
+int pa_bm_free_sequence(pa_block_manager* bm, int64_t seq_id);
+
+/* Tokens of a sequence, or a negative pa_status. */
+int32_t pa_bm_length(const pa_block_manager* bm, int64_t seq_id);
+
+/* Blocks in the free queue (cached ones included), or a negative pa_status. */
+int32_t pa_bm_num_free(const pa_block_manager* bm);
+
+/* The sequence's block table into out[0 .. capacity); *num_blocks receives
+ * its length (PA_ERR_SHAPE, with *num_blocks set, if capacity is short). */
+int pa_bm_block_table(const pa_block_manager* bm, int64_t seq_id, int32_t* out, int32_t capacity,
+                      int32_t* num_blocks);
+
+/* Slots of positions start .. start + count - 1 of a sequence into out. */
+int pa_bm_slots(const pa_block_manager* bm, int64_t seq_id, int32_t start, int32_t count, int64_t* out);
+
+/* Host arrays for a batch: block_tables [num_seqs, max_blocks_per_seq]
+ * (rows padded with `fill`) and context_lens [num_seqs], the inputs of
+ * pa_decode / pa_prefill once copied to the device. */
+int pa_bm_fill_tables(const pa_block_manager* bm, const int64_t* seq_ids, int32_t num_seqs,
+                      int32_t max_blocks_per_seq, int32_t fill, int32_t* block_tables,
+                      int32_t* context_lens);
 
 /* Static, NUL-terminated name of a pa_status code ("unknown status" otherwise). */
 const char* pa_status_string(int status);

@@ -22,3 +22,4 @@ from .api import (  # noqa: F401
     workspace_bytes,
     write_kv,
 )
+from .block_manager import BlockManager, BlockManagerError  # noqa: F401,E402

@@ -16,6 +16,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libpaged_kv.so")
 SOURCES = ["pa_api.hip", "pa_write.hip", "pa_decode.hip", "pa_decode_mfma.hip", "pa_prefill.hip"]
+HOST_SOURCES = ["pa_block_manager.cpp"]      # host-only C++ (no device code)
+HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep the compiler from forming v_pk_{add,mul,fma}_f32.
@@ -57,8 +59,19 @@ def build(verbose: bool = False) -> str:
             print(err, file=sys.stderr)
         return obj
 
-    with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
+    def compile_host(src):
+        obj = os.path.join(objdir, src.replace(".cpp", ".o"))
+        cxx = shutil.which("g++") or shutil.which("c++")
+        if not cxx:
+            raise RuntimeError("no host C++ compiler (g++) found")
+        err = _run([cxx, *HOST_FLAGS, "-I", inc, "-c", os.path.join(CSRC, src), "-o", obj])
+        if verbose and err.strip():
+            print(err, file=sys.stderr)
+        return obj
+
+    with cf.ThreadPoolExecutor(max_workers=len(SOURCES) + len(HOST_SOURCES)) as ex:
+        futs = [ex.submit(compile_one, s) for s in SOURCES] + [ex.submit(compile_host, s) for s in HOST_SOURCES]
+        objs = [f.result() for f in futs]
     tmp = LIB + ".tmp"
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
     os.replace(tmp, LIB)

@@ -227,6 +227,8 @@ const char* pa_status_string(int status) {
     case PA_ERR_ALIGN: return "tensor pointer not 16-byte aligned";
     case PA_ERR_LAUNCH: return "HIP kernel launch failed";
     case PA_ERR_TOO_LARGE: return "sizes exceed the kernels' grid or index limits";
+    case PA_ERR_NO_BLOCKS: return "block manager: not enough free blocks";
+    case PA_ERR_NO_SEQUENCE: return "block manager: unknown sequence";
   }
   return "unknown status";
 }
