@@ -21,6 +21,11 @@ than the three launches.
 Prints ONE JSON line.  `value` = KV bytes the decode must read (sum over
 sequences of n_b * 2 * KVH * D * elem) / mean step time, in GB/s (10^9 B/s).
 
+``--config prefix_serving_host`` times the host block manager (no GPU): 4096
+requests sharing a 1024-token system prompt are admitted (prefix matching and
+allocation), run 128 decode steps of batched appends (each step's
+slot_mapping), and are freed; `value` = appended tokens/s.
+
 ``--config prefill_8b_bf16`` times the paged prefill instead: one step =
 pa_write_kv of every sequence's new chunk, then pa_prefill (causal attention
 of the chunk's queries over the sequence's paged K/V), on the Llama-3-8B
@@ -192,6 +197,82 @@ def _cpu_baseline_prefill(w, budget_s: float):
     }
 
 
+BM_METRIC = "host block manager: decode-step appends/s (+ prompt admissions/s, frees/s)"
+
+
+def run_block_manager(args):
+    """Host-only: the C++ block manager on a serving workload with a shared
+    system prompt -- admit every request (prefix matching and allocation),
+    run decode steps (one batched append per step: the step's slot_mapping),
+    free everything.  The oracle runs a bounded sample of the same workload."""
+    import numpy as np
+
+    import paged_kv_cache_70_amd as pk
+    import oracle.block_manager as OBM
+
+    R, bs, system_len, steps = 4096, 16, 1024, 128
+    rng = np.random.default_rng(7)
+    system = rng.integers(0, 32000, system_len)
+    suffix = rng.integers(64, 1025, R)
+    prompts = [np.concatenate([system, rng.integers(0, 32000, int(n))]) for n in suffix]
+    nb = sum((len(p) + steps + bs - 1) // bs for p in prompts)
+    step_tokens = rng.integers(0, 32000, (steps, R))
+
+    def run(bm, n_req, n_steps, batched):
+        t0 = time.perf_counter()
+        sids = [bm.add_sequence(p)[0] for p in prompts[:n_req]]
+        t1 = time.perf_counter()
+        for s in range(n_steps):
+            if batched:
+                bm.append_batch(sids, step_tokens[s, :n_req])
+            else:
+                for i, sid in enumerate(sids):
+                    bm.append(sid, int(step_tokens[s, i]))
+        t2 = time.perf_counter()
+        for sid in sids:
+            bm.free_sequence(sid)
+        t3 = time.perf_counter()
+        return t1 - t0, t2 - t1, t3 - t2
+
+    for _ in range(max(args.warmup, 1)):
+        run(pk.BlockManager(nb, bs), R, 4, True)
+    times = [run(pk.BlockManager(nb, bs), R, steps, True) for _ in range(max(1, min(args.steps, 5)))]
+    adm, app, fr = (min(t[i] for t in times) for i in range(3))
+    res = {
+        "metric": BM_METRIC,
+        "value": round(R * steps / app, 1),
+        "unit": "appended tokens/s",
+        "n_gpus": 0,
+        "steps": len(times),
+        "warmup": max(args.warmup, 1),
+        "ms_per_step": round(app / steps * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int64",
+        "data": "synthetic (seeded token ids)",
+        "config": {"workload": "prefix_serving_host", "requests": R, "block_size": bs,
+                   "system_prompt_tokens": system_len, "suffix_tokens": [64, 1024], "decode_steps": steps,
+                   "num_blocks": nb},
+        "admissions_per_s": round(R / adm, 1),
+        "prompt_tokens_per_s": round(sum(len(p) for p in prompts) / adm, 1),
+        "frees_per_s": round(R / fr, 1),
+        "ms_per_decode_step": round(app / steps * 1e3, 4),
+        "timing": "best of the timed runs, host wall clock; one decode step = one batched append over every "
+                  "request (its slot_mapping); each run uses a fresh manager",
+        "roofline": None,
+    }
+    if not args.no_cpu_baseline:
+        n_req, n_steps = 256, 16
+        ta, tb, tc = run(OBM.BlockManager(nb, bs), n_req, n_steps, False)
+        res["cpu_baseline"] = {
+            "value": round(n_req * n_steps / tb, 1), "unit": "appended tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n_req} requests, {n_steps} decode steps (Python oracle, one thread); admissions "
+                      f"{n_req / ta:.1f}/s, frees {n_req / tc:.1f}/s",
+        }
+    print(json.dumps(res), flush=True)
+
+
 def run_prefill(args, cfg):
     """Chunked-prefill step: write the chunks' K/V, then paged causal attention."""
     import torch
@@ -321,6 +402,9 @@ def main():
                                   (args.copy_calibration or 256) << 20, TRAFFIC_FILE)
         print(json.dumps(r))
         return
+
+    if args.config == "prefix_serving_host":
+        return run_block_manager(args)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "

@@ -289,6 +289,14 @@ int pa_bm_add_sequence(pa_block_manager* bm, const int64_t* tokens, int32_t n, i
 /* Appends one token; *slot receives its slot (for pa_write_kv). */
 int pa_bm_append(pa_block_manager* bm, int64_t seq_id, int64_t token, int64_t* slot);
 
+/* One decode step: appends tokens[i] to sequence seq_ids[i] for every i (each
+ * id at most once) and writes the slots -- the step's slot_mapping -- into
+ * slots[i].  All or nothing: an unknown id (PA_ERR_NO_SEQUENCE), a repeated
+ * id (PA_ERR_SHAPE) or too few free blocks (PA_ERR_NO_BLOCKS) changes
+ * nothing. */
+int pa_bm_append_batch(pa_block_manager* bm, const int64_t* seq_ids, const int64_t* tokens, int32_t n,
+                       int64_t* slots);
+
 /* Releases a sequence's blocks (shared blocks stay with their other users). */
 int pa_bm_free_sequence(pa_block_manager* bm, int64_t seq_id);
 

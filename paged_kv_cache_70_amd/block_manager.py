@@ -6,6 +6,7 @@ library's C++.
     bm = BlockManager(num_blocks, block_size)
     sid, cached = bm.add_sequence(token_ids)     # cached: leading tokens already in the cache
     slot = bm.append(sid, token_id)              # slot for pa_write_kv
+    slots = bm.append_batch(sids, token_ids)     # one decode step's slot_mapping
     bm.block_table(sid), bm.slots(sid, start, count), bm.length(sid), bm.num_free()
     tables, lens = bm.fill_tables(sids, max_blocks_per_seq)   # host arrays for decode / prefill
     bm.free_sequence(sid)
@@ -42,6 +43,7 @@ def _lib():
             "pa_bm_add_sequence": (ctypes.c_int, [vp, vp, i32, p64, p32]),
             "pa_bm_append": (ctypes.c_int, [vp, i64, i64, p64]),
             "pa_bm_free_sequence": (ctypes.c_int, [vp, i64]),
+            "pa_bm_append_batch": (ctypes.c_int, [vp, vp, vp, i32, vp]),
             "pa_bm_length": (i32, [vp, i64]),
             "pa_bm_num_free": (i32, [vp]),
             "pa_bm_block_table": (ctypes.c_int, [vp, i64, vp, i32, p32]),
@@ -89,6 +91,20 @@ class BlockManager:
         slot = ctypes.c_int64()
         _check("pa_bm_append", self._lib.pa_bm_append(self._h, int(sid), int(token), ctypes.byref(slot)))
         return int(slot.value)
+
+    def append_batch(self, sids, tokens) -> np.ndarray:
+        """One decode step: token tokens[i] onto sequence sids[i]; returns the
+        slots (int64, the step's slot_mapping).  All or nothing."""
+        ids = np.ascontiguousarray(np.asarray(sids, dtype=np.int64))
+        tok = np.ascontiguousarray(np.asarray(tokens, dtype=np.int64))
+        if ids.shape != tok.shape or ids.ndim != 1:
+            raise ValueError("sids and tokens must be 1-D of equal length")
+        slots = np.empty(max(ids.size, 1), dtype=np.int64)
+        n = int(ids.size)
+        _check("pa_bm_append_batch", self._lib.pa_bm_append_batch(
+            self._h, ids.ctypes.data if n else None, tok.ctypes.data if n else None, n,
+            slots.ctypes.data if n else None))
+        return slots[:n]
 
     def free_sequence(self, sid: int) -> None:
         _check("pa_bm_free_sequence", self._lib.pa_bm_free_sequence(self._h, int(sid)))

@@ -58,6 +58,7 @@ struct Sequence {
   std::vector<int64_t> tokens;
   std::vector<int32_t> blocks;
   std::vector<uint64_t> keys;   // keys of the full blocks, in order
+  uint64_t stamp = 0;           // last batched append that listed it
 };
 
 }  // namespace
@@ -74,6 +75,8 @@ struct pa_block_manager {
   std::unordered_map<uint64_t, int32_t> by_key;
   std::unordered_map<int64_t, Sequence> seqs;
   int64_t next_seq = 0;
+  uint64_t batch_stamp = 0;
+  std::vector<Sequence*> batch;   // scratch of pa_bm_append_batch
 
   pa_block_manager(int32_t n, int32_t b)
       : nb(n), bs(b), refs(n, 0), registered(n, 0), key(n, 0), tokens((size_t)n * b, 0),
@@ -122,6 +125,22 @@ struct pa_block_manager {
     return memcmp(&tokens[(size_t)b * bs], toks, sizeof(int64_t) * (size_t)bs) == 0 ? b : -1;
   }
 };
+
+// One sequence's append, after the checks (known id, a block available).
+static int64_t append_one(pa_block_manager* bm, Sequence& s, int64_t token) {
+  const int32_t bs = bm->bs;
+  const int64_t pos = (int64_t)s.tokens.size();
+  if (pos % bs == 0) s.blocks.push_back(bm->take());
+  s.tokens.push_back(token);
+  const int32_t b = s.blocks[(size_t)(pos / bs)];
+  if (pos % bs == bs - 1) {   // the block just filled up
+    const size_t i = (size_t)(pos / bs);
+    const uint64_t k = block_key(i ? s.keys[i - 1] : kNoParent, &s.tokens[i * bs], bs);
+    s.keys.push_back(k);
+    bm->register_block(b, k, &s.tokens[i * bs]);
+  }
+  return (int64_t)b * bs + pos % bs;
+}
 
 extern "C" {
 
@@ -181,22 +200,32 @@ int pa_bm_append(pa_block_manager* bm, int64_t seq_id, int64_t token, int64_t* s
   const auto it = bm->seqs.find(seq_id);
   if (it == bm->seqs.end()) return PA_ERR_NO_SEQUENCE;
   Sequence& s = it->second;
-  const int32_t bs = bm->bs;
-  const int64_t pos = (int64_t)s.tokens.size();
-  if (pos >= INT32_MAX) return PA_ERR_TOO_LARGE;
-  if (pos % bs == 0) {
-    if (bm->nfree == 0) return PA_ERR_NO_BLOCKS;
-    s.blocks.push_back(bm->take());
+  if (s.tokens.size() >= (size_t)INT32_MAX) return PA_ERR_TOO_LARGE;
+  if (s.tokens.size() % (size_t)bm->bs == 0 && bm->nfree == 0) return PA_ERR_NO_BLOCKS;
+  *slot = append_one(bm, s, token);
+  return PA_OK;
+}
+
+int pa_bm_append_batch(pa_block_manager* bm, const int64_t* seq_ids, const int64_t* tokens, int32_t n,
+                       int64_t* slots) {
+  if (!bm || (n > 0 && (!seq_ids || !tokens || !slots))) return PA_ERR_NULL;
+  if (n < 0) return PA_ERR_SHAPE;
+  // all or nothing: every id known and listed once (a stamp per call), blocks enough
+  const uint64_t stamp = ++bm->batch_stamp;
+  bm->batch.resize((size_t)n);
+  int32_t need = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const auto it = bm->seqs.find(seq_ids[i]);
+    if (it == bm->seqs.end()) return PA_ERR_NO_SEQUENCE;
+    Sequence& s = it->second;
+    if (s.stamp == stamp) return PA_ERR_SHAPE;
+    s.stamp = stamp;
+    if (s.tokens.size() >= (size_t)INT32_MAX) return PA_ERR_TOO_LARGE;
+    need += s.tokens.size() % (size_t)bm->bs == 0;
+    bm->batch[(size_t)i] = &s;
   }
-  s.tokens.push_back(token);
-  const int32_t b = s.blocks[(size_t)(pos / bs)];
-  if (pos % bs == bs - 1) {   // the block just filled up
-    const size_t i = (size_t)(pos / bs);
-    const uint64_t k = block_key(i ? s.keys[i - 1] : kNoParent, &s.tokens[i * bs], bs);
-    s.keys.push_back(k);
-    bm->register_block(b, k, &s.tokens[i * bs]);
-  }
-  *slot = (int64_t)b * bs + pos % bs;
+  if (need > bm->nfree) return PA_ERR_NO_BLOCKS;
+  for (int32_t i = 0; i < n; ++i) slots[i] = append_one(bm, *bm->batch[(size_t)i], tokens[i]);
   return PA_OK;
 }
 

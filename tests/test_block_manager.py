@@ -115,3 +115,28 @@ def test_errors_and_edge_cases():
         cpp.fill_tables([sid], 0)
     with pytest.raises(ValueError):
         pk.BlockManager(0, 16)
+
+
+def test_append_batch_matches_oracle_and_is_all_or_nothing():
+    rng = random.Random(5)
+    cpp, ora = _both(40, 4)
+    sids = [ora.add_sequence([rng.randrange(9) for _ in range(rng.randrange(0, 13))])[0] for _ in range(6)]
+    for s in sids:
+        cpp.add_sequence(ora.seqs[s][0])
+    for step in range(12):
+        toks = [rng.randrange(9) for _ in sids]
+        need = sum(ora.length(s) % 4 == 0 for s in sids)
+        if need > ora.num_free():
+            before = cpp.num_free()
+            with pytest.raises(pk.BlockManagerError):
+                cpp.append_batch(sids, toks)
+            assert cpp.num_free() == before
+            break
+        slots = cpp.append_batch(sids, toks).tolist()
+        assert slots == [ora.append(s, t) for s, t in zip(sids, toks)]
+        _same_state(cpp, ora, sids)
+    with pytest.raises(pk.PaError):
+        cpp.append_batch([sids[0], sids[0]], [1, 2])         # a sequence listed twice
+    with pytest.raises(pk.BlockManagerError):
+        cpp.append_batch([sids[0], 999], [1, 2])             # unknown id: nothing appended
+    _same_state(cpp, ora, sids)
