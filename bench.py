@@ -286,7 +286,7 @@ def run_prefill(args, cfg):
     T, H, D = w.q.shape
     kc, vc = w.k_cache, w.v_cache
     out = torch.empty_like(w.q)
-    ws = pk.prefill_workspace(cfg.num_seqs, H, T, kc)
+    ws = pk.prefill_workspace(cfg.num_seqs, H, w.block_tables.shape[1], T, kc)
     flush = None if args.hot else torch.ones(1 << 28, dtype=torch.float32, device=dev)
     flush_sink = torch.zeros((), dtype=torch.float32, device=dev)
 

@@ -197,13 +197,15 @@ int pa_decode_merge(void* out, const int32_t* context_lens,
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * pa_prefill_workspace_bytes — size of the device workspace pa_prefill needs
- * (its work plan: 16 bytes plus 4 per (sequence, query tile) pair, bounded by
- * num_tokens / tile + num_seqs).  Depends only on its arguments.  Returns 0
- * for invalid arguments (including a non-bf16 cache).
+ * pa_prefill_workspace_bytes — size of the device workspace pa_prefill needs.
+ * bf16: its work plan, 16 bytes plus 4 per (sequence, query tile) pair
+ * (bounded by num_tokens / tile + num_seqs).  fp32: 8 bytes per query row
+ * plus the split-KV partial results of one decode per query row (as
+ * pa_decode_workspace_bytes for num_tokens sequences, partitions of 64
+ * blocks).  Depends only on its arguments; 0 for invalid arguments.
  */
-size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t num_tokens,
-                                  const pa_cache_desc* desc);
+size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t max_blocks_per_seq,
+                                  int32_t num_tokens, const pa_cache_desc* desc);
 
 /*
  * pa_prefill — paged attention of a packed (varlen) batch of new query tokens,
@@ -231,13 +233,18 @@ size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t n
  *   query_start_loc   device, [B + 1] int32, non-decreasing from 0 to num_tokens
  *   scale             multiplies q.k before the softmax
  *   num_tokens        T >= 0 (T == 0 enqueues nothing)
- *   desc              host, cache geometry; dtype must be PA_BF16 and layout
- *                     PA_LAYOUT_P09 (PA_ERR_UNSUPPORTED otherwise)
+ *   desc              host, cache geometry; layout PA_LAYOUT_P09
+ *                     (PA_ERR_UNSUPPORTED otherwise).  bf16 runs the
+ *                     matrix-core kernel; fp32 runs one vector-ALU decode per
+ *                     query row over its first (position + 1) tokens (a
+ *                     plain path for small fp32 workloads: num_tokens <= 65535)
  *   workspace         device, >= pa_prefill_workspace_bytes(...) bytes, no
  *                     initial contents required.  Calls that share a
  *                     workspace must not run concurrently.
- * Enqueues a one-workgroup planning kernel (the work list, heaviest first)
- * and the attention kernel, whose workgroups draw work from that list.
+ * bf16 enqueues a one-workgroup planning kernel (the work list, heaviest
+ * first) and the attention kernel, whose workgroups draw work from that list;
+ * fp32 enqueues a per-row kernel (each row's context and table row), the
+ * decode partial kernel and, if needed, the merge.
  * Device-side preconditions as for pa_decode, plus L_b <= n_b (queries at
  * negative positions, if any, get zeros) and query_start_loc as stated
  * (entries are clamped to [0, num_tokens]).  Memory safety holds when they
@@ -324,7 +331,8 @@ int pa_bm_fill_tables(const pa_block_manager* bm, const int64_t* seq_ids, int32_
 /* Static, NUL-terminated name of a pa_status code ("unknown status" otherwise). */
 const char* pa_status_string(int status);
 
-/* ABI version of this header: (major << 16) | minor (2.0: pa_cache_desc.layout). */
+/* ABI version of this header: (major << 16) | minor (2.0: pa_cache_desc.layout;
+ * 2.1: fp32 prefill, pa_prefill_workspace_bytes takes max_blocks_per_seq). */
 int32_t pa_abi_version(void);
 
 #ifdef __cplusplus

@@ -88,7 +88,7 @@ def load_library() -> ctypes.CDLL:
         "pa_decode_partials": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, f32, i32, i32, i32, pdesc, i32, vp, sz, vp]),
         "pa_decode_merge": (ctypes.c_int, [vp, vp, i32, i32, i32, pdesc, i32, vp, sz, vp]),
         "pa_prefill": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, vp, f32, i32, i32, i32, i32, pdesc, vp, sz, vp]),
-        "pa_prefill_workspace_bytes": (sz, [i32, i32, i32, pdesc]),
+        "pa_prefill_workspace_bytes": (sz, [i32, i32, i32, i32, pdesc]),
         "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "pa_abi_version": (i32, []),
     }
@@ -265,9 +265,10 @@ def decode_merge(q_like: torch.Tensor, k_cache: torch.Tensor, block_tables: torc
     return out
 
 
-def prefill_workspace(num_seqs: int, num_heads: int, num_tokens: int, k_cache: torch.Tensor) -> torch.Tensor:
+def prefill_workspace(num_seqs: int, num_heads: int, max_blocks_per_seq: int, num_tokens: int,
+                      k_cache: torch.Tensor) -> torch.Tensor:
     """A prefill workspace of the size pa_prefill_workspace_bytes() gives."""
-    need = int(load_library().pa_prefill_workspace_bytes(num_seqs, num_heads, num_tokens,
+    need = int(load_library().pa_prefill_workspace_bytes(num_seqs, num_heads, max_blocks_per_seq, num_tokens,
                                                          ctypes.byref(cache_desc(k_cache))))
     return torch.empty(max(need, 16), dtype=torch.uint8, device=k_cache.device)
 
@@ -294,7 +295,7 @@ def prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block
     elif out.shape != q.shape or out.dtype != q.dtype:
         raise ValueError("out must be like q")
     if workspace is None:
-        workspace = prefill_workspace(B, H, T, k_cache) if desc.dtype == PA_BF16 else out
+        workspace = prefill_workspace(B, H, W, T, k_cache)
     st = lib.pa_prefill(_dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
                         _dev(block_tables, "block_tables", torch.int32),
                         _dev(context_lens, "context_lens", torch.int32),

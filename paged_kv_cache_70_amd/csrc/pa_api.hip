@@ -181,6 +181,7 @@ static int decode_params(void* out, const void* q, const void* k_cache, const vo
   p.v_cache = v_cache;
   p.tables = block_tables;
   p.ctx = context_lens;
+  p.table_rows = nullptr;
   // The kernels take a positive base-2 scale; the sign goes into q.
   const float s2 = scale * 1.4426950408889634f;   // log2(e)
   p.q_mode = s2 > 0.0f ? 0 : (s2 < 0.0f ? 1 : 2);
@@ -215,7 +216,7 @@ using namespace pa;
 
 extern "C" {
 
-int32_t pa_abi_version(void) { return (2 << 16) | 0; }
+int32_t pa_abi_version(void) { return (2 << 16) | 1; }
 
 const char* pa_status_string(int status) {
   switch (status) {
@@ -332,19 +333,37 @@ int pa_decode_merge(void* out, const int32_t* context_lens, int32_t num_seqs, in
 }
 
 // Prefill launch geometry shared by the workspace query and the call.
+//   bf16: the matrix-core kernel; workspace = its work plan.
+//   fp32: one vector-ALU decode per query row over the first (position + 1)
+//   tokens of its sequence; workspace = per-row contexts and table rows, then
+//   the decode's partial results (partitions of 64 blocks).
 struct PrefillShape {
   int32_t hg, nchunks, tq;
   int64_t max_tiles;
   size_t ws_bytes;
+  size_t meta_bytes;      // fp32: the per-row arrays ahead of the decode workspace
+  Checked dec;            // fp32: the decode plan over num_tokens rows
 };
 
-static int prefill_shape(int32_t B, int32_t H, int32_t T, const pa_cache_desc* d, PrefillShape* out) {
+static int prefill_shape(int32_t B, int32_t H, int32_t W, int32_t T, const pa_cache_desc* d, PrefillShape* out) {
   int st = check_desc(d);
   if (st) return st;
-  if (B <= 0 || H <= 0 || T < 0) return PA_ERR_SHAPE;
+  if (B <= 0 || H <= 0 || W <= 0 || T < 0) return PA_ERR_SHAPE;
   if (H % d->num_kv_heads) return PA_ERR_SHAPE;
-  if (d->dtype != PA_BF16 || d->layout != PA_LAYOUT_P09) return PA_ERR_UNSUPPORTED;
-  PrefillShape p;
+  if (d->layout != PA_LAYOUT_P09) return PA_ERR_UNSUPPORTED;
+  PrefillShape p{};
+  if (d->dtype == PA_F32) {
+    if (T > 65535) return PA_ERR_TOO_LARGE;
+    const int64_t max_len = (int64_t)W * d->block_size;
+    const int32_t P = (int32_t)(max_len < 64LL * d->block_size ? max_len : 64LL * d->block_size);
+    st = check_decode_sizes(T > 0 ? T : 1, H, W, d, P, &p.dec);
+    if (st) return st;
+    p.meta_bytes = ((size_t)T * 2 * sizeof(int32_t) + 15) & ~(size_t)15;
+    p.ws_bytes = p.meta_bytes + p.dec.ws_bytes;
+    if (p.ws_bytes == 0) p.ws_bytes = 16;
+    *out = p;
+    return PA_OK;
+  }
   const int32_t G = H / d->num_kv_heads;
   p.hg = prefill_heads_per_group(G);
   p.nchunks = G / p.hg;
@@ -360,10 +379,10 @@ static int prefill_shape(int32_t B, int32_t H, int32_t T, const pa_cache_desc* d
   return PA_OK;
 }
 
-size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t num_tokens,
-                                  const pa_cache_desc* desc) {
+size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t max_blocks_per_seq,
+                                  int32_t num_tokens, const pa_cache_desc* desc) {
   PrefillShape p;
-  return prefill_shape(num_seqs, num_heads, num_tokens, desc, &p) ? 0 : p.ws_bytes;
+  return prefill_shape(num_seqs, num_heads, max_blocks_per_seq, num_tokens, desc, &p) ? 0 : p.ws_bytes;
 }
 
 int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -373,9 +392,8 @@ int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cach
                void* workspace, size_t workspace_bytes, void* stream) {
   const int32_t B = num_seqs, H = num_heads, W = max_blocks_per_seq;
   PrefillShape shp;
-  int st = prefill_shape(B, H, num_tokens, desc, &shp);
+  int st = prefill_shape(B, H, W, num_tokens, desc, &shp);
   if (st) return st;
-  if (W <= 0) return PA_ERR_SHAPE;
   const int64_t max_len = (int64_t)W * desc->block_size;
   if (max_len > INT_MAX / 2) return PA_ERR_TOO_LARGE;
   if (num_tokens == 0) return PA_OK;
@@ -384,6 +402,24 @@ int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cach
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_ALIGN;
   if (!workspace || workspace_bytes < shp.ws_bytes) return PA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return PA_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (desc->dtype == PA_F32) {
+    int32_t* rows_ctx = static_cast<int32_t*>(workspace);
+    int32_t* rows_tbl = rows_ctx + num_tokens;
+    char* dec_ws = static_cast<char*>(workspace) + shp.meta_bytes;
+    DecodeParams prm;
+    st = decode_params(out, q, k_cache, v_cache, block_tables, rows_ctx, scale, num_tokens, H, W, desc,
+                       dec_ws, workspace_bytes - shp.meta_bytes, shp.dec, &prm);
+    if (st) return st;
+    prm.table_rows = rows_tbl;
+    if (launch_prefill_rows(query_start_loc, context_lens, B, num_tokens, (int32_t)max_len, rows_ctx, rows_tbl, s) !=
+        hipSuccess)
+      return PA_ERR_LAUNCH;
+    if (launch_decode_partials(prm, desc->dtype, desc->head_dim, shp.dec.plan, s) != hipSuccess) return PA_ERR_LAUNCH;
+    if (shp.dec.plan.maxP > 1 && launch_decode_merge(prm, desc->dtype, desc->head_dim, s) != hipSuccess)
+      return PA_ERR_LAUNCH;
+    return PA_OK;
+  }
   PrefillParams p;
   p.hg = shp.hg;
   p.nchunks = shp.nchunks;
@@ -410,9 +446,7 @@ int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cach
   p.bs_log2 = ilog2(desc->block_size);
   p.bs_mask = desc->block_size - 1;
   p.max_tokens = (int32_t)max_len;
-  return launch_prefill_mfma(p, desc->head_dim, static_cast<hipStream_t>(stream)) == hipSuccess
-             ? PA_OK
-             : PA_ERR_LAUNCH;
+  return launch_prefill_mfma(p, desc->head_dim, s) == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
 }  // extern "C"

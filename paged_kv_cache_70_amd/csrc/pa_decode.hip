@@ -265,7 +265,7 @@ __global__ __launch_bounds__(64 * NW) void decode_partial_kernel(const DecodePar
   const uint32_t lane_off = (uint32_t)kvh * D * ESZ + (uint32_t)c * 16 + (uint32_t)tr * row_bytes;
   const char* kc = static_cast<const char*>(prm.k_cache);
   const char* vc = static_cast<const char*>(prm.v_cache);
-  const int32_t* tbl = prm.tables + (size_t)b * prm.W;
+  const int32_t* tbl = prm.tables + (size_t)(prm.table_rows ? prm.table_rows[b] : b) * prm.W;
 
   // Block-table entries of this partition, one per lane (a partition spans at
   // most 64 blocks): each tile takes its physical block id with v_readlane, so

@@ -18,6 +18,7 @@ struct DecodeParams {
   const void* v_cache;
   const int32_t* tables;   // [B, W]
   const int32_t* ctx;      // [B]
+  const int32_t* table_rows;  // nullptr: sequence b reads table row b; else row table_rows[b] (fp32 kernel)
   float scale_log2;        // |scale| * log2(e) > 0: scores are kept in base-2 exponent units
   int32_t q_mode;          // 0: q as given, 1: negate q (scale < 0), 2: zero q (scale == 0)
   int32_t B, H, KVH, W, NB;
@@ -83,6 +84,11 @@ hipError_t launch_write_kv_vllm(void* k_cache, void* v_cache, const void* k, con
 hipError_t launch_decode_partials_vllm(const DecodeParams& prm, int32_t D, hipStream_t stream);
 
 hipError_t launch_prefill_mfma(const PrefillParams& prm, int32_t D, hipStream_t stream);
+
+// fp32 prefill as one decode per query: per query row, its context (position
+// + 1, 0 at a negative position) and its sequence's table row.
+hipError_t launch_prefill_rows(const int32_t* qstart, const int32_t* ctx, int32_t B, int32_t T,
+                               int32_t max_tokens, int32_t* ctx_out, int32_t* rows_out, hipStream_t stream);
 
 hipError_t launch_decode_merge(const DecodeParams& prm, int32_t dtype, int32_t D,
                                hipStream_t stream);

@@ -415,6 +415,43 @@ void prefill_mfma_kernel(const PrefillParams prm) {
   }
 }
 
+// fp32 prefill runs as one decode per query row r: the row's sequence b
+// (query_start_loc[b] <= r < query_start_loc[b + 1], by binary search over
+// the clamped starts) gives its table row, and its position n_b - L_b + i
+// gives its context, position + 1 (0 for a negative position, or a row of no
+// sequence).
+__global__ __launch_bounds__(256) void prefill_rows_kernel(const int32_t* __restrict__ qstart,
+                                                           const int32_t* __restrict__ ctx, int32_t B, int32_t T,
+                                                           int32_t max_tokens, int32_t* __restrict__ ctx_out,
+                                                           int32_t* __restrict__ rows_out) {
+  const int r = blockIdx.x * 256 + threadIdx.x;
+  if (r >= T) return;
+  auto start = [&](int b) { const int v = qstart[b]; return v < 0 ? 0 : (v > T ? T : v); };
+  int lo = 0, hi = B;                          // find the last b with start(b) <= r
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (start(mid) <= r) lo = mid; else hi = mid;
+  }
+  const int b = lo;
+  const int q0 = start(b), q1 = max(start(b + 1), q0);
+  int n = ctx[b];
+  n = n < 0 ? 0 : (n > max_tokens ? max_tokens : n);
+  int c = 0;
+  if (r >= q0 && r < q1) {
+    const int pos = n - (q1 - q0) + (r - q0);
+    c = pos < 0 ? 0 : pos + 1;
+  }
+  ctx_out[r] = c;
+  rows_out[r] = b;
+}
+
+hipError_t launch_prefill_rows(const int32_t* qstart, const int32_t* ctx, int32_t B, int32_t T, int32_t max_tokens,
+                               int32_t* ctx_out, int32_t* rows_out, hipStream_t stream) {
+  hipLaunchKernelGGL(prefill_rows_kernel, dim3((T + 255) / 256), dim3(256), 0, stream, qstart, ctx, B, T, max_tokens,
+                     ctx_out, rows_out);
+  return hipGetLastError();
+}
+
 template <int D, bool WholeTile>
 static hipError_t launch_prefill_d(const PrefillParams& prm, hipStream_t stream) {
   // resident workgroups per CU: LDS (2 x 2 x 64 rows of D bf16) and registers

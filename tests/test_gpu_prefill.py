@@ -56,7 +56,9 @@ def _oracle_caches(w):
 def _check(w, what):
     kc, vc, out = _gpu_step(w)
     ko, vo = _oracle_caches(w)
-    assert np.array_equal(stored_np(kc), ko) and np.array_equal(stored_np(vc), vo), f"{what}: write"
+    bits = lambda a: np.ascontiguousarray(a).view(np.uint8)     # bit patterns: poisoned rows hold NaN
+    assert np.array_equal(bits(stored_np(kc)), bits(ko)) and np.array_equal(bits(stored_np(vc)), bits(vo)), \
+        f"{what}: write"
     ref = O.prefill(stored_np(w.q), ko, vo, stored_np(w.block_tables), stored_np(w.context_lens),
                     stored_np(w.query_start_loc), w.scale, w.cfg.dtype)
     err = assert_matches_oracle(out, ref, w.cfg.dtype, what)
@@ -136,15 +138,32 @@ def test_prefill_full_size_sampled():
         _say(f"prefill_8b_bf16 seq {b} (n={lens[b]}, new={w.new[b]}): max err {err:.2e}")
 
 
-def test_prefill_rejects_f32_and_accepts_empty():
-    kc = torch.zeros((4, 16, 2, 64), dtype=torch.float32, device="cuda")
-    q = torch.zeros((3, 4, 64), dtype=torch.float32, device="cuda")
+@pytest.mark.parametrize("case", [
+    (8, 2, 64, 16, [0, 5, 100, 0], [1, 40, 33, 70]),
+    (8, 2, 128, 8, [3, 0, 200], [17, 64, 5]),
+    (6, 2, 128, 32, [40, 0], [9, 90]),
+], ids=lambda c: f"f32_H{c[0]}_KVH{c[1]}_D{c[2]}_bs{c[3]}")
+def test_prefill_f32(case):
+    """fp32 caches: one decode per query row over its first (position + 1)
+    tokens, held to the fp32 tolerance (max-abs 1e-5)."""
+    H, KVH, D, bs, cached, new = case
+    w = make_prefill_custom(num_heads=H, num_kv_heads=KVH, head_dim=D, block_size=bs, cached=cached,
+                            new=new, dtype="f32", seed=D + bs, device="cuda", poison=True)
+    _check(w, f"f32 H{H} KVH{KVH} D{D} bs{bs}")
+
+
+def test_prefill_f32_long_context_splits_partitions():
+    """fp32 rows whose context spans more than one 64-block partition
+    (partials + merge)."""
+    w = make_prefill_custom(num_heads=4, num_kv_heads=2, head_dim=64, block_size=8, cached=[600],
+                            new=[20], dtype="f32", seed=98, device="cuda")
+    _check(w, "f32 long context")
+
+
+def test_prefill_accepts_empty():
     bt = torch.zeros((1, 1), dtype=torch.int32, device="cuda")
     cl = torch.tensor([3], dtype=torch.int32, device="cuda")
-    qs = torch.tensor([0, 3], dtype=torch.int32, device="cuda")
-    with pytest.raises(pk.PaError):
-        pk.prefill(q, kc, kc, bt, cl, qs, 1.0)
-    kb = kc.to(torch.bfloat16)
+    kb = torch.zeros((4, 16, 2, 64), dtype=torch.bfloat16, device="cuda")
     qe = torch.zeros((0, 4, 64), dtype=torch.bfloat16, device="cuda")
     out = pk.prefill(qe, kb, kb, bt, cl, torch.tensor([0, 0], dtype=torch.int32, device="cuda"), 1.0)
     assert out.shape == (0, 4, 64)
@@ -160,7 +179,8 @@ def test_prefill_workspace_reuse_and_sparse_batches():
                              new=new, seed=94, device="cuda")
     w2 = make_prefill_custom(num_heads=8, num_kv_heads=2, head_dim=128, block_size=16, cached=[10, 0],
                              new=[60, 97], seed=95, device="cuda")
-    ws = pk.prefill_workspace(len(cached), 8, w1.q.shape[0], w1.k_cache)
+    ws = pk.prefill_workspace(len(cached), 8, max(w1.block_tables.shape[1], w2.block_tables.shape[1]),
+                              w1.q.shape[0], w1.k_cache)
     for w, what in ((w1, "sparse batch"), (w2, "second shape, same workspace"), (w1, "sparse batch again")):
         kc, vc = w.k_cache.clone(), w.v_cache.clone()
         pk.write_kv(kc, vc, w.k_new, w.v_new, w.slot_mapping)
@@ -171,3 +191,39 @@ def test_prefill_workspace_reuse_and_sparse_batches():
                         stored_np(w.query_start_loc), w.scale, "bf16")
         err = assert_matches_oracle(out, ref, "bf16", what)
         _say(f"{what}: max err {err:.2e}")
+
+
+def test_prefill_block_size_64_and_long_fresh_prompt():
+    """Block size 64 (four 16-row subtiles per block) and a 700-token fresh
+    prompt spanning many key tiles and query tiles."""
+    w = make_prefill_custom(num_heads=8, num_kv_heads=2, head_dim=128, block_size=64,
+                            cached=[0, 100, 3], new=[700, 45, 129], seed=96, device="cuda", poison=True)
+    _check(w, "bs64")
+
+
+def test_prefill_broken_preconditions_stay_in_bounds():
+    """Inputs that break the documented preconditions still run in bounds:
+    more new queries than context tokens (the queries at negative positions
+    get zeros), a table entry outside the pool (its rows read as zeros), a
+    query_start_loc past num_tokens (clamped).  Only memory safety and the
+    documented zero rows are checked, plus finiteness."""
+    w = make_prefill_custom(num_heads=8, num_kv_heads=2, head_dim=128, block_size=16,
+                            cached=[0, 20], new=[30, 40], seed=97, device="cuda")
+    kc, vc = w.k_cache.clone(), w.v_cache.clone()
+    pk.write_kv(kc, vc, w.k_new, w.v_new, w.slot_mapping)
+    ctx = w.context_lens.clone()
+    ctx[0] = 10                                    # 30 new queries but only 10 tokens of context
+    tables = w.block_tables.clone()
+    tables[1, 0] = 1 << 30                         # a block far outside the pool
+    qsl = w.query_start_loc.clone()
+    out = torch.full_like(w.q, float("nan"))
+    pk.prefill(w.q, kc, vc, tables, ctx, qsl, w.scale, out=out)
+    torch.cuda.synchronize()
+    o = out.float()
+    assert bool(torch.isfinite(o).all())
+    assert bool((o[:20] == 0).all())               # positions -20 .. -1 see no keys
+    qsl2 = qsl.clone()
+    qsl2[2] = 10 ** 6                              # past num_tokens: clamped
+    out2 = pk.prefill(w.q, kc, vc, w.block_tables, w.context_lens, qsl2, w.scale)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out2.float()).all())

@@ -111,7 +111,8 @@ def test_prefill_host_checks():
     f32 = pk.CacheDesc(64, 16, 2, 128, 0)
     call = lambda desc, B=2, H=8, W=4, T=10, ptr=None, ws=None, wsb=0: lib.pa_prefill(
         ptr, ptr, ptr, ptr, ptr, ptr, ptr, 0.1, B, H, W, T, ctypes.byref(desc), ws, wsb, None)
-    assert call(f32) == -3                       # PA_ERR_UNSUPPORTED: prefill is bf16 only
+    assert call(f32) == -1                       # fp32 is accepted (then: null pointers)
+    assert call(pk.CacheDesc(64, 16, 2, 128, 1, 1)) == -3   # vLLM layout: PA_ERR_UNSUPPORTED
     assert call(bf16, H=7) == -2                 # H % KVH != 0
     assert call(bf16, B=0) == -2
     assert call(bf16, T=-1) == -2
@@ -123,11 +124,14 @@ def test_prefill_host_checks():
     assert call(bf16, ptr=16) == -4
     assert call(bf16, ptr=16, ws=16, wsb=27) == -4
     # G = 4 -> 4 heads x 32 tokens per unit: ceil(10 / 32) + 2 = 3 plan entries
-    size = lambda B, H, T, d=bf16: lib.pa_prefill_workspace_bytes(B, H, T, ctypes.byref(d))
+    size = lambda B, H, T, d=bf16, W=4: lib.pa_prefill_workspace_bytes(B, H, W, T, ctypes.byref(d))
     assert size(2, 8, 10) == 16 + 4 * 3
     assert size(2, 4, 10) == 16 + 4 * (1 + 2)    # G = 2 -> 64-token tiles
     assert size(3, 2, 300) == 16 + 4 * (3 + 3)   # G = 1 -> 128-token tiles
-    assert size(2, 8, 10, f32) == 0
+    # fp32: 8 B per row (16-byte aligned), then one decode per row: W = 4 blocks of 16 fit one
+    # partition (no partials); W = 100 -> 2 partitions of 64 blocks: rows * H * 2 * (D + 2) * 4 B
+    assert size(2, 8, 10, f32) == 80 + 0
+    assert size(2, 8, 10, f32, W=100) == 80 + 10 * 8 * 2 * 130 * 4
 
 
 def test_layout_support_matrix():
@@ -138,4 +142,4 @@ def test_layout_support_matrix():
     assert lib.pa_write_kv(None, None, None, None, None, 4, ctypes.byref(vf), None) == -1   # accepted, then null
     assert lib.pa_decode_partition_size(4, 32, 64, ctypes.byref(vb)) > 0
     assert lib.pa_decode_partition_size(4, 32, 64, ctypes.byref(vf)) == -3
-    assert lib.pa_prefill_workspace_bytes(4, 32, 100, ctypes.byref(vb)) == 0
+    assert lib.pa_prefill_workspace_bytes(4, 32, 8, 100, ctypes.byref(vb)) == 0
