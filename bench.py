@@ -26,6 +26,11 @@ requests sharing a 1024-token system prompt are admitted (prefix matching and
 allocation), run 128 decode steps of batched appends (each step's
 slot_mapping), and are freed; `value` = appended tokens/s.
 
+``--config write_65536_bf16`` times pa_write_kv alone at a prefill-sized
+token count: 65,536 tokens (16 prompts of 4096) with the Llama-3-8B shape
+(KVH 8, D 128, bs 16) into shuffled blocks; `value` = bytes moved (K and V rows
+read and written, plus the slots) / mean kernel time, in GB/s.
+
 ``--config prefill_8b_bf16`` times the paged prefill instead: one step =
 pa_write_kv of every sequence's new chunk, then pa_prefill (causal attention
 of the chunk's queries over the sequence's paged K/V), on the Llama-3-8B
@@ -53,30 +58,37 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores, published
 METRIC = "paged decode KV-read GB/s (% of HBM peak) + µs/step; write_kv GB/s"
 PREFILL_METRIC = "paged prefill TFLOP/s (% of bf16 MFMA peak) + µs/step"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_partial_traffic.json")
+WRITE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "write_kv_traffic.json")
 CSRC = os.path.join(ROOT, "paged_kv_cache_70_amd", "csrc")
-# source file of the partial kernel each cache dtype runs
-DECODE_SRC = {"bf16": os.path.join(CSRC, "pa_decode_mfma.hip"), "f32": os.path.join(CSRC, "pa_decode.hip")}
+# the dominant kernel of each bench line ("bf16" / "f32": the decode partial
+# kernel of that cache dtype; "write": the scatter write): its name in traces
+# and its source file
+PARTIAL_KERNELS = {"bf16": "decode_partial_mfma_kernel", "f32": "decode_partial_kernel", "write": "write_kv_kernel"}
+KERNEL_SRC = {"bf16": os.path.join(CSRC, "pa_decode_mfma.hip"), "f32": os.path.join(CSRC, "pa_decode.hip"),
+              "write": os.path.join(CSRC, "pa_write.hip")}
 
 
-def _src_hash(dtype: str) -> str:
-    with open(DECODE_SRC[dtype], "rb") as f:
+def _traffic_file(key: str) -> str:
+    return WRITE_TRAFFIC_FILE if key == "write" else TRAFFIC_FILE
+
+
+def _src_hash(key: str) -> str:
+    with open(KERNEL_SRC[key], "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def _traffic(workload: str, dtype: str):
-    """HBM bytes per partial-kernel launch from the committed rocprofv3 counter
-    summary, if it was taken on this workload and this kernel source."""
+def _traffic(workload: str, key: str):
+    """HBM bytes per launch of the kernel `key` from the committed rocprofv3
+    counter summary, if it was taken on this workload and this kernel source."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(_traffic_file(key)) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("source_sha256_16") != _src_hash(dtype) or t.get("workload") != workload:
+    if t.get("source_sha256_16") != _src_hash(key) or t.get("workload") != workload:
         return None
     return t.get("bytes_per_launch")
 
-
-PARTIAL_KERNELS = {"bf16": "decode_partial_mfma_kernel", "f32": "decode_partial_kernel"}
 CALIB_TAG = "MulFunctor"        # torch.mul(src, 2.0, out=dst): the calibration copy
 
 
@@ -88,19 +100,20 @@ def _counter_rows(path: str, counter: str):
                 if r.get("Counter_Name") == counter]
 
 
-def traffic_from_counters(fetch_csv: str, write_csv: str, workload: str, dtype: str,
+def traffic_from_counters(fetch_csv: str, write_csv: str, workload: str, key: str,
                           calib_bytes: int, out_json: str) -> dict:
-    """HBM bytes per partial-kernel launch from two rocprofv3 --pmc runs of
-    this script (FETCH_SIZE, then WRITE_SIZE; both in KiB per dispatch), each
-    scaled by the same counter's reading for the calibration copy, which reads
-    and writes calib_bytes."""
-    kname = PARTIAL_KERNELS[dtype]
-    res = {"workload": workload, "kernel": kname, "source_sha256_16": _src_hash(dtype),
+    """HBM bytes per launch of the kernel `key` from two rocprofv3 --pmc runs
+    of this script (FETCH_SIZE, then WRITE_SIZE; both in KiB per dispatch),
+    each scaled by the same counter's reading for the calibration copy, which
+    reads and writes calib_bytes."""
+    kname = PARTIAL_KERNELS[key]
+    res = {"workload": workload, "kernel": kname, "source_sha256_16": _src_hash(key),
            "calibration_copy_bytes": calib_bytes}
     total = 0.0
     for key, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         rows = _counter_rows(path, key)
-        kern = [v * 1024 for n, v in rows if n.startswith(kname) or f" {kname}<" in n or f"::{kname}<" in n]
+        kern = [v * 1024 for n, v in rows
+                if n.startswith(kname) or f" {kname}<" in n or f"::{kname}<" in n or f"::{kname}(" in n]
         cal = [v * 1024 for n, v in rows if CALIB_TAG in n]
         if not kern or not cal:
             raise SystemExit(f"{path}: no {key} rows for {kname} ({len(kern)}) or the calibration copy ({len(cal)})")
@@ -373,6 +386,119 @@ def run_prefill(args, cfg):
     print(json.dumps(res), flush=True)
 
 
+def _cpu_baseline_write(w, budget_s: float):
+    """The oracle's write (untuned: one token at a time) on the same
+    workload, repeated while less than budget_s of CPU work has been done,
+    scaled to GB/s of the same bytes."""
+    import oracle as O
+    from tests.gpu_util import stored_np
+
+    kc, vc = stored_np(w.k_cache).copy(), stored_np(w.v_cache).copy()
+    k, v, sl = stored_np(w.k_new), stored_np(w.v_new), stored_np(w.slot_mapping)
+    done, t = 0, 0.0
+    while t < budget_s:
+        t0 = time.perf_counter()
+        O.write_kv(kc, vc, k, v, sl)
+        t += time.perf_counter() - t0
+        done += 1
+    return {
+        "value": round(w.bytes_moved() * done / t / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{done} whole writes of the {w.slot_mapping.numel()} tokens in {t:.1f} s (Python loop "
+                  f"over tokens, NumPy row copies); host has {len(os.sched_getaffinity(0))} usable cores",
+    }
+
+
+def run_write(args, cfg):
+    """The paged KV write on its own, at a prefill-sized token count."""
+    import torch
+
+    import paged_kv_cache_70_amd as pk
+    from synth import make_write
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = make_write(cfg, dev)
+    kc, vc = w.k_cache, w.v_cache
+    flush = None if args.hot else torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    flush_sink = torch.zeros((), dtype=torch.float32, device=dev)
+
+    def write():
+        pk.write_kv(kc, vc, w.k_new, w.v_new, w.slot_mapping)
+
+    def do_flush():
+        if flush is not None:
+            torch.sum(flush, dim=0, out=flush_sink)
+
+    if args.copy_calibration:
+        src = torch.ones(args.copy_calibration << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            do_flush()
+            torch.mul(src, 2.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+
+    for _ in range(args.warmup):
+        do_flush()
+        write()
+    torch.cuda.synchronize()
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        do_flush()
+        events[i][0].record()
+        write()
+        events[i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    st = [a.elapsed_time(b) * 1e3 for a, b in events]
+    us = sum(st) / len(st)
+    nbytes = w.bytes_moved()
+    gbps = nbytes / (us * 1e-6) / 1e9
+    T = w.slot_mapping.numel()
+    res = {
+        "metric": METRIC,
+        "value": round(gbps, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(us / 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded N(0,1) values; 16 prompts' tokens into shuffled physical blocks)",
+        "config": {
+            "workload": cfg.name, "tokens": T, "valid_tokens": w.valid_tokens, "num_kv_heads": cfg.num_kv_heads,
+            "head_dim": cfg.head_dim, "block_size": cfg.block_size, "num_blocks": kc.shape[0],
+            "cache_flush_between_steps": flush is not None,
+        },
+        "bytes_per_step": nbytes,
+        "write_us": round(us, 2),
+        "step_us_p10_p50_p90": [round(sorted(st)[min(len(st) - 1, int(q * len(st)))], 2) for q in (0.1, 0.5, 0.9)],
+        "wall_ms_per_step_incl_flush": round(wall / args.steps * 1e3, 4),
+        "timing": "events around the write kernel alone; bytes = valid K and V rows read and written + 8 B "
+                  "of slot per token",
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(gbps, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(gbps / HBM_PEAK_GBPS, 4),
+            "traffic": _traffic(cfg.name, "write"),
+            "kernel": "write_kv_kernel",
+        },
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = _cpu_baseline_write(w, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -392,14 +518,18 @@ def main():
                          "reading for HBM byte counters)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU run: turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, WRITE_SIZE) of a "
-                         "--copy-calibration run into profiles/decode_partial_traffic.json")
+                         "--copy-calibration run into profiles/decode_partial_traffic.json (decode configs) or "
+                         "profiles/write_kv_traffic.json (write configs)")
     args = ap.parse_args()
 
     if args.traffic_from:
-        from synth import CONFIGS
-        cfg = CONFIGS[args.config]
-        r = traffic_from_counters(*args.traffic_from, cfg.name, cfg.dtype,
-                                  (args.copy_calibration or 256) << 20, TRAFFIC_FILE)
+        from synth import CONFIGS, WRITE_CONFIGS
+        if args.config in WRITE_CONFIGS:
+            name, key = args.config, "write"
+        else:
+            name, key = CONFIGS[args.config].name, CONFIGS[args.config].dtype
+        r = traffic_from_counters(*args.traffic_from, name, key,
+                                  (args.copy_calibration or 256) << 20, _traffic_file(key))
         print(json.dumps(r))
         return
 
@@ -420,9 +550,11 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     pk.load_library()
-    from synth import PREFILL_CONFIGS
+    from synth import PREFILL_CONFIGS, WRITE_CONFIGS
     if args.config in PREFILL_CONFIGS:
         return run_prefill(args, PREFILL_CONFIGS[args.config])
+    if args.config in WRITE_CONFIGS:
+        return run_write(args, WRITE_CONFIGS[args.config])
     cfg = CONFIGS[args.config]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

@@ -58,3 +58,21 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_traffic_of_the_write_kernel(tmp_path):
+    """The write kernel's rows are picked by name (not the vLLM-layout write's),
+    hashed against its own source and written to its own summary."""
+    calib = 256 << 20
+    copy = "void at::native::vectorized_elementwise_kernel<4, AUnaryFunctor<float, float, float, MulFunctor<float>>>"
+    kern = "pa::write_kv_kernel(unsigned int __vector(4)*, unsigned int __vector(4)*, long const*)"
+    vllm = "void pa::write_kv_vllm_kernel<unsigned short>(unsigned int __vector(4)*, unsigned short*)"
+    _csv(tmp_path / "f.csv", "FETCH_SIZE", [(copy, calib / 2048), (kern, 300.0), (vllm, 9e6)])
+    _csv(tmp_path / "w.csv", "WRITE_SIZE", [(copy, calib / 1024), (kern, 200.0), (vllm, 9e6)])
+    r = bench.traffic_from_counters(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"),
+                                    "write_65536_bf16", "write", calib, str(tmp_path / "t.json"))
+    assert r["kernel"] == "write_kv_kernel" and r["fetch_size"]["dispatches"] == 1
+    assert r["fetch_size"]["bytes_per_launch"] == 600 * 1024          # FETCH read half: scale 2
+    assert r["bytes_per_launch"] == 800 * 1024
+    assert r["source_sha256_16"] == bench._src_hash("write") != bench._src_hash("bf16")
+    assert bench._traffic_file("write") != bench._traffic_file("bf16")

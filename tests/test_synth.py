@@ -83,3 +83,26 @@ def test_deterministic_and_poison():
     # poison tails point at NaN blocks that exist
     tbl = a.block_tables.to(torch.int64)
     assert int(tbl.max()) < a.num_blocks
+
+
+def test_write_workload_recipe():
+    """Prompt runs of bs tokens share one block, slots are distinct and inside
+    the pool, padding slots are -1, and the full-size recipe moves ~537 MB."""
+    import dataclasses
+
+    from synth import WRITE_CONFIGS, make_write
+    base = WRITE_CONFIGS["write_65536_bf16"]
+    cfg = dataclasses.replace(base, pad_tokens=7)
+    w = make_write(cfg, num_prompts=4, prompt_len=50)
+    s = w.slot_mapping.tolist()
+    assert len(s) == 4 * 50 + 7 and s.count(-1) == 7 and w.valid_tokens == 200
+    valid = [x for x in s if x >= 0]
+    assert len(set(valid)) == len(valid) and max(valid) < w.k_cache.shape[0] * cfg.block_size
+    for p in range(4):
+        run = valid[p * 50:(p + 1) * 50]
+        for t in range(50):
+            assert run[t] % 16 == t % 16 and run[t] // 16 == run[t - t % 16] // 16
+    S, L = base.num_prompts, base.prompt_len
+    assert S * L == 65536
+    row = base.num_kv_heads * base.head_dim * 2
+    assert S * L * row * 4 + 8 * S * L == 537_395_200
