@@ -20,6 +20,9 @@ than the three launches.
 
 Prints ONE JSON line.  `value` = KV bytes the decode must read (sum over
 sequences of n_b * 2 * KVH * D * elem) / mean step time, in GB/s (10^9 B/s).
+`roofline.achieved` takes the distinct rows instead (`kv_unique_bytes_per_step`:
+a block shared by several tables counts once), the bytes HBM must deliver;
+the two differ only for the prefix-shared workload.
 
 ``--config prefix_serving_host`` times the host block manager (no GPU): 4096
 requests sharing a 1024-token system prompt are admitted (prefix matching and
@@ -57,8 +60,7 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores, published
 METRIC = "paged decode KV-read GB/s (% of HBM peak) + µs/step; write_kv GB/s"
 PREFILL_METRIC = "paged prefill TFLOP/s (% of bf16 MFMA peak) + µs/step"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_partial_traffic.json")
-WRITE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "write_kv_traffic.json")
+PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "paged_kv_cache_70_amd", "csrc")
 # the dominant kernel of each bench line ("bf16" / "f32": the decode partial
 # kernel of that cache dtype; "write": the scatter write): its name in traces
@@ -68,8 +70,9 @@ KERNEL_SRC = {"bf16": os.path.join(CSRC, "pa_decode_mfma.hip"), "f32": os.path.j
               "write": os.path.join(CSRC, "pa_write.hip")}
 
 
-def _traffic_file(key: str) -> str:
-    return WRITE_TRAFFIC_FILE if key == "write" else TRAFFIC_FILE
+def _traffic_file(key: str, workload: str) -> str:
+    """The committed counter summary of kernel `key` on `workload`."""
+    return os.path.join(PROFILES, f"traffic_{PARTIAL_KERNELS[key]}_{workload}.json")
 
 
 def _src_hash(key: str) -> str:
@@ -81,7 +84,7 @@ def _traffic(workload: str, key: str):
     """HBM bytes per launch of the kernel `key` from the committed rocprofv3
     counter summary, if it was taken on this workload and this kernel source."""
     try:
-        with open(_traffic_file(key)) as f:
+        with open(_traffic_file(key, workload)) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
@@ -518,8 +521,7 @@ def main():
                          "reading for HBM byte counters)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU run: turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, WRITE_SIZE) of a "
-                         "--copy-calibration run into profiles/decode_partial_traffic.json (decode configs) or "
-                         "profiles/write_kv_traffic.json (write configs)")
+                         "--copy-calibration run into profiles/traffic_<kernel>_<workload>.json")
     args = ap.parse_args()
 
     if args.traffic_from:
@@ -529,7 +531,7 @@ def main():
         else:
             name, key = CONFIGS[args.config].name, CONFIGS[args.config].dtype
         r = traffic_from_counters(*args.traffic_from, name, key,
-                                  (args.copy_calibration or 256) << 20, _traffic_file(key))
+                                  (args.copy_calibration or 256) << 20, _traffic_file(key, name))
         print(json.dumps(r))
         return
 
@@ -679,6 +681,9 @@ def main():
         return s[min(len(s) - 1, int(q * len(s)))]
 
     kv_bytes = w.kv_bytes()
+    # the HBM roofline takes the distinct rows: a prefix block shared by many
+    # tables is fetched from HBM once and then served from cache
+    kv_unique = w.kv_unique_bytes()
     elem = 4 if cfg.dtype == "f32" else 2
     row = cfg.num_kv_heads * D * elem
     n_valid = int((w.slot_mapping >= 0).sum())
@@ -687,7 +692,7 @@ def main():
     wr_us, k2_us, k3_us = mean(wr), mean(k2), mean(k3)
     dec_us = k2_us + k3_us
     value = kv_bytes / (step_us * 1e-6) / 1e9
-    achieved = kv_bytes / (k2_us * 1e-6) / 1e9
+    achieved = kv_unique / (k2_us * 1e-6) / 1e9
     traffic = _traffic(cfg.name, cfg.dtype) if args.layout == "p09" else None
 
     res = {
@@ -709,7 +714,7 @@ def main():
             "write_tokens": int(w.slot_mapping.numel()), "partition_size": P, "cache_layout": args.layout,
             "cache_flush_between_steps": flush is not None,
         },
-        "hbm_frac_step": round(value / HBM_PEAK_GBPS, 4),
+        "hbm_frac_step": round(kv_unique / (step_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
         "decode_us": round(dec_us, 2),
         "decode_kv_GBps": round(kv_bytes / (dec_us * 1e-6) / 1e9, 1),
         "partial_kernel_us": round(k2_us, 2),
@@ -719,6 +724,7 @@ def main():
         "write_us": round(wr_us, 2),
         "write_GBps": round(write_bytes / (wr_us * 1e-6) / 1e9, 2),
         "kv_bytes_per_step": kv_bytes,
+        "kv_unique_bytes_per_step": kv_unique,
         "wall_ms_per_step_incl_flush": round(wall / args.steps * 1e3, 4),
         "timing": "step = events around the write, partial and merge kernels launched one after another "
                   "(graph_step_us: the same step replayed from a HIP graph); per-kernel times from a second "

@@ -168,6 +168,14 @@ class Workload:
         elem = 4 if c.dtype == "f32" else 2
         return int(self.context_lens.to(torch.int64).sum()) * 2 * c.num_kv_heads * c.head_dim * elem
 
+    def kv_unique_bytes(self) -> int:
+        """Bytes of the distinct K and V rows the decode reads: a block that
+        several tables share counts once (equal to kv_bytes() without
+        sharing).  The least the decode must fetch from HBM."""
+        c = self.cfg
+        elem = 4 if c.dtype == "f32" else 2
+        return int(self.live_slots.numel()) * 2 * c.num_kv_heads * c.head_dim * elem
+
 
 def _draw_lengths(cfg: Config, g: torch.Generator) -> list[int]:
     B = cfg.num_seqs

@@ -42,10 +42,10 @@ def test_traffic_from_counters_scales_by_calibration(tmp_path):
 
 
 def test_traffic_file_ignored_when_stale(tmp_path, monkeypatch):
-    p = tmp_path / "t.json"
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    p = tmp_path / "traffic_decode_partial_mfma_kernel_llama3_8b_bf16.json"
     p.write_text(json.dumps({"workload": "llama3_8b_bf16", "source_sha256_16": "0" * 16,
                              "bytes_per_launch": 5}))
-    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(p))
     assert bench._traffic("llama3_8b_bf16", "bf16") is None
     p.write_text(json.dumps({"workload": "llama3_8b_bf16", "source_sha256_16": bench._src_hash("bf16"),
                              "bytes_per_launch": 5}))
@@ -75,4 +75,4 @@ def test_traffic_of_the_write_kernel(tmp_path):
     assert r["fetch_size"]["bytes_per_launch"] == 600 * 1024          # FETCH read half: scale 2
     assert r["bytes_per_launch"] == 800 * 1024
     assert r["source_sha256_16"] == bench._src_hash("write") != bench._src_hash("bf16")
-    assert bench._traffic_file("write") != bench._traffic_file("bf16")
+    assert bench._traffic_file("write", "w").endswith("traffic_write_kv_kernel_w.json")
