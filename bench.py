@@ -22,7 +22,9 @@ Prints ONE JSON line.  `value` = KV bytes the decode must read (sum over
 sequences of n_b * 2 * KVH * D * elem) / mean step time, in GB/s (10^9 B/s).
 `roofline.achieved` takes the distinct rows instead (`kv_unique_bytes_per_step`:
 a block shared by several tables counts once), the bytes HBM must deliver;
-the two differ only for the prefix-shared workload.
+the two differ only for the prefix-shared workload, which by default decodes
+with pa_decode_shared_prefix and its 2048-token common prefix as the hint
+(`--shared-tokens 0`: plain pa_decode).
 
 ``--config prefix_serving_host`` times the host block manager (no GPU): 4096
 requests sharing a 1024-token system prompt are admitted (prefix matching and
@@ -513,6 +515,9 @@ def main():
     ap.add_argument("--layout", choices=["p09", "vllm"], default="p09",
                     help="cache layout: P09's [NB, bs, KVH, D] (default) or vLLM's packed K [NB, KVH, D/x, bs, x] "
                          "with V [NB, KVH, D, bs] (decode configs, bf16)")
+    ap.add_argument("--shared-tokens", type=int, default=-1,
+                    help="decode with pa_decode_shared_prefix and this hint (default: the workload's common "
+                         "prefix for prefix_shared_bf16, else 0 = pa_decode)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="skip the graph-replay timing")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
@@ -578,9 +583,16 @@ def main():
     def write():
         pk.write_kv(kc, vc, w.k_new, w.v_new, w.slot_mapping)
 
+    shared = args.shared_tokens if args.shared_tokens >= 0 else (
+        int(cfg.ctx[1]) if cfg.ctx[0] == "prefix" else 0)
+
     def partials():
-        pk.decode_partials(w.q, kc, vc, w.block_tables, w.context_lens, w.scale, out=out,
-                           workspace=ws, partition_size=P)
+        if shared:
+            pk.decode_partials_shared_prefix(w.q, kc, vc, w.block_tables, w.context_lens, w.scale, shared,
+                                             out=out, workspace=ws, partition_size=P)
+        else:
+            pk.decode_partials(w.q, kc, vc, w.block_tables, w.context_lens, w.scale, out=out,
+                               workspace=ws, partition_size=P)
 
     def merge():
         pk.decode_merge(w.q, kc, w.block_tables, w.context_lens, out=out, workspace=ws,
@@ -712,6 +724,7 @@ def main():
             "workload": cfg.name, "num_seqs": B, "num_heads": H, "num_kv_heads": cfg.num_kv_heads,
             "head_dim": D, "block_size": cfg.block_size, "context_lens": list(cfg.ctx),
             "write_tokens": int(w.slot_mapping.numel()), "partition_size": P, "cache_layout": args.layout,
+            "shared_prefix_hint_tokens": shared,
             "cache_flush_between_steps": flush is not None,
         },
         "hbm_frac_step": round(kv_unique / (step_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),

@@ -185,6 +185,46 @@ int pa_decode_partials(void* out, const void* q, const void* k_cache, const void
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * pa_decode_shared_prefix — pa_decode for a batch whose tables may begin with
+ * the same blocks: sequences that share a prompt prefix point their tables at
+ * the same physical blocks for it ("PagedAttention kernel：paged KV cache 与
+ * block table", 面试官追问 on prefix sharing).  Same arguments and result as
+ * pa_decode, plus
+ *   shared_tokens   >= 0: a hint that table rows may equal row 0 over their
+ *                   first shared_tokens / block_size entries.  The leading
+ *                   floor(min(shared_tokens, W * bs) / P) whole partitions
+ *                   (P: the partition size in use) are folded for up to
+ *                   16 / G sequences at once (G = num_heads / num_kv_heads
+ *                   query heads of one kv head side by side as the 16 matrix
+ *                   columns), so each shared block is read once per group
+ *                   instead of once per sequence.
+ * The device checks every row: a sequence takes part only if its first
+ * entries over those partitions equal row 0's and its context extends past
+ * them; every other sequence, and any call where G does not divide 16 or is
+ * 16 or more, the fp32 dtype, or more than 4096 sequences, is decoded as by
+ * pa_decode.  The result therefore never depends on the hint being right: a
+ * wrong hint costs only the check.  Output equals pa_decode's within fp32
+ * rounding (per-column softmax state; the lazy rescale may fire at other
+ * tiles).  Workspace: pa_decode_workspace_bytes.  Errors as pa_decode, plus
+ * PA_ERR_SHAPE for shared_tokens < 0.
+ */
+int pa_decode_shared_prefix(void* out, const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, const int32_t* context_lens, float scale,
+                            int32_t num_seqs, int32_t num_heads, int32_t max_blocks_per_seq,
+                            int32_t shared_tokens, const pa_cache_desc* desc, int32_t partition_size,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pa_decode_partials_shared_prefix — the first half of pa_decode_shared_prefix
+ * (as pa_decode_partials is of pa_decode); pa_decode_merge finishes it.
+ */
+int pa_decode_partials_shared_prefix(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                     const int32_t* block_tables, const int32_t* context_lens, float scale,
+                                     int32_t num_seqs, int32_t num_heads, int32_t max_blocks_per_seq,
+                                     int32_t shared_tokens, const pa_cache_desc* desc, int32_t partition_size,
+                                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * pa_decode_merge — second half of pa_decode: for every sequence spanning
  * more than one partition, combines the partial results of pa_decode_partials
  * (max-rescaled sums: out = sum_p e^(m_p - M) acc_p / sum_p e^(m_p - M) l_p)
@@ -332,7 +372,8 @@ int pa_bm_fill_tables(const pa_block_manager* bm, const int64_t* seq_ids, int32_
 const char* pa_status_string(int status);
 
 /* ABI version of this header: (major << 16) | minor (2.0: pa_cache_desc.layout;
- * 2.1: fp32 prefill, pa_prefill_workspace_bytes takes max_blocks_per_seq). */
+ * 2.1: fp32 prefill, pa_prefill_workspace_bytes takes max_blocks_per_seq;
+ * 2.2: pa_decode_shared_prefix, pa_decode_partials_shared_prefix). */
 int32_t pa_abi_version(void);
 
 #ifdef __cplusplus

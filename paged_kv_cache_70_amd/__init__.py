@@ -11,6 +11,8 @@ from .api import (  # noqa: F401
     cache_desc,
     decode,
     decode_merge,
+    decode_partials_shared_prefix,
+    decode_shared_prefix,
     decode_partials,
     library_path,
     load_library,

@@ -31,6 +31,8 @@ __all__ = [
     "decode",
     "decode_partials",
     "decode_merge",
+    "decode_shared_prefix",
+    "decode_partials_shared_prefix",
     "prefill",
     "prefill_workspace",
     "partition_size",
@@ -87,6 +89,10 @@ def load_library() -> ctypes.CDLL:
         "pa_decode": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, f32, i32, i32, i32, pdesc, i32, vp, sz, vp]),
         "pa_decode_partials": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, f32, i32, i32, i32, pdesc, i32, vp, sz, vp]),
         "pa_decode_merge": (ctypes.c_int, [vp, vp, i32, i32, i32, pdesc, i32, vp, sz, vp]),
+        "pa_decode_shared_prefix": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, f32, i32, i32, i32, i32, pdesc, i32,
+                                                    vp, sz, vp]),
+        "pa_decode_partials_shared_prefix": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, f32, i32, i32, i32, i32,
+                                                             pdesc, i32, vp, sz, vp]),
         "pa_prefill": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, vp, f32, i32, i32, i32, i32, pdesc, vp, sz, vp]),
         "pa_prefill_workspace_bytes": (sz, [i32, i32, i32, i32, pdesc]),
         "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -224,14 +230,15 @@ def _decode_args(q, k_cache, v_cache, block_tables, context_lens, out, workspace
 
 
 def _decode_call(fn_name, q, k_cache, v_cache, block_tables, context_lens, scale, out, workspace,
-                 partition_size):
+                 partition_size, shared_tokens=None):
     lib = load_library()
     desc, B, H, W, out, workspace, wbytes = _decode_args(
         q, k_cache, v_cache, block_tables, context_lens, out, workspace, partition_size)
     fn = getattr(lib, fn_name)
+    shared = () if shared_tokens is None else (int(shared_tokens),)
     st = fn(_dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
             _dev(block_tables, "block_tables", torch.int32), _dev(context_lens, "context_lens", torch.int32),
-            float(scale), B, H, W, ctypes.byref(desc), int(partition_size), _dev(workspace, "workspace"),
+            float(scale), B, H, W, *shared, ctypes.byref(desc), int(partition_size), _dev(workspace, "workspace"),
             wbytes, _stream(q))
     _check(fn_name, st)
     return out
@@ -249,6 +256,23 @@ def decode_partials(q, k_cache, v_cache, block_tables, context_lens, scale, *, o
                     partition_size: int = 0) -> torch.Tensor:
     return _decode_call("pa_decode_partials", q, k_cache, v_cache, block_tables, context_lens, scale,
                         out, workspace, partition_size)
+
+
+def decode_shared_prefix(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_tables: torch.Tensor,
+                         context_lens: torch.Tensor, scale: float, shared_tokens: int, *,
+                         out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                         partition_size: int = 0) -> torch.Tensor:
+    """decode() for tables that may share their first ``shared_tokens`` tokens'
+    blocks with row 0 (a common prompt): the same result, with the shared
+    blocks read once per group of sequences instead of once per sequence."""
+    return _decode_call("pa_decode_shared_prefix", q, k_cache, v_cache, block_tables, context_lens, scale, out,
+                        workspace, partition_size, shared_tokens)
+
+
+def decode_partials_shared_prefix(q, k_cache, v_cache, block_tables, context_lens, scale, shared_tokens, *,
+                                  out, workspace, partition_size: int = 0) -> torch.Tensor:
+    return _decode_call("pa_decode_partials_shared_prefix", q, k_cache, v_cache, block_tables, context_lens,
+                        scale, out, workspace, partition_size, shared_tokens)
 
 
 def decode_merge(q_like: torch.Tensor, k_cache: torch.Tensor, block_tables: torch.Tensor,

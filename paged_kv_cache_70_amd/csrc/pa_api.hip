@@ -197,7 +197,24 @@ static int decode_params(void* out, const void* q, const void* k_cache, const vo
   p.maxP = ck.plan.maxP;
   p.nchunks = ck.plan.nchunks;
   p.max_tokens = W * d->block_size;
+  p.SP = 0;
+  p.SG = 0;
+  p.SPB = 0;
   return PA_OK;
+}
+
+// Shared-prefix folding for a hint of `shared_tokens` leading tokens: whole
+// partitions only, and only where a kv head's query heads leave room for at
+// least two sequences in the 16 product columns (bf16 matrix-core kernel).
+static void set_shared_prefix(DecodeParams& p, int32_t shared_tokens, const Checked& ck) {
+  const int32_t G = p.H / p.KVH;
+  if (!ck.plan.use_mfma || shared_tokens <= 0 || G >= 16 || 16 % G) return;
+  const int32_t tokens = shared_tokens < p.max_tokens ? shared_tokens : p.max_tokens;
+  const int32_t SP = tokens / p.P;
+  if (SP <= 0) return;
+  p.SP = SP;
+  p.SG = 16 / G;
+  p.SPB = (SP * p.P + p.bs_mask) >> p.bs_log2;
 }
 
 // Prefill launch shape: query heads per workgroup (the largest of 4, 2, 1
@@ -216,7 +233,7 @@ using namespace pa;
 
 extern "C" {
 
-int32_t pa_abi_version(void) { return (2 << 16) | 1; }
+int32_t pa_abi_version(void) { return (2 << 16) | 2; }
 
 const char* pa_status_string(int status) {
   switch (status) {
@@ -276,7 +293,8 @@ static int decode_common(bool partials, bool merge, void* out, const void* q,
                          const int32_t* block_tables, const int32_t* context_lens, float scale,
                          int32_t num_seqs, int32_t num_heads, int32_t max_blocks_per_seq,
                          const pa_cache_desc* desc, int32_t partition_size, void* workspace,
-                         size_t workspace_bytes, void* stream) {
+                         size_t workspace_bytes, void* stream, int32_t shared_tokens = 0) {
+  if (shared_tokens < 0) return PA_ERR_SHAPE;
   Checked ck;
   int st = check_decode_sizes(num_seqs, num_heads, max_blocks_per_seq, desc, partition_size, &ck);
   if (st) return st;
@@ -288,6 +306,7 @@ static int decode_common(bool partials, bool merge, void* out, const void* q,
   st = decode_params(out, q, k_cache, v_cache, block_tables, context_lens, scale, num_seqs,
                      num_heads, max_blocks_per_seq, desc, workspace, workspace_bytes, ck, &prm);
   if (st) return st;
+  set_shared_prefix(prm, shared_tokens, ck);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (partials) {
     const hipError_t e = desc->layout == PA_LAYOUT_VLLM
@@ -321,6 +340,26 @@ int pa_decode_partials(void* out, const void* q, const void* k_cache, const void
   return decode_common(true, false, out, q, k_cache, v_cache, block_tables, context_lens, scale,
                        num_seqs, num_heads, max_blocks_per_seq, desc, partition_size, workspace,
                        workspace_bytes, stream);
+}
+
+int pa_decode_shared_prefix(void* out, const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, const int32_t* context_lens, float scale,
+                            int32_t num_seqs, int32_t num_heads, int32_t max_blocks_per_seq,
+                            int32_t shared_tokens, const pa_cache_desc* desc, int32_t partition_size,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_common(true, true, out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                       num_seqs, num_heads, max_blocks_per_seq, desc, partition_size, workspace,
+                       workspace_bytes, stream, shared_tokens);
+}
+
+int pa_decode_partials_shared_prefix(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                     const int32_t* block_tables, const int32_t* context_lens, float scale,
+                                     int32_t num_seqs, int32_t num_heads, int32_t max_blocks_per_seq,
+                                     int32_t shared_tokens, const pa_cache_desc* desc, int32_t partition_size,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_common(true, false, out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                       num_seqs, num_heads, max_blocks_per_seq, desc, partition_size, workspace,
+                       workspace_bytes, stream, shared_tokens);
 }
 
 int pa_decode_merge(void* out, const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,

@@ -38,9 +38,14 @@ constexpr int kBuckets = 64;              // length classes of the last-partitio
 // kvh, query-head chunk chunk (up to 16 heads of the kv head's group), tokens
 // [t_begin, t_end) in ntiles 16-token tiles (at least one: an empty unit
 // folds one fully masked tile and writes zeros).  Wave-uniform.
+// A shared unit (ns > 0) folds a shared partition p for ns sequences at once:
+// entries g0 .. g0 + ns - 1 of the list of sequences that share the prefix,
+// their G heads side by side as the 16 columns; b is the first of them (whose
+// table row, equal to theirs over the prefix, gives the blocks).
 struct Unit {
   int b, p, kvh, chunk, np;
   int t_begin, t_end, ntiles;
+  int ns, g0;
 };
 
 __device__ __forceinline__ Unit make_unit(const DecodeParams& prm, int b, int p, int n, int kvh, int chunk) {
@@ -54,7 +59,41 @@ __device__ __forceinline__ Unit make_unit(const DecodeParams& prm, int b, int p,
   u.t_end = min(n, u.t_begin + prm.P);
   const int ntok = u.t_end - u.t_begin;
   u.ntiles = ntok > 0 ? (ntok + 15) >> 4 : 1;
+  u.ns = 0;
+  u.g0 = 0;
   return u;
+}
+
+// Sequence and query head of product column col (lane % 16) of a unit: the
+// unit's sequence and head chunk col, or for a shared unit sequence col / G
+// of its group and head col % G.  Padding columns map to the unit's first
+// sequence and head (masked later).  jn: the shared-prefix sequence list
+// (read only for shared units, which only the persistent form folds:
+// Shared = false compiles them out).
+struct ColHead {
+  int b, h;
+  bool ok;
+};
+template <bool Shared>
+__device__ __forceinline__ ColHead column_head(const DecodeParams& prm, const Unit& u, int col,
+                                               const int32_t* jn) {
+  const int G = prm.H / prm.KVH;
+  ColHead c;
+  if (Shared && u.ns > 0) {
+    const int j = col / G;
+    c.ok = j < u.ns;
+    // padding columns read the group's first member (u.b) from the list too:
+    // a choice between the list and u.b becomes a load through a selected
+    // address, which keeps the unit in scratch memory
+    c.b = jn[u.g0 + (c.ok ? j : 0)];
+    c.h = u.kvh * G + (c.ok ? col - j * G : 0);
+  } else {
+    const int nh = min(16, G - u.chunk * 16);
+    c.ok = col < nh;
+    c.b = u.b;
+    c.h = u.kvh * G + u.chunk * 16 + (c.ok ? col : 0);
+  }
+  return c;
 }
 
 // The neighbour sequence of b (the previous one, or sequence 1 for sequence
@@ -70,14 +109,12 @@ __device__ __forceinline__ int clamp_len(const DecodeParams& prm, int n) {
 
 // Raw Q^T operands of a unit: lane holds q[head col][32 c + 8 grp .. + 8] of
 // its column's head (head 0 of the chunk for padding columns, masked later).
-template <int D>
+template <int D, bool Shared = false>
 __device__ __forceinline__ void load_q(const DecodeParams& prm, const Unit& u, int lane,
-                                       u32x4m (&qr)[Geo<D>::NQK]) {
-  const int G = prm.H / prm.KVH;
-  const int nh = min(16, G - u.chunk * 16);
-  const int col = lane & 15, grp = lane >> 4;
-  const int h = u.kvh * G + u.chunk * 16 + (col < nh ? col : 0);
-  const uint8_t* qrow = static_cast<const uint8_t*>(prm.q) + ((size_t)(u.b * prm.H + h) * D) * 2;
+                                       u32x4m (&qr)[Geo<D>::NQK], const int32_t* jn) {
+  const int grp = lane >> 4;
+  const ColHead c = column_head<Shared>(prm, u, lane & 15, jn);
+  const uint8_t* qrow = static_cast<const uint8_t*>(prm.q) + ((size_t)((size_t)c.b * prm.H + c.h) * D) * 2;
 #pragma unroll
   for (int c = 0; c < Geo<D>::NQK; ++c)
     qr[c] = *reinterpret_cast<const u32x4m*>(qrow + (32 * c + 8 * grp) * 2);
@@ -89,7 +126,8 @@ template <int D>
 __device__ __forceinline__ void q_operands(const DecodeParams& prm, const Unit& u, int lane,
                                            const u32x4m (&qr)[Geo<D>::NQK], bf16x8 (&qop)[Geo<D>::NQK]) {
   const int G = prm.H / prm.KVH;
-  const bool head_ok = (lane & 15) < min(16, G - u.chunk * 16);
+  const int col = lane & 15;
+  const bool head_ok = u.ns > 0 ? col / G < u.ns : col < min(16, G - u.chunk * 16);
   const uint32_t flip = prm.q_mode == 1 ? 0x80008000u : 0u;
   const uint32_t keep = (prm.q_mode == 2 || !head_ok) ? 0u : 0xffffffffu;
 #pragma unroll
@@ -184,14 +222,15 @@ __device__ __forceinline__ void fold_tile(uint32_t ok, const u32x4m (&kr)[Geo<D>
 
 // Writes a finished unit: the final bf16 output of a one-partition sequence,
 // else the fp32 partial (acc, m, l) of partition p for the merge kernel.
-template <int D>
-__device__ __forceinline__ void store_unit(const DecodeParams& prm, const Unit& u, int lane, const Fold<D>& st) {
+template <int D, bool Shared = false>
+__device__ __forceinline__ void store_unit(const DecodeParams& prm, const Unit& u, int lane, const Fold<D>& st,
+                                           const int32_t* jn) {
   constexpr int NPV = Geo<D>::NPV;
-  const int G = prm.H / prm.KVH;
-  const int col = lane & 15, grp = lane >> 4;
-  const bool head_ok = col < min(16, G - u.chunk * 16);
+  const int grp = lane >> 4;
+  const ColHead c = column_head<Shared>(prm, u, lane & 15, jn);
+  const bool head_ok = c.ok;
   const float L = groups_sum(st.lsum);
-  const size_t bh = (size_t)u.b * prm.H + u.kvh * G + u.chunk * 16 + col;
+  const size_t bh = (size_t)c.b * prm.H + c.h;
   // (structured branches only: an early return under the per-lane head_ok
   // would make the compiler treat the caller's later state as divergent)
   if (u.np <= 1) {
@@ -246,7 +285,7 @@ __global__ __launch_bounds__(64) void decode_partial_mfma_grid_kernel(const Deco
   const char* kc = kv_col<D>(prm.k_cache, kvh);
   const char* vc = kv_col<D>(prm.v_cache, kvh);
   u32x4m qr[Gm::NQK];
-  load_q<D>(prm, u, lane, qr);
+  load_q<D>(prm, u, lane, qr, nullptr);
   bf16x8 qop[Gm::NQK];
   q_operands<D>(prm, u, lane, qr, qop);
   const LdsMap<D> map(lane);
@@ -276,7 +315,7 @@ __global__ __launch_bounds__(64) void decode_partial_mfma_grid_kernel(const Deco
     run(CachePolicy<0>{});
   else
     run(CachePolicy<kAuxNT>{});
-  store_unit<D>(prm, u, lane, st);
+  store_unit<D>(prm, u, lane, st, nullptr);
 }
 
 // vLLM's cache layout ("PagedAttention kernel：paged KV cache 与 block table",
@@ -428,7 +467,7 @@ __global__ __launch_bounds__(64) void decode_partial_vllm_kernel(const DecodePar
   const int j_end = (u.t_end + prm.bs_mask) >> prm.bs_log2;
   const int tbl = (j_first + lane < j_end) ? prm.tables[(size_t)b * prm.W + j_first + lane] : -1;
   u32x4m qr[Geo<D>::NQK];
-  load_q<D>(prm, u, lane, qr);
+  load_q<D>(prm, u, lane, qr, nullptr);
   bf16x8 qop[Geo<D>::NQK];
   q_operands<D>(prm, u, lane, qr, qop);
   Fold<D> st;
@@ -449,7 +488,7 @@ __global__ __launch_bounds__(64) void decode_partial_vllm_kernel(const DecodePar
     fold_tile_vllm<D>(okB, Bt, qop, prm.scale_log2, lane, st);
   }
   if (u.ntiles & 1) fold_tile_vllm<D>(okA, A, qop, prm.scale_log2, lane, st);
-  store_unit<D>(prm, u, lane, st);
+  store_unit<D>(prm, u, lane, st, nullptr);
 }
 
 namespace {
@@ -526,11 +565,14 @@ __global__ __launch_bounds__(64 * NW) void decode_partial_mfma_kernel(const Deco
   __shared__ int32_t s_cnt[kBuckets];
   __shared__ uint32_t s_next;         // next unit (in the workgroup's share) to hand out
   __shared__ int32_t s_shared;        // some sequence starts with its neighbour's first block
+  __shared__ int32_t s_nj;            // sequences that fold the shared partitions in shared units
   extern __shared__ int32_t s_list[];
   const int B = prm.B, P = prm.P;
   int32_t* s_first = s_list;          // [B] list index of sequence b's first full pair
   int32_t* s_len = s_list + B;        // [B] clamped context length
   int32_t* s_last = s_list + 2 * B;   // [B] sequences in last-pair order
+  int32_t* s_skip = s_list + 3 * B;   // [B] leading partitions sequence b leaves to shared units (0 or SP)
+  int32_t* s_jn = s_list + 4 * B;     // [s_nj] those sequences, in order
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t NC = gridDim.x, wg = blockIdx.x;
@@ -544,10 +586,36 @@ __global__ __launch_bounds__(64 * NW) void decode_partial_mfma_kernel(const Deco
     const int lt = (n - (np > 1 ? (np - 1) * P : 0) + 15) >> 4;
     return (kBuckets - 1) - lt * (kBuckets - 1) / tmax;
   };
+  // Shared prefix: every wavefront compares a share of the (sequence, entry)
+  // pairs of the shared partitions with row 0 (SP * P <= W * bs keeps every
+  // entry inside its row); a mismatch marks the sequence in s_skip (all
+  // writers store 1).  Loads go out 16 at a time at clamped indices.
+  if (prm.SP > 0) {
+    for (int b = threadIdx.x; b < B; b += 64 * NW) s_skip[b] = 0;
+    __syncthreads();
+    const int spb = prm.SPB;
+    const int total = B * spb;
+    constexpr int kU = 16;
+    for (int e0 = threadIdx.x; e0 < total; e0 += 64 * NW * kU) {
+      int mine[kU], ref[kU], who[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int e = min(e0 + u * 64 * NW, total - 1);
+        const int b = e / spb, j = e - b * spb;
+        who[u] = b;
+        mine[u] = prm.tables[(size_t)b * prm.W + j];
+        ref[u] = prm.tables[j];
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u)
+        if (mine[u] != ref[u]) s_skip[who[u]] = 1;
+    }
+    __syncthreads();
+  }
   if (wave == 0) {
     s_cnt[lane] = 0;
     if (lane == 0) s_next = NW;
-    int carry = 0;
+    int carry = 0, jcarry = 0;
     bool shared = false;
     for (int base = 0; base < B; base += 64) {
       const int b = base + lane;
@@ -561,8 +629,16 @@ __global__ __launch_bounds__(64 * NW) void decode_partial_mfma_kernel(const Deco
         const int e1 = nb >= 0 ? prm.tables[(size_t)nb * prm.W] : -2;
         shared |= __ballot(n > 0 && nn > 0 && e0 == e1) != 0;
       }
+      // Shared prefix: the sequence leaves its first SP partitions to shared
+      // units when its context extends past them and its first SPB table
+      // entries equal row 0's (no mismatch marked above).
+      const bool join = prm.SP > 0 && b < B && n > prm.SP * P && s_skip[b] == 0;
+      const uint64_t jm = __ballot(join);
+      if (join) s_jn[jcarry + __popcll(jm & ((1ull << lane) - 1ull))] = b;
+      jcarry += __popcll(jm);
+      shared |= jm != 0;
       const int np = (n + P - 1) / P;
-      const int f = (b < B && np > 1) ? np - 1 : 0;
+      const int f = (b < B && np > 1) ? np - 1 - (join ? prm.SP : 0) : 0;
       int incl = f;
 #pragma unroll
       for (int d = 1; d < 64; d <<= 1) {
@@ -572,6 +648,7 @@ __global__ __launch_bounds__(64 * NW) void decode_partial_mfma_kernel(const Deco
       if (b < B) {
         s_first[b] = carry + incl - f;
         s_len[b] = n;
+        s_skip[b] = join ? prm.SP : 0;
         atomicAdd(&s_cnt[last_class(n)], 1);
       }
       carry += __builtin_amdgcn_readlane(incl, 63);
@@ -593,39 +670,64 @@ __global__ __launch_bounds__(64 * NW) void decode_partial_mfma_kernel(const Deco
     if (lane == 0) {
       s_shared = shared ? 1 : 0;
       s_cnt[0] = carry;               // pairs of full partitions (the bucket bases are no longer needed)
+      s_nj = jcarry;
     }
   }
   __syncthreads();
 
   const uint32_t F = (uint32_t)__builtin_amdgcn_readfirstlane(s_cnt[0]);   // pairs of full partitions
+  const int nj = __builtin_amdgcn_readfirstlane(s_nj);
+  const int SG = prm.SG > 0 ? prm.SG : 1;
+  // shared pairs (shared partition, group of SG sequences), listed first: they
+  // are full partitions
+  const uint32_t NG = prm.SP > 0 ? (uint32_t)((nj + SG - 1) / SG) : 0u;
+  const uint32_t SPG = (uint32_t)prm.SP * NG;
   const uint32_t upp = (uint32_t)(prm.KVH * prm.nchunks);
-  const uint32_t nunits = (F + (uint32_t)B) * upp;
+  const uint32_t nunits = (SPG + F + (uint32_t)B) * upp;
   const int stride = (B + 63) >> 6;                   // sequences per lane in the first search level
 
+  // (one return path: units built on several paths end up in scratch memory)
   auto describe = [&](uint32_t t) -> Unit {
-    const uint32_t pair = t / upp, sub = t - pair * upp;
-    int b, p;
-    if (pair < F) {
-      // b = the last sequence whose first list index is <= pair: one ballot
-      // over every stride-th sequence, then one inside the chosen stretch
-      const int i1 = lane * stride;
-      const uint64_t m1 = __ballot(i1 < B && (uint32_t)s_first[i1 < B ? i1 : 0] <= pair);
-      const int seg = __popcll(m1) - 1;
-      const int i2 = seg * stride + lane;
-      const uint64_t m2 = __ballot(lane < stride && i2 < B && (uint32_t)s_first[i2 < B ? i2 : 0] <= pair);
-      b = __builtin_amdgcn_readfirstlane(seg * stride + __popcll(m2) - 1);
-      p = (int)(pair - (uint32_t)__builtin_amdgcn_readfirstlane(s_first[b]));
+    uint32_t pair = t / upp;
+    const uint32_t sub = t - pair * upp;
+    int b, p, n, ns = 0, g0 = 0;
+    if (pair < SPG) {
+      // shared partition sp for group g: a unit over [sp P, (sp + 1) P) whose
+      // members all have further partitions (n = (SP + 1) P stands for them)
+      const uint32_t sp = pair / NG, g = pair - sp * NG;
+      g0 = (int)g * SG;
+      ns = min(SG, nj - g0);
+      b = __builtin_amdgcn_readfirstlane(s_jn[g0]);
+      p = (int)sp;
+      n = (prm.SP + 1) * P;
     } else {
-      b = __builtin_amdgcn_readfirstlane(s_last[pair - F]);
-      p = -1;
-    }
-    const int n = __builtin_amdgcn_readfirstlane(s_len[b]);
-    if (p < 0) {
-      const int np = (n + P - 1) / P;
-      p = np > 0 ? np - 1 : 0;
+      pair -= SPG;
+      if (pair < F) {
+        // b = the last sequence whose first list index is <= pair: one ballot
+        // over every stride-th sequence, then one inside the chosen stretch
+        const int i1 = lane * stride;
+        const uint64_t m1 = __ballot(i1 < B && (uint32_t)s_first[i1 < B ? i1 : 0] <= pair);
+        const int seg = __popcll(m1) - 1;
+        const int i2 = seg * stride + lane;
+        const uint64_t m2 = __ballot(lane < stride && i2 < B && (uint32_t)s_first[i2 < B ? i2 : 0] <= pair);
+        b = __builtin_amdgcn_readfirstlane(seg * stride + __popcll(m2) - 1);
+        p = (int)(pair - (uint32_t)__builtin_amdgcn_readfirstlane(s_first[b])) +
+            __builtin_amdgcn_readfirstlane(s_skip[b]);
+      } else {
+        b = __builtin_amdgcn_readfirstlane(s_last[pair - F]);
+        p = -1;
+      }
+      n = __builtin_amdgcn_readfirstlane(s_len[b]);
+      if (p < 0) {
+        const int np = (n + P - 1) / P;
+        p = np > 0 ? np - 1 : 0;
+      }
     }
     const int kvh = (int)(sub / (uint32_t)prm.nchunks);
-    return make_unit(prm, b, p, n, kvh, (int)sub - kvh * prm.nchunks);
+    Unit u = make_unit(prm, b, p, n, kvh, (int)sub - kvh * prm.nchunks);
+    u.ns = ns;
+    u.g0 = g0;
+    return u;
   };
 
   auto walk = [&](auto pol) {
@@ -664,7 +766,7 @@ __global__ __launch_bounds__(64 * NW) void decode_partial_mfma_kernel(const Deco
     next_unit();
 
     u32x4m qr[Gm::NQK], qn[Gm::NQK];
-    load_q<D>(prm, C, lane, qr);
+    load_q<D, true>(prm, C, lane, qr, s_jn);
     bf16x8 qop[Gm::NQK];
     q_operands<D>(prm, C, lane, qr, qop);
     Fold<D> st;
@@ -698,7 +800,7 @@ __global__ __launch_bounds__(64 * NW) void decode_partial_mfma_kernel(const Deco
       if (exhausted && has(kNOk) && (fl & kPending) == 0) {
         L = N;
         l_tile = 0;
-        load_q<D>(prm, N, lane, qn);
+        load_q<D, true>(prm, N, lane, qn, s_jn);
         request_blocks();
       }
       const bool live = (fl & (kDead | kPending | kAlive)) == kAlive;
@@ -715,7 +817,7 @@ __global__ __launch_bounds__(64 * NW) void decode_partial_mfma_kernel(const Deco
       if (!real || !has(kAlive)) return;
       Ops::fold(ok, T, qop, cs, map, lane, st, lds_k, lds_v);
       if (++c_tile < C.ntiles) return;
-      store_unit<D>(prm, C, lane, st);
+      store_unit<D, true>(prm, C, lane, st, s_jn);
       if (!has(kNOk)) {
         fl &= ~kAlive;
         return;
@@ -786,8 +888,8 @@ hipError_t launch_mfma(const DecodeParams& prm, hipStream_t stream) {
   const int cus = device_cus();
   if (prm.B <= kMaxPersistentSeqs && cus > 0) {
     // the list, padded so that a second workgroup never fits on the same CU
-    size_t lds = (size_t)prm.B * 3 * sizeof(int32_t);
-    const size_t fixed = sizeof(uint8_t) * NW * 2 * 16 * 2 * D + 64 * 4 + 8;
+    size_t lds = (size_t)prm.B * 5 * sizeof(int32_t);
+    const size_t fixed = sizeof(uint8_t) * NW * 2 * 16 * 2 * D + 64 * 4 + 12;
     if (lds + fixed < kMinLdsPerCU) lds = kMinLdsPerCU - fixed;
     hipLaunchKernelGGL((decode_partial_mfma_kernel<D, WholeTile, NW, Vllm>), dim3((uint32_t)cus), dim3(64 * NW), lds,
                        stream, prm);

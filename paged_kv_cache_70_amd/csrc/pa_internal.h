@@ -27,6 +27,11 @@ struct DecodeParams {
   int32_t maxP;            // partitions reserved per (b, h) in the workspace
   int32_t nchunks;         // head chunks per kv head (G / heads-per-unit)
   int32_t max_tokens;      // W * bs: context lengths are clamped to this
+  // Shared prefix (bf16 persistent kernel only; 0 elsewhere): the first SP
+  // partitions of every sequence whose first SPB table entries equal row 0's
+  // and whose context extends past them are folded SG sequences per unit
+  // (their G heads side by side as the product's 16 columns).
+  int32_t SP, SG, SPB;
 };
 
 // Launch-shape choices made on the host (pure functions of the sizes).

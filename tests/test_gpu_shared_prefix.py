@@ -1,0 +1,167 @@
+"""pa_decode_shared_prefix on an MI355X, held to the oracle: batches whose
+tables begin with row 0's blocks (a common prompt, as on "PagedAttention
+kernel：paged KV cache 与 block table", 面试官追问) decoded with the shared
+partitions folded several sequences at a time.
+
+Each case mixes sequences that take part (same leading entries, longer than
+the shared partitions) with ones that must not: a context that ends inside or
+exactly at the shared part, an empty context, and a table that differs from
+row 0 in one shared entry.  The hint is also given wrong (too long, zero) and
+for shapes that cannot use it (G = 3, G = 16, fp32), where the call must
+still equal the oracle.  All outputs are compared with the fp64 oracle within
+the dtype's tolerance; the partials + merge halves must equal the one-call
+form bit for bit.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import paged_kv_cache_70_amd as pk
+from synth import CONFIGS, make_custom, make_workload, to_vllm_layout
+from tests.gpu_util import assert_matches_oracle, stored_np
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    pk.load_library()
+    yield
+
+
+def _say(msg):
+    print(f"[gpu-shared-prefix] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def _share(w, rows, k, differ=()):
+    """Point the first k entries of each table row in `rows` at row 0's blocks
+    (and, for rows in `differ`, change entry k // 2 back to its own block)."""
+    tbl = w.block_tables.cpu().clone()
+    for b in rows:
+        own = tbl[b, k // 2].item()
+        tbl[b, :k] = tbl[0, :k]
+        if b in differ:
+            tbl[b, k // 2] = own if own != tbl[0, k // 2].item() else (own + 1) % w.num_blocks
+    w.block_tables = tbl.to(w.block_tables.device)
+    return w
+
+
+def _oracle(w, kc=None, vc=None):
+    kc = stored_np(w.k_cache) if kc is None else kc
+    vc = stored_np(w.v_cache) if vc is None else vc
+    return O.decode(stored_np(w.q), kc, vc, stored_np(w.block_tables), stored_np(w.context_lens), w.scale,
+                    w.cfg.dtype)
+
+
+def _run(w, shared, P, k_cache=None, v_cache=None):
+    kc = w.k_cache if k_cache is None else k_cache
+    vc = w.v_cache if v_cache is None else v_cache
+    B, H, _ = w.q.shape
+    W = w.block_tables.shape[1]
+    ws = pk.new_workspace(B, H, W, kc, P)
+    out = pk.decode_shared_prefix(w.q, kc, vc, w.block_tables, w.context_lens, w.scale, shared,
+                                  workspace=ws, partition_size=P)
+    torch.cuda.synchronize()
+    return out, ws
+
+
+# (H, KVH, D, bs, P, shared tokens, lengths, rows sharing, rows differing in one entry)
+CASES = [
+    # G = 4: groups of 4 sequences; 2 shared partitions of 64; sequence 5 ends at the
+    # shared part (128), 6 inside it, 7 is empty, 8 differs in one shared entry
+    (8, 2, 128, 16, 64, 128, [300, 129, 200, 140, 1000, 128, 70, 0, 400, 260, 131],
+     range(11), (8,)),
+    # G = 8: pairs of sequences; 3 partitions of 32 shared (hint 100 -> 96 tokens), bs 8
+    (16, 2, 64, 8, 32, 100, [97, 500, 96, 150, 99, 33, 256], range(7), ()),
+    # G = 2: 8 sequences per unit; D 256, bs 32
+    (4, 2, 256, 32, 64, 128, [129, 190, 1024, 300, 64, 700, 129, 140, 150, 200], range(10), (3,)),
+    # G = 1: 16 sequences per unit, 20 sequences -> groups of 16 and 4
+    (4, 4, 128, 16, 128, 256, [257 + 13 * i for i in range(20)], range(20), ()),
+    # only some rows share; the rest are ordinary
+    (8, 2, 128, 16, 64, 192, [500, 400, 300, 250, 600, 193], (0, 2, 4, 5), ()),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"H{c[0]}_KVH{c[1]}_D{c[2]}_bs{c[3]}_P{c[4]}_S{c[5]}")
+def test_shared_prefix_matches_oracle(case):
+    H, KVH, D, bs, P, shared, lens, rows, differ = case
+    w = make_custom(num_seqs=len(lens), num_heads=H, num_kv_heads=KVH, head_dim=D, block_size=bs,
+                    dtype="bf16", lens=lens, seed=H * D + bs, device="cuda")
+    w = _share(w, rows, -(-shared // bs), differ)
+    ref = _oracle(w)
+    out, _ = _run(w, shared, P)
+    err = assert_matches_oracle(out, ref, "bf16", f"shared prefix H{H} D{D} bs{bs}")
+    # the same call without the hint, and the two-call form
+    plain = pk.decode(w.q, w.k_cache, w.v_cache, w.block_tables, w.context_lens, w.scale, partition_size=P)
+    assert_matches_oracle(plain, ref, "bf16", "pa_decode")
+    B, H_, _ = w.q.shape
+    ws = pk.new_workspace(B, H_, w.block_tables.shape[1], w.k_cache, P)
+    two = torch.empty_like(w.q)
+    pk.decode_partials_shared_prefix(w.q, w.k_cache, w.v_cache, w.block_tables, w.context_lens, w.scale, shared,
+                                     out=two, workspace=ws, partition_size=P)
+    pk.decode_merge(w.q, w.k_cache, w.block_tables, w.context_lens, out=two, workspace=ws, partition_size=P)
+    torch.cuda.synchronize()
+    assert torch.equal(two.view(torch.int16), out.view(torch.int16)), "partials + merge differ from one call"
+    _say(f"H{H} KVH{KVH} D{D} bs{bs} P{P} shared {shared}: max err {err:.2e}")
+
+
+@pytest.mark.parametrize("hint", [0, 16, 4096, 1 << 30])
+def test_wrong_or_useless_hints(hint):
+    """A hint of nothing, less than a partition, or beyond every table: the
+    result is still the oracle's."""
+    lens = [300, 129, 200, 140, 1000, 128]
+    w = _share(make_custom(num_seqs=6, num_heads=8, num_kv_heads=2, head_dim=128, block_size=16, dtype="bf16",
+                           lens=lens, seed=17, device="cuda"), range(6), 8)
+    out, _ = _run(w, hint, 64)
+    assert_matches_oracle(out, _oracle(w), "bf16", f"hint {hint}")
+
+
+@pytest.mark.parametrize("H,KVH,dtype", [(6, 2, "bf16"), (32, 2, "bf16"), (8, 2, "f32")])
+def test_shapes_that_cannot_share(H, KVH, dtype):
+    """G = 3 (does not divide 16), G = 16 (no room for a second sequence) and
+    fp32 caches fall back to the ordinary decode."""
+    lens = [300, 200, 129, 400]
+    w = _share(make_custom(num_seqs=4, num_heads=H, num_kv_heads=KVH, head_dim=64, block_size=16, dtype=dtype,
+                           lens=lens, seed=H, device="cuda"), range(4), 8)
+    out, _ = _run(w, 128, 64)
+    assert_matches_oracle(out, _oracle(w), dtype, f"H{H} KVH{KVH} {dtype}")
+
+
+def test_vllm_layout():
+    lens = [300, 129, 200, 140, 1000, 128, 70, 0, 400]
+    w = _share(make_custom(num_seqs=9, num_heads=8, num_kv_heads=2, head_dim=128, block_size=16, dtype="bf16",
+                           lens=lens, seed=23, device="cuda"), range(9), 8, (2,))
+    kp, vp = to_vllm_layout(w.k_cache, w.v_cache)
+    out, _ = _run(w, 128, 64, kp, vp)
+    assert_matches_oracle(out, _oracle(w), "bf16", "vLLM layout")
+
+
+def test_prefix_shared_workload_full_size():
+    """The 128-sequence prefix-shared workload (2048 shared tokens, D 256) at
+    the automatic partition size, as the benchmark runs it: sampled sequences
+    against the oracle, every sequence against pa_decode."""
+    w = make_workload(CONFIGS["prefix_shared_bf16"], "cuda")
+    B, H, D = w.q.shape
+    W = w.block_tables.shape[1]
+    P = pk.partition_size(B, H, W, w.k_cache)
+    out, _ = _run(w, 2048, P)
+    plain = pk.decode(w.q, w.k_cache, w.v_cache, w.block_tables, w.context_lens, w.scale)
+    torch.cuda.synchronize()
+    kc, vc = stored_np(w.k_cache), stored_np(w.v_cache)
+    pick = np.random.default_rng(5).choice(B, 12, replace=False)
+    for b in pick:
+        ref = O.decode(stored_np(w.q[b:b + 1]), kc, vc, stored_np(w.block_tables[b:b + 1]),
+                       stored_np(w.context_lens[b:b + 1]), w.scale, "bf16")
+        assert_matches_oracle(out[b:b + 1], ref, "bf16", f"sequence {b}")
+    diff = (out.float() - plain.float()).abs()
+    bound = 2 * (2e-2 + 1e-2 * plain.float().abs())
+    assert bool((diff <= bound).all()), float(diff.max())
+    _say(f"prefix_shared_bf16: P {P}, max |shared - plain| {float(diff.max()):.2e}")

@@ -143,3 +143,21 @@ def test_layout_support_matrix():
     assert lib.pa_decode_partition_size(4, 32, 64, ctypes.byref(vb)) > 0
     assert lib.pa_decode_partition_size(4, 32, 64, ctypes.byref(vf)) == -3
     assert lib.pa_prefill_workspace_bytes(4, 32, 8, 100, ctypes.byref(vb)) == 0
+
+
+def test_shared_prefix_host_checks():
+    """pa_decode_shared_prefix: a negative hint is a shape error; otherwise it
+    checks its arguments exactly as pa_decode does (no launch here)."""
+    lib = pk.load_library()
+    d = _desc()
+    call = lambda fn, shared, out=None, ws=None, wsb=0: getattr(lib, fn)(
+        out, None, None, None, None, None, 0.1, 4, 32, 8, shared, ctypes.byref(d), 0, ws, wsb, None)
+    for fn in ("pa_decode_shared_prefix", "pa_decode_partials_shared_prefix"):
+        assert call(fn, -1) == -2
+        assert call(fn, 0) == -1          # null out / lens, as pa_decode
+        assert call(fn, 1 << 20) == -1    # a hint beyond the table is clamped, not an error
+    # same checks as pa_decode with the same sizes
+    assert lib.pa_decode(None, None, None, None, None, None, 0.1, 4, 32, 8, ctypes.byref(d), 0, None, 0, None) == -1
+    bad = _desc(head_dim=96)
+    assert lib.pa_decode_shared_prefix(None, None, None, None, None, None, 0.1, 4, 32, 8, 64,
+                                       ctypes.byref(bad), 0, None, 0, None) == -3
