@@ -67,9 +67,10 @@ CSRC = os.path.join(ROOT, "paged_kv_cache_70_amd", "csrc")
 # the dominant kernel of each bench line ("bf16" / "f32": the decode partial
 # kernel of that cache dtype; "write": the scatter write): its name in traces
 # and its source file
-PARTIAL_KERNELS = {"bf16": "decode_partial_mfma_kernel", "f32": "decode_partial_kernel", "write": "write_kv_kernel"}
+PARTIAL_KERNELS = {"bf16": "decode_partial_mfma_kernel", "f32": "decode_partial_kernel", "write": "write_kv_kernel",
+                   "prefill": "prefill_mfma_kernel"}
 KERNEL_SRC = {"bf16": os.path.join(CSRC, "pa_decode_mfma.hip"), "f32": os.path.join(CSRC, "pa_decode.hip"),
-              "write": os.path.join(CSRC, "pa_write.hip")}
+              "write": os.path.join(CSRC, "pa_write.hip"), "prefill": os.path.join(CSRC, "pa_prefill.hip")}
 
 
 def _traffic_file(key: str, workload: str) -> str:
@@ -133,6 +134,22 @@ def traffic_from_counters(fetch_csv: str, write_csv: str, workload: str, key: st
         json.dump(res, f, indent=1)
         f.write("\n")
     return res
+
+
+def _calibration_copy(mib: int, dev, do_flush) -> None:
+    """A plain fp32 copy of `mib` MiB, three times (torch.mul(src, 2.0,
+    out=dst): reads and writes mib MiB): the reference reading that scales the
+    HBM byte counters.  Nothing when mib is 0."""
+    if not mib:
+        return
+    import torch
+    src = torch.ones(mib << 18, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        do_flush()
+        torch.mul(src, 2.0, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def _cpu_baseline(w, budget_s: float):
@@ -322,6 +339,7 @@ def run_prefill(args, cfg):
     def ev():
         return torch.cuda.Event(enable_timing=True)
 
+    _calibration_copy(args.copy_calibration, dev, do_flush)
     for _ in range(args.warmup):
         do_flush()
         write()
@@ -382,7 +400,7 @@ def run_prefill(args, cfg):
             "peak": MFMA_BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-            "traffic": None,
+            "traffic": _traffic(cfg.name, "prefill"),
             "kernel": "prefill_mfma_kernel",
         },
     }
@@ -437,14 +455,7 @@ def run_write(args, cfg):
         if flush is not None:
             torch.sum(flush, dim=0, out=flush_sink)
 
-    if args.copy_calibration:
-        src = torch.ones(args.copy_calibration << 18, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            do_flush()
-            torch.mul(src, 2.0, out=dst)
-        torch.cuda.synchronize()
-        del src, dst
+    _calibration_copy(args.copy_calibration, dev, do_flush)
 
     for _ in range(args.warmup):
         do_flush()
@@ -530,9 +541,11 @@ def main():
     args = ap.parse_args()
 
     if args.traffic_from:
-        from synth import CONFIGS, WRITE_CONFIGS
+        from synth import CONFIGS, PREFILL_CONFIGS, WRITE_CONFIGS
         if args.config in WRITE_CONFIGS:
             name, key = args.config, "write"
+        elif args.config in PREFILL_CONFIGS:
+            name, key = args.config, "prefill"
         else:
             name, key = CONFIGS[args.config].name, CONFIGS[args.config].dtype
         r = traffic_from_counters(*args.traffic_from, name, key,
@@ -605,14 +618,7 @@ def main():
     def ev():
         return torch.cuda.Event(enable_timing=True)
 
-    if args.copy_calibration:
-        src = torch.ones(args.copy_calibration << 18, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            do_flush()
-            torch.mul(src, 2.0, out=dst)
-        torch.cuda.synchronize()
-        del src, dst
+    _calibration_copy(args.copy_calibration, dev, do_flush)
 
     for _ in range(args.warmup):
         do_flush()

@@ -238,8 +238,8 @@ int pa_decode_merge(void* out, const int32_t* context_lens,
 
 /*
  * pa_prefill_workspace_bytes — size of the device workspace pa_prefill needs.
- * bf16: its work plan, 16 bytes plus 4 per (sequence, query tile) pair
- * (bounded by num_tokens / tile + num_seqs).  fp32: 8 bytes per query row
+ * bf16: its work plan, 48 bytes (ticket counters) plus 4 per (sequence,
+ * query tile) pair (bounded by num_tokens / tile + num_seqs).  fp32: 8 bytes per query row
  * plus the split-KV partial results of one decode per query row (as
  * pa_decode_workspace_bytes for num_tokens sequences, partitions of 64
  * blocks).  Depends only on its arguments; 0 for invalid arguments.

@@ -413,7 +413,7 @@ static int prefill_shape(int32_t B, int32_t H, int32_t W, int32_t T, const pa_ca
   if (B > 65536 || ((int64_t)T + p.tq - 1) / p.tq > 65536 ||
       p.max_tiles * d->num_kv_heads * p.nchunks > INT_MAX)
     return PA_ERR_TOO_LARGE;
-  p.ws_bytes = 16 + (size_t)p.max_tiles * sizeof(uint32_t);
+  p.ws_bytes = kPrefillHeaderBytes + (size_t)p.max_tiles * sizeof(uint32_t);
   *out = p;
   return PA_OK;
 }
@@ -465,7 +465,7 @@ int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cach
   p.tq = shp.tq;
   p.max_tiles = (int32_t)shp.max_tiles;
   p.tickets = static_cast<int32_t*>(workspace);
-  p.plan = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + 16);
+  p.plan = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + kPrefillHeaderBytes);
   p.out = out;
   p.q = q;
   p.k_cache = k_cache;

@@ -46,6 +46,12 @@ struct DecodePlan {
   int32_t tile_unroll;     // 16-byte loads per K (and per V) per tile and lane
 };
 
+// Prefill workspace header: one ticket counter per class of workgroups (the
+// dies), then the number of plan entries; the plan follows at 48 bytes.
+constexpr int kTicketClasses = 8;
+constexpr size_t kPrefillHeaderBytes = 48;
+static_assert((kTicketClasses + 1) * 4 <= kPrefillHeaderBytes, "prefill header");
+
 // Paged prefill (bf16, matrix cores): a packed batch of new queries per
 // sequence, causal over the sequence's paged K/V.
 struct PrefillParams {
@@ -66,7 +72,7 @@ struct PrefillParams {
   int32_t tq;              // query tokens per workgroup (128 / hg)
   int32_t max_tiles;       // bound on the (sequence, query tile) pairs: T / tq + B
   uint32_t* plan;          // workspace: [max_tiles] (sequence << 16 | query tile), heaviest first
-  int32_t* tickets;        // workspace: [0] next unit, [1] number of plan entries
+  int32_t* tickets;        // workspace: [c] next unit of class c < kTicketClasses, [kTicketClasses] plan entries
 };
 
 bool dtype_ok(int32_t dtype);

@@ -245,9 +245,9 @@ __global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(const Prefil
   __syncthreads();
   hist[c0] = excl;            // hist now holds each class's next write position
   hist[c1] = excl + h0;
+  if (tid < kTicketClasses) prm.tickets[tid] = 0;
   if (tid == kPlanThreads - 1) {
-    prm.tickets[0] = 0;
-    prm.tickets[1] = before + incl;
+    prm.tickets[kTicketClasses] = before + incl;
     budget = prm.max_tiles;
   }
   __syncthreads();
@@ -264,10 +264,18 @@ __global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(const Prefil
 }
 
 // Persistent: a few workgroups per CU, each drawing units (a planned
-// (sequence, query tile) pair times one (kv head, head chunk)) from the ticket
+// (sequence, query tile) pair times one (kv head, head chunk)) from a ticket
 // counter until none is left, heaviest first, so the chip stays full however
 // unequal the units are.  A unit is 4 wavefronts: hg query heads of one kv
 // head x tq query tokens, 32 rows per wavefront (16 for D = 256).
+//
+// Workgroup w runs on die w mod 8 (each die has its own L2).  When the KU
+// (kv head, head chunk) indices split evenly over the dies (KU a multiple of
+// 8, or a divisor of 8), workgroup w draws only the units whose index is
+// congruent to its class w mod ncls, from that class's own counter: every
+// query tile of one kv head then reads that head's K/V through the same L2.
+// Each class has workgroups (the grid has at least KU of them) and covers
+// its indices for every pair; no workgroup waits for another.
 template <int D, bool WholeTile>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 1 : 2)))
 void prefill_mfma_kernel(const PrefillParams prm) {
@@ -282,20 +290,25 @@ void prefill_mfma_kernel(const PrefillParams prm) {
   const int lane = threadIdx.x & 63;
   const int grp = lane >> 4, col = lane & 15;
   const int KU = prm.KVH * prm.nchunks;
-  const int units = min(prm.tickets[1], prm.max_tiles) * KU;
+  const int pairs = min(prm.tickets[kTicketClasses], prm.max_tiles);
+  const int ncls = (KU % kTicketClasses == 0) ? kTicketClasses : (kTicketClasses % KU == 0 ? KU : 1);
+  const int cls = (int)(blockIdx.x % (uint32_t)ncls);
+  const int per = KU / ncls;                        // indices of one class per pair
+  const int units = pairs * per;
   const LdsMap<D> map(lane);
   const uint32_t lane_off = (uint32_t)(lane / PPR) * (uint32_t)(prm.KVH * ROWB) + (uint32_t)(lane % PPR) * 16;
   const int G = prm.H / prm.KVH;
   typedef const __attribute__((address_space(4))) int32_t ctab_t;
 
   for (;;) {
-    if (threadIdx.x == 0) s_ticket = atomicAdd(&prm.tickets[0], 1);
+    if (threadIdx.x == 0) s_ticket = atomicAdd(&prm.tickets[cls], 1);
     __syncthreads();
     const int ticket = __builtin_amdgcn_readfirstlane(s_ticket);
     __syncthreads();
     if (ticket >= units) break;
-    const uint32_t entry = prm.plan[ticket / KU];
-    const int rest = ticket % KU;
+    const int pi = ticket / per;
+    const uint32_t entry = prm.plan[pi];
+    const int rest = cls + ncls * (ticket - pi * per);
     const int chunk = rest % prm.nchunks;
     const int kvh = rest / prm.nchunks;
     const int b = min((int)(entry >> 16), prm.B - 1);

@@ -6,8 +6,9 @@ manager shares the prompt's blocks, reports the cached prefix, and gives the
 slots of the uncached tokens; pa_write_kv writes them and pa_prefill attends
 (chunked prefill over the cached prefix).  Three decode steps follow:
 append -> slot -> pa_write_kv -> pa_decode over tables the manager fills.
-Then one request is freed and re-added: its prefix blocks are revived and only
-its tail is prefilled again.
+Each decode step also runs pa_decode_shared_prefix with the cached prompt
+length the manager reported as the hint.  Then one request is freed and
+re-added: its prefix blocks are revived and only its tail is prefilled again.
 
 The oracle side runs the same flow with the oracle's block manager, write,
 prefill and decode.  K/V rows are a fixed function of (token id, position),
@@ -102,7 +103,7 @@ class Flow:
         ref = O.prefill(stored_np(q), self.ko, self.vo, tab, lens, qsl, self.scale, "bf16")
         return out, ref
 
-    def decode(self, sids):
+    def decode(self, sids, shared_tokens=0):
         steps_tok = [int((7 * s + len(self.tokens[s])) % VOCAB) for s in sids]
         for s, t in zip(sids, steps_tok):
             slot_g, slot_o = self.bm.append(s, t), self.obm.append(s, t)
@@ -111,11 +112,14 @@ class Flow:
         self.write(sids, [len(self.tokens[s]) - 1 for s in sids])
         tab, lens = self.tables(sids)
         q = self.rows(self.qtab, steps_tok, [len(self.tokens[s]) - 1 for s in sids])
-        out = pk.decode(q.cuda(), self.kc, self.vc, torch.from_numpy(tab).cuda(), torch.from_numpy(lens).cuda(),
-                        self.scale)
+        args = (q.cuda(), self.kc, self.vc, torch.from_numpy(tab).cuda(), torch.from_numpy(lens).cuda(), self.scale)
+        out = pk.decode(*args)
+        # the same step with the shared prompt as the hint (partitions of one
+        # block, so that the 48 shared tokens are 3 whole partitions)
+        out_sp = pk.decode_shared_prefix(*args, shared_tokens, partition_size=BS) if shared_tokens else None
         torch.cuda.synchronize()
         ref = O.decode(stored_np(q), self.ko, self.vo, tab, lens, self.scale, "bf16")
-        return out, ref
+        return out, out_sp, ref
 
     def add(self, toks):
         r_g = self.bm.add_sequence(toks)
@@ -140,9 +144,10 @@ def test_serving_flow_with_shared_prompt():
     err = assert_matches_oracle(out, ref, "bf16", "prefill over a shared prompt")
     _say(f"prefill: {sum(len(p) - c for p, c in zip(prompts, cached))} new tokens, max err {err:.2e}")
     for step in range(3):
-        out, ref = f.decode(sids)
+        out, out_sp, ref = f.decode(sids, shared_tokens=cached[1])
         err = assert_matches_oracle(out, ref, "bf16", f"decode step {step}")
-        _say(f"decode step {step}: max err {err:.2e}")
+        err_sp = assert_matches_oracle(out_sp, ref, "bf16", f"shared-prefix decode step {step}")
+        _say(f"decode step {step}: max err {err:.2e} (shared-prefix decode {err_sp:.2e})")
     # free request 2 and bring it back: its full blocks are revived from the cache
     gone = sids[2]
     toks = list(f.tokens[gone])

@@ -125,9 +125,9 @@ def test_prefill_host_checks():
     assert call(bf16, ptr=16, ws=16, wsb=27) == -4
     # G = 4 -> 4 heads x 32 tokens per unit: ceil(10 / 32) + 2 = 3 plan entries
     size = lambda B, H, T, d=bf16, W=4: lib.pa_prefill_workspace_bytes(B, H, W, T, ctypes.byref(d))
-    assert size(2, 8, 10) == 16 + 4 * 3
-    assert size(2, 4, 10) == 16 + 4 * (1 + 2)    # G = 2 -> 64-token tiles
-    assert size(3, 2, 300) == 16 + 4 * (3 + 3)   # G = 1 -> 128-token tiles
+    assert size(2, 8, 10) == 48 + 4 * 3
+    assert size(2, 4, 10) == 48 + 4 * (1 + 2)    # G = 2 -> 64-token tiles
+    assert size(3, 2, 300) == 48 + 4 * (3 + 3)   # G = 1 -> 128-token tiles
     # fp32: 8 B per row (16-byte aligned), then one decode per row: W = 4 blocks of 16 fit one
     # partition (no partials); W = 100 -> 2 partitions of 64 blocks: rows * H * 2 * (D + 2) * 4 B
     assert size(2, 8, 10, f32) == 80 + 0
