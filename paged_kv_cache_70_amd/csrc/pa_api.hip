@@ -212,9 +212,13 @@ static void set_shared_prefix(DecodeParams& p, int32_t shared_tokens, const Chec
   const int32_t tokens = shared_tokens < p.max_tokens ? shared_tokens : p.max_tokens;
   const int32_t SP = tokens / p.P;
   if (SP <= 0) return;
+  const int32_t SPB = (SP * p.P + p.bs_mask) >> p.bs_log2;
+  // the kernel walks the B x SPB (sequence, entry) pairs it checks with int
+  // indices (plus one stride of look-ahead)
+  if ((int64_t)p.B * SPB > (1 << 30)) return;
   p.SP = SP;
   p.SG = 16 / G;
-  p.SPB = (SP * p.P + p.bs_mask) >> p.bs_log2;
+  p.SPB = SPB;
 }
 
 // Prefill launch shape: query heads per workgroup (the largest of 4, 2, 1

@@ -113,6 +113,24 @@ def test_shared_prefix_matches_oracle(case):
     _say(f"H{H} KVH{KVH} D{D} bs{bs} P{P} shared {shared}: max err {err:.2e}")
 
 
+def test_many_sequences_and_a_hint_covering_the_table():
+    """200 sequences (several 64-sequence passes of the list, 50 groups of 4),
+    a few of them too short or with one differing entry; then a hint as long
+    as the whole table: 6 partitions of 64 (384 tokens) are shared, which only
+    row 0 (399 tokens, its own entries) passes, as a group of one."""
+    rng = np.random.default_rng(9)
+    lens = [int(x) for x in rng.integers(1, 400, 200)]
+    lens[0] = 399
+    w = _share(make_custom(num_seqs=200, num_heads=8, num_kv_heads=2, head_dim=64, block_size=16, dtype="bf16",
+                           lens=lens, seed=31, device="cuda"), range(200), 8, (7, 100, 199))
+    ref = _oracle(w)
+    out, _ = _run(w, 128, 64)
+    assert_matches_oracle(out, ref, "bf16", "200 sequences")
+    W = w.block_tables.shape[1]
+    out, _ = _run(w, W * 16, 64)
+    assert_matches_oracle(out, ref, "bf16", "hint = whole table")
+
+
 @pytest.mark.parametrize("hint", [0, 16, 4096, 1 << 30])
 def test_wrong_or_useless_hints(hint):
     """A hint of nothing, less than a partition, or beyond every table: the
