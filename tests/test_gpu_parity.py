@@ -425,3 +425,63 @@ def test_graph_step_padded_batch_new_inputs_each_replay(cfg_name):
         assert _same_bits(kc, ko) and _same_bits(vc, vo), f"{cfg_name} replay {rep}: write"
         err = assert_matches_oracle(out, ref, cfg.dtype, f"{cfg_name} replay {rep}")
         _say(f"graph step {cfg_name} replay {rep} (T={T}, {int(pad.sum())} padding rows): max err {err:.2e}")
+
+
+def test_graph_replay_of_prefill_and_shared_prefix_decode():
+    """pa_prefill (planning kernel, which zeroes its own ticket counters, then
+    the persistent attention kernel) and pa_decode_shared_prefix (the table
+    check, shared units and the merge) captured in one HIP graph: every
+    replay, with eager work between replays, gives the eager result bit for
+    bit, and that result matches the oracle."""
+    _say("graph replay: prefill + shared-prefix decode")
+    from synth import make_prefill_custom
+    wp = make_prefill_custom(num_heads=8, num_kv_heads=2, head_dim=128, block_size=16, cached=[0, 100, 37],
+                             new=[70, 33, 129], dtype="bf16", seed=78, device="cuda")
+    kc, vc = wp.k_cache.clone(), wp.v_cache.clone()
+    pk.write_kv(kc, vc, wp.k_new, wp.v_new, wp.slot_mapping)
+    T, H, _ = wp.q.shape
+    pws = pk.prefill_workspace(3, H, wp.block_tables.shape[1], T, kc)
+    pout = torch.empty_like(wp.q)
+    lens = [300, 129, 200, 140, 1000, 128, 70, 0, 400]
+    wd = make_custom(num_seqs=9, num_heads=8, num_kv_heads=2, head_dim=128, block_size=16, dtype="bf16",
+                     lens=lens, seed=79, device="cuda")
+    tbl = wd.block_tables.cpu().clone()
+    tbl[:, :8] = tbl[0, :8]                                   # a common 128-token prefix
+    wd.block_tables = tbl.cuda()
+    B, W = 9, wd.block_tables.shape[1]
+    dws = pk.new_workspace(B, H, W, wd.k_cache, 64)
+    dout = torch.empty_like(wd.q)
+
+    def step():
+        pk.prefill(wp.q, kc, vc, wp.block_tables, wp.context_lens, wp.query_start_loc, wp.scale, out=pout,
+                   workspace=pws)
+        pk.decode_shared_prefix(wd.q, wd.k_cache, wd.v_cache, wd.block_tables, wd.context_lens, wd.scale, 128,
+                                out=dout, workspace=dws, partition_size=64)
+
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        step()
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+    pe, de = pout.clone(), dout.clone()
+    ko, vo = stored_np(kc), stored_np(vc)
+    assert_matches_oracle(pe, O.prefill(stored_np(wp.q), ko, vo, stored_np(wp.block_tables),
+                                        stored_np(wp.context_lens), stored_np(wp.query_start_loc), wp.scale,
+                                        "bf16"), "bf16", "eager prefill")
+    assert_matches_oracle(de, O.decode(stored_np(wd.q), stored_np(wd.k_cache), stored_np(wd.v_cache),
+                                       stored_np(wd.block_tables), stored_np(wd.context_lens), wd.scale, "bf16"),
+                          "bf16", "eager shared-prefix decode")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    junk = torch.empty(1 << 24, device="cuda")
+    for rep in range(4):
+        pout.fill_(float("nan"))
+        dout.fill_(float("nan"))
+        junk.normal_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(pout.view(torch.int16), pe.view(torch.int16)), f"prefill replay {rep}"
+        assert torch.equal(dout.view(torch.int16), de.view(torch.int16)), f"decode replay {rep}"
