@@ -549,8 +549,8 @@ struct TileOps<D, WholeTile, true> {    // vLLM layout: operands straight from t
 // classes), so that the shortest units come last; each (sequence, partition)
 // pair expands into kv heads x head chunks consecutive units.
 //
-// Workgroup c of NC owns units c, c + NC, c + 2 NC, ... (an equal share of
-// every size class).  Inside the workgroup the units are handed out in that
+// Workgroup c of NC owns one unit of every round of NC units (round k dealt
+// in serpentine order, below).  Inside the workgroup the units are handed out in that
 // order through an LDS counter as wavefronts finish their previous one:
 // wavefronts sharing a CU stream at very different rates, and this lets the
 // faster ones take more units, so that all of a CU's wavefronts finish
@@ -687,6 +687,16 @@ __global__ __launch_bounds__(64 * NW) void decode_partial_mfma_kernel(const Deco
   const int stride = (B + 63) >> 6;                   // sequences per lane in the first search level
 
   // (one return path: units built on several paths end up in scratch memory)
+  // The workgroup's k-th unit: round k of the list, dealt to the workgroups in
+  // order when k is even and in reverse order when k is odd (a serpentine
+  // deal: the list runs from the largest units to the smallest, so a
+  // workgroup that drew a larger unit in one round draws a smaller one in the
+  // next).  Dealing every round in the same order left up to one extra large
+  // unit on some CUs whenever a size class did not fill whole rounds.  Each
+  // round is a bijection onto its NC units, and once a workgroup's share lies
+  // past the list every later share does too.
+  auto share = [&](uint32_t k) { return k * NC + ((k & 1u) ? NC - 1u - wg : wg); };
+
   auto describe = [&](uint32_t t) -> Unit {
     uint32_t pair = t / upp;
     const uint32_t sub = t - pair * upp;
@@ -753,13 +763,13 @@ __global__ __launch_bounds__(64 * NW) void decode_partial_mfma_kernel(const Deco
     auto has = [&](uint32_t f) { return (fl & f) != 0; };
 
     // C: the unit being folded; N: the next one.
-    Unit C = describe(wg + (uint32_t)wave * NC);
+    Unit C = describe(share((uint32_t)wave));
     Unit N = C;
     auto next_unit = [&]() {
       uint32_t k = 0;
       if (lane == 0) k = atomicAdd(&s_next, 1u);
       k = __builtin_amdgcn_readlane(k, 0);
-      const uint32_t un = wg + k * NC;
+      const uint32_t un = share(k);
       fl = un < nunits ? (fl | kNOk) : (fl & ~kNOk);
       if (un < nunits) N = describe(un);
     };
@@ -868,7 +878,7 @@ __global__ __launch_bounds__(64 * NW) void decode_partial_mfma_kernel(const Deco
   // except in vLLM's layout with blocks of 32 or more tokens, where a 16-token
   // tile reads half of every K group and V row of its block and the next tile
   // reads the other half.
-  if (wg + (uint32_t)wave * NC < nunits) {
+  if (share((uint32_t)wave) < nunits) {
     if (__builtin_amdgcn_readfirstlane(s_shared) || (Vllm && prm.bs_log2 >= 5))
       walk(CachePolicy<0>{});
     else
