@@ -65,7 +65,9 @@ typedef enum pa_status {
   PA_ERR_LAUNCH = -6,       /* the HIP runtime rejected a kernel launch */
   PA_ERR_TOO_LARGE = -7,    /* sizes overflow the kernels' 32-bit grid/index limits */
   PA_ERR_NO_BLOCKS = -8,    /* block manager: not enough free blocks (nothing was changed) */
-  PA_ERR_NO_SEQUENCE = -9   /* block manager: unknown sequence id */
+  PA_ERR_NO_SEQUENCE = -9,  /* block manager: unknown sequence id */
+  PA_ERR_NO_MEMORY = -10    /* block manager: host memory ran out inside a call that changes the
+                               manager; its state is then unspecified: destroy it */
 } pa_status;
 
 /* Memory layout of the two caches. */
@@ -323,7 +325,8 @@ int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cach
 typedef struct pa_block_manager pa_block_manager;
 
 /* A manager of num_blocks blocks of block_size tokens; NULL for non-positive
- * sizes or if memory runs out.  Free it with pa_bm_destroy. */
+ * sizes or if memory runs out.  Free it with pa_bm_destroy.  No call lets a
+ * C++ exception out: a failed host allocation returns PA_ERR_NO_MEMORY. */
 pa_block_manager* pa_bm_create(int32_t num_blocks, int32_t block_size);
 void pa_bm_destroy(pa_block_manager* bm);
 

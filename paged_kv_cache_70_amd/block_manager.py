@@ -21,7 +21,7 @@ from .api import PaError, load_library
 
 __all__ = ["BlockManager", "BlockManagerError"]
 
-PA_ERR_NO_BLOCKS, PA_ERR_NO_SEQUENCE = -8, -9
+PA_ERR_NO_BLOCKS, PA_ERR_NO_SEQUENCE, PA_ERR_NO_MEMORY = -8, -9, -10
 
 
 class BlockManagerError(PaError):

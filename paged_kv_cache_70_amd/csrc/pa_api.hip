@@ -251,6 +251,7 @@ const char* pa_status_string(int status) {
     case PA_ERR_TOO_LARGE: return "sizes exceed the kernels' grid or index limits";
     case PA_ERR_NO_BLOCKS: return "block manager: not enough free blocks";
     case PA_ERR_NO_SEQUENCE: return "block manager: unknown sequence";
+    case PA_ERR_NO_MEMORY: return "block manager: host memory ran out (destroy the manager)";
   }
   return "unknown status";
 }

@@ -142,91 +142,112 @@ static int64_t append_one(pa_block_manager* bm, Sequence& s, int64_t token) {
   return (int64_t)b * bs + pos % bs;
 }
 
+// Runs an entry point's body; a C++ exception (a failed host allocation) must
+// not cross the C ABI, so it becomes PA_ERR_NO_MEMORY.
+template <typename F>
+static int guarded(F&& body) {
+  try {
+    return body();
+  } catch (...) {
+    return PA_ERR_NO_MEMORY;
+  }
+}
+
 extern "C" {
 
 pa_block_manager* pa_bm_create(int32_t num_blocks, int32_t block_size) {
   if (num_blocks <= 0 || block_size <= 0) return nullptr;
-  return new (std::nothrow) pa_block_manager(num_blocks, block_size);
+  try {
+    return new pa_block_manager(num_blocks, block_size);
+  } catch (...) {
+    return nullptr;
+  }
 }
 
 void pa_bm_destroy(pa_block_manager* bm) { delete bm; }
 
 int pa_bm_add_sequence(pa_block_manager* bm, const int64_t* tokens, int32_t n, int64_t* seq_id,
                        int32_t* cached_tokens) {
-  if (!bm || !seq_id || (n > 0 && !tokens)) return PA_ERR_NULL;
-  if (n < 0) return PA_ERR_SHAPE;
-  const int32_t bs = bm->bs;
-  const int32_t nfull = n / bs, nblocks = (n + bs - 1) / bs;
-  // plan: leading cached blocks, and the keys of every full block
-  std::vector<uint64_t> keys((size_t)nfull);
-  std::vector<int32_t> reused;
-  uint64_t parent = kNoParent;
-  int32_t revive = 0;
-  for (int32_t i = 0; i < nfull; ++i) {
-    keys[i] = block_key(parent, tokens + (size_t)i * bs, bs);
-    parent = keys[i];
-    if ((int32_t)reused.size() == i) {
-      const int32_t b = bm->lookup(keys[i], tokens + (size_t)i * bs);
-      if (b >= 0) {
-        reused.push_back(b);
-        revive += bm->refs[b] == 0;
+  return guarded([&]() -> int {
+    if (!bm || !seq_id || (n > 0 && !tokens)) return PA_ERR_NULL;
+    if (n < 0) return PA_ERR_SHAPE;
+    const int32_t bs = bm->bs;
+    const int32_t nfull = n / bs, nblocks = (n + bs - 1) / bs;
+    // plan: leading cached blocks, and the keys of every full block
+    std::vector<uint64_t> keys((size_t)nfull);
+    std::vector<int32_t> reused;
+    uint64_t parent = kNoParent;
+    int32_t revive = 0;
+    for (int32_t i = 0; i < nfull; ++i) {
+      keys[i] = block_key(parent, tokens + (size_t)i * bs, bs);
+      parent = keys[i];
+      if ((int32_t)reused.size() == i) {
+        const int32_t b = bm->lookup(keys[i], tokens + (size_t)i * bs);
+        if (b >= 0) {
+          reused.push_back(b);
+          revive += bm->refs[b] == 0;
+        }
       }
     }
-  }
-  if (bm->nfree - revive < nblocks - (int32_t)reused.size()) return PA_ERR_NO_BLOCKS;
-  Sequence s;
-  s.tokens.assign(tokens, tokens + n);
-  s.blocks.reserve((size_t)nblocks);
-  for (int32_t b : reused) {
-    if (bm->refs[b] == 0) bm->unlink(b);
-    ++bm->refs[b];
-    s.blocks.push_back(b);
-  }
-  for (int32_t i = (int32_t)reused.size(); i < nblocks; ++i) {
-    const int32_t b = bm->take();
-    if (i < nfull) bm->register_block(b, keys[i], tokens + (size_t)i * bs);
-    s.blocks.push_back(b);
-  }
-  s.keys = std::move(keys);
-  const int64_t id = bm->next_seq++;
-  if (cached_tokens) *cached_tokens = (int32_t)reused.size() * bs;
-  bm->seqs.emplace(id, std::move(s));
-  *seq_id = id;
-  return PA_OK;
+    if (bm->nfree - revive < nblocks - (int32_t)reused.size()) return PA_ERR_NO_BLOCKS;
+    Sequence s;
+    s.tokens.assign(tokens, tokens + n);
+    s.blocks.reserve((size_t)nblocks);
+    for (int32_t b : reused) {
+      if (bm->refs[b] == 0) bm->unlink(b);
+      ++bm->refs[b];
+      s.blocks.push_back(b);
+    }
+    for (int32_t i = (int32_t)reused.size(); i < nblocks; ++i) {
+      const int32_t b = bm->take();
+      if (i < nfull) bm->register_block(b, keys[i], tokens + (size_t)i * bs);
+      s.blocks.push_back(b);
+    }
+    s.keys = std::move(keys);
+    const int64_t id = bm->next_seq++;
+    if (cached_tokens) *cached_tokens = (int32_t)reused.size() * bs;
+    bm->seqs.emplace(id, std::move(s));
+    *seq_id = id;
+    return PA_OK;
+  });
 }
 
 int pa_bm_append(pa_block_manager* bm, int64_t seq_id, int64_t token, int64_t* slot) {
-  if (!bm || !slot) return PA_ERR_NULL;
-  const auto it = bm->seqs.find(seq_id);
-  if (it == bm->seqs.end()) return PA_ERR_NO_SEQUENCE;
-  Sequence& s = it->second;
-  if (s.tokens.size() >= (size_t)INT32_MAX) return PA_ERR_TOO_LARGE;
-  if (s.tokens.size() % (size_t)bm->bs == 0 && bm->nfree == 0) return PA_ERR_NO_BLOCKS;
-  *slot = append_one(bm, s, token);
-  return PA_OK;
+  return guarded([&]() -> int {
+    if (!bm || !slot) return PA_ERR_NULL;
+    const auto it = bm->seqs.find(seq_id);
+    if (it == bm->seqs.end()) return PA_ERR_NO_SEQUENCE;
+    Sequence& s = it->second;
+    if (s.tokens.size() >= (size_t)INT32_MAX) return PA_ERR_TOO_LARGE;
+    if (s.tokens.size() % (size_t)bm->bs == 0 && bm->nfree == 0) return PA_ERR_NO_BLOCKS;
+    *slot = append_one(bm, s, token);
+    return PA_OK;
+  });
 }
 
 int pa_bm_append_batch(pa_block_manager* bm, const int64_t* seq_ids, const int64_t* tokens, int32_t n,
                        int64_t* slots) {
-  if (!bm || (n > 0 && (!seq_ids || !tokens || !slots))) return PA_ERR_NULL;
-  if (n < 0) return PA_ERR_SHAPE;
-  // all or nothing: every id known and listed once (a stamp per call), blocks enough
-  const uint64_t stamp = ++bm->batch_stamp;
-  bm->batch.resize((size_t)n);
-  int32_t need = 0;
-  for (int32_t i = 0; i < n; ++i) {
-    const auto it = bm->seqs.find(seq_ids[i]);
-    if (it == bm->seqs.end()) return PA_ERR_NO_SEQUENCE;
-    Sequence& s = it->second;
-    if (s.stamp == stamp) return PA_ERR_SHAPE;
-    s.stamp = stamp;
-    if (s.tokens.size() >= (size_t)INT32_MAX) return PA_ERR_TOO_LARGE;
-    need += s.tokens.size() % (size_t)bm->bs == 0;
-    bm->batch[(size_t)i] = &s;
-  }
-  if (need > bm->nfree) return PA_ERR_NO_BLOCKS;
-  for (int32_t i = 0; i < n; ++i) slots[i] = append_one(bm, *bm->batch[(size_t)i], tokens[i]);
-  return PA_OK;
+  return guarded([&]() -> int {
+    if (!bm || (n > 0 && (!seq_ids || !tokens || !slots))) return PA_ERR_NULL;
+    if (n < 0) return PA_ERR_SHAPE;
+    // all or nothing: every id known and listed once (a stamp per call), blocks enough
+    const uint64_t stamp = ++bm->batch_stamp;
+    bm->batch.resize((size_t)n);
+    int32_t need = 0;
+    for (int32_t i = 0; i < n; ++i) {
+      const auto it = bm->seqs.find(seq_ids[i]);
+      if (it == bm->seqs.end()) return PA_ERR_NO_SEQUENCE;
+      Sequence& s = it->second;
+      if (s.stamp == stamp) return PA_ERR_SHAPE;
+      s.stamp = stamp;
+      if (s.tokens.size() >= (size_t)INT32_MAX) return PA_ERR_TOO_LARGE;
+      need += s.tokens.size() % (size_t)bm->bs == 0;
+      bm->batch[(size_t)i] = &s;
+    }
+    if (need > bm->nfree) return PA_ERR_NO_BLOCKS;
+    for (int32_t i = 0; i < n; ++i) slots[i] = append_one(bm, *bm->batch[(size_t)i], tokens[i]);
+    return PA_OK;
+  });
 }
 
 int pa_bm_free_sequence(pa_block_manager* bm, int64_t seq_id) {

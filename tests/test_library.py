@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for code in range(0, -10, -1):
+    for code in range(0, -11, -1):
         s = pk.status_string(code)
         assert s and s != "unknown status"
     assert pk.status_string(-99) == "unknown status"
