@@ -48,6 +48,7 @@ struct Unit {
   int ns, g0;
 };
 
+template <int TOK = 16>
 __device__ __forceinline__ Unit make_unit(const DecodeParams& prm, int b, int p, int n, int kvh, int chunk) {
   Unit u;
   u.b = b;
@@ -58,7 +59,7 @@ __device__ __forceinline__ Unit make_unit(const DecodeParams& prm, int b, int p,
   u.t_begin = p * prm.P;
   u.t_end = min(n, u.t_begin + prm.P);
   const int ntok = u.t_end - u.t_begin;
-  u.ntiles = ntok > 0 ? (ntok + 15) >> 4 : 1;
+  u.ntiles = ntok > 0 ? (ntok + TOK - 1) / TOK : 1;
   u.ns = 0;
   u.g0 = 0;
   return u;
@@ -451,6 +452,107 @@ __device__ __forceinline__ void fold_tile_vllm(uint32_t ok, const VllmTile<D>& T
     st.o[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, T.v[j]), pb, st.o[j], 0, 0, 0);
 }
 
+// 32-token tiles for blocks of 32 tokens or more (a tile then lies in one
+// block): a 16-token tile reads half of every K group and V row of such a
+// block, a 32-token one reads whole K groups (512 bytes for 32 tokens) and
+// whole 64-byte V rows.
+//   K: k[h][c] is the 16-byte group 4 c + l / 16 of token row 16 h + l % 16.
+//   V^T as the A operand of v_mfma_f32_16x16x32_bf16 (d rows x 32 keys): lane
+//     l holds d row 16 j + l % 16 at contraction indices 8 (l / 16) + e, taken
+//     to be keys 4 (l / 16) + e (e < 4) and 16 + 4 (l / 16) + e - 4 (e >= 4):
+//     two 8-byte reads of the row.  The probabilities use the same order:
+//     S accumulator h of lane l holds keys 16 h + 4 (l / 16) + i, so the B
+//     operand is (P of accumulator 0, P of accumulator 1) with no data
+//     movement, and the product sums over all 32 keys.
+template <int D>
+struct VllmTile32 {
+  u32x4m k[2][Geo<D>::NQK];
+  u32x4m v[Geo<D>::NPV];
+};
+
+template <int D, int AUX = 0>
+__device__ __forceinline__ uint32_t load_tile_vllm32(const DecodeParams& prm, int kvh, int t_end, int tile,
+                                                     int ph0, int lane, VllmTile32<D>& T) {
+  constexpr int NQK = Geo<D>::NQK, NPV = Geo<D>::NPV;
+  const int bs_log2 = prm.bs_log2;
+  const int nv = min(32, t_end - tile);
+  const int r = lane & 15, g4 = lane >> 4;
+  const bool ok0 = (unsigned)ph0 < (unsigned)prm.NB;
+  const int k_region = (D / 8) << (bs_log2 + 4), v_region = D << (bs_log2 + 1);   // bytes per (block, kv head)
+  auto rsrc = [&](const void* cache, int region) {
+    const char* base = static_cast<const char*>(cache) + (size_t)(ok0 ? ph0 : 0) * prm.KVH * region + (size_t)kvh * region;
+    return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, ok0 ? region : 0, kRsrcWord3M);
+  };
+  const int row0 = tile & prm.bs_mask;
+  const __amdgpu_buffer_rsrc_t k0 = rsrc(prm.k_cache, k_region);
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int c = 0; c < NQK; ++c) {
+      const uint32_t off = ((uint32_t)((4 * c + g4) << bs_log2) + row0 + 16 * h + r) * 16;
+      T.k[h][c] = __builtin_amdgcn_raw_buffer_load_b128(k0, off, 0, AUX);
+    }
+  const int vlo = min(max(nv - 4 * g4, 0), 4), vhi = min(max(nv - 16 - 4 * g4, 0), 4);   // valid tokens
+  auto keep = [](int vn, int half) {          // mask of the 32-bit word `half` of 4 tokens, vn valid
+    const int k = vn - 2 * half;
+    return k >= 2 ? 0xffffffffu : (k == 1 ? 0x0000ffffu : 0u);
+  };
+  const uint32_t m0 = keep(vlo, 0), m1 = keep(vlo, 1), m2 = keep(vhi, 0), m3 = keep(vhi, 1);
+  const __amdgpu_buffer_rsrc_t v0 = rsrc(prm.v_cache, v_region);
+#pragma unroll
+  for (int j = 0; j < NPV; ++j) {
+    const uint32_t off = ((uint32_t)((16 * j + r) << bs_log2) + row0 + 4 * g4) * 2;
+    const u32x2m lo = __builtin_amdgcn_raw_buffer_load_b64(v0, off, 0, AUX);
+    const u32x2m hi = __builtin_amdgcn_raw_buffer_load_b64(v0, off + 32, 0, AUX);
+    T.v[j] = u32x4m{lo[0] & m0, lo[1] & m1, hi[0] & m2, hi[1] & m3};
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  return ok0 && nv > 0 ? (nv >= 32 ? 0xffffffffu : (1u << nv) - 1u) : 0u;
+}
+
+template <int D>
+__device__ __forceinline__ void fold_tile_vllm32(uint32_t ok, const VllmTile32<D>& T,
+                                                 const bf16x8 (&qop)[Geo<D>::NQK], float cs, int lane, Fold<D>& st) {
+  constexpr int NQK = Geo<D>::NQK, NPV = Geo<D>::NPV;
+  const int grp = lane >> 4;
+  f32x4 s0 = {0.0f, 0.0f, 0.0f, 0.0f}, s1 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int c = 0; c < NQK; ++c) {
+    s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, T.k[0][c]), qop[c], s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, T.k[1][c]), qop[c], s1, 0, 0, 0);
+  }
+  float sc[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    sc[i] = ((ok >> (4 * grp + i)) & 1u) ? s0[i] * cs : -INFINITY;
+    sc[4 + i] = ((ok >> (16 + 4 * grp + i)) & 1u) ? s1[i] * cs : -INFINITY;
+  }
+  float mt = sc[0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) mt = fmaxf(mt, sc[i]);
+  mt = groups_max(mt);
+  if (__builtin_amdgcn_ballot_w64(mt > st.m + kSlackM)) {
+    if (mt > st.m) {
+      const float corr = exp2m(st.m - mt);
+      st.m = mt;
+      st.mneg = -mt;
+      st.lsum *= corr;
+#pragma unroll
+      for (int j = 0; j < NPV; ++j) st.o[j] *= corr;
+    }
+  }
+  bf16x8 pb;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float p = exp2m(sc[i] + st.mneg);
+    st.lsum += p;
+    pb[i] = (__bf16)p;
+  }
+#pragma unroll
+  for (int j = 0; j < NPV; ++j)
+    st.o[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, T.v[j]), pb, st.o[j], 0, 0, 0);
+}
+
 }  // namespace
 
 // One wavefront per unit (kv head and head chunk fastest, partition,
@@ -500,11 +602,11 @@ struct P09Tile {
   u32x4m k[Geo<D>::NI], v[Geo<D>::NI];
 };
 
-template <int D, bool WholeTile, bool Vllm>
+template <int D, bool WholeTile, bool Vllm, int TOK = 16>
 struct TileOps;
 
 template <int D, bool WholeTile>
-struct TileOps<D, WholeTile, false> {   // P09 layout: whole rows, staged through LDS
+struct TileOps<D, WholeTile, false, 16> {   // P09 layout: whole rows, staged through LDS
   using Tile = P09Tile<D>;
   template <int AUX>
   static __device__ __forceinline__ uint32_t load(const DecodeParams& prm, int kvh, int t_end, int tile, bool live,
@@ -520,7 +622,7 @@ struct TileOps<D, WholeTile, false> {   // P09 layout: whole rows, staged throug
 };
 
 template <int D, bool WholeTile>
-struct TileOps<D, WholeTile, true> {    // vLLM layout: operands straight from the blocks
+struct TileOps<D, WholeTile, true, 16> {    // vLLM layout: operands straight from the blocks
   using Tile = VllmTile<D>;
   template <int AUX>
   static __device__ __forceinline__ uint32_t load(const DecodeParams& prm, int kvh, int t_end, int tile, bool live,
@@ -531,6 +633,21 @@ struct TileOps<D, WholeTile, true> {    // vLLM layout: operands straight from t
                                               float cs, const LdsMap<D>&, int lane, Fold<D>& st, uint8_t*,
                                               uint8_t*) {
     fold_tile_vllm<D>(ok, T, qop, cs, lane, st);
+  }
+};
+
+template <int D>
+struct TileOps<D, true, true, 32> {     // vLLM layout, blocks of 32 tokens or more: 32-token tiles
+  using Tile = VllmTile32<D>;
+  template <int AUX>
+  static __device__ __forceinline__ uint32_t load(const DecodeParams& prm, int kvh, int t_end, int tile, bool live,
+                                                  int ph0, int, int lane, uint32_t, Tile& T) {
+    return load_tile_vllm32<D, AUX>(prm, kvh, t_end, tile, live ? ph0 : -1, lane, T);
+  }
+  static __device__ __forceinline__ void fold(uint32_t ok, const Tile& T, const bf16x8 (&qop)[Geo<D>::NQK],
+                                              float cs, const LdsMap<D>&, int lane, Fold<D>& st, uint8_t*,
+                                              uint8_t*) {
+    fold_tile_vllm32<D>(ok, T, qop, cs, lane, st);
   }
 };
 
@@ -555,10 +672,10 @@ struct TileOps<D, WholeTile, true> {    // vLLM layout: operands straight from t
 // wavefronts sharing a CU stream at very different rates, and this lets the
 // faster ones take more units, so that all of a CU's wavefronts finish
 // together.
-template <int D, bool WholeTile, int NW, bool Vllm = false>
+template <int D, bool WholeTile, int NW, bool Vllm = false, int TOK = 16>
 __global__ __launch_bounds__(64 * NW) void decode_partial_mfma_kernel(const DecodeParams prm) {
   using Gm = Geo<D>;
-  using Ops = TileOps<D, WholeTile, Vllm>;
+  using Ops = TileOps<D, WholeTile, Vllm, TOK>;
   using Tile = typename Ops::Tile;
   constexpr int NBUF = 2;   // tiles in flight per wavefront (3 measured no faster)
   __shared__ __attribute__((aligned(16))) uint8_t lds_tiles[NW][2][16 * Gm::ROWB];
@@ -734,7 +851,7 @@ __global__ __launch_bounds__(64 * NW) void decode_partial_mfma_kernel(const Deco
       }
     }
     const int kvh = (int)(sub / (uint32_t)prm.nchunks);
-    Unit u = make_unit(prm, b, p, n, kvh, (int)sub - kvh * prm.nchunks);
+    Unit u = make_unit<TOK>(prm, b, p, n, kvh, (int)sub - kvh * prm.nchunks);
     u.ns = ns;
     u.g0 = g0;
     return u;
@@ -790,7 +907,7 @@ __global__ __launch_bounds__(64 * NW) void decode_partial_mfma_kernel(const Deco
     int l_tile = 0, ph0 = -1, ph1 = -1;
 
     auto request_blocks = [&]() {
-      const int tile = L.t_begin + 16 * l_tile;
+      const int tile = L.t_begin + TOK * l_tile;
       const int j = tile >> prm.bs_log2;
       ph0 = -1;
       ph1 = -1;
@@ -814,7 +931,7 @@ __global__ __launch_bounds__(64 * NW) void decode_partial_mfma_kernel(const Deco
         request_blocks();
       }
       const bool live = (fl & (kDead | kPending | kAlive)) == kAlive;
-      ok = Ops::template load<A>(prm, L.kvh, L.t_end, L.t_begin + 16 * l_tile, live, ph0, ph1, lane, lane_off, T);
+      ok = Ops::template load<A>(prm, L.kvh, L.t_end, L.t_begin + TOK * l_tile, live, ph0, ph1, lane, lane_off, T);
       if (live) {
         ++l_tile;
         if (l_tile < L.ntiles) request_blocks();
@@ -879,7 +996,7 @@ __global__ __launch_bounds__(64 * NW) void decode_partial_mfma_kernel(const Deco
   // tile reads half of every K group and V row of its block and the next tile
   // reads the other half.
   if (share((uint32_t)wave) < nunits) {
-    if (__builtin_amdgcn_readfirstlane(s_shared) || (Vllm && prm.bs_log2 >= 5))
+    if (__builtin_amdgcn_readfirstlane(s_shared) || (Vllm && prm.bs_log2 >= (TOK == 32 ? 6 : 5)))
       walk(CachePolicy<0>{});
     else
       walk(CachePolicy<kAuxNT>{});
@@ -890,6 +1007,17 @@ namespace {
 constexpr int kMaxPersistentSeqs = 4096;   // the pair search covers 64 x 64 sequences
 constexpr size_t kMinLdsPerCU = 82 * 1024; // more than half of a CU's 160 KiB of LDS
 
+template <int D, bool WholeTile, int NW, bool Vllm, int TOK>
+hipError_t launch_persistent(const DecodeParams& prm, int cus, hipStream_t stream) {
+  // the list, padded so that a second workgroup never fits on the same CU
+  size_t lds = (size_t)prm.B * 5 * sizeof(int32_t);
+  const size_t fixed = sizeof(uint8_t) * NW * 2 * 16 * 2 * D + 64 * 4 + 12;
+  if (lds + fixed < kMinLdsPerCU) lds = kMinLdsPerCU - fixed;
+  hipLaunchKernelGGL((decode_partial_mfma_kernel<D, WholeTile, NW, Vllm, TOK>), dim3((uint32_t)cus), dim3(64 * NW),
+                     lds, stream, prm);
+  return hipGetLastError();
+}
+
 template <int D, bool WholeTile, bool Vllm>
 hipError_t launch_mfma(const DecodeParams& prm, hipStream_t stream) {
   // Wavefronts per CU: two per SIMD while a wavefront needs at most half a
@@ -897,13 +1025,14 @@ hipError_t launch_mfma(const DecodeParams& prm, hipStream_t stream) {
   constexpr int NW = D <= 128 ? 8 : 4;
   const int cus = device_cus();
   if (prm.B <= kMaxPersistentSeqs && cus > 0) {
-    // the list, padded so that a second workgroup never fits on the same CU
-    size_t lds = (size_t)prm.B * 5 * sizeof(int32_t);
-    const size_t fixed = sizeof(uint8_t) * NW * 2 * 16 * 2 * D + 64 * 4 + 12;
-    if (lds + fixed < kMinLdsPerCU) lds = kMinLdsPerCU - fixed;
-    hipLaunchKernelGGL((decode_partial_mfma_kernel<D, WholeTile, NW, Vllm>), dim3((uint32_t)cus), dim3(64 * NW), lds,
-                       stream, prm);
-    return hipGetLastError();
+    if constexpr (Vllm && WholeTile && D <= 128) {
+      // vLLM layout, blocks of 32 tokens or more: 32-token tiles, which hold
+      // twice the registers of a 16-token tile (one wavefront per SIMD above
+      // head_dim 64: the same bytes in flight per CU; at head_dim 256 they
+      // would spill, so that size keeps 16-token tiles)
+      if (prm.bs_log2 >= 5) return launch_persistent<D, true, D <= 64 ? 8 : 4, true, 32>(prm, cus, stream);
+    }
+    return launch_persistent<D, WholeTile, NW, Vllm, 16>(prm, cus, stream);
   }
   const dim3 grid(prm.KVH * prm.nchunks, prm.maxP, prm.B);
   if constexpr (Vllm)

@@ -76,6 +76,11 @@ CASES = [
     (64, 16, 2, 8, [3, 64, 250]),
     (256, 16, 2, 4, [17, 48, 700]),
     (128, 16, 1, 16, [33, 129]),
+    # blocks of 32 and 64 tokens: 32-token tiles (head_dim <= 128), tile edges straddled
+    (64, 32, 2, 8, [1, 31, 32, 33, 95, 400]),
+    (128, 64, 2, 4, [1, 63, 64, 65, 300, 1030]),
+    (128, 32, 2, 16, [31, 64, 96, 777]),
+    (256, 32, 2, 4, [7, 33, 500]),              # head_dim 256 keeps 16-token tiles
 ]
 
 
