@@ -36,8 +36,9 @@ constexpr int kBuckets = 64;              // length classes of the last-partitio
 
 // One work unit: partition p of sequence b (n tokens, np partitions), kv head
 // kvh, query-head chunk chunk (up to 16 heads of the kv head's group), tokens
-// [t_begin, t_end) in ntiles 16-token tiles (at least one: an empty unit
-// folds one fully masked tile and writes zeros).  Wave-uniform.
+// [t_begin, t_end) in ntiles tiles of TOK tokens (16; 32 for vLLM's layout
+// with blocks of 32 tokens or more) (at least one: an empty unit folds one
+// fully masked tile and writes zeros).  Wave-uniform.
 // A shared unit (ns > 0) folds a shared partition p for ns sequences at once:
 // entries g0 .. g0 + ns - 1 of the list of sequences that share the prefix,
 // their G heads side by side as the 16 columns; b is the first of them (whose
@@ -992,9 +993,9 @@ __global__ __launch_bounds__(64 * NW) void decode_partial_mfma_kernel(const Deco
   // Blocks shared between sequences (a common prefix) are likely to be read
   // again by other workgroups: keep the default cache policy for them.
   // Otherwise every K/V row is read once, and the loads are non-temporal --
-  // except in vLLM's layout with blocks of 32 or more tokens, where a 16-token
-  // tile reads half of every K group and V row of its block and the next tile
-  // reads the other half.
+  // except in vLLM's layout when a tile reads only part of every K group and V
+  // row of its block (16-token tiles in blocks of 32 or more, 32-token tiles in
+  // blocks of 64 or more) and the next tile reads the rest.
   if (share((uint32_t)wave) < nunits) {
     if (__builtin_amdgcn_readfirstlane(s_shared) || (Vllm && prm.bs_log2 >= (TOK == 32 ? 6 : 5)))
       walk(CachePolicy<0>{});
