@@ -320,6 +320,9 @@ def run_prefill(args, cfg):
     w = make_prefill(cfg, dev)
     T, H, D = w.q.shape
     kc, vc = w.k_cache, w.v_cache
+    if args.layout == "vllm":
+        from synth import to_vllm_layout
+        kc, vc = to_vllm_layout(kc, vc)
     out = torch.empty_like(w.q)
     ws = pk.prefill_workspace(cfg.num_seqs, H, w.block_tables.shape[1], T, kc)
     flush = None if args.hot else torch.ones(1 << 28, dtype=torch.float32, device=dev)
@@ -384,7 +387,7 @@ def run_prefill(args, cfg):
         "config": {
             "workload": cfg.name, "num_seqs": cfg.num_seqs, "num_heads": H, "num_kv_heads": cfg.num_kv_heads,
             "head_dim": D, "block_size": cfg.block_size, "cached_tokens": w.cached, "new_tokens": w.new,
-            "query_tokens": T, "cache_flush_between_steps": flush is not None,
+            "query_tokens": T, "cache_layout": args.layout, "cache_flush_between_steps": flush is not None,
         },
         "flops_per_step": flops,
         "prefill_kernel_us": round(ak_us, 2),
@@ -400,7 +403,7 @@ def run_prefill(args, cfg):
             "peak": MFMA_BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-            "traffic": _traffic(cfg.name, "prefill"),
+            "traffic": _traffic(cfg.name, "prefill") if args.layout == "p09" else None,
             "kernel": "prefill_mfma_kernel",
         },
     }
@@ -525,7 +528,7 @@ def main():
     ap.add_argument("--hot", action="store_true", help="do not flush the last-level cache between steps")
     ap.add_argument("--layout", choices=["p09", "vllm"], default="p09",
                     help="cache layout: P09's [NB, bs, KVH, D] (default) or vLLM's packed K [NB, KVH, D/x, bs, x] "
-                         "with V [NB, KVH, D, bs] (decode configs, bf16)")
+                         "with V [NB, KVH, D, bs] (bf16 decode and prefill configs)")
     ap.add_argument("--shared-tokens", type=int, default=-1,
                     help="decode with pa_decode_shared_prefix and this hint (default: the workload's common "
                          "prefix for prefix_shared_bf16, else 0 = pa_decode)")

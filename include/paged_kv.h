@@ -275,11 +275,12 @@ size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t m
  *   query_start_loc   device, [B + 1] int32, non-decreasing from 0 to num_tokens
  *   scale             multiplies q.k before the softmax
  *   num_tokens        T >= 0 (T == 0 enqueues nothing)
- *   desc              host, cache geometry; layout PA_LAYOUT_P09
- *                     (PA_ERR_UNSUPPORTED otherwise).  bf16 runs the
- *                     matrix-core kernel; fp32 runs one vector-ALU decode per
- *                     query row over its first (position + 1) tokens (a
- *                     plain path for small fp32 workloads: num_tokens <= 65535)
+ *   desc              host, cache geometry.  bf16 runs the matrix-core
+ *                     kernel, in either layout; fp32 runs one vector-ALU
+ *                     decode per query row over its first (position + 1)
+ *                     tokens (a plain path for small fp32 workloads:
+ *                     num_tokens <= 65535), PA_LAYOUT_P09 only
+ *                     (PA_ERR_UNSUPPORTED otherwise)
  *   workspace         device, >= pa_prefill_workspace_bytes(...) bytes, no
  *                     initial contents required.  Calls that share a
  *                     workspace must not run concurrently.

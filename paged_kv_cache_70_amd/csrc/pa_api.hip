@@ -394,9 +394,9 @@ static int prefill_shape(int32_t B, int32_t H, int32_t W, int32_t T, const pa_ca
   if (st) return st;
   if (B <= 0 || H <= 0 || W <= 0 || T < 0) return PA_ERR_SHAPE;
   if (H % d->num_kv_heads) return PA_ERR_SHAPE;
-  if (d->layout != PA_LAYOUT_P09) return PA_ERR_UNSUPPORTED;
   PrefillShape p{};
   if (d->dtype == PA_F32) {
+    if (d->layout != PA_LAYOUT_P09) return PA_ERR_UNSUPPORTED;   // the fp32 path decodes per row
     if (T > 65535) return PA_ERR_TOO_LARGE;
     const int64_t max_len = (int64_t)W * d->block_size;
     const int32_t P = (int32_t)(max_len < 64LL * d->block_size ? max_len : 64LL * d->block_size);
@@ -490,6 +490,7 @@ int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cach
   p.bs_log2 = ilog2(desc->block_size);
   p.bs_mask = desc->block_size - 1;
   p.max_tokens = (int32_t)max_len;
+  p.vllm = desc->layout == PA_LAYOUT_VLLM ? 1 : 0;
   return launch_prefill_mfma(p, desc->head_dim, s) == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 

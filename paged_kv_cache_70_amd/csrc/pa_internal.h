@@ -73,6 +73,7 @@ struct PrefillParams {
   int32_t max_tiles;       // bound on the (sequence, query tile) pairs: T / tq + B
   uint32_t* plan;          // workspace: [max_tiles] (sequence << 16 | query tile), heaviest first
   int32_t* tickets;        // workspace: [c] next unit of class c < kTicketClasses, [kTicketClasses] plan entries
+  int32_t vllm;            // caches in vLLM's layout (K [NB, KVH, D/8, bs, 8], V [NB, KVH, D, bs])
 };
 
 bool dtype_ok(int32_t dtype);

@@ -58,12 +58,21 @@ struct PState {
   f32x4 o[D / 16][QB];
 };
 
+typedef uint32_t u32x2m __attribute__((ext_vector_type(2)));
+
+// V staged as [d][64 keys] (128 bytes per d row; the vLLM layout's
+// orientation): 8-byte chunk c (keys 4c .. 4c + 3) of row d is stored at chunk
+// c ^ vt_swz(d).  vt_swz is even, so a 16-byte pair of chunks stays a pair;
+// the 16 lanes of a staging write (8 rows of one parity x 2 pairs) and the 32
+// lanes of an operand read (16 rows x 2 chunks) fall in distinct banks.
+__device__ __forceinline__ int vt_swz(int d) { return (((d >> 1) & 3) << 2) | (((d >> 3) & 1) << 1); }
+
 // Folds one staged 64-key tile (keys t0 ..) into the state; masked
 // (wavefront-uniform): apply the causal mask key <= qpos.  Operand reads run
 // one group ahead of the products that use them (K: one 16-key block, V: one
 // 16-column d block), pinned in that order by scheduling barriers, so LDS
 // latency hides behind the previous group's products.
-template <int D, int kQB = query_blocks<D>()>
+template <int D, int kQB = query_blocks<D>(), bool VT = false>
 __device__ __forceinline__ void fold_keys(const uint8_t* __restrict__ lk, const uint8_t* __restrict__ lv,
                                           bool masked, int t0, const int (&qpos)[kQB],
                                           const bf16x8 (&qop)[kQB][Geo<D>::NQK], float cs,
@@ -79,6 +88,21 @@ __device__ __forceinline__ void fold_keys(const uint8_t* __restrict__ lk, const 
   // V^T operand of d block j for key pair kk: two transposing reads (keys
   // 32 kk + 4 grp + i and 32 kk + 16 + 4 grp + i of d column 16 j + lane % 16).
   auto read_v = [&](int j, bf16x8 (&a)[kNKB / 2]) {
+    if constexpr (VT) {
+      // V staged as [d][64 keys] (vLLM's orientation): the same operand is two
+      // plain 8-byte reads of row d = 16 j + lane % 16, chunks 8 kk + grp and
+      // 8 kk + 4 + grp (4 keys each), at their swizzled places
+      const int d = 16 * j + (lane & 15);
+      const uint8_t* row = lv + d * (kKeyTile * 2);
+      const int f = vt_swz(d);
+#pragma unroll
+      for (int kk = 0; kk < kNKB / 2; ++kk) {
+        const u32x2m v0 = *reinterpret_cast<const u32x2m*>(row + ((8 * kk + grp) ^ f) * 8);
+        const u32x2m v1 = *reinterpret_cast<const u32x2m*>(row + ((8 * kk + 4 + grp) ^ f) * 8);
+        a[kk] = __builtin_bit_cast(bf16x8, u32x4m{v0[0], v0[1], v1[0], v1[1]});
+      }
+      return;
+    }
     const int d = 16 * j + map.dv;
     const int off = (map.tv * PPR + ((d >> 3) ^ swz<PPR>(map.tv))) * 16 + (d & 7) * 2;
 #pragma unroll
@@ -263,6 +287,88 @@ __global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(const Prefil
   }
 }
 
+// One wavefront's 16-key subtile (keys t .. t + 15) of kv head kvh with the
+// caches in vLLM's layout ("PagedAttention kernel：paged KV cache 与 block
+// table", 深入原理: K [NB, KVH, D/8, bs, 8], V [NB, KVH, D, bs]), in staging
+// order: kr[i] is the 16-byte group 4 i + lane / 16 of key t + lane % 16 (the
+// 16 lanes of a group read 256 contiguous bytes); vr[i] is keys t + 8 h ..
+// + 7 of d row q / 2, q = 64 i + lane, h = q % 2.  Buffer loads with one
+// resource per block (empty outside the pool or past kend: zeros); for blocks
+// of 8 tokens the subtile's second half is block ph1, reached through a
+// second resource.  V elements of keys at or past kend are zeroed; K rows
+// there are only ever under the causal mask.
+template <int D, bool WholeTile>
+__device__ __forceinline__ void load_subtile_vllm(const PrefillParams& prm, int kvh, int kend, int t, bool live,
+                                                  int ph0, int ph1, int lane, u32x4m (&kr)[Geo<D>::NI],
+                                                  u32x4m (&vr)[Geo<D>::NI]) {
+  constexpr int NI = Geo<D>::NI;
+  constexpr uint32_t kFar = 0x80000000u;   // a byte offset past every resource's end
+  const int bs_log2 = prm.bs_log2;
+  const int k_region = (D / 8) << (bs_log2 + 4), v_region = D << (bs_log2 + 1);   // bytes per (block, kv head)
+  auto rsrc = [&](const void* cache, int blk, int region) {
+    const bool ok = live && (unsigned)blk < (unsigned)prm.NB;
+    const char* base = static_cast<const char*>(cache) + ((size_t)(ok ? blk : 0) * prm.KVH + kvh) * region;
+    return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, ok ? region : 0, kRsrcWord3M);
+  };
+  const int tk = lane & 15;
+  {
+    const __amdgpu_buffer_rsrc_t k0 = rsrc(prm.k_cache, ph0, k_region);
+    const int row = WholeTile ? (t & prm.bs_mask) + tk : (tk & 7);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const uint32_t off = ((uint32_t)((4 * i + (lane >> 4)) << bs_log2) + row) * 16;
+      if constexpr (WholeTile) {
+        kr[i] = __builtin_amdgcn_raw_buffer_load_b128(k0, off, 0, 0);
+      } else {
+        const __amdgpu_buffer_rsrc_t k1 = rsrc(prm.k_cache, ph1, k_region);
+        const u32x4m a = __builtin_amdgcn_raw_buffer_load_b128(k0, tk < 8 ? off : kFar, 0, 0);
+        const u32x4m b = __builtin_amdgcn_raw_buffer_load_b128(k1, tk < 8 ? kFar : off, 0, 0);
+        kr[i] = a | b;
+      }
+    }
+  }
+  {
+    const __amdgpu_buffer_rsrc_t v0 = rsrc(prm.v_cache, ph0, v_region);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int q = 64 * i + lane, d = q >> 1, h = q & 1;
+      const int row = WholeTile ? (t & prm.bs_mask) + 8 * h : 0;
+      const uint32_t off = ((uint32_t)(d << bs_log2) + row) * 2;
+      u32x4m w;
+      if constexpr (WholeTile) {
+        w = __builtin_amdgcn_raw_buffer_load_b128(v0, off, 0, 0);
+      } else {
+        const __amdgpu_buffer_rsrc_t v1 = rsrc(prm.v_cache, ph1, v_region);
+        const u32x4m a = __builtin_amdgcn_raw_buffer_load_b128(v0, h ? kFar : off, 0, 0);
+        const u32x4m b = __builtin_amdgcn_raw_buffer_load_b128(v1, h ? off : kFar, 0, 0);
+        w = a | b;
+      }
+      const int vn = min(max(kend - (t + 8 * h), 0), 8);   // valid keys of these 8
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] &= vn >= 2 * e + 2 ? 0xffffffffu : (vn == 2 * e + 1 ? 0x0000ffffu : 0u);
+      vr[i] = w;
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Staging of a vLLM-layout subtile: K pieces to their place in the [key][d]
+// tile (the P09 layout, so the K operand reads are shared), V pieces to the
+// [d][64 keys] tile at chunk pair 4 wave + 2 h (keys 16 wave + 8 h ..).
+template <int D>
+__device__ __forceinline__ void stage_subtile_vllm(uint8_t* lk, uint8_t* lv, int wave, int lane,
+                                                   const u32x4m (&kr)[Geo<D>::NI], const u32x4m (&vr)[Geo<D>::NI]) {
+  constexpr int NI = Geo<D>::NI, PPR = Geo<D>::PPR;
+  const int tk = lane & 15;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int pc = 4 * i + (lane >> 4);
+    *reinterpret_cast<u32x4m*>(lk + (tk * PPR + (pc ^ swz<PPR>(tk))) * 16) = kr[i];
+    const int q = 64 * i + lane, d = q >> 1, c = 4 * wave + 2 * (q & 1);
+    *reinterpret_cast<u32x4m*>(lv + d * (kKeyTile * 2) + (c ^ vt_swz(d)) * 8) = vr[i];
+  }
+}
+
 // Persistent: a few workgroups per CU, each drawing units (a planned
 // (sequence, query tile) pair times one (kv head, head chunk)) from a ticket
 // counter until none is left, heaviest first, so the chip stays full however
@@ -276,7 +382,7 @@ __global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(const Prefil
 // query tile of one kv head then reads that head's K/V through the same L2.
 // Each class has workgroups (the grid has at least KU of them) and covers
 // its indices for every pair; no workgroup waits for another.
-template <int D, bool WholeTile>
+template <int D, bool WholeTile, bool Vllm>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 1 : 2)))
 void prefill_mfma_kernel(const PrefillParams prm) {
   using Gm = Geo<D>;
@@ -365,9 +471,16 @@ void prefill_mfma_kernel(const PrefillParams prm) {
       int ph0 = 0, ph1 = 0;
       if (live) ph0 = trow[j];
       if (!WholeTile && t + 8 < kend) ph1 = trow[j + 1];
-      (void)load_tile<D, WholeTile, 0>(prm, kc, vc, kend, t, live, ph0, ph1, lane_off, kr, vr);
+      if constexpr (Vllm)
+        load_subtile_vllm<D, WholeTile>(prm, kvh, kend, t, live, ph0, ph1, lane, kr, vr);
+      else
+        (void)load_tile<D, WholeTile, 0>(prm, kc, vc, kend, t, live, ph0, ph1, lane_off, kr, vr);
     };
     auto stage = [&](int buf, const u32x4m (&kr)[NI], const u32x4m (&vr)[NI]) {
+      if constexpr (Vllm) {
+        stage_subtile_vllm<D>(lds_kv[buf][0] + wave * 16 * ROWB, lds_kv[buf][1], wave, lane, kr, vr);
+        return;
+      }
       uint8_t* lk = lds_kv[buf][0] + wave * 16 * ROWB;
       uint8_t* lv = lds_kv[buf][1] + wave * 16 * ROWB;
 #pragma unroll
@@ -402,7 +515,8 @@ void prefill_mfma_kernel(const PrefillParams prm) {
       const int t0 = it * kKeyTile;
       if (w_valid > 0 && t0 <= wpos_hi) {
         const bool masked = t0 + kKeyTile - 1 > wpos_lo;
-        fold_keys<D>(lds_kv[buf][0], lds_kv[buf][1], masked, t0, qpos, qop, prm.scale_log2, map, lane, st);
+        fold_keys<D, kQB, Vllm>(lds_kv[buf][0], lds_kv[buf][1], masked, t0, qpos, qop, prm.scale_log2, map, lane,
+                                st);
       }
       if (more) stage(buf ^ 1, kr, vr);
       __syncthreads();
@@ -465,7 +579,7 @@ hipError_t launch_prefill_rows(const int32_t* qstart, const int32_t* ctx, int32_
   return hipGetLastError();
 }
 
-template <int D, bool WholeTile>
+template <int D, bool WholeTile, bool Vllm>
 static hipError_t launch_prefill_d(const PrefillParams& prm, hipStream_t stream) {
   // resident workgroups per CU: LDS (2 x 2 x 64 rows of D bf16) and registers
   constexpr int kPerCU = D >= 256 ? 1 : (D >= 128 ? 2 : 3);
@@ -474,18 +588,26 @@ static hipError_t launch_prefill_d(const PrefillParams& prm, hipStream_t stream)
   int64_t grid = (int64_t)(cus > 0 ? cus : 256) * kPerCU;
   if (grid > units) grid = units;
   hipLaunchKernelGGL(prefill_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, prm);
-  hipLaunchKernelGGL((prefill_mfma_kernel<D, WholeTile>), dim3((unsigned)grid), dim3(kWaves * 64), 0, stream, prm);
+  hipLaunchKernelGGL((prefill_mfma_kernel<D, WholeTile, Vllm>), dim3((unsigned)grid), dim3(kWaves * 64), 0, stream,
+                     prm);
   return hipGetLastError();
 }
 
-hipError_t launch_prefill_mfma(const PrefillParams& prm, int32_t D, hipStream_t stream) {
+template <bool Vllm>
+static hipError_t launch_prefill_layout(const PrefillParams& prm, int32_t D, hipStream_t stream) {
   const bool whole = prm.bs_log2 >= 4;
   switch (D) {
-    case 64: return whole ? launch_prefill_d<64, true>(prm, stream) : launch_prefill_d<64, false>(prm, stream);
-    case 128: return whole ? launch_prefill_d<128, true>(prm, stream) : launch_prefill_d<128, false>(prm, stream);
-    case 256: return whole ? launch_prefill_d<256, true>(prm, stream) : launch_prefill_d<256, false>(prm, stream);
+    case 64: return whole ? launch_prefill_d<64, true, Vllm>(prm, stream) : launch_prefill_d<64, false, Vllm>(prm, stream);
+    case 128:
+      return whole ? launch_prefill_d<128, true, Vllm>(prm, stream) : launch_prefill_d<128, false, Vllm>(prm, stream);
+    case 256:
+      return whole ? launch_prefill_d<256, true, Vllm>(prm, stream) : launch_prefill_d<256, false, Vllm>(prm, stream);
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_prefill_mfma(const PrefillParams& prm, int32_t D, hipStream_t stream) {
+  return prm.vllm ? launch_prefill_layout<true>(prm, D, stream) : launch_prefill_layout<false>(prm, D, stream);
 }
 
 }  // namespace pa

@@ -89,6 +89,29 @@ def test_prefill_small(case):
     _check(w, f"H{H} KVH{KVH} D{D} bs{bs} cached {cached} new {new}")
 
 
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"vllm_H{c[0]}_KVH{c[1]}_D{c[2]}_bs{c[3]}")
+def test_prefill_vllm_layout(case):
+    """The same cases with the caches in vLLM's layout (K [NB, KVH, D/8, bs, 8],
+    V [NB, KVH, D, bs]): write and prefill there, the written caches equal to
+    the oracle's (packed) bit for bit, the output to the oracle's prefill."""
+    from synth import to_vllm_layout
+    H, KVH, D, bs, cached, new = case
+    w = make_prefill_custom(num_heads=H, num_kv_heads=KVH, head_dim=D, block_size=bs, cached=cached,
+                            new=new, seed=len(cached) * 7 + D + bs + 1, device="cuda", poison=True)
+    kp, vp = to_vllm_layout(w.k_cache, w.v_cache)
+    pk.write_kv(kp, vp, w.k_new, w.v_new, w.slot_mapping)
+    out = pk.prefill(w.q, kp, vp, w.block_tables, w.context_lens, w.query_start_loc, w.scale)
+    torch.cuda.synchronize()
+    ko, vo = _oracle_caches(w)
+    bits = lambda a: np.ascontiguousarray(a).view(np.uint8)
+    assert np.array_equal(bits(stored_np(kp)), bits(O.pack_k_vllm(ko, "bf16"))), "K cache (vLLM layout)"
+    assert np.array_equal(bits(stored_np(vp)), bits(O.pack_v_vllm(vo))), "V cache (vLLM layout)"
+    ref = O.prefill(stored_np(w.q), ko, vo, stored_np(w.block_tables), stored_np(w.context_lens),
+                    stored_np(w.query_start_loc), w.scale, "bf16")
+    err = assert_matches_oracle(out, ref, "bf16", f"vLLM layout H{H} KVH{KVH} D{D} bs{bs}")
+    _say(f"vLLM layout H{H} KVH{KVH} D{D} bs{bs}: max err {err:.2e}")
+
+
 def test_prefill_fresh_and_single_token():
     """Whole fresh prefills (cached 0) and one-token contexts."""
     w = make_prefill_custom(num_heads=8, num_kv_heads=2, head_dim=128, block_size=16,

@@ -146,9 +146,6 @@ def test_vllm_layout_rejects_f32_decode_and_prefill():
     cl = torch.ones((1,), dtype=torch.int32, device="cuda")
     with pytest.raises(pk.PaError):
         pk.decode(q, kc, vc, bt, cl, 1.0, workspace=torch.empty(16, dtype=torch.uint8, device="cuda"))
-    kb = torch.zeros((4, 2, 8, 16, 8), dtype=torch.bfloat16, device="cuda")
-    vb = torch.zeros((4, 2, 64, 16), dtype=torch.bfloat16, device="cuda")
-    qb = torch.zeros((1, 4, 64), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(pk.PaError):
-        pk.prefill(qb, kb, vb, bt, cl, torch.tensor([0, 1], dtype=torch.int32, device="cuda"), 1.0,
+        pk.prefill(q, kc, vc, bt, cl, torch.tensor([0, 1], dtype=torch.int32, device="cuda"), 1.0,
                    workspace=torch.empty(64, dtype=torch.uint8, device="cuda"))
