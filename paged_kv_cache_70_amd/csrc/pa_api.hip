@@ -268,6 +268,8 @@ int pa_write_kv(void* k_cache, void* v_cache, const void* k, const void* v,
     return PA_ERR_ALIGN;
   const int64_t row_bytes = (int64_t)desc->num_kv_heads * desc->head_dim * elem_bytes(desc->dtype);
   if ((int64_t)num_tokens * (row_bytes / 16) > (int64_t)UINT_MAX - 256) return PA_ERR_TOO_LARGE;
+  // the vLLM-layout write spreads a row's 16-byte groups over grid.y, 32 per workgroup
+  if (desc->layout == PA_LAYOUT_VLLM && (row_bytes / 16 + 31) / 32 > 65535) return PA_ERR_TOO_LARGE;
   const int64_t num_slots = (int64_t)desc->num_blocks * desc->block_size;
   hipError_t e = desc->layout == PA_LAYOUT_VLLM
                      ? launch_write_kv_vllm(k_cache, v_cache, k, v, slot_mapping, num_tokens, (int32_t)row_bytes,

@@ -40,49 +40,89 @@ __global__ __launch_bounds__(256) void write_kv_kernel(
 
 // The same scatter into vLLM's cache layout ("PagedAttention kernel：paged KV
 // cache 与 block table", 深入原理): K [NB, KVH, D/x, bs, x] with x elements =
-// 16 bytes, V [NB, KVH, D, bs].  One thread per 16-byte group of x elements
-// (token, kv head, group g): the K group is one 16-byte store at
-// (block, head, g, offset); its x V elements go to x rows d = g x + e of
-// (block, head), each at column `offset` (stride bs elements).
+// 16 bytes, V [NB, KVH, D, bs].  Row r = h * D + d of (block, head) holds one
+// element per token slot, so consecutive slots of a block are adjacent
+// elements of a row (and, for K, adjacent 16-byte groups).
+//
+// A workgroup takes 16 new tokens and 32 of their 16-byte groups.  Stores run
+// with the token as the fastest lane index: when the 16 tokens occupy
+// consecutive slots (any prefill chunk, whatever its offset in the block),
+// each K group becomes one 256-byte run and each V row one 32-byte run, so a
+// wave's V store covers four adjacent rows.  V is first staged in LDS with
+// coalesced 16-byte reads, then read back transposed.
+constexpr int kWTok = 16;        // tokens per workgroup
+constexpr int kWGrp = 32;        // 16-byte groups per workgroup
+constexpr int kWRow = kWGrp * 16 + 16;   // LDS bytes per token row (16 bytes of padding)
+
 template <typename E>
 __global__ __launch_bounds__(256) void write_kv_vllm_kernel(
     u32x4* __restrict__ k_cache, E* __restrict__ v_cache,
-    const u32x4* __restrict__ k, const E* __restrict__ v,
-    const int64_t* __restrict__ slots, uint32_t total_groups, uint32_t row_groups,
+    const u32x4* __restrict__ k, const u32x4* __restrict__ v,
+    const int64_t* __restrict__ slots, uint32_t num_tokens, uint32_t row_groups,
     int32_t bs_log2, int64_t num_slots) {
   constexpr uint32_t X = 16 / sizeof(E);
-  const uint32_t idx = blockIdx.x * 256u + threadIdx.x;
-  if (idx >= total_groups) return;
-  const uint32_t tok = idx / row_groups;
-  const uint32_t rem = idx - tok * row_groups;     // kv head * (D / x) + group
-  const int64_t s = slots[tok];
-  if (s < 0 || s >= num_slots) return;
-  const size_t blk = (size_t)(s >> bs_log2);
-  const size_t off = (size_t)(s & ((1 << bs_log2) - 1));
-  const size_t col = (blk * row_groups + rem) << bs_log2;   // (block, head, group) row of bs columns
-  k_cache[col + off] = k[idx];
-  const E* src = v + (size_t)idx * X;
+  __shared__ __attribute__((aligned(16))) unsigned char tile[kWTok * kWRow];
+  const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint32_t t0 = blockIdx.x * kWTok;
+  const uint32_t g0 = blockIdx.y * kWGrp;
+
+  // Stage V: 16 rows of up to 32 groups, 32 consecutive threads per token row.
 #pragma unroll
-  for (uint32_t e = 0; e < X; ++e) v_cache[((col * X) + ((size_t)e << bs_log2)) + off] = src[e];
+  for (uint32_t j = 0; j < kWTok * kWGrp / 256; ++j) {
+    const uint32_t idx = tid + 256u * j, i = idx / kWGrp, q = idx % kWGrp;
+    u32x4 val = {0u, 0u, 0u, 0u};
+    if (t0 + i < num_tokens && g0 + q < row_groups)
+      val = __builtin_nontemporal_load(&v[(size_t)(t0 + i) * row_groups + g0 + q]);
+    *reinterpret_cast<u32x4*>(tile + i * kWRow + q * 16) = val;
+  }
+
+  // This lane's token: slot, block and offset (invalid slots and tokens past
+  // the end store nothing).
+  const uint32_t i = lane & (kWTok - 1);
+  const int64_t s = (t0 + i < num_tokens) ? slots[t0 + i] : -1;
+  const bool live = s >= 0 && s < num_slots;
+  const size_t blk = live ? (size_t)(s >> bs_log2) : 0;
+  const size_t off = live ? (size_t)(s & ((1 << bs_log2) - 1)) : 0;
+
+  // K: lane (token i, group q); one 16-byte load and store per group.
+#pragma unroll
+  for (uint32_t j = 0; j < kWGrp / 16; ++j) {
+    const uint32_t q = (lane >> 4) + 4u * wave + 16u * j;
+    if (live && g0 + q < row_groups) {
+      const u32x4 kv = __builtin_nontemporal_load(&k[(size_t)(t0 + i) * row_groups + g0 + q]);
+      k_cache[((blk * row_groups + g0 + q) << bs_log2) + off] = kv;
+    }
+  }
+  __syncthreads();
+
+  // V: lane (token i, element e of the slice); four adjacent rows per wave
+  // store.  The padded LDS row stride puts the 16 tokens on distinct banks.
+  const uint32_t elems = min((uint32_t)kWGrp, row_groups - g0) * X;
+  const size_t row0 = (size_t)g0 * X;
+  const size_t rows = (size_t)row_groups * X;
+  const E* trow = reinterpret_cast<const E*>(tile + i * kWRow);
+#pragma unroll 4
+  for (uint32_t e = (lane >> 4) + 4u * wave; e < kWGrp * X; e += 16u) {
+    if (live && e < elems) v_cache[((blk * rows + row0 + e) << bs_log2) + off] = trow[e];
+  }
 }
 
 hipError_t launch_write_kv_vllm(void* k_cache, void* v_cache, const void* k, const void* v,
                                 const int64_t* slots, int32_t T, int32_t row_bytes, int32_t elem_bytes,
                                 int32_t bs_log2, int64_t num_slots, hipStream_t stream) {
   const uint32_t row_groups = (uint32_t)row_bytes / 16u;
-  const uint64_t total = (uint64_t)T * row_groups;
-  if (total == 0) return hipSuccess;
-  const uint32_t grid = (uint32_t)((total + 255u) / 256u);
+  if (T <= 0 || row_groups == 0) return hipSuccess;
+  const dim3 grid((uint32_t)((T + kWTok - 1) / kWTok), (row_groups + kWGrp - 1) / kWGrp);
   if (elem_bytes == 2)
-    hipLaunchKernelGGL(write_kv_vllm_kernel<uint16_t>, dim3(grid), dim3(256), 0, stream,
+    hipLaunchKernelGGL(write_kv_vllm_kernel<uint16_t>, grid, dim3(256), 0, stream,
                        static_cast<u32x4*>(k_cache), static_cast<uint16_t*>(v_cache),
-                       static_cast<const u32x4*>(k), static_cast<const uint16_t*>(v), slots,
-                       (uint32_t)total, row_groups, bs_log2, num_slots);
+                       static_cast<const u32x4*>(k), static_cast<const u32x4*>(v), slots,
+                       (uint32_t)T, row_groups, bs_log2, num_slots);
   else
-    hipLaunchKernelGGL(write_kv_vllm_kernel<uint32_t>, dim3(grid), dim3(256), 0, stream,
+    hipLaunchKernelGGL(write_kv_vllm_kernel<uint32_t>, grid, dim3(256), 0, stream,
                        static_cast<u32x4*>(k_cache), static_cast<uint32_t*>(v_cache),
-                       static_cast<const u32x4*>(k), static_cast<const uint32_t*>(v), slots,
-                       (uint32_t)total, row_groups, bs_log2, num_slots);
+                       static_cast<const u32x4*>(k), static_cast<const u32x4*>(v), slots,
+                       (uint32_t)T, row_groups, bs_log2, num_slots);
   return hipGetLastError();
 }
 

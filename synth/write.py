@@ -18,7 +18,7 @@ import torch
 
 from .workloads import torch_dtype
 
-__all__ = ["WriteConfig", "WRITE_CONFIGS", "WriteWorkload", "make_write"]
+__all__ = ["WriteConfig", "WRITE_CONFIGS", "WriteWorkload", "make_write", "make_write_chunks"]
 
 
 @dataclass(frozen=True)
@@ -93,5 +93,47 @@ def make_write(cfg: WriteConfig, device="cpu", *, num_prompts: int | None = None
     rnd = lambda *s: torch.randn(s, generator=gv, device=device, dtype=torch.float32).to(dt)
     k_cache, v_cache = rnd(NB, bs, KVH, D), rnd(NB, bs, KVH, D)
     k_new, v_new = rnd(T, KVH, D), rnd(T, KVH, D)
+    return WriteWorkload(cfg=cfg, k_cache=k_cache, v_cache=v_cache, k_new=k_new, v_new=v_new,
+                         slot_mapping=slots.to(device), valid_tokens=valid)
+
+
+def make_write_chunks(*, num_kv_heads: int, head_dim: int, block_size: int, dtype: str, cached, new,
+                      pad_tokens: int = 0, seed: int = 0, device="cpu") -> WriteWorkload:
+    """Chunked-prefill writes: sequence i already holds cached[i] tokens and
+    writes new[i] more, so its run of slots starts at offset cached[i] % bs of
+    a block and crosses block boundaries wherever the chunk does.  Blocks come
+    from one shuffled pool (10% spare); ``pad_tokens`` slots of -1 are spread
+    through the batch."""
+    device = torch.device(device)
+    bs, KVH, D = block_size, num_kv_heads, head_dim
+    gm = torch.Generator().manual_seed(7000 + seed)
+    gv = torch.Generator(device=device).manual_seed(8000 + seed)
+    per = [-(-(c + n) // bs) for c, n in zip(cached, new)]
+    live = sum(per)
+    NB = live + max(1, int(math.ceil(live * 0.10)))
+    perm = torch.randperm(NB, generator=gm)[:live]
+    runs, at = [], 0
+    for c, n, m in zip(cached, new, per):
+        table = perm[at:at + m]
+        at += m
+        pos = torch.arange(c, c + n)
+        runs.append(table[pos // bs] * bs + pos % bs)
+    slots = torch.cat(runs) if runs else torch.empty(0, dtype=torch.int64)
+    valid = slots.numel()
+    if pad_tokens:
+        T = valid + pad_tokens
+        where = torch.randperm(T, generator=gm)[:pad_tokens]
+        mask = torch.ones(T, dtype=torch.bool)
+        mask[where] = False
+        full = torch.full((T,), -1, dtype=torch.int64)
+        full[mask] = slots
+        slots = full
+    T = slots.numel()
+    dt = torch_dtype(dtype)
+    rnd = lambda *s: torch.randn(s, generator=gv, device=device, dtype=torch.float32).to(dt)
+    k_cache, v_cache = rnd(NB, bs, KVH, D), rnd(NB, bs, KVH, D)
+    k_new, v_new = rnd(T, KVH, D), rnd(T, KVH, D)
+    cfg = WriteConfig(name="chunks", dtype=dtype, num_prompts=len(new), prompt_len=max(new, default=0),
+                      num_kv_heads=KVH, head_dim=D, block_size=bs, pad_tokens=pad_tokens, seed=seed)
     return WriteWorkload(cfg=cfg, k_cache=k_cache, v_cache=v_cache, k_new=k_new, v_new=v_new,
                          slot_mapping=slots.to(device), valid_tokens=valid)
