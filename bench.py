@@ -448,6 +448,10 @@ def run_write(args, cfg):
     torch.cuda.set_device(dev)
     w = make_write(cfg, dev)
     kc, vc = w.k_cache, w.v_cache
+    vllm = args.layout == "vllm"
+    if vllm:
+        from synth import to_vllm_layout
+        kc, vc = to_vllm_layout(kc, vc)
     flush = None if args.hot else torch.ones(1 << 28, dtype=torch.float32, device=dev)
     flush_sink = torch.zeros((), dtype=torch.float32, device=dev)
 
@@ -495,7 +499,7 @@ def run_write(args, cfg):
         "config": {
             "workload": cfg.name, "tokens": T, "valid_tokens": w.valid_tokens, "num_kv_heads": cfg.num_kv_heads,
             "head_dim": cfg.head_dim, "block_size": cfg.block_size, "num_blocks": kc.shape[0],
-            "cache_flush_between_steps": flush is not None,
+            "cache_layout": args.layout, "cache_flush_between_steps": flush is not None,
         },
         "bytes_per_step": nbytes,
         "write_us": round(us, 2),
@@ -509,8 +513,8 @@ def run_write(args, cfg):
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(gbps / HBM_PEAK_GBPS, 4),
-            "traffic": _traffic(cfg.name, "write"),
-            "kernel": "write_kv_kernel",
+            "traffic": None if vllm else _traffic(cfg.name, "write"),
+            "kernel": "write_kv_vllm_kernel" if vllm else "write_kv_kernel",
         },
     }
     if not args.no_cpu_baseline:
@@ -528,7 +532,7 @@ def main():
     ap.add_argument("--hot", action="store_true", help="do not flush the last-level cache between steps")
     ap.add_argument("--layout", choices=["p09", "vllm"], default="p09",
                     help="cache layout: P09's [NB, bs, KVH, D] (default) or vLLM's packed K [NB, KVH, D/x, bs, x] "
-                         "with V [NB, KVH, D, bs] (bf16 decode and prefill configs)")
+                         "with V [NB, KVH, D, bs] (bf16 decode, prefill and write configs)")
     ap.add_argument("--shared-tokens", type=int, default=-1,
                     help="decode with pa_decode_shared_prefix and this hint (default: the workload's common "
                          "prefix for prefix_shared_bf16, else 0 = pa_decode)")
