@@ -265,10 +265,12 @@ size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t m
  *   kvh = h / (H / KVH); fp32 scores and softmax, out rounded to bf16.
  * With L_b = 1 for every b this is pa_decode.
  *
- *   out               device, [num_tokens, H, D] bf16 (written; rows of no
- *                     sequence are left untouched)
- *   q                 device, [num_tokens, H, D] bf16
- *   k_cache, v_cache  device, [NB, bs, KVH, D] bf16
+ *   out               device, [num_tokens, H, D] in the cache dtype (written;
+ *                     rows of no sequence are left untouched)
+ *   q                 device, [num_tokens, H, D] in the cache dtype
+ *   k_cache, v_cache  device, [NB, bs, KVH, D] (PA_LAYOUT_P09), or for bf16
+ *                     in PA_LAYOUT_VLLM K [NB, KVH, D/8, bs, 8] and
+ *                     V [NB, KVH, D, bs]
  *   block_tables      device, [B, max_blocks_per_seq] int32; row b's first
  *                     ceil(n_b / bs) entries are read
  *   context_lens      device, [B] int32, n_b (new tokens included)
