@@ -79,7 +79,7 @@ typedef enum pa_layout {
      k_cache [num_blocks, num_kv_heads, head_dim / x, block_size, x] with x
      elements = 16 bytes (8 for bf16, 4 for fp32), v_cache [num_blocks,
      num_kv_heads, head_dim, block_size].  Supported by pa_write_kv (both
-     dtypes) and the decode entry points (bf16 only). */
+     dtypes), the decode entry points and pa_prefill (bf16 only). */
   PA_LAYOUT_VLLM = 1
 } pa_layout;
 
@@ -108,6 +108,13 @@ typedef struct pa_cache_desc {
  *   num_tokens        T >= 0; T == 0 enqueues nothing and returns PA_OK
  *   desc              host, cache geometry
  *   stream            hipStream_t
+ * Returns PA_OK once the kernel is enqueued (asynchronous: nothing waits for
+ * it), or PA_ERR_NULL / PA_ERR_SHAPE / PA_ERR_UNSUPPORTED / PA_ERR_ALIGN,
+ * PA_ERR_TOO_LARGE when T * KVH * D * elem / 16 exceeds 32 bits (or, in
+ * PA_LAYOUT_VLLM, a row holds more than 65535 * 32 sixteen-byte groups), and
+ * PA_ERR_LAUNCH.  Slots at or past num_blocks * bs are skipped like padding;
+ * valid slots must be distinct: two tokens with the same slot leave an
+ * unspecified mix of their rows, 16 bytes at a time.
  */
 int pa_write_kv(void* k_cache, void* v_cache, const void* k, const void* v,
                 const int64_t* slot_mapping, int32_t num_tokens,
