@@ -114,7 +114,7 @@ typedef struct pa_cache_desc {
  * PA_LAYOUT_VLLM, a row holds more than 65535 * 32 sixteen-byte groups), and
  * PA_ERR_LAUNCH.  Slots at or past num_blocks * bs are skipped like padding;
  * valid slots must be distinct: two tokens with the same slot leave an
- * unspecified mix of their rows, 16 bytes at a time.
+ * unspecified mix of their rows.
  */
 int pa_write_kv(void* k_cache, void* v_cache, const void* k, const void* v,
                 const int64_t* slot_mapping, int32_t num_tokens,
