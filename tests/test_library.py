@@ -70,6 +70,20 @@ def test_argument_checks_without_launch():
     assert lib.pa_decode(*a) == -5
 
 
+def test_write_size_limits_without_launch():
+    """Sizes past the write kernels' 32-bit grid limits are refused before
+    anything is enqueued (16-byte-aligned stand-in pointers, never read)."""
+    lib = pk.load_library()
+    fake = ctypes.c_void_p(0x1000)
+    ptrs = (fake,) * 5
+    # P09: T * (row bytes / 16) beyond 32 bits
+    big_t = _desc(num_kv_heads=8, head_dim=128)
+    assert lib.pa_write_kv(*ptrs, 2**31 - 1, ctypes.byref(big_t), None) == -7
+    # vLLM layout: one token, but a row of more than 65535 * 32 sixteen-byte groups
+    wide = _desc(num_kv_heads=70000, head_dim=256, layout=1)
+    assert lib.pa_write_kv(*ptrs, 1, ctypes.byref(wide), None) == -7
+
+
 def test_workspace_and_partition_queries():
     lib = pk.load_library()
     d = _desc()
