@@ -381,12 +381,50 @@ int pa_bm_fill_tables(const pa_block_manager* bm, const int64_t* seq_ids, int32_
                       int32_t max_blocks_per_seq, int32_t fill, int32_t* block_tables,
                       int32_t* context_lens);
 
+/*
+ * pa_decode_append — one decode step that appends each sequence's new token:
+ * the same result as pa_write_kv of the new rows followed by pa_decode, in two
+ * kernels instead of three.  The write and gather steps of "P09 · Paged KV 写入
+ * + decode attention" (题面速览, decode shape trace) and the partition merge of
+ * "PagedAttention kernel：paged KV cache 与 block table" (深入原理, v2).
+ *
+ * Sequence b owns one new token (its K/V rows k_new[b], v_new[b]) unless
+ * slot_mapping[b] < 0 or >= num_blocks * bs.  It attends to its cached_lens[b]
+ * cached tokens, gathered through block_tables as in pa_decode, plus the new
+ * token. The output equals pa_decode with context_lens[b] = cached_lens[b] + 1
+ * after the new token was written at slot_mapping[b], which must be the slot
+ * of position cached_lens[b] in b's table.  The partial kernel reads only the
+ * cached tokens; the merge kernel reads the new token from k_new / v_new, folds
+ * it into the softmax and copies its rows, bit for bit, into the slot.
+ *
+ *   out, q            device, [num_seqs, H, D] of desc->dtype
+ *   k_cache, v_cache  device, desc->layout (PA_LAYOUT_VLLM: bf16 only); the new
+ *                     rows are written into them
+ *   k_new, v_new      device, [num_seqs, KVH, D] of desc->dtype
+ *   slot_mapping      device, [num_seqs] int64
+ *   cached_lens       device, [num_seqs] int32, tokens already in the cache
+ *                     (clamped to [0, max_blocks_per_seq * bs])
+ *   workspace         device, >= pa_decode_append_workspace_bytes(...) bytes
+ *   others            as for pa_decode
+ * Returns as pa_decode (PA_ERR_WORKSPACE when the workspace is missing or
+ * short).  Valid slots must be distinct.  Calls sharing a workspace must not
+ * run concurrently.
+ */
+size_t pa_decode_append_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t max_blocks_per_seq,
+                                        const pa_cache_desc* desc, int32_t partition_size);
+int pa_decode_append(void* out, const void* q, void* k_cache, void* v_cache, const void* k_new,
+                     const void* v_new, const int64_t* slot_mapping, const int32_t* block_tables,
+                     const int32_t* cached_lens, float scale, int32_t num_seqs, int32_t num_heads,
+                     int32_t max_blocks_per_seq, const pa_cache_desc* desc, int32_t partition_size,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static, NUL-terminated name of a pa_status code ("unknown status" otherwise). */
 const char* pa_status_string(int status);
 
 /* ABI version of this header: (major << 16) | minor (2.0: pa_cache_desc.layout;
  * 2.1: fp32 prefill, pa_prefill_workspace_bytes takes max_blocks_per_seq;
- * 2.2: pa_decode_shared_prefix, pa_decode_partials_shared_prefix). */
+ * 2.2: pa_decode_shared_prefix, pa_decode_partials_shared_prefix;
+ * 2.3: pa_decode_append, pa_decode_append_workspace_bytes). */
 int32_t pa_abi_version(void);
 
 #ifdef __cplusplus

@@ -10,12 +10,14 @@ from .api import (  # noqa: F401
     abi_version,
     cache_desc,
     decode,
+    decode_append,
     decode_merge,
     decode_partials_shared_prefix,
     decode_shared_prefix,
     decode_partials,
     library_path,
     load_library,
+    new_append_workspace,
     new_workspace,
     partition_size,
     prefill,

@@ -33,6 +33,8 @@ __all__ = [
     "decode_merge",
     "decode_shared_prefix",
     "decode_partials_shared_prefix",
+    "decode_append",
+    "new_append_workspace",
     "prefill",
     "prefill_workspace",
     "partition_size",
@@ -95,6 +97,9 @@ def load_library() -> ctypes.CDLL:
                                                              pdesc, i32, vp, sz, vp]),
         "pa_prefill": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, vp, f32, i32, i32, i32, i32, pdesc, vp, sz, vp]),
         "pa_prefill_workspace_bytes": (sz, [i32, i32, i32, i32, pdesc]),
+        "pa_decode_append_workspace_bytes": (sz, [i32, i32, i32, pdesc, i32]),
+        "pa_decode_append": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, vp, vp, vp, f32, i32, i32, i32, pdesc, i32,
+                                            vp, sz, vp]),
         "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "pa_abi_version": (i32, []),
     }
@@ -273,6 +278,47 @@ def decode_partials_shared_prefix(q, k_cache, v_cache, block_tables, context_len
                                   out, workspace, partition_size: int = 0) -> torch.Tensor:
     return _decode_call("pa_decode_partials_shared_prefix", q, k_cache, v_cache, block_tables, context_lens,
                         scale, out, workspace, partition_size, shared_tokens)
+
+
+def new_append_workspace(num_seqs: int, num_heads: int, max_blocks_per_seq: int, k_cache: torch.Tensor,
+                         partition_size: int = 0) -> torch.Tensor:
+    """A workspace of the size pa_decode_append_workspace_bytes() gives."""
+    desc = cache_desc(k_cache)
+    need = load_library().pa_decode_append_workspace_bytes(num_seqs, num_heads, max_blocks_per_seq,
+                                                           ctypes.byref(desc), int(partition_size))
+    if need == 0:
+        raise ValueError("unsupported decode sizes")
+    return torch.empty(need, dtype=torch.uint8, device=k_cache.device)
+
+
+def decode_append(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, k_new: torch.Tensor,
+                  v_new: torch.Tensor, slot_mapping: torch.Tensor, block_tables: torch.Tensor,
+                  cached_lens: torch.Tensor, scale: float, *, out: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None, partition_size: int = 0) -> torch.Tensor:
+    """One decode step that appends sequence b's new token (k_new[b], v_new[b]
+    at slot_mapping[b], none where the slot is negative): the output of
+    write_kv followed by decode with context_lens = cached_lens + 1, and the
+    same cache contents, from two kernels."""
+    lib = load_library()
+    if workspace is None and q.dim() == 3 and block_tables.dim() == 2:
+        workspace = new_append_workspace(q.shape[0], q.shape[1], block_tables.shape[1], k_cache, partition_size)
+    desc, B, H, W, out, workspace, wbytes = _decode_args(q, k_cache, v_cache, block_tables, cached_lens, out,
+                                                         workspace, partition_size)
+    row = (desc.num_kv_heads, desc.head_dim)
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        if tuple(t.shape) != (B, *row) or t.dtype != k_cache.dtype:
+            raise ValueError(f"{name} must be [{B}, {row[0]}, {row[1]}] of {k_cache.dtype}")
+    if tuple(slot_mapping.shape) != (B,):
+        raise ValueError("slot_mapping must be [num_seqs]")
+    st = lib.pa_decode_append(_dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                              _dev(k_new, "k_new"), _dev(v_new, "v_new"),
+                              _dev(slot_mapping, "slot_mapping", torch.int64),
+                              _dev(block_tables, "block_tables", torch.int32),
+                              _dev(cached_lens, "cached_lens", torch.int32), float(scale), B, H, W,
+                              ctypes.byref(desc), int(partition_size), _dev(workspace, "workspace"), wbytes,
+                              _stream(q))
+    _check("pa_decode_append", st)
+    return out
 
 
 def decode_merge(q_like: torch.Tensor, k_cache: torch.Tensor, block_tables: torch.Tensor,

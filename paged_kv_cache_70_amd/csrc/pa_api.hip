@@ -200,6 +200,7 @@ static int decode_params(void* out, const void* q, const void* k_cache, const vo
   p.SP = 0;
   p.SG = 0;
   p.SPB = 0;
+  p.append = 0;
   return PA_OK;
 }
 
@@ -237,7 +238,7 @@ using namespace pa;
 
 extern "C" {
 
-int32_t pa_abi_version(void) { return (2 << 16) | 2; }
+int32_t pa_abi_version(void) { return (2 << 16) | 3; }
 
 const char* pa_status_string(int status) {
   switch (status) {
@@ -293,6 +294,48 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t ma
   if (check_decode_sizes(num_seqs, num_heads, max_blocks_per_seq, desc, partition_size, &ck))
     return 0;
   return ck.ws_bytes;
+}
+
+size_t pa_decode_append_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t max_blocks_per_seq,
+                                        const pa_cache_desc* desc, int32_t partition_size) {
+  Checked ck;
+  if (check_decode_sizes(num_seqs, num_heads, max_blocks_per_seq, desc, partition_size, &ck)) return 0;
+  // every sequence stores its partials, so one partition per (b, h) at least
+  return (size_t)num_seqs * num_heads * ck.plan.maxP * ((size_t)desc->head_dim + 2) * sizeof(float);
+}
+
+int pa_decode_append(void* out, const void* q, void* k_cache, void* v_cache, const void* k_new,
+                     const void* v_new, const int64_t* slot_mapping, const int32_t* block_tables,
+                     const int32_t* cached_lens, float scale, int32_t num_seqs, int32_t num_heads,
+                     int32_t max_blocks_per_seq, const pa_cache_desc* desc, int32_t partition_size,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  Checked ck;
+  int st = check_decode_sizes(num_seqs, num_heads, max_blocks_per_seq, desc, partition_size, &ck);
+  if (st) return st;
+  if (!q || !k_cache || !v_cache || !k_new || !v_new || !slot_mapping || !block_tables) return PA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_new) || !aligned16(v_new))
+    return PA_ERR_ALIGN;
+  ck.ws_bytes = pa_decode_append_workspace_bytes(num_seqs, num_heads, max_blocks_per_seq, desc, partition_size);
+  DecodeParams prm;
+  st = decode_params(out, q, k_cache, v_cache, block_tables, cached_lens, scale, num_seqs, num_heads,
+                     max_blocks_per_seq, desc, workspace, workspace_bytes, ck, &prm);
+  if (st) return st;
+  prm.append = 1;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = desc->layout == PA_LAYOUT_VLLM
+                           ? launch_decode_partials_vllm(prm, desc->head_dim, s)
+                           : ck.plan.use_mfma ? launch_decode_partials_mfma(prm, desc->head_dim, s)
+                                              : launch_decode_partials(prm, desc->dtype, desc->head_dim, ck.plan, s);
+  if (e != hipSuccess) return PA_ERR_LAUNCH;
+  AppendArgs ap;
+  ap.k_new = k_new;
+  ap.v_new = v_new;
+  ap.slots = slot_mapping;
+  ap.k_cache = k_cache;
+  ap.v_cache = v_cache;
+  ap.num_slots = (int64_t)desc->num_blocks * desc->block_size;
+  ap.vllm = desc->layout == PA_LAYOUT_VLLM;
+  return launch_decode_merge_append(prm, ap, desc->dtype, desc->head_dim, s) == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
 static int decode_common(bool partials, bool merge, void* out, const void* q,

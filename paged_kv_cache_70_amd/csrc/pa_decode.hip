@@ -443,7 +443,7 @@ __global__ __launch_bounds__(64 * NW) void decode_partial_kernel(const DecodePar
     }
   }
 
-  const bool single = nparts <= 1;
+  const bool single = nparts <= 1 && !prm.append;
   if (tr == 0) {
 #pragma unroll
     for (int g = 0; g < GC; ++g) {
@@ -555,6 +555,154 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const DecodeParams prm
 }
 
 // ---------------------------------------------------------------------------
+// K3 for the append step: the merge also folds in each sequence's new token,
+// read from k_new / v_new rather than the cache, and writes that token's rows
+// into its slot.  The partial kernel of the same step read only the tokens
+// already cached (context_lens counts them), so no kernel of the step reads a
+// row written in it.  The new token is one more term of the softmax: score
+// s = q . k_new in the partials' base-2 units, weight 2^(s - M), value v_new.
+// ---------------------------------------------------------------------------
+template <typename E>
+__device__ __forceinline__ void load4(const void* base, size_t idx, float (&f)[4]) {
+  if constexpr (E::EPV == 8) {
+    const uint2 w = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(base) + idx);
+    f[0] = __uint_as_float(w.x << 16);
+    f[1] = __uint_as_float(w.x & 0xffff0000u);
+    f[2] = __uint_as_float(w.y << 16);
+    f[3] = __uint_as_float(w.y & 0xffff0000u);
+  } else {
+    const float4 v = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + idx);
+    f[0] = v.x;
+    f[1] = v.y;
+    f[2] = v.z;
+    f[3] = v.w;
+  }
+}
+
+template <typename E, int D, bool Vllm>
+__global__ __launch_bounds__(64) void decode_merge_append_kernel(const DecodeParams prm, const AppendArgs ap) {
+  // Lane layout as in decode_merge_kernel: lane (sub, dl) holds d = dl .. dl + 3
+  // of partition rows sub, sub + PPI, ...
+  constexpr int LPP = D / 4;
+  constexpr int PPI = 64 / LPP;
+  constexpr int KMAX = PPI * 16 <= 64 ? 16 : 64 / PPI;
+  constexpr int R = PPI * KMAX;
+  typedef float f4 __attribute__((ext_vector_type(4)));
+  const int h = blockIdx.x;
+  const int b = blockIdx.y;
+  const int lane = threadIdx.x;
+  const int sub = lane / LPP;
+  const int dl = (lane % LPP) * 4;
+  const size_t bh = (size_t)b * prm.H + h;
+  const int kvh = h / (prm.H / prm.KVH);
+  int n = prm.ctx[b];
+  n = n < 0 ? 0 : (n > prm.max_tokens ? prm.max_tokens : n);
+  const int nparts = max(1, (n + prm.P - 1) / prm.P);   // the partial kernel stored all of them
+  const int64_t slot = ap.slots[b];
+  const bool has_new = slot >= 0 && slot < ap.num_slots;
+  const float* ml = prm.ws_ml + bh * prm.maxP * 2;
+  const float* acc = prm.ws_acc + bh * prm.maxP * D;
+
+  float Mrun = -INFINITY, Lrun = 0.0f;
+  f4 o = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int r0 = 0; r0 < nparts; r0 += R) {
+    const int cnt = min(R, nparts - r0);
+    f4 a[KMAX];
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+      const int i = sub + PPI * k;
+      a[k] = i < cnt ? *reinterpret_cast<const f4*>(acc + (size_t)(r0 + i) * D + dl) : f4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    const float2 mlv = lane < cnt ? *reinterpret_cast<const float2*>(ml + (size_t)(r0 + lane) * 2)
+                                  : make_float2(-INFINITY, 0.0f);
+    const float M = fmaxf(Mrun, wave_max(mlv.x));
+    const float w = mlv.x == -INFINITY ? 0.0f : exp2_fast(mlv.x - M);
+    const float fo = Mrun == -INFINITY ? 0.0f : exp2_fast(Mrun - M);
+    Lrun = Lrun * fo + wave_sum(w * mlv.y);
+    o *= fo;
+    Mrun = M;
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) o += __shfl(w, sub + PPI * k) * a[k];
+  }
+
+  const size_t row = ((size_t)b * prm.KVH + kvh) * D + dl;   // this lane's d's of k_new / v_new
+  if (has_new) {
+    float qf[4], kf[4], vf[4];
+    load4<E>(prm.q, bh * D + dl, qf);
+    load4<E>(ap.k_new, row, kf);
+    load4<E>(ap.v_new, row, vf);
+    float dot = qf[0] * kf[0] + qf[1] * kf[1] + qf[2] * kf[2] + qf[3] * kf[3];
+#pragma unroll
+    for (int off = 1; off < LPP; off <<= 1) dot += __shfl_xor(dot, off);
+    // the partials' scores are (+-q or 0) . k times |scale| log2(e)
+    const float sc = prm.q_mode == 2 ? 0.0f : (prm.q_mode == 1 ? -dot : dot) * prm.scale_log2;
+    const float M = fmaxf(Mrun, sc);
+    const float fo = Mrun == -INFINITY ? 0.0f : exp2_fast(Mrun - M);
+    const float fn = exp2_fast(sc - M);
+    Lrun = Lrun * fo + fn;
+    o *= fo;
+    if (sub == 0) o += fn * f4{vf[0], vf[1], vf[2], vf[3]};
+    Mrun = M;
+  }
+#pragma unroll
+  for (int off = LPP; off < 64; off <<= 1) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] += __shfl_xor(o[e], off);
+  }
+  if (sub == 0) {
+    const float inv = Lrun > 0.0f ? 1.0f / Lrun : 0.0f;
+    float v[E::EPV];
+    if constexpr (E::EPV == 4) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = o[e] * inv;
+      E::store(prm.out, bh * D + dl, v);
+    } else {
+      float w4[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w4[e] = __shfl_down(o[e], 1) * inv;
+      if ((lane & 1) == 0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { v[e] = o[e] * inv; v[4 + e] = w4[e]; }
+        E::store(prm.out, bh * D + dl, v);
+      }
+    }
+  }
+
+  // The new token's K and V rows of this kv head, copied bit for bit into
+  // its slot by the kv head's first query head.
+  if (has_new && sub == 0 && h % (prm.H / prm.KVH) == 0) {
+    const size_t blk = (size_t)(slot >> prm.bs_log2);
+    const size_t off = (size_t)(slot & prm.bs_mask);
+    const size_t bs = (size_t)1 << prm.bs_log2;
+    if constexpr (Vllm) {
+      // K [NB, KVH, D/8, bs, 8]: d .. d + 3 lie in one 8-element group
+      const size_t kb = (blk * prm.KVH + kvh) * D;   // element base of the (block, head) K and V blocks
+      const uint2 kw = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(ap.k_new) + row);
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(ap.k_cache) + kb * bs + (size_t)(dl >> 3) * bs * 8 +
+                                off * 8 + (dl & 7)) = kw;
+      // V [NB, KVH, D, bs]: element d at column off of row d
+      const uint16_t* vs = static_cast<const uint16_t*>(ap.v_new) + row;
+      uint16_t* vd = static_cast<uint16_t*>(ap.v_cache) + (kb + dl) * bs + off;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) vd[(size_t)e * bs] = vs[e];
+    } else {
+      const size_t dst = (size_t)slot * prm.KVH * D + (size_t)kvh * D + dl;
+      if constexpr (E::EPV == 8) {
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(ap.k_cache) + dst) =
+            *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(ap.k_new) + row);
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(ap.v_cache) + dst) =
+            *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(ap.v_new) + row);
+      } else {
+        *reinterpret_cast<uint4*>(static_cast<uint32_t*>(ap.k_cache) + dst) =
+            *reinterpret_cast<const uint4*>(static_cast<const uint32_t*>(ap.k_new) + row);
+        *reinterpret_cast<uint4*>(static_cast<uint32_t*>(ap.v_cache) + dst) =
+            *reinterpret_cast<const uint4*>(static_cast<const uint32_t*>(ap.v_new) + row);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 template <typename E, int D, int GC, int U, int KG, int NW>
@@ -654,6 +802,26 @@ static hipError_t launch_merge_e(const DecodeParams& prm, int32_t D, hipStream_t
 hipError_t launch_decode_merge(const DecodeParams& prm, int32_t dtype, int32_t D,
                                hipStream_t stream) {
   return dtype == 0 ? launch_merge_e<F32>(prm, D, stream) : launch_merge_e<BF16>(prm, D, stream);
+}
+
+template <typename E, bool Vllm>
+static hipError_t launch_merge_append_e(const DecodeParams& prm, const AppendArgs& ap, int32_t D,
+                                        hipStream_t stream) {
+  const dim3 grid(prm.H, prm.B);
+  switch (D) {
+    case 64: hipLaunchKernelGGL((decode_merge_append_kernel<E, 64, Vllm>), grid, dim3(64), 0, stream, prm, ap); break;
+    case 128: hipLaunchKernelGGL((decode_merge_append_kernel<E, 128, Vllm>), grid, dim3(64), 0, stream, prm, ap); break;
+    case 256: hipLaunchKernelGGL((decode_merge_append_kernel<E, 256, Vllm>), grid, dim3(64), 0, stream, prm, ap); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_merge_append(const DecodeParams& prm, const AppendArgs& ap, int32_t dtype, int32_t D,
+                                      hipStream_t stream) {
+  if (dtype == 0) return ap.vllm ? hipErrorInvalidValue : launch_merge_append_e<F32, false>(prm, ap, D, stream);
+  return ap.vllm ? launch_merge_append_e<BF16, true>(prm, ap, D, stream)
+                 : launch_merge_append_e<BF16, false>(prm, ap, D, stream);
 }
 
 }  // namespace pa

@@ -222,8 +222,9 @@ __device__ __forceinline__ void fold_tile(uint32_t ok, const u32x4m (&kr)[Geo<D>
   }
 }
 
-// Writes a finished unit: the final bf16 output of a one-partition sequence,
-// else the fp32 partial (acc, m, l) of partition p for the merge kernel.
+// Writes a finished unit: the final bf16 output of a one-partition sequence
+// (outside the append step), else the fp32 partial (acc, m, l) of partition p
+// for the merge kernel.
 template <int D, bool Shared = false>
 __device__ __forceinline__ void store_unit(const DecodeParams& prm, const Unit& u, int lane, const Fold<D>& st,
                                            const int32_t* jn) {
@@ -235,7 +236,7 @@ __device__ __forceinline__ void store_unit(const DecodeParams& prm, const Unit& 
   const size_t bh = (size_t)c.b * prm.H + c.h;
   // (structured branches only: an early return under the per-lane head_ok
   // would make the compiler treat the caller's later state as divergent)
-  if (u.np <= 1) {
+  if (u.np <= 1 && !prm.append) {
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
     uint16_t* outp = static_cast<uint16_t*>(prm.out) + bh * D;
     if (head_ok) {

@@ -32,6 +32,21 @@ struct DecodeParams {
   // and whose context extends past them are folded SG sequences per unit
   // (their G heads side by side as the product's 16 columns).
   int32_t SP, SG, SPB;
+  // Append step: every unit stores its (acc, m, l) partial, a sequence's only
+  // partition included, for the merge that folds in the new token.
+  int32_t append;
+};
+
+// The append step's new token per sequence (row b of k_new / v_new is
+// sequence b's), written into the caches by the merge that folds it in.
+struct AppendArgs {
+  const void* k_new;         // [B, KVH, D]
+  const void* v_new;
+  const int64_t* slots;      // [B]; negative or >= num_slots: no new token
+  void* k_cache;             // the caches, in the layout below
+  void* v_cache;
+  int64_t num_slots;         // NB * bs
+  int32_t vllm;              // 0: [NB, bs, KVH, D]; 1: vLLM's K and V blocks
 };
 
 // Launch-shape choices made on the host (pure functions of the sizes).
@@ -104,5 +119,7 @@ hipError_t launch_prefill_rows(const int32_t* qstart, const int32_t* ctx, int32_
 
 hipError_t launch_decode_merge(const DecodeParams& prm, int32_t dtype, int32_t D,
                                hipStream_t stream);
+hipError_t launch_decode_merge_append(const DecodeParams& prm, const AppendArgs& ap, int32_t dtype, int32_t D,
+                                      hipStream_t stream);
 
 }  // namespace pa
