@@ -13,10 +13,13 @@ of the previous step.  The flush reads rather than writes: a written buffer
 would leave dirty lines whose write-back would share the timed step's
 bandwidth.  ``--hot`` skips the flush.
 
-The timed step is the three kernels (write, partials, merge) launched one
-after another on one stream.  The same step captured in a HIP graph and
-replayed is timed too (`graph_step_us`): on this stack a replay takes longer
-than the three launches.
+The timed step is one pa_decode_append call when the workload's write is
+exactly one newest token per sequence (its partial kernel over the cached
+tokens, then a merge that folds in and writes each new token: two kernels),
+else the three kernels (write, partials, merge) launched one after another
+on one stream; `three_kernel_step_us` reports the latter either way.  The
+three-kernel step captured in a HIP graph and replayed is timed too
+(`graph_step_us`): on this stack a replay takes longer than the launches.
 
 Prints ONE JSON line.  `value` = KV bytes the decode must read (sum over
 sequences of n_b * 2 * KVH * D * elem) / mean step time, in GB/s (10^9 B/s).
@@ -538,6 +541,9 @@ def main():
                          "prefix for prefix_shared_bf16, else 0 = pa_decode)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="skip the graph-replay timing")
+    ap.add_argument("--step", choices=["auto", "append", "three"], default="auto",
+                    help="decode step timed as the step: pa_decode_append (two kernels), or write + partial + "
+                         "merge; auto takes the append step when the write is one newest token per sequence")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="before the steps, run a plain fp32 copy of MIB MiB three times (the reference "
@@ -618,6 +624,32 @@ def main():
         pk.decode_merge(w.q, kc, w.block_tables, w.context_lens, out=out, workspace=ws,
                         partition_size=P)
 
+    # The append step (pa_decode_append: the partial kernel over the cached
+    # tokens, then one merge that folds in and writes each sequence's new
+    # token) does the same work as write + decode when the write is exactly
+    # one newest token (position n_b - 1) per sequence.
+    bsz = cfg.block_size
+    ctx_h = w.context_lens.cpu().to(torch.int64)
+    tbl_h = w.block_tables.cpu().to(torch.int64)
+    live = ctx_h > 0
+    pos = (ctx_h - 1).clamp(min=0)
+    newest = torch.where(live, tbl_h[torch.arange(B), pos // bsz] * bsz + pos % bsz, torch.full_like(ctx_h, -1))
+    sm = w.slot_mapping.cpu()
+    use_append = args.step == "append" or (
+        args.step == "auto" and not shared and sm.numel() == int(live.sum()) and bool((sm >= 0).all())
+        and torch.equal(torch.sort(sm).values, torch.sort(newest[live]).values))
+    if use_append:
+        row_of = {int(x): i for i, x in enumerate(sm.tolist())}
+        idx = torch.tensor([row_of.get(int(x), 0) for x in newest.tolist()], dtype=torch.int64, device=dev)
+        app_k, app_v = w.k_new.index_select(0, idx), w.v_new.index_select(0, idx)
+        app_slots = newest.to(dev)
+        cached = (ctx_h - live.to(torch.int64)).to(torch.int32).to(dev)
+        aws = pk.new_append_workspace(B, H, W, kc, P)
+
+    def append_step():
+        pk.decode_append(w.q, kc, vc, app_k, app_v, app_slots, w.block_tables, cached, w.scale, out=out,
+                         workspace=aws, partition_size=P)
+
     def do_flush():
         if flush is not None:
             torch.sum(flush, dim=0, out=flush_sink)
@@ -649,6 +681,23 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     st = [a.elapsed_time(b) * 1e3 for a, b in events]          # µs
+    st3 = st
+    if use_append:
+        # the same steps as the append entry point: two kernels
+        for _ in range(args.warmup):
+            do_flush()
+            append_step()
+        aev = [(ev(), ev()) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            do_flush()
+            aev[i][0].record()
+            append_step()
+            aev[i][1].record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        st = [a.elapsed_time(b) * 1e3 for a, b in aev]
 
     # The same steps again, with events around each kernel: the partial kernel's
     # duration feeds the roofline; write and merge are reported beside it.
@@ -746,15 +795,20 @@ def main():
         "partial_kernel_us": round(k2_us, 2),
         "merge_kernel_us": round(k3_us, 2),
         "step_us_p10_p50_p90": [round(pct(st, q), 2) for q in (0.1, 0.5, 0.9)],
+        "step_kernels": "pa_decode_append (partial + merge-append)" if use_append else "write + partial + merge",
+        "three_kernel_step_us": round(mean(st3), 2),
         "graph_step_us": round(mean(gst), 2) if gst else None,
         "write_us": round(wr_us, 2),
         "write_GBps": round(write_bytes / (wr_us * 1e-6) / 1e9, 2),
         "kv_bytes_per_step": kv_bytes,
         "kv_unique_bytes_per_step": kv_unique,
         "wall_ms_per_step_incl_flush": round(wall / args.steps * 1e3, 4),
-        "timing": "step = events around the write, partial and merge kernels launched one after another "
-                  "(graph_step_us: the same step replayed from a HIP graph); per-kernel times from a second "
-                  "pass with events around each kernel (each includes ~1-3 us of event/launch gap)",
+        "timing": ("step = events around one pa_decode_append call (partial kernel over the cached tokens, "
+                   "then a merge that folds in and writes each sequence's new token); three_kernel_step_us: "
+                   "write, partial and merge kernels launched one after another" if use_append else
+                   "step = events around the write, partial and merge kernels launched one after another") +
+                  " (graph_step_us: the three-kernel step replayed from a HIP graph); per-kernel times from a "
+                  "second pass with events around each kernel (each includes ~1-3 us of event/launch gap)",
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 1),
