@@ -18,7 +18,7 @@ import torch
 
 from .workloads import torch_dtype
 
-__all__ = ["WriteConfig", "WRITE_CONFIGS", "WriteWorkload", "make_write", "make_write_chunks"]
+__all__ = ["WriteConfig", "WRITE_CONFIGS", "WriteWorkload", "make_write", "make_write_chunks", "make_new_rows"]
 
 
 @dataclass(frozen=True)
@@ -137,3 +137,14 @@ def make_write_chunks(*, num_kv_heads: int, head_dim: int, block_size: int, dtyp
                       num_kv_heads=KVH, head_dim=D, block_size=bs, pad_tokens=pad_tokens, seed=seed)
     return WriteWorkload(cfg=cfg, k_cache=k_cache, v_cache=v_cache, k_new=k_new, v_new=v_new,
                          slot_mapping=slots.to(device), valid_tokens=valid)
+
+
+def make_new_rows(num_seqs: int, num_kv_heads: int, head_dim: int, dtype: str, seed: int, device="cpu"):
+    """One new token's K and V rows per sequence, [num_seqs, KVH, D] each:
+    N(0, 1) drawn in fp32 on ``device`` and rounded to the cache dtype."""
+    device = torch.device(device)
+    g = torch.Generator(device=device).manual_seed(9000 + seed)
+    dt = torch_dtype(dtype)
+    k = torch.randn(num_seqs, num_kv_heads, head_dim, generator=g, device=device, dtype=torch.float32).to(dt)
+    v = torch.randn(num_seqs, num_kv_heads, head_dim, generator=g, device=device, dtype=torch.float32).to(dt)
+    return k, v

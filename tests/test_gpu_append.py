@@ -20,7 +20,7 @@ import torch
 
 import oracle as O
 import paged_kv_cache_70_amd as pk
-from synth import CONFIGS, make_custom, make_workload, to_vllm_layout
+from synth import CONFIGS, make_custom, make_new_rows, make_workload, to_vllm_layout
 from tests.gpu_util import assert_matches_oracle, stored_np
 
 pytestmark = pytest.mark.gpu
@@ -55,10 +55,8 @@ def _step(w, no_new=(), vllm=False, partition_size=0):
     cached = np.where(has, n - 1, n)
     slots = np.array([tbl[b, (n[b] - 1) // bs] * bs + (n[b] - 1) % bs if has[b] else -1 for b in range(B)],
                      dtype=np.int64)
-    g = torch.Generator(device=w.q.device).manual_seed(B * 131 + int(n.sum()) % 1000)
     KVH, D = w.k_cache.shape[2], w.k_cache.shape[3]
-    k_new = torch.randn(B, KVH, D, generator=g, device=w.q.device).to(w.k_cache.dtype)
-    v_new = torch.randn(B, KVH, D, generator=g, device=w.q.device).to(w.k_cache.dtype)
+    k_new, v_new = make_new_rows(B, KVH, D, w.cfg.dtype, B * 131 + int(n.sum()) % 1000, w.q.device)
     # oracle: write the new rows, then decode over cached + new
     ko, vo = stored_np(w.k_cache).copy(), stored_np(w.v_cache).copy()
     O.write_kv(ko, vo, stored_np(k_new), stored_np(v_new), slots)
@@ -126,10 +124,8 @@ def _step_full(w):
     slots = torch.from_numpy(np.array([tbl[b, (n[b] - 1) // bs] * bs + (n[b] - 1) % bs for b in range(B)],
                                       dtype=np.int64)).to(w.q.device)
     cached = (w.context_lens - 1).to(torch.int32)
-    g = torch.Generator(device=w.q.device).manual_seed(3)
     KVH, D = w.k_cache.shape[2], w.k_cache.shape[3]
-    k_new = torch.randn(B, KVH, D, generator=g, device=w.q.device).to(w.k_cache.dtype)
-    v_new = torch.randn(B, KVH, D, generator=g, device=w.q.device).to(w.k_cache.dtype)
+    k_new, v_new = make_new_rows(B, KVH, D, "bf16", 3, w.q.device)
     k1, v1 = w.k_cache.clone(), w.v_cache.clone()
     pk.write_kv(k1, v1, k_new, v_new, slots)
     plain = pk.decode(w.q, k1, v1, w.block_tables, w.context_lens, w.scale)
