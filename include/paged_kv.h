@@ -20,7 +20,8 @@
  *     current device can access); "host" pointers are ordinary host memory.
  *   - Every tensor is dense row-major (C-contiguous) with the stated shape and
  *     at least 16-byte aligned.  The caller owns every buffer; the library
- *     allocates nothing and keeps no state between calls.
+ *     allocates nothing and keeps no state between calls (the one exception
+ *     is pa_decode_noalloc's static device scratch area).
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL means
  *     the legacy default stream).  No call synchronises the host.
  *   - Return value: PA_OK (0) or a negative pa_status.  Argument errors are
@@ -66,8 +67,11 @@ typedef enum pa_status {
   PA_ERR_TOO_LARGE = -7,    /* sizes overflow the kernels' 32-bit grid/index limits */
   PA_ERR_NO_BLOCKS = -8,    /* block manager: not enough free blocks (nothing was changed) */
   PA_ERR_NO_SEQUENCE = -9,  /* block manager: unknown sequence id */
-  PA_ERR_NO_MEMORY = -10    /* block manager: host memory ran out inside a call that changes the
+  PA_ERR_NO_MEMORY = -10,   /* block manager: host memory ran out inside a call that changes the
                                manager; its state is then unspecified: destroy it */
+  PA_ERR_SCRATCH = -11      /* pa_decode_noalloc: the call needs more than the library's static
+                               scratch area of PA_NOALLOC_SCRATCH_BYTES, or the device address of
+                               that area could not be obtained */
 } pa_status;
 
 /* Memory layout of the two caches. */
@@ -418,13 +422,40 @@ int pa_decode_append(void* out, const void* q, void* k_cache, void* v_cache, con
                      int32_t max_blocks_per_seq, const pa_cache_desc* desc, int32_t partition_size,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * pa_decode_noalloc — pa_decode for callers that cannot allocate device
+ * memory (code being captured into a HIP graph, tight serving loops,
+ * harnesses that forbid hipMalloc): the same arguments without the
+ * workspace, and the same result, bit for bit, as pa_decode with the same
+ * partition size.  The split-KV partial results go to a static device array
+ * of PA_NOALLOC_SCRATCH_BYTES held by the library on every GPU it runs on
+ * until the process ends; the call itself allocates nothing and calls no
+ * allocating runtime or library routine.
+ *   - The need is pa_decode_workspace_bytes(...) for the same sizes; a call
+ *     that needs more returns PA_ERR_SCRATCH before anything is enqueued.
+ *   - The area's device address is looked up once per device, on that
+ *     device's first call (the stream's device must be current, as for
+ *     every entry point); a failed lookup returns PA_ERR_SCRATCH.
+ *   - Every call on one GPU shares that GPU's area and leaves its partial
+ *     results there; none need be cleared (a call writes every slot it
+ *     reads).  Calls that overlap on one GPU (concurrent streams, or
+ *     threads) race: order them on one stream.
+ * Other errors as pa_decode.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int pa_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, const int32_t* context_lens, float scale,
+                      int32_t num_seqs, int32_t num_heads, int32_t max_blocks_per_seq,
+                      const pa_cache_desc* desc, int32_t partition_size, void* stream);
+
 /* Static, NUL-terminated name of a pa_status code ("unknown status" otherwise). */
 const char* pa_status_string(int status);
 
 /* ABI version of this header: (major << 16) | minor (2.0: pa_cache_desc.layout;
  * 2.1: fp32 prefill, pa_prefill_workspace_bytes takes max_blocks_per_seq;
  * 2.2: pa_decode_shared_prefix, pa_decode_partials_shared_prefix;
- * 2.3: pa_decode_append, pa_decode_append_workspace_bytes). */
+ * 2.3: pa_decode_append, pa_decode_append_workspace_bytes;
+ * 2.4: pa_decode_noalloc, PA_ERR_SCRATCH). */
 int32_t pa_abi_version(void);
 
 #ifdef __cplusplus

@@ -34,6 +34,8 @@ __all__ = [
     "decode_shared_prefix",
     "decode_partials_shared_prefix",
     "decode_append",
+    "decode_noalloc",
+    "NOALLOC_SCRATCH_BYTES",
     "new_append_workspace",
     "prefill",
     "prefill_workspace",
@@ -50,6 +52,7 @@ _LIB: Optional[ctypes.CDLL] = None
 PA_F32, PA_BF16 = 0, 1
 _DTYPES = {torch.float32: PA_F32, torch.bfloat16: PA_BF16}
 PA_LAYOUT_P09, PA_LAYOUT_VLLM = 0, 1
+NOALLOC_SCRATCH_BYTES = 32 << 20      # PA_NOALLOC_SCRATCH_BYTES of the header
 
 
 class PaError(RuntimeError):
@@ -100,6 +103,7 @@ def load_library() -> ctypes.CDLL:
         "pa_decode_append_workspace_bytes": (sz, [i32, i32, i32, pdesc, i32]),
         "pa_decode_append": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, vp, vp, vp, f32, i32, i32, i32, pdesc, i32,
                                             vp, sz, vp]),
+        "pa_decode_noalloc": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, f32, i32, i32, i32, pdesc, i32, vp]),
         "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "pa_abi_version": (i32, []),
     }
@@ -255,6 +259,30 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_
     """Paged decode attention; returns ``out`` [B, H, D] in q's dtype."""
     return _decode_call("pa_decode", q, k_cache, v_cache, block_tables, context_lens, scale, out,
                         workspace, partition_size)
+
+
+def decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_tables: torch.Tensor,
+                   context_lens: torch.Tensor, scale: float, *, out: torch.Tensor,
+                   partition_size: int = 0) -> torch.Tensor:
+    """decode() without a workspace: the partial results go to the library's
+    static device scratch area (pa_decode_noalloc), so nothing is allocated
+    here either: ``out`` must be given."""
+    lib = load_library()
+    desc = cache_desc(k_cache)
+    _check_v(k_cache, v_cache, desc)
+    if q.dim() != 3 or q.dtype != k_cache.dtype or q.shape[2] != desc.head_dim:
+        raise ValueError("q must be [num_seqs, num_heads, head_dim] of the cache dtype")
+    B, H, _ = q.shape
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or tuple(context_lens.shape) != (B,):
+        raise ValueError("block_tables must be [num_seqs, max_blocks_per_seq] and context_lens [num_seqs]")
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must be like q")
+    st = lib.pa_decode_noalloc(_dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                               _dev(block_tables, "block_tables", torch.int32),
+                               _dev(context_lens, "context_lens", torch.int32), float(scale), B, H,
+                               block_tables.shape[1], ctypes.byref(desc), int(partition_size), _stream(q))
+    _check("pa_decode_noalloc", st)
+    return out
 
 
 def decode_partials(q, k_cache, v_cache, block_tables, context_lens, scale, *, out, workspace,

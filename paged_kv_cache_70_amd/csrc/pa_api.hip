@@ -1,7 +1,10 @@
 // C-ABI entry points declared in include/paged_kv.h: argument checks, launch
 // planning and kernel launches on the caller's stream.  No allocation, no
-// host synchronisation, no state kept between calls.
+// host synchronisation, no state kept between calls, apart from the static
+// device scratch area of pa_decode_noalloc (and its per-device address).
 #include <limits.h>
+
+#include <atomic>
 
 #include "../../include/paged_kv.h"
 #include "pa_internal.h"
@@ -222,6 +225,29 @@ static void set_shared_prefix(DecodeParams& p, int32_t shared_tokens, const Chec
   p.SPB = SPB;
 }
 
+// Static scratch area of pa_decode_noalloc, for callers that cannot allocate:
+// the decode's split-KV partial results.  Each GPU the library runs on holds
+// its own copy (at its own address) until the process ends.  In host code
+// `scratch` is only a stand-in for that device symbol: its device address is
+// looked up per device with hipGetSymbolAddress and used everywhere instead.
+static __device__ __align__(256) uint8_t scratch[PA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+static std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// Device address of the current device's scratch area (nullptr on failure).
+// The lookup is idempotent, so two threads racing on a device's first call
+// both store the same address.
+static void* scratch_address() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+  g_scratch_ptr[dev].store(p, std::memory_order_release);
+  return p;
+}
+
 // Prefill launch shape: query heads per workgroup (the largest of 4, 2, 1
 // dividing G) and query tokens per workgroup (4 wavefronts x 32 queries, 16
 // for head_dim 256, shared by hg heads).
@@ -238,7 +264,7 @@ using namespace pa;
 
 extern "C" {
 
-int32_t pa_abi_version(void) { return (2 << 16) | 3; }
+int32_t pa_abi_version(void) { return (2 << 16) | 4; }
 
 const char* pa_status_string(int status) {
   switch (status) {
@@ -253,6 +279,7 @@ const char* pa_status_string(int status) {
     case PA_ERR_NO_BLOCKS: return "block manager: not enough free blocks";
     case PA_ERR_NO_SEQUENCE: return "block manager: unknown sequence";
     case PA_ERR_NO_MEMORY: return "block manager: host memory ran out (destroy the manager)";
+    case PA_ERR_SCRATCH: return "pa_decode_noalloc: more scratch needed than the static area holds, or its address is unavailable";
   }
   return "unknown status";
 }
@@ -410,6 +437,25 @@ int pa_decode_partials_shared_prefix(void* out, const void* q, const void* k_cac
   return decode_common(true, false, out, q, k_cache, v_cache, block_tables, context_lens, scale,
                        num_seqs, num_heads, max_blocks_per_seq, desc, partition_size, workspace,
                        workspace_bytes, stream, shared_tokens);
+}
+
+int pa_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, const int32_t* context_lens, float scale,
+                      int32_t num_seqs, int32_t num_heads, int32_t max_blocks_per_seq,
+                      const pa_cache_desc* desc, int32_t partition_size, void* stream) {
+  Checked ck;
+  int st = check_decode_sizes(num_seqs, num_heads, max_blocks_per_seq, desc, partition_size, &ck);
+  if (st) return st;
+  if (ck.ws_bytes > PA_NOALLOC_SCRATCH_BYTES) return PA_ERR_SCRATCH;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_NULL;
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_ALIGN;
+  void* ws = nullptr;
+  if (ck.ws_bytes) {
+    ws = scratch_address();
+    if (!ws) return PA_ERR_SCRATCH;
+  }
+  return decode_common(true, true, out, q, k_cache, v_cache, block_tables, context_lens, scale, num_seqs,
+                       num_heads, max_blocks_per_seq, desc, partition_size, ws, ck.ws_bytes, stream);
 }
 
 int pa_decode_merge(void* out, const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for code in range(0, -11, -1):
+    for code in range(0, -12, -1):
         s = pk.status_string(code)
         assert s and s != "unknown status"
     assert pk.status_string(-99) == "unknown status"
@@ -177,3 +177,22 @@ def test_shared_prefix_host_checks():
     bad = _desc(head_dim=96)
     assert lib.pa_decode_shared_prefix(None, None, None, None, None, None, 0.1, 4, 32, 8, 64,
                                        ctypes.byref(bad), 0, None, 0, None) == -3
+
+
+def test_noalloc_host_checks():
+    """pa_decode_noalloc: the same host checks as pa_decode, and a call whose
+    partial results would exceed the static scratch area is refused with
+    PA_ERR_SCRATCH before any device work (no launch here)."""
+    lib = pk.load_library()
+    d = _desc()
+    call = lambda B, H, W, P=0, ptr=None: lib.pa_decode_noalloc(
+        ptr, ptr, ptr, ptr, ptr, ptr, 0.1, B, H, W, ctypes.byref(d), P, None)
+    assert call(4, 30, 8) == -2                 # H % KVH != 0
+    assert call(4, 32, 8, P=24) == -3           # partition not a multiple of bs
+    assert call(4, 32, 8) == -1                 # null tensors
+    assert call(4, 32, 8, ptr=0x1008) == -5     # misaligned
+    need = lib.pa_decode_workspace_bytes(4096, 64, 4096, ctypes.byref(d), 64)
+    assert need > pk.NOALLOC_SCRATCH_BYTES
+    assert call(4096, 64, 4096, P=64) == -11
+    assert call(4096, 64, 4096, P=64, ptr=0x1000) == -11
+    assert lib.pa_decode_workspace_bytes(64, 32, 256, ctypes.byref(d), 0) <= pk.NOALLOC_SCRATCH_BYTES
