@@ -155,6 +155,43 @@ def _calibration_copy(mib: int, dev, do_flush) -> None:
     del src, dst
 
 
+def _read_ceiling(nbytes: int, args, dev, do_flush) -> dict:
+    """The streaming-read ceiling of nbytes on this device, in this process:
+    pa_measure_read (16-byte loads, non-temporal like the decode's) over a
+    buffer of that size, timed with events like the step (flushed before each
+    read unless --hot), at a few workgroup counts per CU; the best is the
+    ceiling."""
+    import torch
+
+    import paged_kv_cache_70_amd as pk
+    nbytes = max(16, nbytes // 16 * 16)
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    res = {}
+    for wpc in (2, 4, 8):
+        for _ in range(max(2, args.warmup // 2)):
+            do_flush()
+            pk.measure_read(buf, sink, workgroups_per_cu=wpc)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for a, b in evs:
+            do_flush()
+            a.record()
+            pk.measure_read(buf, sink, workgroups_per_cu=wpc)
+            b.record()
+        torch.cuda.synchronize()
+        us = sum(a.elapsed_time(b) for a, b in evs) / len(evs) * 1e3
+        res[wpc] = us
+    del buf
+    wpc = min(res, key=res.get)
+    return {"GBps": round(nbytes / (res[wpc] * 1e-6) / 1e9, 1), "bytes": nbytes, "us": round(res[wpc], 2),
+            "workgroups_per_cu": wpc, "nontemporal": True,
+            "us_by_workgroups_per_cu": {str(k): round(v, 2) for k, v in res.items()},
+            "what": "pa_measure_read: one pass of 16-byte non-temporal loads over a buffer of the step's distinct "
+                    "KV bytes, events around the kernel, same flush as the step"}
+
+
 def _cpu_baseline(w, budget_s: float):
     """The oracle (fp64 NumPy, untuned) on a bounded sample of the same
     workload: whole sequences in a fixed shuffled order, cycling through the
@@ -162,7 +199,7 @@ def _cpu_baseline(w, budget_s: float):
     GB/s of KV rows read."""
     import numpy as np
     import oracle as O
-    from tests.gpu_util import stored_np
+    from synth import stored_np
 
     cfg = w.cfg
     kc, vc = stored_np(w.k_cache), stored_np(w.v_cache)
@@ -202,7 +239,7 @@ def _cpu_baseline_prefill(w, budget_s: float):
     algorithmic flops."""
     import numpy as np
     import oracle as O
-    from tests.gpu_util import stored_np
+    from synth import stored_np
 
     cfg = w.cfg
     kc, vc = stored_np(w.k_cache).copy(), stored_np(w.v_cache).copy()
@@ -420,7 +457,7 @@ def _cpu_baseline_write(w, budget_s: float):
     workload, repeated while less than budget_s of CPU work has been done,
     scaled to GB/s of the same bytes."""
     import oracle as O
-    from tests.gpu_util import stored_np
+    from synth import stored_np
 
     kc, vc = stored_np(w.k_cache).copy(), stored_np(w.v_cache).copy()
     k, v, sl = stored_np(w.k_new), stored_np(w.v_new), stored_np(w.slot_mapping)
@@ -635,12 +672,17 @@ def main():
     pos = (ctx_h - 1).clamp(min=0)
     newest = torch.where(live, tbl_h[torch.arange(B), pos // bsz] * bsz + pos % bsz, torch.full_like(ctx_h, -1))
     sm = w.slot_mapping.cpu()
-    use_append = args.step == "append" or (
-        args.step == "auto" and not shared and sm.numel() == int(live.sum()) and bool((sm >= 0).all())
-        and torch.equal(torch.sort(sm).values, torch.sort(newest[live]).values))
+    newest_write = (sm.numel() == int(live.sum()) and bool((sm >= 0).all())
+                    and torch.equal(torch.sort(sm).values, torch.sort(newest[live]).values))
+    if args.step == "append" and (not newest_write or not bool(live.all()) or shared):
+        print(f"--step append needs a write of exactly one newest token per sequence and no shared-prefix hint; "
+              f"{cfg.name}'s write is not that (use --step three or auto)", file=sys.stderr)
+        sys.exit(2)
+    use_append = args.step == "append" or (args.step == "auto" and not shared and newest_write)
     if use_append:
         row_of = {int(x): i for i, x in enumerate(sm.tolist())}
-        idx = torch.tensor([row_of.get(int(x), 0) for x in newest.tolist()], dtype=torch.int64, device=dev)
+        idx = torch.tensor([row_of[int(x)] if x >= 0 else 0 for x in newest.tolist()], dtype=torch.int64,
+                           device=dev)
         app_k, app_v = w.k_new.index_select(0, idx), w.v_new.index_select(0, idx)
         app_slots = newest.to(dev)
         cached = (ctx_h - live.to(torch.int64)).to(torch.int32).to(dev)
@@ -750,9 +792,32 @@ def main():
         torch.cuda.synchronize()
         gst = [a.elapsed_time(b) * 1e3 for a, b in gev]
 
+    # Hot steps: the same step without the flush before it (the last-level
+    # cache may still hold rows of the step before); reported beside the
+    # flushed number, labelled as hot.
+    hot = []
+    if flush is not None:
+        for _ in range(args.warmup):
+            append_step() if use_append else (write(), partials(), merge())
+        hev = [(ev(), ev()) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            hev[i][0].record()
+            if use_append:
+                append_step()
+            else:
+                write()
+                partials()
+                merge()
+            hev[i][1].record()
+        torch.cuda.synchronize()
+        hot = [a.elapsed_time(b) * 1e3 for a, b in hev]
+
     def pct(x, q):
         s = sorted(x)
         return s[min(len(s) - 1, int(q * len(s)))]
+
+    ceiling = _read_ceiling(w.kv_unique_bytes(), args, dev, do_flush)
 
     kv_bytes = w.kv_bytes()
     # the HBM roofline takes the distinct rows: a prefix block shared by many
@@ -790,6 +855,13 @@ def main():
             "cache_flush_between_steps": flush is not None,
         },
         "hbm_frac_step": round(kv_unique / (step_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+        "hbm_frac_three_kernel_step": round(kv_unique / (mean(st3) * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+        "ceiling_GBps": ceiling["GBps"],
+        "frac_of_ceiling": round(achieved / ceiling["GBps"], 4),
+        "step_frac_of_ceiling": round(kv_unique / (step_us * 1e-6) / 1e9 / ceiling["GBps"], 4),
+        "ceiling_read": ceiling,
+        "hot_step_us": round(mean(hot), 2) if hot else None,
+        "hot_hbm_frac_step": round(kv_unique / (mean(hot) * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4) if hot else None,
         "decode_us": round(dec_us, 2),
         "decode_kv_GBps": round(kv_bytes / (dec_us * 1e-6) / 1e9, 1),
         "partial_kernel_us": round(k2_us, 2),

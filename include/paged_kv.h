@@ -28,7 +28,8 @@
  *     detected on the host before anything is enqueued; PA_ERR_LAUNCH reports
  *     a failed kernel launch.  pa_status_string() names each code.
  *   - Device-side preconditions (not checked on the host, since that would
- *     need a device-to-host copy): non-negative slots are < num_blocks *
+ *     need a device-to-host copy; the opt-in pa_check_* calls test them on
+ *     the device): non-negative slots are < num_blocks *
  *     block_size and pairwise distinct; for j < ceil(n_b / bs),
  *     0 <= block_tables[b, j] < num_blocks; 0 <= context_lens[b] <=
  *     max_blocks_per_seq * block_size.  The kernels stay memory-safe when they
@@ -189,7 +190,14 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
  * online softmax.  Sequences that fit in one partition (and n == 0) get their
  * final output written to `out`; the others leave fp32 partial results in
  * `workspace` for pa_decode_merge (or for a merge of partitions computed
- * elsewhere).
+ * elsewhere).  Workspace layout, with P the partition size in use and
+ * maxP = ceil(max_blocks_per_seq * bs / P):
+ *   acc  fp32 [B, H, maxP, D] at byte 0,
+ *   ml   fp32 [B, H, maxP, 2] right after acc: (m, l) per partition,
+ * where partition p of sequence b and head h holds acc = sum_t 2^(s_t - m) v_t
+ * and l = sum_t 2^(s_t - m) over its tokens t, s_t = scale * log2(e) * q.k_t
+ * and m a reference at least the largest s_t minus 8 (not necessarily the
+ * maximum), so that acc / l is the softmax-weighted V of the partition alone.
  */
 int pa_decode_partials(void* out, const void* q, const void* k_cache, const void* v_cache,
                        const int32_t* block_tables, const int32_t* context_lens, float scale,
@@ -448,6 +456,69 @@ int pa_decode_noalloc(void* out, const void* q, const void* k_cache, const void*
                       int32_t num_seqs, int32_t num_heads, int32_t max_blocks_per_seq,
                       const pa_cache_desc* desc, int32_t partition_size, void* stream);
 
+/*
+ * Checked mode (opt-in).  The device-side preconditions above are not tested
+ * by the write, decode and prefill kernels, which stay memory-safe when they
+ * are broken and report nothing -- the silent failures "P09 · Paged KV 写入 +
+ * decode attention" warns of: a -1 slot used as an index overwrites the last
+ * row with no error or warning (直觉与类比), and garbage table entries give an
+ * index error or silently wrong K/V (易错点).  The pa_check_* calls enqueue
+ * kernels that test them and OR one bit per kind of violation into
+ * *error_word (device, uint32, set with atomics; the caller zeroes it before
+ * the checks it wants to collect and reads it after they ran).  Enqueue them
+ * on the same stream before (or instead of) the call they guard; they read
+ * only what that call reads and write only *error_word and their workspace.
+ */
+typedef enum pa_check_flag {
+  PA_CHECK_SLOT_RANGE = 1,       /* a slot >= num_blocks * block_size (negative slots are padding) */
+  PA_CHECK_SLOT_DUPLICATE = 2,   /* two tokens with the same valid slot */
+  PA_CHECK_TABLE_RANGE = 4,      /* block_tables[b, j] outside [0, num_blocks) for some j < ceil(n_b / bs) */
+  PA_CHECK_CONTEXT_RANGE = 8,    /* context_lens[b] < 0 or > max_blocks_per_seq * block_size */
+  PA_CHECK_QUERY_RANGE = 16      /* prefill: query_start_loc not non-decreasing from 0 to num_tokens, or a
+                                    sequence with more new queries than tokens (L_b > n_b) */
+} pa_check_flag;
+
+/* Bytes of the slot bitmap pa_check_write needs: one bit per cache slot
+ * (num_blocks * block_size), rounded up to 4-byte words; 0 for an invalid desc. */
+size_t pa_check_write_workspace_bytes(const pa_cache_desc* desc);
+
+/* Checks a write's slot_mapping [num_tokens] (device int64): sets
+ * PA_CHECK_SLOT_RANGE and PA_CHECK_SLOT_DUPLICATE.  workspace: device,
+ * 4-byte aligned, >= pa_check_write_workspace_bytes(desc), no initial contents
+ * (a fill kernel clears it).  Calls sharing a workspace must not overlap.
+ * Returns PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE,
+ * PA_ERR_ALIGN, PA_ERR_TOO_LARGE or PA_ERR_LAUNCH; num_tokens == 0 enqueues nothing. */
+int pa_check_write(const int64_t* slot_mapping, int32_t num_tokens, const pa_cache_desc* desc,
+                   uint32_t* error_word, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Checks a decode's block_tables [B, W] and context_lens [B] (device int32;
+ * for pa_decode_append pass its cached_lens): sets PA_CHECK_CONTEXT_RANGE and
+ * PA_CHECK_TABLE_RANGE, reading only the entries the decode reads. */
+int pa_check_decode(const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                    int32_t max_blocks_per_seq, const pa_cache_desc* desc, uint32_t* error_word, void* stream);
+
+/* pa_check_decode plus the prefill's query_start_loc [B + 1] (device int32)
+ * against num_tokens and the context lengths: also sets PA_CHECK_QUERY_RANGE. */
+int pa_check_prefill(const int32_t* block_tables, const int32_t* context_lens, const int32_t* query_start_loc,
+                     int32_t num_seqs, int32_t max_blocks_per_seq, int32_t num_tokens, const pa_cache_desc* desc,
+                     uint32_t* error_word, void* stream);
+
+/*
+ * pa_measure_read — a measurement helper, not a step of the method: reads
+ * the `bytes` bytes of `buf` once with 16-byte loads (non-temporal when
+ * `nontemporal` is nonzero, as the decode's KV loads are), thread t of the
+ * grid taking 16-byte units t, t + S, t + 2 S, ... (S threads in all), spread
+ * over workgroups_per_cu workgroups of 256 threads per compute unit.  Its rate,
+ * timed beside the decode, is the streaming-read ceiling of the same byte
+ * count on the same device.
+ *   buf    device, 16-byte aligned, bytes a multiple of 16 (0: nothing enqueued)
+ *   sink   device, one uint32 the kernel may write (it keeps the loads live)
+ * Returns PA_OK, PA_ERR_NULL, PA_ERR_ALIGN, PA_ERR_SHAPE (bytes not a multiple
+ * of 16, workgroups_per_cu outside 1..64) or PA_ERR_LAUNCH.
+ */
+int pa_measure_read(const void* buf, size_t bytes, int32_t workgroups_per_cu, int32_t nontemporal,
+                    uint32_t* sink, void* stream);
+
 /* Static, NUL-terminated name of a pa_status code ("unknown status" otherwise). */
 const char* pa_status_string(int status);
 
@@ -455,7 +526,8 @@ const char* pa_status_string(int status);
  * 2.1: fp32 prefill, pa_prefill_workspace_bytes takes max_blocks_per_seq;
  * 2.2: pa_decode_shared_prefix, pa_decode_partials_shared_prefix;
  * 2.3: pa_decode_append, pa_decode_append_workspace_bytes;
- * 2.4: pa_decode_noalloc, PA_ERR_SCRATCH). */
+ * 2.4: pa_decode_noalloc, PA_ERR_SCRATCH; 2.5: checked mode (pa_check_*),
+ * pa_measure_read). */
 int32_t pa_abi_version(void);
 
 #ifdef __cplusplus

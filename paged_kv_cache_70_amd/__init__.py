@@ -8,8 +8,16 @@ from .api import (  # noqa: F401
     NOALLOC_SCRATCH_BYTES,
     CacheDesc,
     PaError,
+    CHECK_CONTEXT_RANGE,
+    CHECK_QUERY_RANGE,
+    CHECK_SLOT_DUPLICATE,
+    CHECK_SLOT_RANGE,
+    CHECK_TABLE_RANGE,
     abi_version,
     cache_desc,
+    check_decode,
+    check_prefill,
+    check_write,
     decode,
     decode_append,
     decode_merge,
@@ -19,6 +27,7 @@ from .api import (  # noqa: F401
     decode_partials,
     library_path,
     load_library,
+    measure_read,
     new_append_workspace,
     new_workspace,
     partition_size,

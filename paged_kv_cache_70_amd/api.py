@@ -35,6 +35,10 @@ __all__ = [
     "decode_partials_shared_prefix",
     "decode_append",
     "decode_noalloc",
+    "measure_read",
+    "check_write",
+    "check_decode",
+    "check_prefill",
     "NOALLOC_SCRATCH_BYTES",
     "new_append_workspace",
     "prefill",
@@ -104,6 +108,11 @@ def load_library() -> ctypes.CDLL:
         "pa_decode_append": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, vp, vp, vp, f32, i32, i32, i32, pdesc, i32,
                                             vp, sz, vp]),
         "pa_decode_noalloc": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, f32, i32, i32, i32, pdesc, i32, vp]),
+        "pa_measure_read": (ctypes.c_int, [vp, sz, i32, i32, vp, vp]),
+        "pa_check_write_workspace_bytes": (sz, [pdesc]),
+        "pa_check_write": (ctypes.c_int, [vp, i32, pdesc, vp, vp, sz, vp]),
+        "pa_check_decode": (ctypes.c_int, [vp, vp, i32, i32, pdesc, vp, vp]),
+        "pa_check_prefill": (ctypes.c_int, [vp, vp, vp, i32, i32, i32, pdesc, vp, vp]),
         "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "pa_abi_version": (i32, []),
     }
@@ -361,6 +370,71 @@ def decode_merge(q_like: torch.Tensor, k_cache: torch.Tensor, block_tables: torc
                              workspace.numel() * workspace.element_size(), _stream(out))
     _check("pa_decode_merge", st)
     return out
+
+
+# Bits of the checked mode's error word (pa_check_flag in the header).
+CHECK_SLOT_RANGE, CHECK_SLOT_DUPLICATE, CHECK_TABLE_RANGE, CHECK_CONTEXT_RANGE, CHECK_QUERY_RANGE = 1, 2, 4, 8, 16
+
+
+def _error_word(err: torch.Tensor) -> int:
+    if err.numel() != 1 or err.dtype not in (torch.int32,):
+        raise ValueError("error_word must be a one-element int32 device tensor")
+    return _dev(err, "error_word")
+
+
+def check_write(slot_mapping: torch.Tensor, k_cache: torch.Tensor, error_word: torch.Tensor, *,
+                workspace: Optional[torch.Tensor] = None) -> None:
+    """Checked mode: OR CHECK_SLOT_RANGE / CHECK_SLOT_DUPLICATE into
+    ``error_word`` (zeroed by the caller) for a write's slot_mapping."""
+    lib = load_library()
+    desc = cache_desc(k_cache)
+    if slot_mapping.dim() != 1:
+        raise ValueError("slot_mapping must be 1-D")
+    if workspace is None:
+        need = int(lib.pa_check_write_workspace_bytes(ctypes.byref(desc)))
+        workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=slot_mapping.device)
+    st = lib.pa_check_write(_dev(slot_mapping, "slot_mapping", torch.int64), slot_mapping.shape[0],
+                            ctypes.byref(desc), _error_word(error_word), _dev(workspace, "workspace"),
+                            workspace.numel() * workspace.element_size(), _stream(slot_mapping))
+    _check("pa_check_write", st)
+
+
+def check_decode(block_tables: torch.Tensor, context_lens: torch.Tensor, k_cache: torch.Tensor,
+                 error_word: torch.Tensor) -> None:
+    """Checked mode: OR CHECK_CONTEXT_RANGE / CHECK_TABLE_RANGE into ``error_word``."""
+    desc = cache_desc(k_cache)
+    if block_tables.dim() != 2 or tuple(context_lens.shape) != (block_tables.shape[0],):
+        raise ValueError("block_tables must be [B, W] and context_lens [B]")
+    st = load_library().pa_check_decode(_dev(block_tables, "block_tables", torch.int32),
+                                        _dev(context_lens, "context_lens", torch.int32), block_tables.shape[0],
+                                        block_tables.shape[1], ctypes.byref(desc), _error_word(error_word),
+                                        _stream(block_tables))
+    _check("pa_check_decode", st)
+
+
+def check_prefill(block_tables: torch.Tensor, context_lens: torch.Tensor, query_start_loc: torch.Tensor,
+                  num_tokens: int, k_cache: torch.Tensor, error_word: torch.Tensor) -> None:
+    """Checked mode: check_decode's flags plus CHECK_QUERY_RANGE."""
+    desc = cache_desc(k_cache)
+    B = block_tables.shape[0]
+    if block_tables.dim() != 2 or tuple(context_lens.shape) != (B,) or tuple(query_start_loc.shape) != (B + 1,):
+        raise ValueError("block_tables must be [B, W], context_lens [B] and query_start_loc [B + 1]")
+    st = load_library().pa_check_prefill(_dev(block_tables, "block_tables", torch.int32),
+                                         _dev(context_lens, "context_lens", torch.int32),
+                                         _dev(query_start_loc, "query_start_loc", torch.int32), B,
+                                         block_tables.shape[1], int(num_tokens), ctypes.byref(desc),
+                                         _error_word(error_word), _stream(block_tables))
+    _check("pa_check_prefill", st)
+
+
+def measure_read(buf: torch.Tensor, sink: torch.Tensor, *, workgroups_per_cu: int = 4,
+                 nontemporal: bool = True) -> None:
+    """Measurement helper: one streaming read of all of ``buf`` (16-byte
+    loads) on the current stream; ``sink`` is a device int32/uint32 word."""
+    nbytes = buf.numel() * buf.element_size()
+    st = load_library().pa_measure_read(_dev(buf, "buf"), nbytes, int(workgroups_per_cu), int(bool(nontemporal)),
+                                        _dev(sink, "sink"), _stream(buf))
+    _check("pa_measure_read", st)
 
 
 def prefill_workspace(num_seqs: int, num_heads: int, max_blocks_per_seq: int, num_tokens: int,

@@ -15,7 +15,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libpaged_kv.so")
-SOURCES = ["pa_api.hip", "pa_write.hip", "pa_decode.hip", "pa_decode_mfma.hip", "pa_prefill.hip"]
+SOURCES = ["pa_api.hip", "pa_write.hip", "pa_decode.hip", "pa_decode_mfma.hip", "pa_prefill.hip", "pa_measure.hip",
+           "pa_check.hip"]
 HOST_SOURCES = ["pa_block_manager.cpp"]      # host-only C++ (no device code)
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall"]
 ARCH = "gfx950"

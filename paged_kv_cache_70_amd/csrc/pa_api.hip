@@ -264,7 +264,7 @@ using namespace pa;
 
 extern "C" {
 
-int32_t pa_abi_version(void) { return (2 << 16) | 4; }
+int32_t pa_abi_version(void) { return (2 << 16) | 5; }
 
 const char* pa_status_string(int status) {
   switch (status) {

@@ -8,7 +8,8 @@
 // for the layouts where both products are dense contractions worth the matrix
 // cores: every 16-token tile of one kv head gives
 //   S   = K_tile (16 x D) . Q^T (D x 16 query-head columns)   v_mfma_f32_16x16x32_bf16
-//   O^T += V_tile^T (D x 16) . P^T (16 x 16)                   v_mfma_f32_16x16x16_bf16
+//   O^T += V_tile^T (D x 16) . P^T (16 x 16)                   v_mfma_f32_16x16x32_bf16
+//                                    (P as hi + lo, V twice along the contraction)
 // with up to 16 query heads of the kv head's GQA group as the 16 columns.
 //
 // Data movement per tile: 16-byte buffer loads (coalesced runs of whole
@@ -22,8 +23,9 @@
 // softmax rescaling and the final division are per-lane.
 //
 // The scores are exact products of bf16 values summed in fp32; the
-// probabilities enter the PV product rounded to bf16 (the running sums l use
-// the unrounded fp32 values).
+// probabilities enter the PV product as a pair of bf16 values whose sum is
+// the fp32 probability to about 2^-17 relative (split_bf16), and the running
+// sums l add the fp32 values, so the weighted sum is fp32 softmax . V.
 #include <math.h>
 
 #include "pa_mfma_tile.h"
@@ -144,6 +146,27 @@ __device__ __forceinline__ void q_operands(const DecodeParams& prm, const Unit& 
   }
 }
 
+// Probabilities as the B operand of the P.V products, carried exactly enough
+// for fp32: p = hi + lo with hi = bf16(p) (round to nearest even) and
+// lo = bf16(p - hi) (p - hi is exact in fp32), so hi + lo is p to about
+// 2^-17 relative.  For a 16-token tile the pair fills one 16x16x32 product:
+// contraction index 8 g + e holds token 4 g + (e mod 4) of lane group g, with
+// hi for e < 4 and lo for e >= 4, and the A operand holds that token's V
+// elements twice -- the sum runs over every token's hi and lo term at the
+// cost of the single 16x16x16 product that a bf16-rounded P would take.
+__device__ __forceinline__ void split_bf16(const float* p, bf16x4& hi, bf16x4& lo) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const __bf16 h = (__bf16)p[i];
+    hi[i] = h;
+    lo[i] = (__bf16)(p[i] - (float)h);
+  }
+}
+__device__ __forceinline__ bf16x8 twice(bf16x4 v) { return __builtin_shufflevector(v, v, 0, 1, 2, 3, 0, 1, 2, 3); }
+__device__ __forceinline__ bf16x8 join(bf16x4 a, bf16x4 b) {
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
 // Online-softmax state of one unit: column col's reference maximum m (base-2
 // units, uniform over the four groups) and -m, this lane's share of the
 // running sum, and the O^T accumulators.
@@ -207,10 +230,10 @@ __device__ __forceinline__ void fold_tile(uint32_t ok, const u32x4m (&kr)[Geo<D>
     pr[i] = exp2m(sc[i] + st.mneg);
     st.lsum += pr[i];
   }
-  bf16x4 pb;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) pb[i] = (__bf16)pr[i];
-  // O^T += V_tile^T . P^T, one 16-column d chunk per product.
+  bf16x4 ph, pl;
+  split_bf16(pr, ph, pl);
+  const bf16x8 pb = join(ph, pl);
+  // O^T += V_tile^T . (P_hi + P_lo)^T, one 16-column d chunk per product.
 #pragma unroll
   for (int j = 0; j < NPV; ++j) {
     const int d = 16 * j + map.dv;
@@ -218,7 +241,7 @@ __device__ __forceinline__ void fold_tile(uint32_t ok, const u32x4m (&kr)[Geo<D>
     const int addr = (map.tv * PPR + (pc ^ swz<PPR>(map.tv))) * 16 + (d & 7) * 2;
     const s16x4 vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (__attribute__((address_space(3))) s16x4*)(lds_v + addr));
-    st.o[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, vt), pb, st.o[j], 0, 0, 0);
+    st.o[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(twice(__builtin_bit_cast(bf16x4, vt)), pb, st.o[j], 0, 0, 0);
   }
 }
 
@@ -326,7 +349,8 @@ __global__ __launch_bounds__(64) void decode_partial_mfma_grid_kernel(const Deco
 // a 16-token tile load straight from the block in operand order, with no LDS:
 //   K (A of S = K Q^T): lane l takes the 16-byte group 4 c + l / 16 of token
 //     row l % 16; the 16 lanes of a group read 256 contiguous bytes;
-//   V^T (A of O^T += V^T P^T, 16x16x16): lane l takes tokens 4 (l / 16) .. + 3
+//   V^T (A of O^T += V^T P^T; 16x16x32 with the V elements twice, as for the
+//     LDS-staged tiles): lane l takes tokens 4 (l / 16) .. + 3
 //     of d row 16 j + l % 16, 8 contiguous bytes.
 // Rows past the partition's end, and blocks outside the pool, are not loaded
 // (zeros); V elements of rows past the end are zeroed, so stale values never
@@ -417,8 +441,8 @@ __device__ __forceinline__ uint32_t load_tile_vllm(const DecodeParams& prm, int 
 }
 
 // Folds a tile held in registers: S = K . Q^T, the same online softmax as the
-// LDS-staged tiles (scores masked by row validity, lazy rescale, bf16 P^T), and
-// O^T += V^T . P^T.
+// LDS-staged tiles (scores masked by row validity, lazy rescale, P^T as a
+// hi + lo pair of bf16), and O^T += V^T . P^T.
 template <int D>
 __device__ __forceinline__ void fold_tile_vllm(uint32_t ok, const VllmTile<D>& T, const bf16x8 (&qop)[Geo<D>::NQK],
                                                float cs, int lane, Fold<D>& st) {
@@ -442,16 +466,19 @@ __device__ __forceinline__ void fold_tile_vllm(uint32_t ok, const VllmTile<D>& T
       for (int j = 0; j < NPV; ++j) st.o[j] *= corr;
     }
   }
-  bf16x4 pb;
+  float pr[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const float p = exp2m(sc[i] + st.mneg);
-    st.lsum += p;
-    pb[i] = (__bf16)p;
+    pr[i] = exp2m(sc[i] + st.mneg);
+    st.lsum += pr[i];
   }
+  bf16x4 ph, pl;
+  split_bf16(pr, ph, pl);
+  const bf16x8 pb = join(ph, pl);
 #pragma unroll
   for (int j = 0; j < NPV; ++j)
-    st.o[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, T.v[j]), pb, st.o[j], 0, 0, 0);
+    st.o[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(twice(__builtin_bit_cast(bf16x4, T.v[j])), pb, st.o[j], 0, 0,
+                                                      0);
 }
 
 // 32-token tiles for blocks of 32 tokens or more (a tile then lies in one
@@ -543,16 +570,23 @@ __device__ __forceinline__ void fold_tile_vllm32(uint32_t ok, const VllmTile32<D
       for (int j = 0; j < NPV; ++j) st.o[j] *= corr;
     }
   }
-  bf16x8 pb;
+  float pr[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const float p = exp2m(sc[i] + st.mneg);
-    st.lsum += p;
-    pb[i] = (__bf16)p;
+    pr[i] = exp2m(sc[i] + st.mneg);
+    st.lsum += pr[i];
   }
+  // P = hi + lo as two products over the tile's 32 keys
+  bf16x4 h0, l0, h1, l1;
+  split_bf16(pr, h0, l0);
+  split_bf16(pr + 4, h1, l1);
+  const bf16x8 phi = join(h0, h1), plo = join(l0, l1);
 #pragma unroll
-  for (int j = 0; j < NPV; ++j)
-    st.o[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, T.v[j]), pb, st.o[j], 0, 0, 0);
+  for (int j = 0; j < NPV; ++j) {
+    const bf16x8 a = __builtin_bit_cast(bf16x8, T.v[j]);
+    st.o[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, phi, st.o[j], 0, 0, 0);
+    st.o[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, plo, st.o[j], 0, 0, 0);
+  }
 }
 
 }  // namespace

@@ -38,6 +38,7 @@ __all__ = [
     "make_custom",
     "torch_dtype",
     "bits_view",
+    "stored_np",
     "SENTINEL",
     "TAIL_FILL",
     "to_vllm_layout",
@@ -141,6 +142,17 @@ def bits_view(t: torch.Tensor) -> torch.Tensor:
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16)
     raise TypeError(t.dtype)
+
+
+def stored_np(t: torch.Tensor):
+    """The stored values of ``t`` on the host, unconverted: float32 as is,
+    bfloat16 as its 16-bit patterns (which the oracle widens exactly)."""
+    import numpy as np
+
+    t = t.detach().to("cpu").contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
 
 
 @dataclasses.dataclass

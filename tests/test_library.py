@@ -196,3 +196,24 @@ def test_noalloc_host_checks():
     assert call(4096, 64, 4096, P=64) == -11
     assert call(4096, 64, 4096, P=64, ptr=0x1000) == -11
     assert lib.pa_decode_workspace_bytes(64, 32, 256, ctypes.byref(d), 0) <= pk.NOALLOC_SCRATCH_BYTES
+
+
+def test_checked_mode_host_checks():
+    """pa_check_*: argument errors are reported before any launch, and the
+    write check's bitmap holds one bit per slot."""
+    lib = pk.load_library()
+    d = _desc(num_blocks=100, block_size=16)
+    assert lib.pa_check_write_workspace_bytes(ctypes.byref(d)) == (100 * 16 + 31) // 32 * 4
+    assert lib.pa_check_write_workspace_bytes(ctypes.byref(_desc(block_size=12))) == 0
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.pa_check_write(fake, 4, ctypes.byref(d), None, fake, 1 << 20, None) == -1      # no error word
+    assert lib.pa_check_write(None, 4, ctypes.byref(d), fake, fake, 1 << 20, None) == -1
+    assert lib.pa_check_write(fake, -1, ctypes.byref(d), fake, fake, 1 << 20, None) == -2
+    assert lib.pa_check_write(fake, 0, ctypes.byref(d), fake, None, 0, None) == 0             # nothing to check
+    assert lib.pa_check_write(fake, 4, ctypes.byref(d), fake, fake, 199, None) == -4          # short bitmap
+    assert lib.pa_check_write(fake, 4, ctypes.byref(d), fake, ctypes.c_void_p(0x1002), 1 << 20, None) == -5
+    assert lib.pa_check_decode(fake, fake, 0, 4, ctypes.byref(d), fake, None) == -2
+    assert lib.pa_check_decode(None, fake, 2, 4, ctypes.byref(d), fake, None) == -1
+    assert lib.pa_check_decode(fake, fake, 2, 1 << 30, ctypes.byref(d), fake, None) == -7
+    assert lib.pa_check_prefill(fake, fake, None, 2, 4, 10, ctypes.byref(d), fake, None) == -1
+    assert lib.pa_check_prefill(fake, fake, fake, 2, 4, -1, ctypes.byref(d), fake, None) == -2
