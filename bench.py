@@ -168,7 +168,7 @@ def _read_ceiling(nbytes: int, args, dev, do_flush) -> dict:
     buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
     sink = torch.zeros(1, dtype=torch.int32, device=dev)
     res = {}
-    for wpc in (2, 4, 8):
+    for wpc in (1, 2, 4):
         for _ in range(max(2, args.warmup // 2)):
             do_flush()
             pk.measure_read(buf, sink, workgroups_per_cu=wpc)
@@ -189,7 +189,8 @@ def _read_ceiling(nbytes: int, args, dev, do_flush) -> dict:
             "workgroups_per_cu": wpc, "nontemporal": True,
             "us_by_workgroups_per_cu": {str(k): round(v, 2) for k, v in res.items()},
             "what": "pa_measure_read: one pass of 16-byte non-temporal loads over a buffer of the step's distinct "
-                    "KV bytes, events around the kernel, same flush as the step"}
+                    "KV bytes, one contiguous chunk per workgroup, events around the kernel, same flush as the "
+                    "step; the best of 1, 2 and 4 workgroups per CU"}
 
 
 def _cpu_baseline(w, budget_s: float):
@@ -562,6 +563,118 @@ def run_write(args, cfg):
     print(json.dumps(res), flush=True)
 
 
+def run_graph_compare(args, cfg):
+    """Eager write + decode steps against the same step replayed from a HIP
+    graph: steps bracketed by events after the flush (the bench's method),
+    then back-to-back steps with no flush and no events (wall clock), which
+    shows the host's enqueue cost.  Under rocprofv3 --kernel-trace the first
+    warmup + steps step groups are eager and the last warmup + steps are
+    replays (--trace-summary splits them so)."""
+    import torch
+
+    import paged_kv_cache_70_amd as pk
+    from synth import make_workload
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = make_workload(cfg, dev)
+    B, H, D = w.q.shape
+    W = w.block_tables.shape[1]
+    kc, vc = w.k_cache.clone(), w.v_cache.clone()
+    ws = pk.new_workspace(B, H, W, kc)
+    out = torch.empty_like(w.q)
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    sink = torch.zeros((), dtype=torch.float32, device=dev)
+
+    def step():
+        pk.write_kv(kc, vc, w.k_new, w.v_new, w.slot_mapping)
+        pk.decode(w.q, kc, vc, w.block_tables, w.context_lens, w.scale, out=out, workspace=ws)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            torch.sum(flush, dim=0, out=sink)
+            fn()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for a, b in evs:
+            torch.sum(flush, dim=0, out=sink)
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in evs) / len(evs) * 1e3
+
+    eager = timed(step)
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        step()
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    graph = timed(g.replay)
+    M = 200
+
+    def wall(fn, sync):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(M):
+            fn()
+        if sync:
+            torch.cuda.synchronize()
+        t = (time.perf_counter() - t0) / M * 1e6
+        torch.cuda.synchronize()
+        return t
+
+    res = {
+        "config": {"workload": cfg.name},
+        "step": "pa_write_kv + pa_decode",
+        "eager_step_us": round(eager, 2), "graph_step_us": round(graph, 2),
+        "back_to_back_us_per_step": {"eager": round(wall(step, True), 2), "graph": round(wall(g.replay, True), 2)},
+        "host_enqueue_us_per_step": {"eager": round(wall(step, False), 2), "graph": round(wall(g.replay, False), 2)},
+        "timing": "eager/graph_step_us: events around one step after a 1 GiB read flush, mean of --steps; "
+                  "back-to-back: wall clock of 200 steps with no flush and no events; host enqueue: the same "
+                  "without waiting for the GPU",
+    }
+    print(json.dumps(res), flush=True)
+
+
+def trace_summary(csv_path: str, groups: int) -> None:
+    """Summary of a rocprofv3 --kernel-trace CSV of a --graph-compare run: the
+    library's kernels that follow each flush form one step; the first `groups`
+    steps are eager, the last `groups` graph replays.  Prints, per kind, the
+    time from the flush kernel's end to the step's first kernel, the gaps
+    between the step's kernels, the step's span and each kernel's duration."""
+    import csv
+    rows = sorted(csv.DictReader(open(csv_path)), key=lambda r: int(r["Start_Timestamp"]))
+    ks = [(r["Kernel_Name"].split("(")[0], int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in rows]
+    steps = []
+    for i, (n, a, b) in enumerate(ks):
+        if "write_kv_kernel" in n and i > 0 and "reduce_kernel" in ks[i - 1][0]:
+            j, st = i, []
+            while j < len(ks) and "pa::" in ks[j][0]:
+                st.append(ks[j])
+                j += 1
+            steps.append((ks[i - 1][2], st))
+    print("| step | steps | flush end -> first kernel (us) | gaps between the step's kernels (us) | "
+          "first start -> last end (us) | kernel durations (us) |")
+    print("|---|---|---|---|---|---|")
+    for lab, sts in (("eager", steps[:groups]), ("graph replay", steps[-groups:])):
+        g0 = [st[0][1] - fe for fe, st in sts]
+        span = [st[-1][2] - st[0][1] for fe, st in sts]
+        inner = [y[1] - x[2] for fe, st in sts for x, y in zip(st, st[1:])]
+        durs = {}
+        for fe, st in sts:
+            for n, a, b in st:
+                durs.setdefault(n.replace("void ", "").split("<")[0], []).append(b - a)
+        print(f"| {lab} | {len(sts)} | {sum(g0) / len(g0) / 1e3:.2f} | {sum(inner) / max(1, len(inner)) / 1e3:.2f} | "
+              f"{sum(span) / len(span) / 1e3:.2f} | " +
+              ", ".join(f"{k} {sum(v) / len(v) / 1e3:.2f}" for k, v in durs.items()) + " |")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -585,6 +698,10 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="before the steps, run a plain fp32 copy of MIB MiB three times (the reference "
                          "reading for HBM byte counters)")
+    ap.add_argument("--graph-compare", action="store_true",
+                    help="time the write + decode step eagerly and replayed from a HIP graph (see run_graph_compare)")
+    ap.add_argument("--trace-summary", metavar="KERNEL_TRACE_CSV",
+                    help="no GPU run: summarise a rocprofv3 kernel trace of a --graph-compare run")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU run: turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, WRITE_SIZE) of a "
                          "--copy-calibration run into profiles/traffic_<kernel>_<workload>.json")
@@ -602,6 +719,9 @@ def main():
                                   (args.copy_calibration or 256) << 20, _traffic_file(key, name))
         print(json.dumps(r))
         return
+
+    if args.trace_summary:
+        return trace_summary(args.trace_summary, args.warmup + args.steps)
 
     if args.config == "prefix_serving_host":
         return run_block_manager(args)
@@ -625,6 +745,8 @@ def main():
         return run_prefill(args, PREFILL_CONFIGS[args.config])
     if args.config in WRITE_CONFIGS:
         return run_write(args, WRITE_CONFIGS[args.config])
+    if args.graph_compare:
+        return run_graph_compare(args, CONFIGS[args.config])
     cfg = CONFIGS[args.config]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

@@ -506,15 +506,15 @@ int pa_check_prefill(const int32_t* block_tables, const int32_t* context_lens, c
 /*
  * pa_measure_read — a measurement helper, not a step of the method: reads
  * the `bytes` bytes of `buf` once with 16-byte loads (non-temporal when
- * `nontemporal` is nonzero, as the decode's KV loads are), thread t of the
- * grid taking 16-byte units t, t + S, t + 2 S, ... (S threads in all), spread
- * over workgroups_per_cu workgroups of 256 threads per compute unit.  Its rate,
- * timed beside the decode, is the streaming-read ceiling of the same byte
- * count on the same device.
+ * `nontemporal` is nonzero, as the decode's KV loads are): workgroups_per_cu
+ * workgroups of 256 threads per compute unit, each streaming one contiguous
+ * chunk of the buffer.  Its rate, timed beside the decode, is the
+ * streaming-read ceiling of the same byte count on the same device.
  *   buf    device, 16-byte aligned, bytes a multiple of 16 (0: nothing enqueued)
  *   sink   device, one uint32 the kernel may write (it keeps the loads live)
  * Returns PA_OK, PA_ERR_NULL, PA_ERR_ALIGN, PA_ERR_SHAPE (bytes not a multiple
- * of 16, workgroups_per_cu outside 1..64) or PA_ERR_LAUNCH.
+ * of 16, workgroups_per_cu outside 1..64), PA_ERR_TOO_LARGE (a chunk of 2 GiB
+ * or more) or PA_ERR_LAUNCH.
  */
 int pa_measure_read(const void* buf, size_t bytes, int32_t workgroups_per_cu, int32_t nontemporal,
                     uint32_t* sink, void* stream);

@@ -65,6 +65,7 @@ static int32_t rows_per_wave(const pa_cache_desc* d) {
 // kv heads per wavefront: as many of a token's (adjacent) kv heads as one
 // load instruction covers, so each instruction reads contiguous runs.
 static int32_t kv_per_wave(const pa_cache_desc* d) {
+  if (d->layout == PA_LAYOUT_VLLM) return 1;   // a token's kv heads are not adjacent there
   int32_t kg = rows_per_wave(d);
   while (d->num_kv_heads % kg) kg >>= 1;
   return kg;
@@ -126,7 +127,6 @@ static int check_decode_sizes(int32_t B, int32_t H, int32_t W, const pa_cache_de
   if (st) return st;
   if (B <= 0 || H <= 0 || W <= 0) return PA_ERR_SHAPE;
   if (H % d->num_kv_heads) return PA_ERR_SHAPE;
-  if (d->layout == PA_LAYOUT_VLLM && d->dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
   if (partition_size < 0 || (partition_size && partition_size % d->block_size) ||
       partition_size > kMaxBlocksPerPartition * d->block_size)
     return PA_ERR_UNSUPPORTED;
@@ -155,6 +155,7 @@ static int check_decode_sizes(int32_t B, int32_t H, int32_t W, const pa_cache_de
   p.maxP = (int32_t)maxP;
   p.waves_per_unit = p.use_mfma ? 1 : waves_per_unit(B, d, p);
   p.tile_unroll = tile_unroll(d);
+  p.vllm = d->layout == PA_LAYOUT_VLLM;
   out->plan = p;
   const int64_t slots = (int64_t)B * H * maxP;
   out->ws_bytes = maxP > 1 ? (size_t)slots * ((size_t)d->head_dim + 2) * sizeof(float) : 0;
@@ -205,6 +206,17 @@ static int decode_params(void* out, const void* q, const void* k_cache, const vo
   p.SPB = 0;
   p.append = 0;
   return PA_OK;
+}
+
+// The partial kernel for the cache dtype and layout: bf16 on the matrix cores
+// (the P09 or the vLLM-layout tile loads), fp32 on the vector ALUs (either
+// layout, chosen by plan.vllm).
+static hipError_t launch_partials(const DecodeParams& prm, const pa_cache_desc* desc, const Checked& ck,
+                                  hipStream_t s) {
+  if (ck.plan.use_mfma)
+    return desc->layout == PA_LAYOUT_VLLM ? launch_decode_partials_vllm(prm, desc->head_dim, s)
+                                          : launch_decode_partials_mfma(prm, desc->head_dim, s);
+  return launch_decode_partials(prm, desc->dtype, desc->head_dim, ck.plan, s);
 }
 
 // Shared-prefix folding for a hint of `shared_tokens` leading tokens: whole
@@ -349,11 +361,7 @@ int pa_decode_append(void* out, const void* q, void* k_cache, void* v_cache, con
   if (st) return st;
   prm.append = 1;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const hipError_t e = desc->layout == PA_LAYOUT_VLLM
-                           ? launch_decode_partials_vllm(prm, desc->head_dim, s)
-                           : ck.plan.use_mfma ? launch_decode_partials_mfma(prm, desc->head_dim, s)
-                                              : launch_decode_partials(prm, desc->dtype, desc->head_dim, ck.plan, s);
-  if (e != hipSuccess) return PA_ERR_LAUNCH;
+  if (launch_partials(prm, desc, ck, s) != hipSuccess) return PA_ERR_LAUNCH;
   AppendArgs ap;
   ap.k_new = k_new;
   ap.v_new = v_new;
@@ -386,12 +394,7 @@ static int decode_common(bool partials, bool merge, void* out, const void* q,
   set_shared_prefix(prm, shared_tokens, ck);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (partials) {
-    const hipError_t e = desc->layout == PA_LAYOUT_VLLM
-                             ? launch_decode_partials_vllm(prm, desc->head_dim, s)
-                             : ck.plan.use_mfma
-                                   ? launch_decode_partials_mfma(prm, desc->head_dim, s)
-                                   : launch_decode_partials(prm, desc->dtype, desc->head_dim, ck.plan, s);
-    if (e != hipSuccess) return PA_ERR_LAUNCH;
+    if (launch_partials(prm, desc, ck, s) != hipSuccess) return PA_ERR_LAUNCH;
   }
   if (merge && ck.plan.maxP > 1 &&
       launch_decode_merge(prm, desc->dtype, desc->head_dim, s) != hipSuccess)
@@ -487,7 +490,6 @@ static int prefill_shape(int32_t B, int32_t H, int32_t W, int32_t T, const pa_ca
   if (H % d->num_kv_heads) return PA_ERR_SHAPE;
   PrefillShape p{};
   if (d->dtype == PA_F32) {
-    if (d->layout != PA_LAYOUT_P09) return PA_ERR_UNSUPPORTED;   // the fp32 path decodes per row
     if (T > 65535) return PA_ERR_TOO_LARGE;
     const int64_t max_len = (int64_t)W * d->block_size;
     const int32_t P = (int32_t)(max_len < 64LL * d->block_size ? max_len : 64LL * d->block_size);

@@ -192,7 +192,15 @@ __device__ __forceinline__ u32x4 load16(const void* p) {
 // the same softmax.  Raising m rescales the accumulators by 2^(m_old - m_new).
 constexpr float kRescaleSlack = 8.0f;
 
-template <typename E, int D, int GC, int U, int KG, int NW>
+// VL: the caches are in vLLM's layout ("PagedAttention kernel：paged KV cache 与
+// block table", 深入原理): K [NB, KVH, D/x, bs, x] with x = 16 bytes of
+// elements, so the lane's 16-byte piece c of a token's K row is group c of the
+// (block, kv head)'s [D/x][bs][x] region; V [NB, KVH, D, bs], so its EPV
+// elements of a token are EPV 4-byte-or-smaller reads bs elements apart (fp32:
+// four 4-byte loads per piece).  The tile, the lanes' rows and the fold are
+// the same as in the P09 layout; only the load offsets change (KG = 1: a
+// token's kv heads are not adjacent there).
+template <typename E, int D, int GC, int U, int KG, int NW, bool VL = false>
 __global__ __launch_bounds__(64 * NW) void decode_partial_kernel(const DecodeParams prm) {
   constexpr int EPV = E::EPV;
   constexpr int LPT = D / EPV;       // lanes per (token, kv head) row of D elements
@@ -282,9 +290,35 @@ __global__ __launch_bounds__(64 * NW) void decode_partial_kernel(const DecodePar
   // return zeros without touching memory.
   u32x4 kA[U], vA[U], kB[U], vB[U];
 
+  // vLLM layout: per-lane offsets inside a (block, kv head) region, and the
+  // region's byte size (the same for K and V: D * bs elements)
+  const uint32_t vl_region = (uint32_t)D * ESZ << prm.bs_log2;
+  const uint32_t vl_k_off = (((uint32_t)c << prm.bs_log2) + (uint32_t)tr) * 16;
+  const uint32_t vl_v_off = (((uint32_t)(c * EPV) << prm.bs_log2) + (uint32_t)tr) * ESZ;
   auto load_tile = [&](int tile, u32x4 (&kr)[U], u32x4 (&vr)[U]) -> bool {
     const int phys = __builtin_amdgcn_readlane(tbl_v, (tile >> prm.bs_log2) - j_first);
     const bool ok = (unsigned)phys < (unsigned)prm.NB;
+    if constexpr (VL) {
+      static_assert(KG == 1 && E::EPV == 4, "vLLM layout: fp32, one kv head per row of lanes");
+      // one resource over the (block, kv head) region, empty outside the pool
+      // (KG = 1: kvh is the same for every lane)
+      const size_t boff = (size_t)(ok ? phys : 0) * blk_bytes + (size_t)kvh * vl_region;
+      const int nrec = ok ? (int)vl_region : 0;
+      const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(kc + boff), (short)0, nrec, kRsrcWord3);
+      const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vc + boff), (short)0, nrec, kRsrcWord3);
+      const uint32_t t0 = (uint32_t)(tile & prm.bs_mask);     // the tile's first row in its block
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        kr[u] = __builtin_amdgcn_raw_buffer_load_b128(rk, vl_k_off, (t0 + u * TR) * 16, 0);
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          vr[u][e] = __builtin_amdgcn_raw_buffer_load_b32(rv, vl_v_off + ((uint32_t)e << prm.bs_log2) * ESZ,
+                                                          (t0 + u * TR) * ESZ, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      return ok;
+    }
     const size_t off = (size_t)(ok ? phys : 0) * blk_bytes + (size_t)(tile & prm.bs_mask) * row_bytes;
     const int nrec = ok ? (int)tile_bytes : 0;
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(kc + off), (short)0, nrec, kRsrcWord3);
@@ -675,16 +709,27 @@ __global__ __launch_bounds__(64) void decode_merge_append_kernel(const DecodePar
     const size_t off = (size_t)(slot & prm.bs_mask);
     const size_t bs = (size_t)1 << prm.bs_log2;
     if constexpr (Vllm) {
-      // K [NB, KVH, D/8, bs, 8]: d .. d + 3 lie in one 8-element group
       const size_t kb = (blk * prm.KVH + kvh) * D;   // element base of the (block, head) K and V blocks
-      const uint2 kw = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(ap.k_new) + row);
-      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(ap.k_cache) + kb * bs + (size_t)(dl >> 3) * bs * 8 +
-                                off * 8 + (dl & 7)) = kw;
-      // V [NB, KVH, D, bs]: element d at column off of row d
-      const uint16_t* vs = static_cast<const uint16_t*>(ap.v_new) + row;
-      uint16_t* vd = static_cast<uint16_t*>(ap.v_cache) + (kb + dl) * bs + off;
+      if constexpr (E::EPV == 8) {
+        // K [NB, KVH, D/8, bs, 8]: d .. d + 3 lie in one 8-element group
+        const uint2 kw = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(ap.k_new) + row);
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(ap.k_cache) + kb * bs + (size_t)(dl >> 3) * bs * 8 +
+                                  off * 8 + (dl & 7)) = kw;
+        // V [NB, KVH, D, bs]: element d at column off of row d
+        const uint16_t* vs = static_cast<const uint16_t*>(ap.v_new) + row;
+        uint16_t* vd = static_cast<uint16_t*>(ap.v_cache) + (kb + dl) * bs + off;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) vd[(size_t)e * bs] = vs[e];
+        for (int e = 0; e < 4; ++e) vd[(size_t)e * bs] = vs[e];
+      } else {
+        // fp32: K [NB, KVH, D/4, bs, 4]: d .. d + 3 are exactly group d / 4
+        const uint4 kw = *reinterpret_cast<const uint4*>(static_cast<const uint32_t*>(ap.k_new) + row);
+        *reinterpret_cast<uint4*>(static_cast<uint32_t*>(ap.k_cache) + kb * bs + (size_t)(dl >> 2) * bs * 4 +
+                                  off * 4) = kw;
+        const uint32_t* vs = static_cast<const uint32_t*>(ap.v_new) + row;
+        uint32_t* vd = static_cast<uint32_t*>(ap.v_cache) + (kb + dl) * bs + off;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vd[(size_t)e * bs] = vs[e];
+      }
     } else {
       const size_t dst = (size_t)slot * prm.KVH * D + (size_t)kvh * D + dl;
       if constexpr (E::EPV == 8) {
@@ -706,20 +751,27 @@ __global__ __launch_bounds__(64) void decode_merge_append_kernel(const DecodePar
 // launchers
 // ---------------------------------------------------------------------------
 template <typename E, int D, int GC, int U, int KG, int NW>
-static hipError_t launch_partial_nw(const DecodeParams& prm, hipStream_t stream) {
+static hipError_t launch_partial_nw(const DecodeParams& prm, bool vllm, hipStream_t stream) {
   constexpr size_t kLds = NW > 1 ? (size_t)NW * 64 * GC * (E::EPV + 2) * sizeof(float) : 0;
   dim3 grid((prm.KVH / KG) * prm.nchunks, prm.maxP, prm.B);
-  hipLaunchKernelGGL((decode_partial_kernel<E, D, GC, U, KG, NW>), grid, dim3(64 * NW), kLds, stream, prm);
+  if (vllm) {
+    if constexpr (KG == 1 && E::EPV == 4)
+      hipLaunchKernelGGL((decode_partial_kernel<E, D, GC, U, KG, NW, true>), grid, dim3(64 * NW), kLds, stream, prm);
+    else
+      return hipErrorInvalidValue;
+  } else {
+    hipLaunchKernelGGL((decode_partial_kernel<E, D, GC, U, KG, NW>), grid, dim3(64 * NW), kLds, stream, prm);
+  }
   return hipGetLastError();
 }
 
 template <typename E, int D, int GC, int U, int KG>
-static hipError_t launch_partial_u(const DecodeParams& prm, int NW, hipStream_t stream) {
+static hipError_t launch_partial_u(const DecodeParams& prm, int NW, bool vllm, hipStream_t stream) {
   switch (NW) {
-    case 1: return launch_partial_nw<E, D, GC, U, KG, 1>(prm, stream);
-    case 2: return launch_partial_nw<E, D, GC, U, KG, 2>(prm, stream);
+    case 1: return launch_partial_nw<E, D, GC, U, KG, 1>(prm, vllm, stream);
+    case 2: return launch_partial_nw<E, D, GC, U, KG, 2>(prm, vllm, stream);
     case 4:
-      if constexpr (GC <= 4) return launch_partial_nw<E, D, GC, U, KG, 4>(prm, stream);
+      if constexpr (GC <= 4) return launch_partial_nw<E, D, GC, U, KG, 4>(prm, vllm, stream);
       break;
   }
   return hipErrorInvalidValue;
@@ -735,12 +787,12 @@ static hipError_t launch_partial_kg(const DecodeParams& prm, const DecodePlan& p
   } else {
     constexpr int TR = RPW / KG;
     switch (plan.tile_unroll) {
-      case 4: return launch_partial_u<E, D, GC, 4, KG>(prm, plan.waves_per_unit, stream);
+      case 4: return launch_partial_u<E, D, GC, 4, KG>(prm, plan.waves_per_unit, plan.vllm, stream);
       case 2:
-        if constexpr (TR >= 4) return launch_partial_u<E, D, GC, 2, KG>(prm, plan.waves_per_unit, stream);
+        if constexpr (TR >= 4) return launch_partial_u<E, D, GC, 2, KG>(prm, plan.waves_per_unit, plan.vllm, stream);
         break;
       case 1:
-        if constexpr (TR >= 8) return launch_partial_u<E, D, GC, 1, KG>(prm, plan.waves_per_unit, stream);
+        if constexpr (TR >= 8) return launch_partial_u<E, D, GC, 1, KG>(prm, plan.waves_per_unit, plan.vllm, stream);
         break;
     }
     return hipErrorInvalidValue;
@@ -819,7 +871,8 @@ static hipError_t launch_merge_append_e(const DecodeParams& prm, const AppendArg
 
 hipError_t launch_decode_merge_append(const DecodeParams& prm, const AppendArgs& ap, int32_t dtype, int32_t D,
                                       hipStream_t stream) {
-  if (dtype == 0) return ap.vllm ? hipErrorInvalidValue : launch_merge_append_e<F32, false>(prm, ap, D, stream);
+  if (dtype == 0) return ap.vllm ? launch_merge_append_e<F32, true>(prm, ap, D, stream)
+                                 : launch_merge_append_e<F32, false>(prm, ap, D, stream);
   return ap.vllm ? launch_merge_append_e<BF16, true>(prm, ap, D, stream)
                  : launch_merge_append_e<BF16, false>(prm, ap, D, stream);
 }

@@ -59,6 +59,7 @@ struct DecodePlan {
   int32_t kv_per_wave;     // kv heads whose rows one load instruction covers (KG)
   int32_t waves_per_unit;  // wavefronts of a workgroup sharing one unit's tiles (NW)
   int32_t tile_unroll;     // 16-byte loads per K (and per V) per tile and lane
+  int32_t vllm;            // caches in vLLM's layout (vector-ALU kernel: fp32 only)
 };
 
 // Prefill workspace header: one ticket counter per class of workgroups (the

@@ -15,26 +15,34 @@ typedef uint32_t u32x4r __attribute__((ext_vector_type(4)));
 constexpr int kReadThreads = 256;
 constexpr int kReadUnroll = 8;   // independent 16-byte loads in flight per lane
 
-// Thread t reads 16-byte units t, t + S, t + 2 S, ... (S = all threads of the
-// grid), kReadUnroll at a time; one instruction of a wavefront covers 1 KiB
-// of contiguous bytes.  The loaded words are folded into an XOR that is
-// stored only if it equals `tag`, a kernel argument the compiler cannot see
-// through, so the loads stay live (sink is a valid word either way).
-template <bool NT>
-__global__ __launch_bounds__(kReadThreads) void stream_read_kernel(const u32x4r* __restrict__ buf, uint64_t n16,
+// Workgroup w of G reads the w-th of G contiguous chunks of the buffer, 256
+// threads side by side (4 KiB per round of one load each) and kReadUnroll
+// loads in flight per lane, through a buffer resource over its chunk (loads
+// past the chunk's end read zeros; aux 2 = non-temporal).  One contiguous
+// stream per workgroup measured fastest of the access orders tried on
+// MI355X (grid-strided 1 KiB pieces: 6% slower on 538 MB).  The loaded words
+// are folded into an XOR that is stored only if it equals `tag`, a kernel
+// argument the compiler cannot see through, so the loads stay live (sink is a
+// valid word either way).
+template <int AUX>
+__global__ __launch_bounds__(kReadThreads) void stream_read_kernel(const char* __restrict__ buf, uint64_t n16,
                                                                    uint32_t* __restrict__ sink, uint32_t tag) {
-  const uint64_t stride = (uint64_t)gridDim.x * kReadThreads;
-  uint64_t i = (uint64_t)blockIdx.x * kReadThreads + threadIdx.x;
+  const uint64_t chunk = (n16 + gridDim.x - 1) / gridDim.x;      // 16-byte units per workgroup
+  const uint64_t lo = (uint64_t)blockIdx.x * chunk;
+  const uint64_t hi = lo + chunk < n16 ? lo + chunk : n16;
+  if (lo >= hi) return;
+  const uint32_t cnt = (uint32_t)(hi - lo);                      // < 2^27 by the host check
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(buf + lo * 16), (short)0, (int)(cnt * 16u), 0x00020000);
   u32x4r acc = {0u, 0u, 0u, 0u};
-  for (; i + (kReadUnroll - 1) * stride < n16; i += kReadUnroll * stride) {
+  for (uint32_t i = threadIdx.x; i < cnt; i += kReadUnroll * kReadThreads) {
     u32x4r v[kReadUnroll];
 #pragma unroll
     for (int k = 0; k < kReadUnroll; ++k)
-      v[k] = NT ? __builtin_nontemporal_load(buf + i + k * stride) : buf[i + k * stride];
+      v[k] = __builtin_bit_cast(u32x4r, __builtin_amdgcn_raw_buffer_load_b128(r, (i + k * kReadThreads) * 16u, 0, AUX));
 #pragma unroll
     for (int k = 0; k < kReadUnroll; ++k) acc ^= v[k];
   }
-  for (; i < n16; i += stride) acc ^= NT ? __builtin_nontemporal_load(buf + i) : buf[i];
   const uint32_t x = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
   if (x == tag) sink[0] = x;
 }
@@ -53,14 +61,17 @@ extern "C" int pa_measure_read(const void* buf, size_t bytes, int32_t workgroups
   if (bytes == 0) return PA_OK;
   const int cus = device_cus();
   if (cus <= 0) return PA_ERR_LAUNCH;
-  const dim3 grid((uint32_t)(cus * workgroups_per_cu));
+  const uint64_t groups = (uint64_t)cus * workgroups_per_cu;
+  const uint64_t n16 = bytes / 16;
+  // a workgroup's chunk is addressed by one buffer resource with 32-bit byte offsets
+  if ((n16 + groups - 1) / groups >= (1ull << 27)) return PA_ERR_TOO_LARGE;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  const u32x4r* p = static_cast<const u32x4r*>(buf);
+  const char* p = static_cast<const char*>(buf);
   if (nontemporal)
-    hipLaunchKernelGGL((stream_read_kernel<true>), grid, dim3(kReadThreads), 0, s, p, (uint64_t)(bytes / 16), sink,
+    hipLaunchKernelGGL((stream_read_kernel<2>), dim3((uint32_t)groups), dim3(kReadThreads), 0, s, p, n16, sink,
                        0x9E3779B9u);
   else
-    hipLaunchKernelGGL((stream_read_kernel<false>), grid, dim3(kReadThreads), 0, s, p, (uint64_t)(bytes / 16), sink,
+    hipLaunchKernelGGL((stream_read_kernel<0>), dim3((uint32_t)groups), dim3(kReadThreads), 0, s, p, n16, sink,
                        0x9E3779B9u);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }

@@ -138,14 +138,85 @@ def test_decode_vllm_matches_p09_layout_kernel():
     assert (a.float() - b.float()).abs().max().item() <= 2e-2
 
 
-def test_vllm_layout_rejects_f32_decode_and_prefill():
-    kc = torch.zeros((4, 2, 16, 16, 4), dtype=torch.float32, device="cuda")   # D = 64, x = 4
-    vc = torch.zeros((4, 2, 64, 16), dtype=torch.float32, device="cuda")
-    q = torch.zeros((1, 4, 64), dtype=torch.float32, device="cuda")
-    bt = torch.zeros((1, 1), dtype=torch.int32, device="cuda")
-    cl = torch.ones((1,), dtype=torch.int32, device="cuda")
-    with pytest.raises(pk.PaError):
-        pk.decode(q, kc, vc, bt, cl, 1.0, workspace=torch.empty(16, dtype=torch.uint8, device="cuda"))
-    with pytest.raises(pk.PaError):
-        pk.prefill(q, kc, vc, bt, cl, torch.tensor([0, 1], dtype=torch.int32, device="cuda"), 1.0,
-                   workspace=torch.empty(64, dtype=torch.uint8, device="cuda"))
+# fp32 caches in vLLM's layout (x = 4 elements per 16-byte K group): the
+# vector-ALU decode kernel (D, bs, KVH, G, lengths)
+F32_CASES = [
+    (64, 16, 2, 4, [1, 16, 40, 200, 193]),
+    (128, 8, 2, 3, [1, 8, 9, 77, 300]),
+    (256, 32, 1, 2, [5, 32, 33, 500]),
+    (64, 64, 4, 1, [63, 64, 65, 1000]),
+]
+
+
+@pytest.mark.parametrize("case", F32_CASES, ids=lambda c: f"f32_D{c[0]}_bs{c[1]}_KVH{c[2]}_G{c[3]}")
+@pytest.mark.parametrize("partition_size", [0, 64])
+def test_decode_vllm_layout_f32(case, partition_size):
+    """fp32 write then decode in vLLM's layout on NaN-poisoned pools with
+    99999 table tails, held to the fp32 tolerance (max-abs 1e-5)."""
+    D, bs, KVH, G, lens = case
+    if partition_size and partition_size % bs:
+        pytest.skip("partition must be a block multiple")
+    w = make_custom(num_seqs=len(lens), num_heads=KVH * G, num_kv_heads=KVH, head_dim=D, block_size=bs,
+                    dtype="f32", lens=lens, seed=D + bs + KVH + 1, device="cuda", poison=True)
+    kc, vc = _gpu_write(w)
+    out = pk.decode(w.q, kc, vc, w.block_tables, w.context_lens, w.scale, partition_size=partition_size)
+    torch.cuda.synchronize()
+    kp, vp = _oracle(w)
+    assert np.array_equal(_bits(stored_np(kc)), _bits(kp)) and np.array_equal(_bits(stored_np(vc)), _bits(vp))
+    ref = O.decode_vllm(stored_np(w.q), kp, vp, stored_np(w.block_tables), stored_np(w.context_lens), w.scale,
+                        "f32")
+    err = assert_matches_oracle(out, ref, "f32", f"f32 vllm D{D} bs{bs} P{partition_size}")
+    _say(f"f32 D{D} bs{bs} KVH{KVH} G{G} P{partition_size}: max err {err:.2e}")
+
+
+def test_tiny_f32_config_vllm_layout():
+    """The tiny fp32 workload (n = 1 and 192 included, one -1 padding row) in
+    vLLM's layout: write bit for bit, decode at several partition sizes."""
+    w = make_workload(CONFIGS["tiny_f32"], "cuda")
+    kc, vc = _gpu_write(w)
+    kp, vp = _oracle(w)
+    assert np.array_equal(_bits(stored_np(kc)), _bits(kp)) and np.array_equal(_bits(stored_np(vc)), _bits(vp))
+    ref = O.decode_vllm(stored_np(w.q), kp, vp, stored_np(w.block_tables), stored_np(w.context_lens), w.scale,
+                        "f32")
+    for P in (0, 16, 48, 128):
+        out = pk.decode(w.q, kc, vc, w.block_tables, w.context_lens, w.scale, partition_size=P)
+        torch.cuda.synchronize()
+        assert_matches_oracle(out, ref, "f32", f"tiny_f32 vllm P={P}")
+
+
+def test_prefill_and_append_vllm_layout_f32():
+    """fp32 prefill (one decode per query row) and the fp32 append step on
+    caches in vLLM's layout."""
+    from synth import make_new_rows, make_prefill_custom
+    wp = make_prefill_custom(num_heads=8, num_kv_heads=2, head_dim=64, block_size=16, cached=[0, 37, 200],
+                             new=[20, 33, 9], dtype="f32", seed=71, device="cuda", poison=True)
+    kc, vc = to_vllm_layout(wp.k_cache, wp.v_cache)
+    pk.write_kv(kc, vc, wp.k_new, wp.v_new, wp.slot_mapping)
+    out = pk.prefill(wp.q, kc, vc, wp.block_tables, wp.context_lens, wp.query_start_loc, wp.scale)
+    torch.cuda.synchronize()
+    ko, vo = stored_np(wp.k_cache).copy(), stored_np(wp.v_cache).copy()
+    O.write_kv(ko, vo, stored_np(wp.k_new), stored_np(wp.v_new), stored_np(wp.slot_mapping))
+    assert np.array_equal(_bits(stored_np(kc)), _bits(O.pack_k_vllm(ko, "f32")))
+    ref = O.prefill(stored_np(wp.q), ko, vo, stored_np(wp.block_tables), stored_np(wp.context_lens),
+                    stored_np(wp.query_start_loc), wp.scale, "f32")
+    err = assert_matches_oracle(out, ref, "f32", "f32 vllm prefill")
+    _say(f"f32 vLLM-layout prefill: max err {err:.2e}")
+    # append step: every sequence's newest token is new
+    w = make_custom(num_seqs=4, num_heads=8, num_kv_heads=2, head_dim=128, block_size=16, dtype="f32",
+                    lens=[1, 17, 64, 300], seed=72, device="cuda", poison=True)
+    B = 4
+    n = stored_np(w.context_lens).astype(np.int64)
+    tbl = stored_np(w.block_tables)
+    slots = np.array([tbl[b, (n[b] - 1) // 16] * 16 + (n[b] - 1) % 16 for b in range(B)], dtype=np.int64)
+    k_new, v_new = make_new_rows(B, 2, 128, "f32", 73, "cuda")
+    kc, vc = to_vllm_layout(w.k_cache, w.v_cache)
+    out = pk.decode_append(w.q, kc, vc, k_new, v_new, torch.from_numpy(slots).cuda(), w.block_tables,
+                           (w.context_lens - 1).to(torch.int32), w.scale, partition_size=64)
+    torch.cuda.synchronize()
+    ko, vo = stored_np(w.k_cache).copy(), stored_np(w.v_cache).copy()
+    O.write_kv(ko, vo, stored_np(k_new), stored_np(v_new), slots)
+    assert np.array_equal(_bits(stored_np(kc)), _bits(O.pack_k_vllm(ko, "f32")))
+    assert np.array_equal(_bits(stored_np(vc)), _bits(O.pack_v_vllm(vo)))
+    ref = O.decode(stored_np(w.q), ko, vo, tbl, stored_np(w.context_lens), w.scale, "f32")
+    err = assert_matches_oracle(out, ref, "f32", "f32 vllm append")
+    _say(f"f32 vLLM-layout append step: caches bit-exact, max err {err:.2e}")

@@ -127,7 +127,7 @@ def test_prefill_host_checks():
         ptr, ptr, ptr, ptr, ptr, ptr, ptr, 0.1, B, H, W, T, ctypes.byref(desc), ws, wsb, None)
     assert call(f32) == -1                       # fp32 is accepted (then: null pointers)
     assert call(pk.CacheDesc(64, 16, 2, 128, 1, 1)) == -1   # vLLM layout, bf16: accepted (then null)
-    assert call(pk.CacheDesc(64, 16, 2, 128, 0, 1)) == -3   # vLLM layout, fp32: PA_ERR_UNSUPPORTED
+    assert call(pk.CacheDesc(64, 16, 2, 128, 0, 1)) == -1   # vLLM layout, fp32: accepted (then null)
     assert call(bf16, H=7) == -2                 # H % KVH != 0
     assert call(bf16, B=0) == -2
     assert call(bf16, T=-1) == -2
@@ -150,15 +150,19 @@ def test_prefill_host_checks():
 
 
 def test_layout_support_matrix():
-    """The vLLM cache layout: the write takes both dtypes, the decode and the
-    prefill bf16 only (fp32 is reported before any launch)."""
+    """vLLM's cache layout is accepted by the write, the decode and the
+    prefill in both dtypes (fp32 decode: one kv head per row of lanes)."""
     lib = pk.load_library()
     vb, vf = _desc(layout=1), _desc(layout=1, dtype=0)
     assert lib.pa_write_kv(None, None, None, None, None, 4, ctypes.byref(vf), None) == -1   # accepted, then null
     assert lib.pa_decode_partition_size(4, 32, 64, ctypes.byref(vb)) > 0
-    assert lib.pa_decode_partition_size(4, 32, 64, ctypes.byref(vf)) == -3
+    assert lib.pa_decode_partition_size(4, 32, 64, ctypes.byref(vf)) > 0
     assert lib.pa_prefill_workspace_bytes(4, 32, 8, 100, ctypes.byref(vb)) > 0
-    assert lib.pa_prefill_workspace_bytes(4, 32, 8, 100, ctypes.byref(vf)) == 0
+    assert lib.pa_prefill_workspace_bytes(4, 32, 8, 100, ctypes.byref(vf)) > 0
+    # same sizes, same workspace need in either layout
+    pf = _desc(dtype=0)
+    assert lib.pa_decode_workspace_bytes(4, 32, 64, ctypes.byref(vf), 64) == \
+        lib.pa_decode_workspace_bytes(4, 32, 64, ctypes.byref(pf), 64)
 
 
 def test_shared_prefix_host_checks():
