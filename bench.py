@@ -642,12 +642,14 @@ def run_graph_compare(args, cfg):
     print(json.dumps(res), flush=True)
 
 
-def trace_summary(csv_path: str, groups: int) -> None:
+def trace_summary(csv_path: str, warmup: int, steps_timed: int) -> None:
     """Summary of a rocprofv3 --kernel-trace CSV of a --graph-compare run: the
-    library's kernels that follow each flush form one step; the first `groups`
-    steps are eager, the last `groups` graph replays.  Prints, per kind, the
-    time from the flush kernel's end to the step's first kernel, the gaps
-    between the step's kernels, the step's span and each kernel's duration."""
+    library's kernels from a write that follows a flush up to the next write
+    form one step; of the flushed steps, the first warmup + steps are eager
+    (the timed ones after the warm-up are summarised) and the last `steps`
+    are the timed graph replays.  Prints, per kind, the time from the flush
+    kernel's end to the step's first kernel, the gaps between the step's
+    kernels, the step's span and each kernel's duration."""
     import csv
     rows = sorted(csv.DictReader(open(csv_path)), key=lambda r: int(r["Start_Timestamp"]))
     ks = [(r["Kernel_Name"].split("(")[0], int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in rows]
@@ -655,14 +657,14 @@ def trace_summary(csv_path: str, groups: int) -> None:
     for i, (n, a, b) in enumerate(ks):
         if "write_kv_kernel" in n and i > 0 and "reduce_kernel" in ks[i - 1][0]:
             j, st = i, []
-            while j < len(ks) and "pa::" in ks[j][0]:
+            while j < len(ks) and "pa::" in ks[j][0] and (j == i or "write_kv_kernel" not in ks[j][0]):
                 st.append(ks[j])
                 j += 1
             steps.append((ks[i - 1][2], st))
     print("| step | steps | flush end -> first kernel (us) | gaps between the step's kernels (us) | "
           "first start -> last end (us) | kernel durations (us) |")
     print("|---|---|---|---|---|---|")
-    for lab, sts in (("eager", steps[:groups]), ("graph replay", steps[-groups:])):
+    for lab, sts in (("eager", steps[warmup:warmup + steps_timed]), ("graph replay", steps[-steps_timed:])):
         g0 = [st[0][1] - fe for fe, st in sts]
         span = [st[-1][2] - st[0][1] for fe, st in sts]
         inner = [y[1] - x[2] for fe, st in sts for x, y in zip(st, st[1:])]
@@ -721,7 +723,7 @@ def main():
         return
 
     if args.trace_summary:
-        return trace_summary(args.trace_summary, args.warmup + args.steps)
+        return trace_summary(args.trace_summary, args.warmup, args.steps)
 
     if args.config == "prefix_serving_host":
         return run_block_manager(args)
