@@ -742,13 +742,43 @@ __global__ __launch_bounds__(64 * NW) void decode_partial_mfma_kernel(const Deco
   // Shared prefix: every wavefront compares a share of the (sequence, entry)
   // pairs of the shared partitions with row 0 (SP * P <= W * bs keeps every
   // entry inside its row); a mismatch marks the sequence in s_skip (all
-  // writers store 1).  Loads go out 16 at a time at clamped indices.
+  // writers store 1).  Loads go out 16 at a time at clamped indices.  When
+  // the rows are 16-byte aligned (the table 16-byte aligned, W a multiple of
+  // 4) a load compares 4 entries: the quads cover entries up to
+  // 4 * ceil(SPB / 4) <= W, and entries past SPB are ignored.
   if (prm.SP > 0) {
     for (int b = threadIdx.x; b < B; b += 64 * NW) s_skip[b] = 0;
     __syncthreads();
     const int spb = prm.SPB;
-    const int total = B * spb;
     constexpr int kU = 16;
+    const bool quads = (prm.W & 3) == 0 && (reinterpret_cast<uintptr_t>(prm.tables) & 15u) == 0;
+    if (quads) {
+      typedef int32_t i32x4t __attribute__((ext_vector_type(4)));
+      const i32x4t* t4 = reinterpret_cast<const i32x4t*>(prm.tables);
+      const int spb4 = (spb + 3) >> 2, w4 = prm.W >> 2;
+      const int total4 = B * spb4;
+      for (int e0 = threadIdx.x; e0 < total4; e0 += 64 * NW * kU) {
+        i32x4t mine[kU], ref[kU];
+        int who[kU], jq[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          const int e = min(e0 + u * 64 * NW, total4 - 1);
+          const int b = e / spb4, j = e - b * spb4;
+          who[u] = b;
+          jq[u] = j;
+          mine[u] = t4[(size_t)b * w4 + j];
+          ref[u] = t4[j];
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          bool diff = false;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) diff |= (4 * jq[u] + i < spb) && mine[u][i] != ref[u][i];
+          if (diff) s_skip[who[u]] = 1;
+        }
+      }
+    }
+    const int total = quads ? 0 : B * spb;
     for (int e0 = threadIdx.x; e0 < total; e0 += 64 * NW * kU) {
       int mine[kU], ref[kU], who[kU];
 #pragma unroll

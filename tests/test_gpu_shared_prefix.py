@@ -182,3 +182,34 @@ def test_prefix_shared_workload_full_size():
     diff = (out.float() - plain.float()).abs()
     _say(f"prefix_shared_bf16: P {P}, all {B} sequences: max err {err:.2e} (pa_decode {err_plain:.2e}), "
          f"max |shared - plain| {float(diff.max()):.2e}")
+
+
+@pytest.mark.parametrize("extra", [0, 1, 2, 3, "misaligned"])
+def test_table_check_widths_and_alignment(extra):
+    """The shared-prefix table check reads 4 entries per load when the rows
+    are 16-byte aligned and one otherwise: table widths W of every residue
+    mod 4 (tails filled with 99999), and a table whose first entry is not
+    16-byte aligned, give the oracle's result; a row differing in the last
+    shared entry is caught by both forms."""
+    lens = [300, 129, 200, 140, 1000, 128, 70, 0, 400, 260, 131]
+    w = make_custom(num_seqs=len(lens), num_heads=8, num_kv_heads=2, head_dim=128, block_size=16, dtype="bf16",
+                    lens=lens, seed=91, device="cuda")
+    w = _share(w, range(len(lens)), 8, ())
+    tbl = w.block_tables.cpu().clone()
+    tbl[3, 7] = (tbl[3, 7] + 1) % w.num_blocks          # the last shared entry differs for row 3
+    B, W = tbl.shape
+    pad = 0 if extra == "misaligned" else (4 - W % 4 + extra) % 4
+    wide = torch.full((B, W + pad), 99999, dtype=torch.int32)
+    wide[:, :W] = tbl
+    if extra == "misaligned":
+        store = torch.zeros(B * W + 1, dtype=torch.int32, device="cuda")
+        t = store[1:].view(B, W)
+        t.copy_(wide.cuda())
+        assert t.is_contiguous() and t.data_ptr() % 16 != 0
+        w.block_tables = t
+    else:
+        w.block_tables = wide.cuda()
+    ref = _oracle(w)
+    out, _ = _run(w, 128, 64)
+    err = assert_matches_oracle(out, ref, "bf16", f"table width {w.block_tables.shape[1]} ({extra})")
+    _say(f"table width {w.block_tables.shape[1]} ({extra}): max err {err:.2e}")
