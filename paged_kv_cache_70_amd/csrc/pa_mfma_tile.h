@@ -40,9 +40,13 @@ __device__ __forceinline__ float groups_sum(float x) {
 }
 
 // LDS slot swizzle: 16-byte piece pc of token row t is stored at piece
-// pc ^ sw(t) of the row.  sw is a permutation of the 16 rows' residues so that
-// the K operand reads (16 rows, one piece each) and the transposed V reads
-// (4 rows, two adjacent pieces each) fall in distinct bank groups.
+// pc ^ sw(t) of the row, sw a permutation of the 16 rows' residues.  It was
+// chosen to spread the K operand reads (16 rows, one piece each) and the
+// transposed V reads (4 rows, two adjacent pieces each) over the banks, but
+// the hardware conflict counter (SQ_LDS_BANK_CONFLICT) reads about one
+// conflict cycle per LDS instruction with it, as with the identity and the
+// other swizzles tried, and none of them changed the kernels' times: which
+// instruction carries the conflicts is not established.
 template <int PPR>
 __device__ __forceinline__ int swz(int t) {
   if constexpr (PPR >= 16)

@@ -44,12 +44,13 @@ __global__ __launch_bounds__(256) void write_kv_kernel(
 // element per token slot, so consecutive slots of a block are adjacent
 // elements of a row (and, for K, adjacent 16-byte groups).
 //
-// A workgroup takes 16 new tokens and 32 of their 16-byte groups.  Stores run
-// with the token as the fastest lane index: when the 16 tokens occupy
+// A workgroup takes 16 new tokens and 32 of their 16-byte groups.  K stores
+// run with the token as the fastest lane index: when the 16 tokens occupy
 // consecutive slots (any prefill chunk, whatever its offset in the block),
-// each K group becomes one 256-byte run and each V row one 32-byte run, so a
-// wave's V store covers four adjacent rows.  V is first staged in LDS with
-// coalesced 16-byte reads, then read back transposed.
+// each K group becomes one 256-byte run.  V is first staged in LDS with
+// coalesced 16-byte reads, then read back transposed; runs of 16 bytes of
+// tokens (8 bf16, 4 fp32) in consecutive slots of one block, aligned, are
+// stored as one 16-byte store per V row.
 constexpr int kWTok = 16;        // tokens per workgroup
 constexpr int kWGrp = 32;        // 16-byte groups per workgroup
 constexpr int kWRow = kWGrp * 16 + 16;   // LDS bytes per token row (16 bytes of padding)
@@ -76,11 +77,31 @@ __global__ __launch_bounds__(256) void write_kv_vllm_kernel(
     *reinterpret_cast<u32x4*>(tile + i * kWRow + q * 16) = val;
   }
 
-  // This lane's token: slot, block and offset (invalid slots and tokens past
-  // the end store nothing).
+  // Each token's slot, block and offset, and for each run of GT = 16 bytes /
+  // element consecutive tokens whether they fill GT consecutive slots of one
+  // block starting at a multiple of GT (then one 16-byte store covers the run
+  // in every V row).  Invalid slots and tokens past the end store nothing.
+  constexpr uint32_t GT = X;                 // tokens per 16-byte V run
+  constexpr uint32_t NRUN = kWTok / GT;
+  __shared__ int64_t s_slot[kWTok];
+  __shared__ int32_t s_run[NRUN];
+  if (tid < kWTok) {
+    const int64_t sl = (t0 + tid < num_tokens) ? slots[t0 + tid] : -1;
+    s_slot[tid] = (sl >= 0 && sl < num_slots) ? sl : -1;
+  }
+  __syncthreads();
+  if (tid < NRUN) {
+    const int64_t first = s_slot[tid * GT];
+    bool run = first >= 0 && (first & (GT - 1)) == 0 && ((first & ((1 << bs_log2) - 1)) + GT) <= (1u << bs_log2);
+#pragma unroll
+    for (uint32_t j = 1; j < GT; ++j) run = run && s_slot[tid * GT + j] == first + (int64_t)j;
+    s_run[tid] = run ? 1 : 0;
+  }
+
+  // This lane's token for the K stores.
   const uint32_t i = lane & (kWTok - 1);
-  const int64_t s = (t0 + i < num_tokens) ? slots[t0 + i] : -1;
-  const bool live = s >= 0 && s < num_slots;
+  const int64_t s = s_slot[i];
+  const bool live = s >= 0;
   const size_t blk = live ? (size_t)(s >> bs_log2) : 0;
   const size_t off = live ? (size_t)(s & ((1 << bs_log2) - 1)) : 0;
 
@@ -95,15 +116,35 @@ __global__ __launch_bounds__(256) void write_kv_vllm_kernel(
   }
   __syncthreads();
 
-  // V: lane (token i, element e of the slice); four adjacent rows per wave
-  // store.  The padded LDS row stride puts the 16 tokens on distinct banks.
+  // V: thread (element e of the slice, run r of GT tokens).  A run of
+  // consecutive aligned slots is one 16-byte store of its GT elements of row e
+  // (gathered from the staged rows); otherwise each live token of the run
+  // stores its own element.  The padded LDS row stride puts the tokens of a
+  // run on distinct banks.
   const uint32_t elems = min((uint32_t)kWGrp, row_groups - g0) * X;
   const size_t row0 = (size_t)g0 * X;
   const size_t rows = (size_t)row_groups * X;
-  const E* trow = reinterpret_cast<const E*>(tile + i * kWRow);
-#pragma unroll 4
-  for (uint32_t e = (lane >> 4) + 4u * wave; e < kWGrp * X; e += 16u) {
-    if (live && e < elems) v_cache[((blk * rows + row0 + e) << bs_log2) + off] = trow[e];
+  for (uint32_t w = tid; w < kWGrp * X * NRUN; w += 256u) {
+    const uint32_t e = w / NRUN, r = w % NRUN;
+    if (e >= elems) continue;
+    E vals[GT];
+#pragma unroll
+    for (uint32_t j = 0; j < GT; ++j) vals[j] = reinterpret_cast<const E*>(tile + (r * GT + j) * kWRow)[e];
+    if (s_run[r]) {
+      const int64_t first = s_slot[r * GT];
+      const size_t b0 = (size_t)(first >> bs_log2), o0 = (size_t)(first & ((1 << bs_log2) - 1));
+      u32x4 pk;
+      __builtin_memcpy(&pk, vals, 16);
+      *reinterpret_cast<u32x4*>(v_cache + ((b0 * rows + row0 + e) << bs_log2) + o0) = pk;
+    } else {
+#pragma unroll
+      for (uint32_t j = 0; j < GT; ++j) {
+        const int64_t sj = s_slot[r * GT + j];
+        if (sj >= 0)
+          v_cache[(((size_t)(sj >> bs_log2) * rows + row0 + e) << bs_log2) + (size_t)(sj & ((1 << bs_log2) - 1))] =
+              vals[j];
+      }
+    }
   }
 }
 
