@@ -193,6 +193,36 @@ def _read_ceiling(nbytes: int, args, dev, do_flush) -> dict:
                     "step; the best of 1, 2 and 4 workgroups per CU"}
 
 
+def _mfma_ceiling(args, dev) -> dict:
+    """The matrix-core ceiling on this device, in this process: pa_measure_mfma
+    (independent bf16 16x16x32 products, no memory traffic) timed with events
+    at one, two and four workgroups of 4 wavefronts per CU; the best is the ceiling."""
+    import torch
+
+    import paged_kv_cache_70_amd as pk
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    iters = 8192
+    res = {}
+    for wpc in (1, 2, 4):
+        pk.measure_mfma(sink, iters, workgroups_per_cu=wpc)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(5)]
+        torch.cuda.synchronize()
+        flops = 0
+        for a, b in evs:
+            a.record()
+            flops = pk.measure_mfma(sink, iters, workgroups_per_cu=wpc)
+            b.record()
+        torch.cuda.synchronize()
+        us = sum(a.elapsed_time(b) for a, b in evs) / len(evs) * 1e3
+        res[wpc] = (flops / (us * 1e-6) / 1e12, us)
+    wpc = max(res, key=lambda k: res[k][0])
+    return {"TFLOPS": round(res[wpc][0], 1), "workgroups_per_cu": wpc, "us": round(res[wpc][1], 2),
+            "TFLOPS_by_workgroups_per_cu": {str(k): round(v[0], 1) for k, v in res.items()},
+            "what": "pa_measure_mfma: 8 independent v_mfma_f32_16x16x32_bf16 chains per wavefront on register "
+                    f"operands, {iters} rounds, events around the kernel; the best of 1, 2 and 4 workgroups of 4 "
+                    "wavefronts per CU"}
+
+
 def _cpu_baseline(w, budget_s: float):
     """The oracle (fp64 NumPy, untuned) on a bounded sample of the same
     workload: whole sequences in a fixed shuffled order, cycling through the
@@ -448,6 +478,10 @@ def run_prefill(args, cfg):
             "kernel": "prefill_mfma_kernel",
         },
     }
+    ceil = _mfma_ceiling(args, dev)
+    res["mfma_ceiling_TFLOPS"] = ceil["TFLOPS"]
+    res["frac_of_mfma_ceiling"] = round(achieved / ceil["TFLOPS"], 4)
+    res["mfma_ceiling"] = ceil
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = _cpu_baseline_prefill(w, args.cpu_budget)
     print(json.dumps(res), flush=True)

@@ -519,6 +519,18 @@ int pa_check_prefill(const int32_t* block_tables, const int32_t* context_lens, c
 int pa_measure_read(const void* buf, size_t bytes, int32_t workgroups_per_cu, int32_t nontemporal,
                     uint32_t* sink, void* stream);
 
+/*
+ * pa_measure_mfma — a measurement helper, not a step of the method: every
+ * wavefront of workgroups_per_cu workgroups of 256 threads per compute unit
+ * runs `iters` rounds of 8 independent v_mfma_f32_16x16x32_bf16 products on
+ * register operands (16,384 flops each; no memory traffic).  Its rate, timed
+ * beside the prefill, is the matrix-core ceiling the device sustains.
+ *   sink   device, one uint32 the kernel may write (it keeps the products live)
+ * Returns PA_OK, PA_ERR_NULL, PA_ERR_SHAPE (iters <= 0, workgroups_per_cu
+ * outside 1..8) or PA_ERR_LAUNCH.
+ */
+int pa_measure_mfma(int32_t iters, int32_t workgroups_per_cu, uint32_t* sink, void* stream);
+
 /* Static, NUL-terminated name of a pa_status code ("unknown status" otherwise). */
 const char* pa_status_string(int status);
 

@@ -27,6 +27,7 @@ from .api import (  # noqa: F401
     decode_partials,
     library_path,
     load_library,
+    measure_mfma,
     measure_read,
     new_append_workspace,
     new_workspace,

@@ -36,6 +36,7 @@ __all__ = [
     "decode_append",
     "decode_noalloc",
     "measure_read",
+    "measure_mfma",
     "check_write",
     "check_decode",
     "check_prefill",
@@ -109,6 +110,7 @@ def load_library() -> ctypes.CDLL:
                                             vp, sz, vp]),
         "pa_decode_noalloc": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, f32, i32, i32, i32, pdesc, i32, vp]),
         "pa_measure_read": (ctypes.c_int, [vp, sz, i32, i32, vp, vp]),
+        "pa_measure_mfma": (ctypes.c_int, [i32, i32, vp, vp]),
         "pa_check_write_workspace_bytes": (sz, [pdesc]),
         "pa_check_write": (ctypes.c_int, [vp, i32, pdesc, vp, vp, sz, vp]),
         "pa_check_decode": (ctypes.c_int, [vp, vp, i32, i32, pdesc, vp, vp]),
@@ -435,6 +437,16 @@ def measure_read(buf: torch.Tensor, sink: torch.Tensor, *, workgroups_per_cu: in
     st = load_library().pa_measure_read(_dev(buf, "buf"), nbytes, int(workgroups_per_cu), int(bool(nontemporal)),
                                         _dev(sink, "sink"), _stream(buf))
     _check("pa_measure_read", st)
+
+
+def measure_mfma(sink: torch.Tensor, iters: int, *, workgroups_per_cu: int = 1) -> int:
+    """Measurement helper: independent bf16 matrix products on every wavefront
+    (pa_measure_mfma); returns the flops enqueued."""
+    lib = load_library()
+    st = lib.pa_measure_mfma(int(iters), int(workgroups_per_cu), _dev(sink, "sink"), _stream(sink))
+    _check("pa_measure_mfma", st)
+    cus = torch.cuda.get_device_properties(sink.device).multi_processor_count
+    return cus * workgroups_per_cu * 4 * int(iters) * 8 * 16384
 
 
 def prefill_workspace(num_seqs: int, num_heads: int, max_blocks_per_seq: int, num_tokens: int,

@@ -1,8 +1,9 @@
-// Measurement helper (not a step of the method): a plain streaming read of a
-// device buffer with 16-byte loads, the access width of the decode's KV
-// gather, optionally non-temporal like the decode's loads.  Timed beside the
-// decode on the same box, its rate is the ceiling a gather of the same byte
-// count is measured against.
+// Measurement helpers (not steps of the method), timed beside the kernels on
+// the same device: a plain streaming read of a device buffer with 16-byte
+// loads, the access width of the decode's KV gather, optionally non-temporal
+// like the decode's loads (the ceiling a gather of the same byte count is
+// measured against); and a run of independent bf16 matrix products with no
+// memory traffic (the ceiling of the prefill's products).
 #include "../../include/paged_kv.h"
 #include "pa_internal.h"
 
@@ -47,6 +48,36 @@ __global__ __launch_bounds__(kReadThreads) void stream_read_kernel(const char* _
   if (x == tag) sink[0] = x;
 }
 
+// Matrix-core throughput: every wavefront runs `iters` rounds of 8
+// independent v_mfma_f32_16x16x32_bf16 chains on register operands (no
+// memory traffic), the product the bf16 prefill issues.  One wavefront per
+// SIMD keeps the pipe fed with 8 chains; the accumulators are folded into a
+// store guarded like the read's, so the products stay live.
+constexpr int kMfmaChains = 8;
+__global__ __launch_bounds__(256) void mfma_peak_kernel(int iters, uint32_t* __restrict__ sink, uint32_t tag) {
+  typedef __bf16 bf16x8m __attribute__((ext_vector_type(8)));
+  typedef float f32x4m __attribute__((ext_vector_type(4)));
+  const float x = (float)(threadIdx.x & 7) * 0.001f;
+  bf16x8m a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (__bf16)(x + (float)i);
+    b[i] = (__bf16)(x - (float)i);
+  }
+  f32x4m c[kMfmaChains];
+#pragma unroll
+  for (int k = 0; k < kMfmaChains; ++k) c[k] = f32x4m{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int k = 0; k < kMfmaChains; ++k) c[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c[k], 0, 0, 0);
+  }
+  float acc = 0.0f;
+#pragma unroll
+  for (int k = 0; k < kMfmaChains; ++k) acc += c[k][0] + c[k][1] + c[k][2] + c[k][3];
+  const uint32_t y = __float_as_uint(acc);
+  if (y == tag) sink[0] = y;
+}
+
 }  // namespace
 
 }  // namespace pa
@@ -73,5 +104,15 @@ extern "C" int pa_measure_read(const void* buf, size_t bytes, int32_t workgroups
   else
     hipLaunchKernelGGL((stream_read_kernel<0>), dim3((uint32_t)groups), dim3(kReadThreads), 0, s, p, n16, sink,
                        0x9E3779B9u);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+extern "C" int pa_measure_mfma(int32_t iters, int32_t workgroups_per_cu, uint32_t* sink, void* stream) {
+  if (!sink) return PA_ERR_NULL;
+  if (iters <= 0 || workgroups_per_cu <= 0 || workgroups_per_cu > 8) return PA_ERR_SHAPE;
+  const int cus = device_cus();
+  if (cus <= 0) return PA_ERR_LAUNCH;
+  hipLaunchKernelGGL(mfma_peak_kernel, dim3((uint32_t)(cus * workgroups_per_cu)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), iters, sink, 0x9E3779B9u);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
