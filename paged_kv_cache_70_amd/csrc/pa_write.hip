@@ -50,7 +50,9 @@ __global__ __launch_bounds__(256) void write_kv_kernel(
 // each K group becomes one 256-byte run.  V is first staged in LDS with
 // coalesced 16-byte reads, then read back transposed; runs of 16 bytes of
 // tokens (8 bf16, 4 fp32) in consecutive slots of one block, aligned, are
-// stored as one 16-byte store per V row.
+// stored as one 16-byte store per V row.  A workgroup with no such run (a
+// decode step's tokens, one per sequence) stores V element by element with
+// the token as the fastest lane index.
 constexpr int kWTok = 16;        // tokens per workgroup
 constexpr int kWGrp = 32;        // 16-byte groups per workgroup
 constexpr int kWRow = kWGrp * 16 + 16;   // LDS bytes per token row (16 bytes of padding)
@@ -67,70 +69,98 @@ __global__ __launch_bounds__(256) void write_kv_vllm_kernel(
   const uint32_t t0 = blockIdx.x * kWTok;
   const uint32_t g0 = blockIdx.y * kWGrp;
 
-  // Stage V: 16 rows of up to 32 groups, 32 consecutive threads per token row.
-#pragma unroll
-  for (uint32_t j = 0; j < kWTok * kWGrp / 256; ++j) {
-    const uint32_t idx = tid + 256u * j, i = idx / kWGrp, q = idx % kWGrp;
-    u32x4 val = {0u, 0u, 0u, 0u};
-    if (t0 + i < num_tokens && g0 + q < row_groups)
-      val = __builtin_nontemporal_load(&v[(size_t)(t0 + i) * row_groups + g0 + q]);
-    *reinterpret_cast<u32x4*>(tile + i * kWRow + q * 16) = val;
-  }
-
-  // Each token's slot, block and offset, and for each run of GT = 16 bytes /
-  // element consecutive tokens whether they fill GT consecutive slots of one
-  // block starting at a multiple of GT (then one 16-byte store covers the run
-  // in every V row).  Invalid slots and tokens past the end store nothing.
-  constexpr uint32_t GT = X;                 // tokens per 16-byte V run
-  constexpr uint32_t NRUN = kWTok / GT;
-  __shared__ int64_t s_slot[kWTok];
-  __shared__ int32_t s_run[NRUN];
-  if (tid < kWTok) {
-    const int64_t sl = (t0 + tid < num_tokens) ? slots[t0 + tid] : -1;
-    s_slot[tid] = (sl >= 0 && sl < num_slots) ? sl : -1;
-  }
-  __syncthreads();
-  if (tid < NRUN) {
-    const int64_t first = s_slot[tid * GT];
-    bool run = first >= 0 && (first & (GT - 1)) == 0 && ((first & ((1 << bs_log2) - 1)) + GT) <= (1u << bs_log2);
-#pragma unroll
-    for (uint32_t j = 1; j < GT; ++j) run = run && s_slot[tid * GT + j] == first + (int64_t)j;
-    s_run[tid] = run ? 1 : 0;
-  }
-
-  // This lane's token for the K stores.
+  // Every load is issued before the first barrier: this lane's slot (token
+  // i = lane mod 16), V's 16-byte pieces for the LDS stage, then the K groups
+  // this lane stores, which wait only for the slot.  For a few tokens (a
+  // decode step) the kernel is latency-bound, and the V and K loads overlap.
   const uint32_t i = lane & (kWTok - 1);
-  const int64_t s = s_slot[i];
+  int64_t s = (t0 + i < num_tokens) ? slots[t0 + i] : -1;
+  constexpr uint32_t NV = kWTok * kWGrp / 256;
+  u32x4 vreg[NV];
+#pragma unroll
+  for (uint32_t j = 0; j < NV; ++j) {
+    const uint32_t idx = tid + 256u * j, ti = idx / kWGrp, q = idx % kWGrp;
+    vreg[j] = u32x4{0u, 0u, 0u, 0u};
+    if (t0 + ti < num_tokens && g0 + q < row_groups)
+      vreg[j] = __builtin_nontemporal_load(&v[(size_t)(t0 + ti) * row_groups + g0 + q]);
+  }
+  s = (s >= 0 && s < num_slots) ? s : -1;   // invalid slots and tokens past the end store nothing
   const bool live = s >= 0;
   const size_t blk = live ? (size_t)(s >> bs_log2) : 0;
   const size_t off = live ? (size_t)(s & ((1 << bs_log2) - 1)) : 0;
-
   // K: lane (token i, group q); one 16-byte load and store per group.
+  constexpr uint32_t NK = kWGrp / 16;
+  u32x4 kreg[NK];
 #pragma unroll
-  for (uint32_t j = 0; j < kWGrp / 16; ++j) {
+  for (uint32_t j = 0; j < NK; ++j) {
     const uint32_t q = (lane >> 4) + 4u * wave + 16u * j;
-    if (live && g0 + q < row_groups) {
-      const u32x4 kv = __builtin_nontemporal_load(&k[(size_t)(t0 + i) * row_groups + g0 + q]);
-      k_cache[((blk * row_groups + g0 + q) << bs_log2) + off] = kv;
-    }
+    kreg[j] = u32x4{0u, 0u, 0u, 0u};
+    if (live && g0 + q < row_groups) kreg[j] = __builtin_nontemporal_load(&k[(size_t)(t0 + i) * row_groups + g0 + q]);
+  }
+
+  // Stage V: 16 rows of up to 32 groups, 32 consecutive threads per token row.
+#pragma unroll
+  for (uint32_t j = 0; j < NV; ++j) {
+    const uint32_t idx = tid + 256u * j, ti = idx / kWGrp, q = idx % kWGrp;
+    *reinterpret_cast<u32x4*>(tile + ti * kWRow + q * 16) = vreg[j];
+  }
+
+  // Runs: GT = 16 bytes / element consecutive tokens that fill GT
+  // consecutive slots of one block starting at a multiple of GT (then one
+  // 16-byte store covers the run in every V row).  Every wave holds the 16
+  // slots in lanes 0-15, so a ballot of "this token continues its run" gives
+  // the run flags, the same in every wave.
+  constexpr uint32_t GT = X;                 // tokens per 16-byte V run
+  constexpr uint32_t NRUN = kWTok / GT;
+  constexpr uint64_t kRunBits = (1ull << GT) - 1;
+  const int64_t prev = __shfl_up(s, 1u);
+  const bool starts = (i & (GT - 1)) == 0;
+  const bool link = starts ? (live && (s & (GT - 1)) == 0 && (off + GT) <= (1u << bs_log2))
+                           : (live && prev >= 0 && s == prev + 1);
+  const uint64_t links = __ballot(link);
+  bool any_run = false;
+#pragma unroll
+  for (uint32_t r = 0; r < NRUN; ++r) any_run |= ((links >> (r * GT)) & kRunBits) == kRunBits;
+
+  // Threads 0-15 are lanes 0-15 of wave 0: token tid.
+  __shared__ int64_t s_slot[kWTok];
+  if (tid < kWTok) s_slot[tid] = s;
+
+#pragma unroll
+  for (uint32_t j = 0; j < NK; ++j) {
+    const uint32_t q = (lane >> 4) + 4u * wave + 16u * j;
+    if (live && g0 + q < row_groups) k_cache[((blk * row_groups + g0 + q) << bs_log2) + off] = kreg[j];
   }
   __syncthreads();
 
-  // V: thread (element e of the slice, run r of GT tokens).  A run of
-  // consecutive aligned slots is one 16-byte store of its GT elements of row e
-  // (gathered from the staged rows); otherwise each live token of the run
-  // stores its own element.  The padded LDS row stride puts the tokens of a
-  // run on distinct banks.
   const uint32_t elems = min((uint32_t)kWGrp, row_groups - g0) * X;
   const size_t row0 = (size_t)g0 * X;
   const size_t rows = (size_t)row_groups * X;
+
+  // V without runs (the decode step's one token per sequence): lane (token i,
+  // element e), four adjacent rows of one token per wave store, block and
+  // offset computed once per lane.
+  if (!any_run) {
+    const E* trow = reinterpret_cast<const E*>(tile + i * kWRow);
+#pragma unroll 4
+    for (uint32_t e = (lane >> 4) + 4u * wave; e < kWGrp * X; e += 16u) {
+      if (live && e < elems) v_cache[((blk * rows + row0 + e) << bs_log2) + off] = trow[e];
+    }
+    return;
+  }
+
+  // V with runs: thread (element e of the slice, run r of GT tokens).  A run
+  // of consecutive aligned slots is one 16-byte store of its GT elements of
+  // row e (gathered from the staged rows); otherwise each live token of the
+  // run stores its own element.  The padded LDS row stride puts the tokens of
+  // a run on distinct banks.
   for (uint32_t w = tid; w < kWGrp * X * NRUN; w += 256u) {
     const uint32_t e = w / NRUN, r = w % NRUN;
     if (e >= elems) continue;
     E vals[GT];
 #pragma unroll
     for (uint32_t j = 0; j < GT; ++j) vals[j] = reinterpret_cast<const E*>(tile + (r * GT + j) * kWRow)[e];
-    if (s_run[r]) {
+    if (((links >> (r * GT)) & kRunBits) == kRunBits) {
       const int64_t first = s_slot[r * GT];
       const size_t b0 = (size_t)(first >> bs_log2), o0 = (size_t)(first & ((1 << bs_log2) - 1));
       u32x4 pk;
