@@ -83,8 +83,8 @@ typedef enum pa_layout {
   /* vLLM's, "PagedAttention kernel：paged KV cache 与 block table", 深入原理:
      k_cache [num_blocks, num_kv_heads, head_dim / x, block_size, x] with x
      elements = 16 bytes (8 for bf16, 4 for fp32), v_cache [num_blocks,
-     num_kv_heads, head_dim, block_size].  Supported by pa_write_kv (both
-     dtypes), the decode entry points and pa_prefill (bf16 only). */
+     num_kv_heads, head_dim, block_size].  Supported by pa_write_kv, the
+     decode entry points and pa_prefill, in both dtypes. */
   PA_LAYOUT_VLLM = 1
 } pa_layout;
 
@@ -159,7 +159,7 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads,
  *   out                 device, [B, H, D] of desc->dtype (written)
  *   q                   device, [B, H, D] of desc->dtype
  *   k_cache, v_cache    device, in desc->layout ([NB, bs, KVH, D] for PA_LAYOUT_P09)
- *                       of desc->dtype (PA_LAYOUT_VLLM: bf16 only)
+ *                       of desc->dtype
  *   block_tables        device, [B, max_blocks_per_seq] int32; only the first
  *                       ceil(context_lens[b] / bs) entries of row b are read
  *   context_lens        device, [B] int32, tokens of each sequence (0 gives zeros)
@@ -410,8 +410,7 @@ int pa_bm_fill_tables(const pa_block_manager* bm, const int64_t* seq_ids, int32_
  * it into the softmax and copies its rows, bit for bit, into the slot.
  *
  *   out, q            device, [num_seqs, H, D] of desc->dtype
- *   k_cache, v_cache  device, desc->layout (PA_LAYOUT_VLLM: bf16 only); the new
- *                     rows are written into them
+ *   k_cache, v_cache  device, desc->layout; the new rows are written into them
  *   k_new, v_new      device, [num_seqs, KVH, D] of desc->dtype
  *   slot_mapping      device, [num_seqs] int64
  *   cached_lens       device, [num_seqs] int32, tokens already in the cache

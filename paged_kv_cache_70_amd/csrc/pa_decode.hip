@@ -596,20 +596,30 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const DecodeParams prm
 // row written in it.  The new token is one more term of the softmax: score
 // s = q . k_new in the partials' base-2 units, weight 2^(s - M), value v_new.
 // ---------------------------------------------------------------------------
+// Four consecutive elements as raw bits (bf16: 8 bytes in .x, .y; fp32: 16
+// bytes), and the same widened to float.
 template <typename E>
-__device__ __forceinline__ void load4(const void* base, size_t idx, float (&f)[4]) {
+__device__ __forceinline__ uint4 raw4(const void* base, size_t idx) {
   if constexpr (E::EPV == 8) {
     const uint2 w = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(base) + idx);
+    return uint4{w.x, w.y, 0u, 0u};
+  } else {
+    return *reinterpret_cast<const uint4*>(static_cast<const uint32_t*>(base) + idx);
+  }
+}
+
+template <typename E>
+__device__ __forceinline__ void widen4(const uint4& w, float (&f)[4]) {
+  if constexpr (E::EPV == 8) {
     f[0] = __uint_as_float(w.x << 16);
     f[1] = __uint_as_float(w.x & 0xffff0000u);
     f[2] = __uint_as_float(w.y << 16);
     f[3] = __uint_as_float(w.y & 0xffff0000u);
   } else {
-    const float4 v = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + idx);
-    f[0] = v.x;
-    f[1] = v.y;
-    f[2] = v.z;
-    f[3] = v.w;
+    f[0] = __uint_as_float(w.x);
+    f[1] = __uint_as_float(w.y);
+    f[2] = __uint_as_float(w.z);
+    f[3] = __uint_as_float(w.w);
   }
 }
 
@@ -637,6 +647,55 @@ __global__ __launch_bounds__(64) void decode_merge_append_kernel(const DecodePar
   const float* ml = prm.ws_ml + bh * prm.maxP * 2;
   const float* acc = prm.ws_acc + bh * prm.maxP * D;
 
+  // The new token's q, k and v are read first, and the kv head's first query
+  // head stores its K and V rows into the slot at once (bit for bit), so the
+  // copy drains while the partials are merged.  The partial kernel read only
+  // the cached tokens, never this slot.
+  const size_t row = ((size_t)b * prm.KVH + kvh) * D + dl;   // this lane's d's of k_new / v_new
+  uint4 qraw = {0u, 0u, 0u, 0u}, kraw = {0u, 0u, 0u, 0u}, vraw = {0u, 0u, 0u, 0u};
+  if (has_new) {
+    qraw = raw4<E>(prm.q, bh * D + dl);
+    kraw = raw4<E>(ap.k_new, row);
+    vraw = raw4<E>(ap.v_new, row);
+  }
+  if (has_new && sub == 0 && h % (prm.H / prm.KVH) == 0) {
+    const size_t blk = (size_t)(slot >> prm.bs_log2);
+    const size_t off = (size_t)(slot & prm.bs_mask);
+    const size_t bs = (size_t)1 << prm.bs_log2;
+    if constexpr (Vllm) {
+      const size_t kb = (blk * prm.KVH + kvh) * D;   // element base of the (block, head) K and V blocks
+      if constexpr (E::EPV == 8) {
+        // K [NB, KVH, D/8, bs, 8]: d .. d + 3 lie in one 8-element group
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(ap.k_cache) + kb * bs + (size_t)(dl >> 3) * bs * 8 +
+                                  off * 8 + (dl & 7)) = uint2{kraw.x, kraw.y};
+        // V [NB, KVH, D, bs]: element d at column off of row d
+        uint16_t* vd = static_cast<uint16_t*>(ap.v_cache) + (kb + dl) * bs + off;
+        vd[0] = (uint16_t)(vraw.x & 0xffffu);
+        vd[bs] = (uint16_t)(vraw.x >> 16);
+        vd[2 * bs] = (uint16_t)(vraw.y & 0xffffu);
+        vd[3 * bs] = (uint16_t)(vraw.y >> 16);
+      } else {
+        // fp32: K [NB, KVH, D/4, bs, 4]: d .. d + 3 are exactly group d / 4
+        *reinterpret_cast<uint4*>(static_cast<uint32_t*>(ap.k_cache) + kb * bs + (size_t)(dl >> 2) * bs * 4 +
+                                  off * 4) = kraw;
+        uint32_t* vd = static_cast<uint32_t*>(ap.v_cache) + (kb + dl) * bs + off;
+        vd[0] = vraw.x;
+        vd[bs] = vraw.y;
+        vd[2 * bs] = vraw.z;
+        vd[3 * bs] = vraw.w;
+      }
+    } else {
+      const size_t dst = (size_t)slot * prm.KVH * D + (size_t)kvh * D + dl;
+      if constexpr (E::EPV == 8) {
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(ap.k_cache) + dst) = uint2{kraw.x, kraw.y};
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(ap.v_cache) + dst) = uint2{vraw.x, vraw.y};
+      } else {
+        *reinterpret_cast<uint4*>(static_cast<uint32_t*>(ap.k_cache) + dst) = kraw;
+        *reinterpret_cast<uint4*>(static_cast<uint32_t*>(ap.v_cache) + dst) = vraw;
+      }
+    }
+  }
+
   float Mrun = -INFINITY, Lrun = 0.0f;
   f4 o = {0.0f, 0.0f, 0.0f, 0.0f};
   for (int r0 = 0; r0 < nparts; r0 += R) {
@@ -659,12 +718,11 @@ __global__ __launch_bounds__(64) void decode_merge_append_kernel(const DecodePar
     for (int k = 0; k < KMAX; ++k) o += __shfl(w, sub + PPI * k) * a[k];
   }
 
-  const size_t row = ((size_t)b * prm.KVH + kvh) * D + dl;   // this lane's d's of k_new / v_new
   if (has_new) {
     float qf[4], kf[4], vf[4];
-    load4<E>(prm.q, bh * D + dl, qf);
-    load4<E>(ap.k_new, row, kf);
-    load4<E>(ap.v_new, row, vf);
+    widen4<E>(qraw, qf);
+    widen4<E>(kraw, kf);
+    widen4<E>(vraw, vf);
     float dot = qf[0] * kf[0] + qf[1] * kf[1] + qf[2] * kf[2] + qf[3] * kf[3];
 #pragma unroll
     for (int off = 1; off < LPP; off <<= 1) dot += __shfl_xor(dot, off);
@@ -698,50 +756,6 @@ __global__ __launch_bounds__(64) void decode_merge_append_kernel(const DecodePar
 #pragma unroll
         for (int e = 0; e < 4; ++e) { v[e] = o[e] * inv; v[4 + e] = w4[e]; }
         E::store(prm.out, bh * D + dl, v);
-      }
-    }
-  }
-
-  // The new token's K and V rows of this kv head, copied bit for bit into
-  // its slot by the kv head's first query head.
-  if (has_new && sub == 0 && h % (prm.H / prm.KVH) == 0) {
-    const size_t blk = (size_t)(slot >> prm.bs_log2);
-    const size_t off = (size_t)(slot & prm.bs_mask);
-    const size_t bs = (size_t)1 << prm.bs_log2;
-    if constexpr (Vllm) {
-      const size_t kb = (blk * prm.KVH + kvh) * D;   // element base of the (block, head) K and V blocks
-      if constexpr (E::EPV == 8) {
-        // K [NB, KVH, D/8, bs, 8]: d .. d + 3 lie in one 8-element group
-        const uint2 kw = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(ap.k_new) + row);
-        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(ap.k_cache) + kb * bs + (size_t)(dl >> 3) * bs * 8 +
-                                  off * 8 + (dl & 7)) = kw;
-        // V [NB, KVH, D, bs]: element d at column off of row d
-        const uint16_t* vs = static_cast<const uint16_t*>(ap.v_new) + row;
-        uint16_t* vd = static_cast<uint16_t*>(ap.v_cache) + (kb + dl) * bs + off;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) vd[(size_t)e * bs] = vs[e];
-      } else {
-        // fp32: K [NB, KVH, D/4, bs, 4]: d .. d + 3 are exactly group d / 4
-        const uint4 kw = *reinterpret_cast<const uint4*>(static_cast<const uint32_t*>(ap.k_new) + row);
-        *reinterpret_cast<uint4*>(static_cast<uint32_t*>(ap.k_cache) + kb * bs + (size_t)(dl >> 2) * bs * 4 +
-                                  off * 4) = kw;
-        const uint32_t* vs = static_cast<const uint32_t*>(ap.v_new) + row;
-        uint32_t* vd = static_cast<uint32_t*>(ap.v_cache) + (kb + dl) * bs + off;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) vd[(size_t)e * bs] = vs[e];
-      }
-    } else {
-      const size_t dst = (size_t)slot * prm.KVH * D + (size_t)kvh * D + dl;
-      if constexpr (E::EPV == 8) {
-        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(ap.k_cache) + dst) =
-            *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(ap.k_new) + row);
-        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(ap.v_cache) + dst) =
-            *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(ap.v_new) + row);
-      } else {
-        *reinterpret_cast<uint4*>(static_cast<uint32_t*>(ap.k_cache) + dst) =
-            *reinterpret_cast<const uint4*>(static_cast<const uint32_t*>(ap.k_new) + row);
-        *reinterpret_cast<uint4*>(static_cast<uint32_t*>(ap.v_cache) + dst) =
-            *reinterpret_cast<const uint4*>(static_cast<const uint32_t*>(ap.v_new) + row);
       }
     }
   }

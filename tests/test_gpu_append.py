@@ -90,14 +90,31 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("vllm", [False, True], ids=["p09", "vllm"])
 @pytest.mark.parametrize("case", CASES, ids=lambda c: f"{c[0]}_H{c[1]}_KVH{c[2]}_D{c[3]}_bs{c[4]}_P{c[5]}")
-def test_append_matches_write_then_decode(case):
+def test_append_matches_write_then_decode(case, vllm):
+    """Poisoned caches (every row that no sequence reads holds NaN), in both
+    layouts."""
     dtype, H, KVH, D, bs, P, lens, no_new = case
     w = make_custom(num_seqs=len(lens), num_heads=H, num_kv_heads=KVH, head_dim=D, block_size=bs, dtype=dtype,
                     lens=lens, seed=H + D + bs, device="cuda", poison=True)
-    out, ref = _step(w, no_new, partition_size=P)
+    out, ref = _step(w, no_new, vllm=vllm, partition_size=P)
     err = assert_matches_oracle(out, ref, dtype, f"append {dtype} H{H} D{D} bs{bs} P{P}")
-    _say(f"{dtype} H{H} KVH{KVH} D{D} bs{bs} P{P}: max err {err:.2e}")
+    _say(f"{dtype} H{H} KVH{KVH} D{D} bs{bs} P{P} {'vllm' if vllm else 'p09'}: max err {err:.2e}")
+
+
+@pytest.mark.parametrize("vllm", [False, True], ids=["p09", "vllm"])
+def test_append_beyond_persistent_list(vllm):
+    """4,100 sequences: more than the bf16 persistent kernel's list holds
+    (4,096), so the partials run in the grid form (the P09 layout's
+    matrix-core grid kernel, the vLLM layout's own)."""
+    rng = np.random.default_rng(4100)
+    lens = [int(x) for x in rng.integers(1, 40, size=4100)]
+    w = make_custom(num_seqs=len(lens), num_heads=8, num_kv_heads=2, head_dim=64, block_size=16, dtype="bf16",
+                    lens=lens, seed=4100, device="cuda")
+    out, ref = _step(w, (7, 4099), vllm=vllm)
+    err = assert_matches_oracle(out, ref, "bf16", "4,100 sequences")
+    _say(f"4,100 sequences ({'vllm' if vllm else 'p09'}): caches bit-exact, max err {err:.2e}")
 
 
 def test_append_padding_sequences_and_vllm_layout():
