@@ -1046,7 +1046,7 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
-            "kernel": PARTIAL_KERNELS[cfg.dtype] if args.layout == "p09" else "decode_partial_vllm_kernel",
+            "kernel": PARTIAL_KERNELS[cfg.dtype],
         },
     }
     if not args.no_cpu_baseline:
