@@ -72,8 +72,14 @@ CSRC = os.path.join(ROOT, "paged_kv_cache_70_amd", "csrc")
 # and its source file
 PARTIAL_KERNELS = {"bf16": "decode_partial_mfma_kernel", "f32": "decode_partial_kernel", "write": "write_kv_kernel",
                    "prefill": "prefill_mfma_kernel"}
-KERNEL_SRC = {"bf16": os.path.join(CSRC, "pa_decode_mfma.hip"), "f32": os.path.join(CSRC, "pa_decode.hip"),
-              "write": os.path.join(CSRC, "pa_write.hip"), "prefill": os.path.join(CSRC, "pa_prefill.hip")}
+# the sources each kernel is compiled from (its file, the shared parameter
+# structs, and the tile helpers the matrix-core kernels share)
+_INTERNAL = os.path.join(CSRC, "pa_internal.h")
+_TILE = os.path.join(CSRC, "pa_mfma_tile.h")
+KERNEL_SRC = {"bf16": [os.path.join(CSRC, "pa_decode_mfma.hip"), _INTERNAL, _TILE],
+              "f32": [os.path.join(CSRC, "pa_decode.hip"), _INTERNAL],
+              "write": [os.path.join(CSRC, "pa_write.hip"), _INTERNAL],
+              "prefill": [os.path.join(CSRC, "pa_prefill.hip"), _INTERNAL, _TILE]}
 
 
 def _traffic_file(key: str, workload: str) -> str:
@@ -82,8 +88,11 @@ def _traffic_file(key: str, workload: str) -> str:
 
 
 def _src_hash(key: str) -> str:
-    with open(KERNEL_SRC[key], "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SRC[key]:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def _traffic(workload: str, key: str):
