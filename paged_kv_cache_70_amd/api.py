@@ -53,6 +53,7 @@ __all__ = [
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB: Optional[ctypes.CDLL] = None
+_LIB_PATH: Optional[str] = None
 
 PA_F32, PA_BF16 = 0, 1
 _DTYPES = {torch.float32: PA_F32, torch.bfloat16: PA_BF16}
@@ -81,12 +82,16 @@ def library_path() -> str:
     return os.path.join(_HERE, "libpaged_kv.so")
 
 
-def load_library() -> ctypes.CDLL:
-    """Load the in-tree library (built by ``paged_kv_cache_70_amd.build``)."""
-    global _LIB
+def load_library(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load the in-tree library (built by ``paged_kv_cache_70_amd.build``):
+    ``libpaged_kv.so``, or the build at ``path`` (the timeline build).  One
+    build per process: asking for another once one is loaded is an error."""
+    global _LIB, _LIB_PATH
     if _LIB is not None:
+        if path is not None and os.path.abspath(path) != _LIB_PATH:
+            raise RuntimeError(f"{_LIB_PATH} is already loaded in this process; cannot load {path}")
         return _LIB
-    path = library_path()
+    path = path or library_path()
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with `python -m paged_kv_cache_70_amd.build`")
     lib = ctypes.CDLL(path)
@@ -118,11 +123,15 @@ def load_library() -> ctypes.CDLL:
         "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "pa_abi_version": (i32, []),
     }
+    if hasattr(lib, "pa_timeline_read"):          # the timeline build
+        sig["pa_timeline_read"] = (ctypes.c_int, [vp, sz])
+        sig["pa_timeline_reset"] = (ctypes.c_int, [])
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
     _LIB = lib
+    _LIB_PATH = os.path.abspath(path)
     return lib
 
 

@@ -1,4 +1,7 @@
-"""Build ``libpaged_kv.so`` (the C-ABI library) in-tree with hipcc for gfx950.
+"""Build ``libpaged_kv.so`` (the C-ABI library) in-tree with hipcc for gfx950,
+and beside it ``libpaged_kv_timeline.so``: the same library with the
+persistent decode kernel built with -DPA_TIMELINE (per-wavefront and per-unit
+timestamps, read by ``paged_kv_cache_70_amd.timeline``; not used otherwise).
 
 Usage: ``python -m paged_kv_cache_70_amd.build`` (or ``build()`` from Python).
 Every call recompiles.  Sources are compiled in parallel, then linked.
@@ -15,6 +18,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libpaged_kv.so")
+TIMELINE_LIB = os.path.join(PKG, "libpaged_kv_timeline.so")
+TIMELINE_SOURCE = "pa_decode_mfma.hip"
 SOURCES = ["pa_api.hip", "pa_write.hip", "pa_decode.hip", "pa_decode_mfma.hip", "pa_prefill.hip", "pa_measure.hip",
            "pa_check.hip"]
 HOST_SOURCES = ["pa_block_manager.cpp"]      # host-only C++ (no device code)
@@ -52,9 +57,9 @@ def build(verbose: bool = False) -> str:
     os.makedirs(objdir, exist_ok=True)
     inc = os.path.join(ROOT, "include")
 
-    def compile_one(src):
-        obj = os.path.join(objdir, src.replace(".hip", ".o"))
-        cmd = [hipcc, *HIP_FLAGS, "-I", inc, "-c", os.path.join(CSRC, src), "-o", obj]
+    def compile_one(src, defines=()):
+        obj = os.path.join(objdir, src.replace(".hip", "_timeline.o" if defines else ".o"))
+        cmd = [hipcc, *HIP_FLAGS, *defines, "-I", inc, "-c", os.path.join(CSRC, src), "-o", obj]
         err = _run(cmd)
         if verbose and err.strip():
             print(err, file=sys.stderr)
@@ -70,12 +75,17 @@ def build(verbose: bool = False) -> str:
             print(err, file=sys.stderr)
         return obj
 
-    with cf.ThreadPoolExecutor(max_workers=len(SOURCES) + len(HOST_SOURCES)) as ex:
+    with cf.ThreadPoolExecutor(max_workers=len(SOURCES) + len(HOST_SOURCES) + 1) as ex:
         futs = [ex.submit(compile_one, s) for s in SOURCES] + [ex.submit(compile_host, s) for s in HOST_SOURCES]
+        tl_fut = ex.submit(compile_one, TIMELINE_SOURCE, ("-DPA_TIMELINE",))
         objs = [f.result() for f in futs]
-    tmp = LIB + ".tmp"
-    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
-    os.replace(tmp, LIB)
+        tl_obj = tl_fut.result()
+    for out, parts in ((LIB, objs),
+                       (TIMELINE_LIB, [tl_obj if os.path.basename(o) == TIMELINE_SOURCE.replace(".hip", ".o") else o
+                                       for o in objs])):
+        tmp = out + ".tmp"
+        _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *parts])
+        os.replace(tmp, out)
     return LIB
 
 

@@ -30,6 +30,32 @@
 
 #include "pa_mfma_tile.h"
 
+#ifdef PA_TIMELINE
+// Timeline build only (compiled with -DPA_TIMELINE into a separate library;
+// the library proper contains none of this).  The persistent kernel records
+// per wavefront its s_memrealtime stamps (100 MHz) at entry, when the unit
+// list is ready and at exit, with its hardware ids; and per unit its
+// description with the stamps of its start and end.  Lane 0 writes them with
+// vector stores; pa_timeline_read copies the buffer to the host.
+// Layout (64-bit words): [0] units recorded; [16 + 4 w ..) wavefront w =
+// workgroup * NW + wave; [kTlUnitBase + 4 u ..) unit record u.
+#include "../../include/paged_kv.h"
+namespace pa {
+constexpr int kTlWords = 1 << 16, kTlUnitBase = 32768, kTlMaxUnits = 8000;
+__device__ uint64_t g_timeline[kTlWords];
+}  // namespace pa
+extern "C" int pa_timeline_read(void* dst, size_t bytes) {
+  if (!dst || bytes > sizeof(uint64_t) * pa::kTlWords) return PA_ERR_SHAPE;
+  return hipMemcpyFromSymbol(dst, HIP_SYMBOL(pa::g_timeline), bytes, 0, hipMemcpyDeviceToHost) == hipSuccess
+             ? PA_OK : PA_ERR_LAUNCH;
+}
+extern "C" int pa_timeline_reset() {
+  static uint64_t zero[pa::kTlWords];
+  return hipMemcpyToSymbol(HIP_SYMBOL(pa::g_timeline), zero, sizeof(zero), 0, hipMemcpyHostToDevice) == hipSuccess
+             ? PA_OK : PA_ERR_LAUNCH;
+}
+#endif
+
 namespace pa {
 
 namespace {
@@ -729,6 +755,9 @@ __global__ __launch_bounds__(64 * NW) void decode_partial_mfma_kernel(const Deco
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t NC = gridDim.x, wg = blockIdx.x;
+#ifdef PA_TIMELINE
+  const uint64_t tl_entry = __builtin_amdgcn_s_memrealtime();
+#endif
   uint8_t* lds_k = lds_tiles[wave][0];
   uint8_t* lds_v = lds_tiles[wave][1];
 
@@ -858,6 +887,9 @@ __global__ __launch_bounds__(64 * NW) void decode_partial_mfma_kernel(const Deco
   }
   __syncthreads();
 
+#ifdef PA_TIMELINE
+  const uint64_t tl_list = __builtin_amdgcn_s_memrealtime();
+#endif
   const uint32_t F = (uint32_t)__builtin_amdgcn_readfirstlane(s_cnt[0]);   // pairs of full partitions
   const int nj = __builtin_amdgcn_readfirstlane(s_nj);
   const int SG = prm.SG > 0 ? prm.SG : 1;
@@ -965,6 +997,9 @@ __global__ __launch_bounds__(64 * NW) void decode_partial_mfma_kernel(const Deco
     Fold<D> st;
     st.reset();
     int c_tile = 0;            // tiles of C folded
+#ifdef PA_TIMELINE
+    uint64_t tl_unit = __builtin_amdgcn_s_memrealtime();
+#endif
     // Producer cursor: the next tile to load is tile l_tile of unit L (C, or
     // N once taken, whose q then goes to qn), with block ids ph0/ph1
     // requested by scalar loads when the cursor moved there (dead: there is
@@ -1011,6 +1046,22 @@ __global__ __launch_bounds__(64 * NW) void decode_partial_mfma_kernel(const Deco
       Ops::fold(ok, T, qop, cs, map, lane, st, lds_k, lds_v);
       if (++c_tile < C.ntiles) return;
       store_unit<D, true>(prm, C, lane, st, s_jn);
+#ifdef PA_TIMELINE
+      {
+        const uint64_t now = __builtin_amdgcn_s_memrealtime();
+        if (lane == 0) {
+          const uint32_t u = atomicAdd(reinterpret_cast<unsigned int*>(&g_timeline[0]), 1u);
+          if (u < (uint32_t)kTlMaxUnits) {
+            uint64_t* r = g_timeline + kTlUnitBase + (size_t)u * 4;
+            r[0] = ((uint64_t)wg << 8) | (uint64_t)wave;
+            r[1] = ((uint64_t)C.b << 40) | ((uint64_t)C.p << 24) | ((uint64_t)C.kvh << 16) | (uint64_t)C.ntiles;
+            r[2] = tl_unit;
+            r[3] = now;
+          }
+        }
+        tl_unit = now;
+      }
+#endif
       if (!has(kNOk)) {
         fl &= ~kAlive;
         return;
@@ -1067,6 +1118,20 @@ __global__ __launch_bounds__(64 * NW) void decode_partial_mfma_kernel(const Deco
     else
       walk(CachePolicy<kAuxNT>{});
   }
+#ifdef PA_TIMELINE
+  const uint64_t tl_exit = __builtin_amdgcn_s_memrealtime();
+  const size_t wrec = (size_t)wg * NW + (size_t)wave;
+  if (lane == 0 && 16 + 4 * wrec + 4 <= (size_t)kTlUnitBase) {
+    uint64_t* r = g_timeline + 16 + 4 * wrec;
+    r[0] = tl_entry;
+    r[1] = tl_list;
+    r[2] = tl_exit;
+    // XCC_ID (hardware register 20), the wavefronts per workgroup, and HW_ID
+    // (register 4)
+    r[3] = (uint64_t)__builtin_amdgcn_s_getreg((4 << 11) | 20) | ((uint64_t)NW << 8) |
+           ((uint64_t)__builtin_amdgcn_s_getreg((31 << 11) | 4) << 32);
+  }
+#endif
 }
 
 namespace {

@@ -32,6 +32,19 @@ def test_library_exports_every_declared_symbol():
     assert pk.abi_version() >> 16 == 2
 
 
+def test_timeline_build_is_separate():
+    """The timeline build (the persistent decode kernel with -DPA_TIMELINE)
+    exports the header's symbols plus its two timeline calls; the library
+    proper has neither timeline call.  Loaded with ctypes directly: the
+    binding keeps one build per process."""
+    from paged_kv_cache_70_amd.build import LIB, TIMELINE_LIB
+    tl = ctypes.CDLL(TIMELINE_LIB)
+    for n in _declared() + ["pa_timeline_read", "pa_timeline_reset"]:
+        assert hasattr(tl, n), n
+    lib = ctypes.CDLL(LIB)
+    assert not hasattr(lib, "pa_timeline_read") and not hasattr(lib, "pa_timeline_reset")
+
+
 def test_status_strings():
     for code in range(0, -12, -1):
         s = pk.status_string(code)
