@@ -768,6 +768,17 @@ __global__ __launch_bounds__(64 * NW) void decode_partial_mfma_kernel(const Deco
     const int lt = (n - (np > 1 ? (np - 1) * P : 0) + 15) >> 4;
     return (kBuckets - 1) - lt * (kBuckets - 1) / tmax;
   };
+  // Every wavefront first copies each sequence's clamped length and its first
+  // table entry (every row has one) into LDS, so that the list wavefront reads
+  // them from LDS: one round trip to memory instead of one per 64 sequences.
+  // s_last holds the entries until the list wavefront overwrites it with the
+  // last-pair order, after its last use of them.
+  for (int b = threadIdx.x; b < B; b += 64 * NW) {
+    s_len[b] = clamp_len(prm, prm.ctx[b]);
+    s_last[b] = prm.tables[(size_t)b * prm.W];
+    s_skip[b] = 0;
+  }
+  __syncthreads();
   // Shared prefix: every wavefront compares a share of the (sequence, entry)
   // pairs of the shared partitions with row 0 (SP * P <= W * bs keeps every
   // entry inside its row); a mismatch marks the sequence in s_skip (all
@@ -776,8 +787,6 @@ __global__ __launch_bounds__(64 * NW) void decode_partial_mfma_kernel(const Deco
   // 4) a load compares 4 entries: the quads cover entries up to
   // 4 * ceil(SPB / 4) <= W, and entries past SPB are ignored.
   if (prm.SP > 0) {
-    for (int b = threadIdx.x; b < B; b += 64 * NW) s_skip[b] = 0;
-    __syncthreads();
     const int spb = prm.SPB;
     constexpr int kU = 16;
     const bool quads = (prm.W & 3) == 0 && (reinterpret_cast<uintptr_t>(prm.tables) & 15u) == 0;
@@ -831,14 +840,14 @@ __global__ __launch_bounds__(64 * NW) void decode_partial_mfma_kernel(const Deco
     bool shared = false;
     for (int base = 0; base < B; base += 64) {
       const int b = base + lane;
-      const int n = b < B ? clamp_len(prm, prm.ctx[b]) : 0;
+      const int n = b < B ? s_len[b] : 0;
       {
         // entry 0 of every table row exists; it is compared only when both
         // sequences use it
         const int nb = b < B ? neighbour(prm, b) : -1;
-        const int nn = nb >= 0 ? clamp_len(prm, prm.ctx[nb]) : 0;
-        const int e0 = b < B ? prm.tables[(size_t)b * prm.W] : -1;
-        const int e1 = nb >= 0 ? prm.tables[(size_t)nb * prm.W] : -2;
+        const int nn = nb >= 0 ? s_len[nb] : 0;
+        const int e0 = b < B ? s_last[b] : -1;
+        const int e1 = nb >= 0 ? s_last[nb] : -2;
         shared |= __ballot(n > 0 && nn > 0 && e0 == e1) != 0;
       }
       // Shared prefix: the sequence leaves its first SP partitions to shared
@@ -859,7 +868,6 @@ __global__ __launch_bounds__(64 * NW) void decode_partial_mfma_kernel(const Deco
       }
       if (b < B) {
         s_first[b] = carry + incl - f;
-        s_len[b] = n;
         s_skip[b] = join ? prm.SP : 0;
         atomicAdd(&s_cnt[last_class(n)], 1);
       }
