@@ -204,7 +204,7 @@ def _read_ceiling(nbytes: int, args, dev, do_flush) -> dict:
 
 def _mfma_ceiling(args, dev) -> dict:
     """The matrix-core ceiling on this device, in this process: pa_measure_mfma
-    (independent bf16 16x16x32 products, no memory traffic) timed with events
+    (independent bf16 32x32x16 products, no memory traffic) timed with events
     at one, two and four workgroups of 4 wavefronts per CU; the best is the ceiling."""
     import torch
 
@@ -227,7 +227,7 @@ def _mfma_ceiling(args, dev) -> dict:
     wpc = max(res, key=lambda k: res[k][0])
     return {"TFLOPS": round(res[wpc][0], 1), "workgroups_per_cu": wpc, "us": round(res[wpc][1], 2),
             "TFLOPS_by_workgroups_per_cu": {str(k): round(v[0], 1) for k, v in res.items()},
-            "what": "pa_measure_mfma: 8 independent v_mfma_f32_16x16x32_bf16 chains per wavefront on register "
+            "what": "pa_measure_mfma: 4 independent v_mfma_f32_32x32x16_bf16 chains per wavefront on register "
                     f"operands, {iters} rounds, events around the kernel; the best of 1, 2 and 4 workgroups of 4 "
                     "wavefronts per CU"}
 

@@ -521,8 +521,8 @@ int pa_measure_read(const void* buf, size_t bytes, int32_t workgroups_per_cu, in
 /*
  * pa_measure_mfma — a measurement helper, not a step of the method: every
  * wavefront of workgroups_per_cu workgroups of 256 threads per compute unit
- * runs `iters` rounds of 8 independent v_mfma_f32_16x16x32_bf16 products on
- * register operands (16,384 flops each; no memory traffic).  Its rate, timed
+ * runs `iters` rounds of 4 independent v_mfma_f32_32x32x16_bf16 products on
+ * register operands (32,768 flops each; no memory traffic).  Its rate, timed
  * beside the prefill, is the matrix-core ceiling the device sustains.
  *   sink   device, one uint32 the kernel may write (it keeps the products live)
  * Returns PA_OK, PA_ERR_NULL, PA_ERR_SHAPE (iters <= 0, workgroups_per_cu

@@ -455,7 +455,7 @@ def measure_mfma(sink: torch.Tensor, iters: int, *, workgroups_per_cu: int = 1) 
     st = lib.pa_measure_mfma(int(iters), int(workgroups_per_cu), _dev(sink, "sink"), _stream(sink))
     _check("pa_measure_mfma", st)
     cus = torch.cuda.get_device_properties(sink.device).multi_processor_count
-    return cus * workgroups_per_cu * 4 * int(iters) * 8 * 16384
+    return cus * workgroups_per_cu * 4 * int(iters) * 4 * 32768     # 4 wavefronts x 4 products of 32x32x16
 
 
 def prefill_workspace(num_seqs: int, num_heads: int, max_blocks_per_seq: int, num_tokens: int,

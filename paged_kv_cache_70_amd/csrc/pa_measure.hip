@@ -48,15 +48,18 @@ __global__ __launch_bounds__(kReadThreads) void stream_read_kernel(const char* _
   if (x == tag) sink[0] = x;
 }
 
-// Matrix-core throughput: every wavefront runs `iters` rounds of 8
-// independent v_mfma_f32_16x16x32_bf16 chains on register operands (no
-// memory traffic), the product the bf16 prefill issues.  One wavefront per
-// SIMD keeps the pipe fed with 8 chains; the accumulators are folded into a
-// store guarded like the read's, so the products stay live.
-constexpr int kMfmaChains = 8;
+// Matrix-core throughput: every wavefront runs `iters` rounds of 4
+// independent v_mfma_f32_32x32x16_bf16 chains on register operands (no
+// memory traffic).  The 32x32 product keeps its accumulators in place from
+// one round to the next; the same loop written with 16x16x32 products comes
+// out of the compiler with accumulator register moves between the products
+// (tens of them per round), and measures the moves, not the matrix pipe.
+// The accumulators are folded into a store guarded like the read's, so the
+// products stay live.
+constexpr int kMfmaChains = 4;
 __global__ __launch_bounds__(256) void mfma_peak_kernel(int iters, uint32_t* __restrict__ sink, uint32_t tag) {
   typedef __bf16 bf16x8m __attribute__((ext_vector_type(8)));
-  typedef float f32x4m __attribute__((ext_vector_type(4)));
+  typedef float f32x16m __attribute__((ext_vector_type(16)));
   const float x = (float)(threadIdx.x & 7) * 0.001f;
   bf16x8m a, b;
 #pragma unroll
@@ -64,16 +67,20 @@ __global__ __launch_bounds__(256) void mfma_peak_kernel(int iters, uint32_t* __r
     a[i] = (__bf16)(x + (float)i);
     b[i] = (__bf16)(x - (float)i);
   }
-  f32x4m c[kMfmaChains];
+  f32x16m c[kMfmaChains];
 #pragma unroll
-  for (int k = 0; k < kMfmaChains; ++k) c[k] = f32x4m{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int k = 0; k < kMfmaChains; ++k)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) c[k][j] = 0.0f;
   for (int it = 0; it < iters; ++it) {
 #pragma unroll
-    for (int k = 0; k < kMfmaChains; ++k) c[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c[k], 0, 0, 0);
+    for (int k = 0; k < kMfmaChains; ++k) c[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c[k], 0, 0, 0);
   }
   float acc = 0.0f;
 #pragma unroll
-  for (int k = 0; k < kMfmaChains; ++k) acc += c[k][0] + c[k][1] + c[k][2] + c[k][3];
+  for (int k = 0; k < kMfmaChains; ++k)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc += c[k][j];
   const uint32_t y = __float_as_uint(acc);
   if (y == tag) sink[0] = y;
 }
