@@ -963,7 +963,10 @@ __global__ __launch_bounds__(64 * NW) void decode_partial_mfma_kernel(const Deco
     return u;
   };
 
-  auto walk = [&](auto pol) {
+  // Folds units from list index t_first on, drawing further ones from the
+  // workgroup's queue while they lie below t_stop; returns the first unit
+  // drawn at or past t_stop (a later walk starts there).
+  auto walk = [&](auto pol, uint32_t t_first, uint32_t t_stop) -> uint32_t {
     constexpr int A = decltype(pol)::aux;
     const LdsMap<D> map(lane);
     const uint32_t lane_off = (uint32_t)(lane / Gm::PPR) * (uint32_t)(prm.KVH * Gm::ROWB) + (uint32_t)(lane % Gm::PPR) * 16;
@@ -986,15 +989,17 @@ __global__ __launch_bounds__(64 * NW) void decode_partial_mfma_kernel(const Deco
     auto has = [&](uint32_t f) { return (fl & f) != 0; };
 
     // C: the unit being folded; N: the next one.
-    Unit C = describe(share((uint32_t)wave));
+    Unit C = describe(t_first);
     Unit N = C;
+    uint32_t carry = nunits;
     auto next_unit = [&]() {
       uint32_t k = 0;
       if (lane == 0) k = atomicAdd(&s_next, 1u);
       k = __builtin_amdgcn_readlane(k, 0);
       const uint32_t un = share(k);
-      fl = un < nunits ? (fl | kNOk) : (fl & ~kNOk);
-      if (un < nunits) N = describe(un);
+      fl = un < t_stop ? (fl | kNOk) : (fl & ~kNOk);
+      carry = un < t_stop ? carry : un;
+      if (un < t_stop) N = describe(un);
     };
     next_unit();
 
@@ -1113,18 +1118,26 @@ __global__ __launch_bounds__(64 * NW) void decode_partial_mfma_kernel(const Deco
         consume(rC, okC, tC);
       } while (has(kAlive));
     }
+    return carry;
   };
   // Blocks shared between sequences (a common prefix) are likely to be read
   // again by other workgroups: keep the default cache policy for them.
   // Otherwise every K/V row is read once, and the loads are non-temporal --
   // except in vLLM's layout when a tile reads only part of every K group and V
   // row of its block (16-token tiles in blocks of 32 or more, 32-token tiles in
-  // blocks of 64 or more) and the next tile reads the rest.
-  if (share((uint32_t)wave) < nunits) {
-    if (__builtin_amdgcn_readfirstlane(s_shared) || (Vllm && prm.bs_log2 >= (TOK == 32 ? 6 : 5)))
-      walk(CachePolicy<0>{});
-    else
-      walk(CachePolicy<kAuxNT>{});
+  // blocks of 64 or more) and the next tile reads the rest.  With the
+  // shared-prefix hint, the shared units come first in the list: a wavefront
+  // walks those at the default policy, then starts a second walk, non-temporal,
+  // at its first private unit (one pipeline restart per wavefront, and no
+  // branch inside the tile loop).  Without the hint, blocks found shared
+  // between neighbours keep the default policy for every unit.
+  {
+    uint32_t t = share((uint32_t)wave);
+    const bool all_default = (Vllm && prm.bs_log2 >= (TOK == 32 ? 6 : 5)) ||
+                             (SPG == 0u && __builtin_amdgcn_readfirstlane(s_shared) != 0);
+    const uint32_t default_end = all_default ? nunits : SPG * upp;
+    if (t < default_end) t = walk(CachePolicy<0>{}, t, default_end);
+    if (t < nunits) walk(CachePolicy<kAuxNT>{}, t, nunits);
   }
 #ifdef PA_TIMELINE
   const uint64_t tl_exit = __builtin_amdgcn_s_memrealtime();
