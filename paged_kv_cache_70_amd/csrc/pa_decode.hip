@@ -514,6 +514,55 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
+// Partition rows of one (sequence, head) that the merge-append kernel loads
+// before the context length arrives: the first min(maxP, kMergeEarlyRows).
+// They lie inside the workspace's maxP >= 1 rows of that (sequence, head)
+// whatever the length; rows past the sequence's partitions hold stale or
+// unwritten values and are dropped by selects (never multiplied by a zero
+// weight, which would keep a stale NaN).  The plain merge kernel does not
+// load early: a quarter of its wavefronts (single-partition sequences) leave
+// at once, and early loads there measured slower.
+constexpr int kMergeEarlyRows = 8;
+
+typedef float mf4 __attribute__((ext_vector_type(4)));
+
+template <int D, int PPI, int KPRE>
+__device__ __forceinline__ void early_rows(const float* acc, const float* ml, int early, int sub, int dl, int lane,
+                                           mf4 (&pre)[KPRE], float2& mlpre) {
+  // Every lane loads (at a row index clamped to early - 1 < maxP) and then
+  // selects: loads under a lane condition each get a branch of their own,
+  // and the compiler waits for them inside it.
+#pragma unroll
+  for (int k = 0; k < KPRE; ++k) {
+    const int i = sub + PPI * k;
+    const mf4 v = *reinterpret_cast<const mf4*>(acc + (size_t)min(i, early - 1) * D + dl);
+    pre[k] = i < early ? v : mf4{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+  const float2 m = *reinterpret_cast<const float2*>(ml + (size_t)min(lane, early - 1) * 2);
+  mlpre = lane < early ? m : make_float2(-INFINITY, 0.0f);
+}
+
+// The rows of the round starting at partition r0 (cnt of them): in round 0
+// the early rows come from pre / mlpre, the rest are loaded now.  Rows i <
+// PPI * KPRE of round 0 are early rows or lie past maxP >= cnt.
+template <int D, int PPI, int KMAX, int KPRE>
+__device__ __forceinline__ void round_rows(const float* acc, const float* ml, int r0, int cnt, int early, int sub,
+                                           int dl, int lane, const mf4 (&pre)[KPRE], float2 mlpre, mf4 (&a)[KMAX],
+                                           float2& mlv) {
+#pragma unroll
+  for (int k = 0; k < KMAX; ++k) {
+    const int i = sub + PPI * k;
+    if (k < KPRE && r0 == 0)
+      a[k] = i < cnt ? pre[k] : mf4{0.0f, 0.0f, 0.0f, 0.0f};
+    else
+      a[k] = i < cnt ? *reinterpret_cast<const mf4*>(acc + (size_t)(r0 + i) * D + dl) : mf4{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+  if (r0 == 0 && lane < early)
+    mlv = lane < cnt ? mlpre : make_float2(-INFINITY, 0.0f);
+  else
+    mlv = lane < cnt ? *reinterpret_cast<const float2*>(ml + (size_t)(r0 + lane) * 2) : make_float2(-INFINITY, 0.0f);
+}
+
 template <typename E, int D>
 __global__ __launch_bounds__(64) void decode_merge_kernel(const DecodeParams prm) {
   // One wavefront per (sequence, head).  A partial accumulator row is D fp32
@@ -632,6 +681,8 @@ __global__ __launch_bounds__(64) void decode_merge_append_kernel(const DecodePar
   constexpr int KMAX = PPI * 16 <= 64 ? 16 : 64 / PPI;
   constexpr int R = PPI * KMAX;
   typedef float f4 __attribute__((ext_vector_type(4)));
+  constexpr int KPRE = kMergeEarlyRows / PPI;
+  static_assert(kMergeEarlyRows % PPI == 0 && KPRE <= KMAX, "early rows fill whole loads of round 0");
   const int h = blockIdx.x;
   const int b = blockIdx.y;
   const int lane = threadIdx.x;
@@ -639,25 +690,29 @@ __global__ __launch_bounds__(64) void decode_merge_append_kernel(const DecodePar
   const int dl = (lane % LPP) * 4;
   const size_t bh = (size_t)b * prm.H + h;
   const int kvh = h / (prm.H / prm.KVH);
+  const float* ml = prm.ws_ml + bh * prm.maxP * 2;
+  const float* acc = prm.ws_acc + bh * prm.maxP * D;
+
+  // Every load that needs neither the length nor the slot goes out first:
+  // the new token's q, k and v (rows b of q, k_new and v_new exist whatever
+  // the slot) and the first partial rows (early_rows), so the kernel makes one
+  // trip to memory instead of two.  The kv head's first query head then
+  // stores the new K and V rows into the slot (bit for bit), so the copy
+  // drains while the partials are merged.  The partial kernel read only the
+  // cached tokens, never this slot.
+  const size_t row = ((size_t)b * prm.KVH + kvh) * D + dl;   // this lane's d's of k_new / v_new
+  const uint4 qraw = raw4<E>(prm.q, bh * D + dl);
+  const uint4 kraw = raw4<E>(ap.k_new, row);
+  const uint4 vraw = raw4<E>(ap.v_new, row);
+  const int early = min(prm.maxP, kMergeEarlyRows);
+  f4 pre[KPRE];
+  float2 mlpre;
+  early_rows<D, PPI, KPRE>(acc, ml, early, sub, dl, lane, pre, mlpre);
   int n = prm.ctx[b];
   n = n < 0 ? 0 : (n > prm.max_tokens ? prm.max_tokens : n);
   const int nparts = max(1, (n + prm.P - 1) / prm.P);   // the partial kernel stored all of them
   const int64_t slot = ap.slots[b];
   const bool has_new = slot >= 0 && slot < ap.num_slots;
-  const float* ml = prm.ws_ml + bh * prm.maxP * 2;
-  const float* acc = prm.ws_acc + bh * prm.maxP * D;
-
-  // The new token's q, k and v are read first, and the kv head's first query
-  // head stores its K and V rows into the slot at once (bit for bit), so the
-  // copy drains while the partials are merged.  The partial kernel read only
-  // the cached tokens, never this slot.
-  const size_t row = ((size_t)b * prm.KVH + kvh) * D + dl;   // this lane's d's of k_new / v_new
-  uint4 qraw = {0u, 0u, 0u, 0u}, kraw = {0u, 0u, 0u, 0u}, vraw = {0u, 0u, 0u, 0u};
-  if (has_new) {
-    qraw = raw4<E>(prm.q, bh * D + dl);
-    kraw = raw4<E>(ap.k_new, row);
-    vraw = raw4<E>(ap.v_new, row);
-  }
   if (has_new && sub == 0 && h % (prm.H / prm.KVH) == 0) {
     const size_t blk = (size_t)(slot >> prm.bs_log2);
     const size_t off = (size_t)(slot & prm.bs_mask);
@@ -701,13 +756,8 @@ __global__ __launch_bounds__(64) void decode_merge_append_kernel(const DecodePar
   for (int r0 = 0; r0 < nparts; r0 += R) {
     const int cnt = min(R, nparts - r0);
     f4 a[KMAX];
-#pragma unroll
-    for (int k = 0; k < KMAX; ++k) {
-      const int i = sub + PPI * k;
-      a[k] = i < cnt ? *reinterpret_cast<const f4*>(acc + (size_t)(r0 + i) * D + dl) : f4{0.0f, 0.0f, 0.0f, 0.0f};
-    }
-    const float2 mlv = lane < cnt ? *reinterpret_cast<const float2*>(ml + (size_t)(r0 + lane) * 2)
-                                  : make_float2(-INFINITY, 0.0f);
+    float2 mlv;
+    round_rows<D, PPI, KMAX, KPRE>(acc, ml, r0, cnt, early, sub, dl, lane, pre, mlpre, a, mlv);
     const float M = fmaxf(Mrun, wave_max(mlv.x));
     const float w = mlv.x == -INFINITY ? 0.0f : exp2_fast(mlv.x - M);
     const float fo = Mrun == -INFINITY ? 0.0f : exp2_fast(Mrun - M);
