@@ -133,6 +133,20 @@ __device__ __forceinline__ int neighbour(const DecodeParams& prm, int b) {
   return b > 0 ? b - 1 : (prm.B > 1 ? 1 : -1);
 }
 
+// Inclusive prefix sum over the 64 lanes of a wavefront with data-parallel
+// moves (no LDS round trips): row shifts by 1, 2, 4 and 8 scan each row of 16
+// lanes, then lane 15's sum is broadcast into rows 1 and 3 and lane 31's into
+// rows 2 and 3.  Lanes a move leaves out keep 0.
+__device__ __forceinline__ int wave_inclusive_sum(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);   // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);   // row_bcast:31
+  return x;
+}
+
 __device__ __forceinline__ int clamp_len(const DecodeParams& prm, int n) {
   return n < 0 ? 0 : (n > prm.max_tokens ? prm.max_tokens : n);
 }
@@ -768,32 +782,81 @@ __global__ __launch_bounds__(64 * NW) void decode_partial_mfma_kernel(const Deco
     const int lt = (n - (np > 1 ? (np - 1) * P : 0) + 15) >> 4;
     return (kBuckets - 1) - lt * (kBuckets - 1) / tmax;
   };
-  // Every wavefront first copies each sequence's clamped length and its first
-  // table entry (every row has one) into LDS, so that the list wavefront reads
-  // them from LDS: one round trip to memory instead of one per 64 sequences.
-  // s_last holds the entries until the list wavefront overwrites it with the
-  // last-pair order, after its last use of them.
-  for (int b = threadIdx.x; b < B; b += 64 * NW) {
-    s_len[b] = clamp_len(prm, prm.ctx[b]);
-    s_last[b] = prm.tables[(size_t)b * prm.W];
-    s_skip[b] = 0;
-  }
-  __syncthreads();
   // Shared prefix: every wavefront compares a share of the (sequence, entry)
   // pairs of the shared partitions with row 0 (SP * P <= W * bs keeps every
   // entry inside its row); a mismatch marks the sequence in s_skip (all
   // writers store 1).  Loads go out 16 at a time at clamped indices.  When
   // the rows are 16-byte aligned (the table 16-byte aligned, W a multiple of
   // 4) a load compares 4 entries: the quads cover entries up to
-  // 4 * ceil(SPB / 4) <= W, and entries past SPB are ignored.
+  // 4 * ceil(SPB / 4) <= W, and entries past SPB are ignored.  When a row's
+  // quads fit in the workgroup, thread t keeps quad column j = t mod spb4 for
+  // rows t / spb4 + k * rpp (row 0's quad is loaded once), and its first 16
+  // rows' loads go out before the length copy below, so that both wait for
+  // memory together (the first pass is compared into a register mask, and
+  // marked after the barrier that orders the marks after the zeroing).
+  //
+  // Every wavefront also copies each sequence's clamped length and its first
+  // table entry (every row has one) into LDS, so that the list wavefront reads
+  // them from LDS: one round trip to memory instead of one per 64 sequences.
+  // s_last holds the entries until the list wavefront overwrites it with the
+  // last-pair order, after its last use of them.
+  const int b_first = (int)threadIdx.x;
+  int len_first = 0, ent_first = 0;
+  if (b_first < B) {
+    len_first = prm.ctx[b_first];
+    ent_first = prm.tables[(size_t)b_first * prm.W];
+  }
+  typedef int32_t i32x4t __attribute__((ext_vector_type(4)));
+  constexpr int kU = 16;
+  const int spb = prm.SPB;
+  const bool quads = prm.SP > 0 && (prm.W & 3) == 0 && (reinterpret_cast<uintptr_t>(prm.tables) & 15u) == 0;
+  const i32x4t* t4 = reinterpret_cast<const i32x4t*>(prm.tables);
+  const int spb4 = (spb + 3) >> 2, w4 = prm.W >> 2;
+  const int rpp = quads ? (64 * NW) / spb4 : 0;       // rows per pass of the workgroup
+  const bool fixed_col = rpp > 0 && (int)threadIdx.x < rpp * spb4;
+  const int jcol = fixed_col ? (int)threadIdx.x % spb4 : 0;
+  const int brow = fixed_col ? (int)threadIdx.x / spb4 : 0;
+  i32x4t ref4 = {0, 0, 0, 0}, mine4[kU];
+  auto differs = [&](const i32x4t& m) {
+    bool diff = false;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) diff |= (4 * jcol + i < spb) && m[i] != ref4[i];
+    return diff;
+  };
+  uint32_t miss = 0;   // bit u: row brow + u * rpp of the first pass differs from row 0
+  if (fixed_col) {
+    ref4 = t4[jcol];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) mine4[u] = t4[(size_t)min(brow + u * rpp, B - 1) * w4 + jcol];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) miss |= differs(mine4[u]) ? 1u << u : 0u;
+  }
+  if (b_first < B) {
+    s_len[b_first] = clamp_len(prm, len_first);
+    s_last[b_first] = ent_first;
+    s_skip[b_first] = 0;
+  }
+  for (int b = b_first + 64 * NW; b < B; b += 64 * NW) {
+    s_len[b] = clamp_len(prm, prm.ctx[b]);
+    s_last[b] = prm.tables[(size_t)b * prm.W];
+    s_skip[b] = 0;
+  }
+  __syncthreads();
   if (prm.SP > 0) {
-    const int spb = prm.SPB;
-    constexpr int kU = 16;
-    const bool quads = (prm.W & 3) == 0 && (reinterpret_cast<uintptr_t>(prm.tables) & 15u) == 0;
-    if (quads) {
-      typedef int32_t i32x4t __attribute__((ext_vector_type(4)));
-      const i32x4t* t4 = reinterpret_cast<const i32x4t*>(prm.tables);
-      const int spb4 = (spb + 3) >> 2, w4 = prm.W >> 2;
+    if (fixed_col) {
+      for (int b0 = brow;; b0 += rpp * kU) {
+#pragma unroll
+        for (int u = 0; u < kU; ++u)
+          if (((miss >> u) & 1u) && b0 + u * rpp < B) s_skip[b0 + u * rpp] = 1;
+        if (b0 + rpp * kU >= B) break;
+#pragma unroll
+        for (int u = 0; u < kU; ++u) mine4[u] = t4[(size_t)min(b0 + rpp * kU + u * rpp, B - 1) * w4 + jcol];
+        miss = 0;
+#pragma unroll
+        for (int u = 0; u < kU; ++u) miss |= differs(mine4[u]) ? 1u << u : 0u;
+      }
+    }
+    if (quads && rpp == 0) {
       const int total4 = B * spb4;
       for (int e0 = threadIdx.x; e0 < total4; e0 += 64 * NW * kU) {
         i32x4t mine[kU], ref[kU];
@@ -816,7 +879,7 @@ __global__ __launch_bounds__(64 * NW) void decode_partial_mfma_kernel(const Deco
         }
       }
     }
-    const int total = quads ? 0 : B * spb;
+    const int total = quads ? 0 : B * spb;   // rows not 16-byte aligned: one entry per load
     for (int e0 = threadIdx.x; e0 < total; e0 += 64 * NW * kU) {
       int mine[kU], ref[kU], who[kU];
 #pragma unroll
@@ -860,12 +923,7 @@ __global__ __launch_bounds__(64 * NW) void decode_partial_mfma_kernel(const Deco
       shared |= jm != 0;
       const int np = (n + P - 1) / P;
       const int f = (b < B && np > 1) ? np - 1 - (join ? prm.SP : 0) : 0;
-      int incl = f;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const int y = __shfl_up(incl, d);
-        if (lane >= d) incl += y;
-      }
+      const int incl = wave_inclusive_sum(f);
       if (b < B) {
         s_first[b] = carry + incl - f;
         s_skip[b] = join ? prm.SP : 0;
@@ -875,13 +933,7 @@ __global__ __launch_bounds__(64 * NW) void decode_partial_mfma_kernel(const Deco
     }
     {
       const int c = s_cnt[lane];
-      int incl = c;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const int y = __shfl_up(incl, d);
-        if (lane >= d) incl += y;
-      }
-      s_cnt[lane] = incl - c;
+      s_cnt[lane] = wave_inclusive_sum(c) - c;
     }
     for (int base = 0; base < B; base += 64) {
       const int b = base + lane;
