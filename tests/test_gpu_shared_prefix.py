@@ -213,3 +213,40 @@ def test_table_check_widths_and_alignment(extra):
     out, _ = _run(w, 128, 64)
     err = assert_matches_oracle(out, ref, "bf16", f"table width {w.block_tables.shape[1]} ({extra})")
     _say(f"table width {w.block_tables.shape[1]} ({extra}): max err {err:.2e}")
+
+
+@pytest.mark.parametrize("case", ["two_passes", "row_wider_than_workgroup"])
+def test_table_check_passes_and_wide_rows(case):
+    """The table check's two quad forms. With rows of 384 shared entries (96
+    quads) a 512-thread workgroup keeps one quad column per thread over 5 rows
+    at a time (32 threads idle), 80 rows per pass: 96 sequences take a second
+    pass, whose rows 85 and 95 differ from row 0 in the first and last shared
+    entry.  With rows of 2112 shared entries (528 quads, more than the
+    workgroup has threads) the check falls back to the (sequence, quad) walk.
+    Both give the oracle's result."""
+    rng = np.random.default_rng(23)
+    if case == "two_passes":
+        bs, P, shared = 16, 1024, 6144
+        lens = [int(x) for x in rng.integers(6145, 6657, 96)]
+        lens[0], lens[5], lens[6], lens[7] = 6656, 6144, 100, 0
+        differ = {3: 192, 85: 0, 95: 383}
+    else:
+        bs, P, shared = 8, 512, 16896
+        lens = [17120, 17000, 16950, 16897, 16896, 5000]
+        differ = {2: 2111, 3: 1000}
+    w = make_custom(num_seqs=len(lens), num_heads=8, num_kv_heads=2, head_dim=64, block_size=bs, dtype="bf16",
+                    lens=lens, seed=57, device="cuda")
+    spb = shared // P * P // bs
+    w = _share(w, range(len(lens)), spb, ())
+    tbl = w.block_tables.cpu().clone()
+    for b, j in differ.items():
+        tbl[b, j] = (tbl[b, j] + 1) % w.num_blocks
+    w.block_tables = tbl.to(w.block_tables.device)
+    B, W = tbl.shape
+    assert W % 4 == 0 and w.block_tables.data_ptr() % 16 == 0, "the quad forms need 16-byte aligned rows"
+    quads = -(-spb // 4)
+    assert (quads <= 512) == (case == "two_passes")
+    ref = _oracle(w)
+    out, _ = _run(w, shared, P)
+    err = assert_matches_oracle(out, ref, "bf16", f"table check {case}")
+    _say(f"table check {case}: {B} sequences, {spb} shared entries ({quads} quads), max err {err:.2e}")
