@@ -72,6 +72,9 @@ CSRC = os.path.join(ROOT, "paged_kv_cache_70_amd", "csrc")
 # and its source file
 PARTIAL_KERNELS = {"bf16": "decode_partial_mfma_kernel", "f32": "decode_partial_kernel", "write": "write_kv_kernel",
                    "prefill": "prefill_mfma_kernel"}
+# where vLLM's cache layout runs another kernel (the bf16 decode and the
+# prefill run the same templates with the layout as a parameter)
+VLLM_KERNELS = {"f32": "decode_partial_vllm_kernel", "write": "write_kv_vllm_kernel"}
 # the sources each kernel is compiled from (its file, the shared parameter
 # structs, and the tile helpers the matrix-core kernels share)
 _INTERNAL = os.path.join(CSRC, "pa_internal.h")
@@ -82,28 +85,39 @@ KERNEL_SRC = {"bf16": [os.path.join(CSRC, "pa_decode_mfma.hip"), _INTERNAL, _TIL
               "prefill": [os.path.join(CSRC, "pa_prefill.hip"), _INTERNAL, _TILE]}
 
 
-def _traffic_file(key: str, workload: str) -> str:
-    """The committed counter summary of kernel `key` on `workload`."""
-    return os.path.join(PROFILES, f"traffic_{PARTIAL_KERNELS[key]}_{workload}.json")
+def _kernel_name(key: str, layout: str = "p09") -> str:
+    """The dominant kernel of bench line `key` in cache layout `layout`."""
+    return VLLM_KERNELS.get(key, PARTIAL_KERNELS[key]) if layout == "vllm" else PARTIAL_KERNELS[key]
 
 
-def _src_hash(key: str) -> str:
+def _traffic_file(key: str, workload: str, layout: str = "p09") -> str:
+    """The committed counter summary of kernel `key` on `workload` (in vLLM's
+    cache layout: a file of its own)."""
+    suffix = "_vllm" if layout == "vllm" else ""
+    return os.path.join(PROFILES, f"traffic_{_kernel_name(key, layout)}_{workload}{suffix}.json")
+
+
+def _src_hash(key: str, layout: str = "p09") -> str:
+    # the fp32 decode in vLLM's layout is compiled from the matrix-core kernel's file
+    srcs = KERNEL_SRC["bf16"] if (key == "f32" and layout == "vllm") else KERNEL_SRC[key]
     h = hashlib.sha256()
-    for path in KERNEL_SRC[key]:
+    for path in srcs:
         with open(path, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def _traffic(workload: str, key: str):
+def _traffic(workload: str, key: str, layout: str = "p09"):
     """HBM bytes per launch of the kernel `key` from the committed rocprofv3
-    counter summary, if it was taken on this workload and this kernel source."""
+    counter summary, if it was taken on this workload, in this cache layout,
+    and on this kernel source."""
     try:
-        with open(_traffic_file(key, workload)) as f:
+        with open(_traffic_file(key, workload, layout)) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("source_sha256_16") != _src_hash(key) or t.get("workload") != workload:
+    if (t.get("source_sha256_16") != _src_hash(key, layout) or t.get("workload") != workload
+            or t.get("layout", "p09") != layout):
         return None
     return t.get("bytes_per_launch")
 
@@ -119,13 +133,13 @@ def _counter_rows(path: str, counter: str):
 
 
 def traffic_from_counters(fetch_csv: str, write_csv: str, workload: str, key: str,
-                          calib_bytes: int, out_json: str) -> dict:
-    """HBM bytes per launch of the kernel `key` from two rocprofv3 --pmc runs
-    of this script (FETCH_SIZE, then WRITE_SIZE; both in KiB per dispatch),
-    each scaled by the same counter's reading for the calibration copy, which
-    reads and writes calib_bytes."""
-    kname = PARTIAL_KERNELS[key]
-    res = {"workload": workload, "kernel": kname, "source_sha256_16": _src_hash(key),
+                          calib_bytes: int, out_json: str, layout: str = "p09") -> dict:
+    """HBM bytes per launch of the kernel `key` (in cache layout `layout`)
+    from two rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE;
+    both in KiB per dispatch), each scaled by the same counter's reading for
+    the calibration copy, which reads and writes calib_bytes."""
+    kname = _kernel_name(key, layout)
+    res = {"workload": workload, "kernel": kname, "layout": layout, "source_sha256_16": _src_hash(key, layout),
            "calibration_copy_bytes": calib_bytes}
     total = 0.0
     for key, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
@@ -483,7 +497,7 @@ def run_prefill(args, cfg):
             "peak": MFMA_BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-            "traffic": _traffic(cfg.name, "prefill") if args.layout == "p09" else None,
+            "traffic": _traffic(cfg.name, "prefill", args.layout),
             "kernel": "prefill_mfma_kernel",
         },
     }
@@ -597,7 +611,7 @@ def run_write(args, cfg):
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(gbps / HBM_PEAK_GBPS, 4),
-            "traffic": None if vllm else _traffic(cfg.name, "write"),
+            "traffic": _traffic(cfg.name, "write", args.layout),
             "kernel": "write_kv_vllm_kernel" if vllm else "write_kv_kernel",
         },
     }
@@ -749,7 +763,8 @@ def main():
                     help="no GPU run: summarise a rocprofv3 kernel trace of a --graph-compare run")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU run: turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, WRITE_SIZE) of a "
-                         "--copy-calibration run into profiles/traffic_<kernel>_<workload>.json")
+                         "--copy-calibration run into profiles/traffic_<kernel>_<workload>.json "
+                         "(..._<workload>_vllm.json with --layout vllm)")
     args = ap.parse_args()
 
     if args.traffic_from:
@@ -761,7 +776,8 @@ def main():
         else:
             name, key = CONFIGS[args.config].name, CONFIGS[args.config].dtype
         r = traffic_from_counters(*args.traffic_from, name, key,
-                                  (args.copy_calibration or 256) << 20, _traffic_file(key, name))
+                                  (args.copy_calibration or 256) << 20, _traffic_file(key, name, args.layout),
+                                  args.layout)
         print(json.dumps(r))
         return
 
@@ -999,7 +1015,7 @@ def main():
     dec_us = k2_us + k3_us
     value = kv_bytes / (step_us * 1e-6) / 1e9
     achieved = kv_unique / (k2_us * 1e-6) / 1e9
-    traffic = _traffic(cfg.name, cfg.dtype) if args.layout == "p09" else None
+    traffic = _traffic(cfg.name, cfg.dtype, args.layout)
 
     res = {
         "metric": METRIC,
@@ -1055,7 +1071,7 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
-            "kernel": PARTIAL_KERNELS[cfg.dtype],
+            "kernel": _kernel_name(cfg.dtype, args.layout),
         },
     }
     if not args.no_cpu_baseline:

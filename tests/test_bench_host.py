@@ -76,3 +76,27 @@ def test_traffic_of_the_write_kernel(tmp_path):
     assert r["bytes_per_launch"] == 800 * 1024
     assert r["source_sha256_16"] == bench._src_hash("write") != bench._src_hash("bf16")
     assert bench._traffic_file("write", "w").endswith("traffic_write_kv_kernel_w.json")
+
+
+def test_traffic_in_vllm_layout(tmp_path, monkeypatch):
+    """In vLLM's cache layout the write's counters come from the vLLM-layout
+    kernel and go to a summary of their own, which a P09-layout line never
+    reads (and the other way round)."""
+    calib = 256 << 20
+    copy = "void at::native::vectorized_elementwise_kernel<4, AUnaryFunctor<float, float, float, MulFunctor<float>>>"
+    kern = "pa::write_kv_kernel(unsigned int __vector(4)*, unsigned int __vector(4)*, long const*)"
+    vllm = "void pa::write_kv_vllm_kernel<unsigned short>(unsigned int __vector(4)*, unsigned short*)"
+    _csv(tmp_path / "f.csv", "FETCH_SIZE", [(copy, calib / 2048), (kern, 9e6), (vllm, 300.0)])
+    _csv(tmp_path / "w.csv", "WRITE_SIZE", [(copy, calib / 1024), (kern, 9e6), (vllm, 200.0)])
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    out = bench._traffic_file("write", "w", "vllm")
+    assert out.endswith("traffic_write_kv_vllm_kernel_w_vllm.json")
+    r = bench.traffic_from_counters(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), "w", "write", calib, out,
+                                    "vllm")
+    assert r["kernel"] == "write_kv_vllm_kernel" and r["layout"] == "vllm"
+    assert r["bytes_per_launch"] == 800 * 1024
+    assert bench._traffic("w", "write", "vllm") == 800 * 1024
+    assert bench._traffic("w", "write") is None
+    # the bf16 decode runs one template in both layouts: the layouts still keep separate files
+    assert bench._traffic_file("bf16", "c", "vllm").endswith("traffic_decode_partial_mfma_kernel_c_vllm.json")
+    assert bench._src_hash("f32", "vllm") == bench._src_hash("bf16") != bench._src_hash("f32")
