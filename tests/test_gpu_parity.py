@@ -474,3 +474,33 @@ def test_graph_replay_of_prefill_and_shared_prefix_decode():
         torch.cuda.synchronize()
         assert torch.equal(pout.view(torch.int16), pe.view(torch.int16)), f"prefill replay {rep}"
         assert torch.equal(dout.view(torch.int16), de.view(torch.int16)), f"decode replay {rep}"
+
+
+@pytest.mark.parametrize("B", [15, 16, 17, 33, 48, 63, 64, 65, 127, 129])
+def test_unit_list_across_lane_rows_and_chunks(B):
+    """The persistent kernel's unit list takes prefix sums of each sequence's
+    full partitions over 64-lane chunks of the batch, 16 lanes to a row.
+    Batch sizes on both sides of the row and chunk edges, with one-block
+    partitions so that the counts run into the hundreds (and some sequences
+    have none: n <= P, or n = 0), must give the oracle's result for every
+    sequence, with the partials + merge halves bit-equal to the one call."""
+    rng = np.random.default_rng(1000 + B)
+    lens = [int(x) for x in rng.integers(1, 700, B)]
+    lens[B // 2] = 0
+    lens[-1] = 16
+    w = make_custom(num_seqs=B, num_heads=8, num_kv_heads=2, head_dim=128, block_size=16, dtype="bf16",
+                    lens=lens, seed=B, device="cuda")
+    ref = O.decode(stored_np(w.q), stored_np(w.k_cache), stored_np(w.v_cache), stored_np(w.block_tables),
+                   stored_np(w.context_lens), w.scale, "bf16")
+    W = w.block_tables.shape[1]
+    for P in (16, 48):
+        out = pk.decode(w.q, w.k_cache, w.v_cache, w.block_tables, w.context_lens, w.scale, partition_size=P)
+        ws = pk.new_workspace(B, 8, W, w.k_cache, P)
+        two = torch.empty_like(w.q)
+        pk.decode_partials(w.q, w.k_cache, w.v_cache, w.block_tables, w.context_lens, w.scale, out=two,
+                           workspace=ws, partition_size=P)
+        pk.decode_merge(w.q, w.k_cache, w.block_tables, w.context_lens, out=two, workspace=ws, partition_size=P)
+        torch.cuda.synchronize()
+        err = assert_matches_oracle(out, ref, "bf16", f"B={B} P={P}")
+        assert torch.equal(two.view(torch.int16), out.view(torch.int16)), f"B={B} P={P}: two calls differ"
+        _say(f"unit list B={B} P={P}: max err {err:.2e}")
